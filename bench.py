@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of the ternary MoE FFN hot path on one MI355X.
+
+Default workload (stack24_b1): batch-1 decode through 24 stacked ternary MoE FFN layers
+(d_model 2048, 256 experts, expert width 512, top-8, pre-RMSNorm, residual between layers,
+attention replaced by identity), steps chained (step t+1 decodes step t's output), captured as a
+hipGraph of 256 consecutive steps and replayed.  A step is one token through all 24 layers.
+
+Prints ONE JSON line: tokens/s of the whole job, the roofline view of the step (algorithmic HBM
+bytes per step / measured time per step against the 8 TB/s HBM peak) and the CPU oracle's rate on a
+bounded sample of the same workload.
+
+Other workloads (--workload): layer_b1 (one layer, batch 1), batched_b64 / batched_b64_int8 (one
+layer, 64 tokens grouped by expert); single-layer workloads rotate 8 independently seeded layer
+copies so that the 256 MB last-level cache never holds the layer being timed.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+import synth  # noqa: E402
+import ternary_weight_moe_amd as tw  # noqa: E402
+from ternary_weight_moe_amd import accounting  # noqa: E402
+
+METRIC = "decode tok/s, 24-layer ternary MoE FFN stack, B=1; achieved HBM GB/s vs peak"
+KERNEL_SRC = os.path.join(ROOT, "ternary_weight_moe_amd", "csrc", "tw_kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per step from committed rocprofv3 counter runs, if they were taken on the current
+    kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return d.get("hbm_bytes_per_step")
+
+
+def build_layer(wl, l, device="cuda", keep_cpu=False, pre=None):
+    w = synth.layer_weights(wl, l, device=device)
+    layer = tw.MoELayer.from_ternary(w["w_router"], w["t_gate"], w["t_up"], w["t_down"],
+                                     w["s_gate"], w["s_up"], w["s_down"], top_k=wl.top_k,
+                                     pre_rmsnorm=wl.pre_rmsnorm if pre is None else pre)
+    cpu = {k: v.cpu() for k, v in w.items()} if keep_cpu else None
+    del w
+    return layer, cpu
+
+
+def time_graph(step_fn, n_graph, warmup, steps):
+    """Captures n_graph consecutive steps in one graph; replays warmup/n_graph times untimed and
+    steps/n_graph times timed.  Returns (total seconds, per-replay seconds list)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for t in range(2):
+            step_fn(t)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t in range(n_graph):
+            step_fn(t)
+    torch.cuda.synchronize()
+    for _ in range(max(1, warmup // n_graph)):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = steps // n_graph
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for r in range(reps):
+        g.replay()
+        ev[r + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[r].elapsed_time(ev[r + 1]) / 1e3 for r in range(reps)]
+    return ev[0].elapsed_time(ev[reps]) / 1e3, per
+
+
+def cpu_baseline_stack(cpu_layers, wl, n_tokens):
+    import oracle
+    ors = [oracle.Layer(c["w_router"], c["t_gate"], c["t_up"], c["t_down"], c["s_gate"],
+                        c["s_up"], c["s_down"], pre_rmsnorm=wl.pre_rmsnorm, top_k=wl.top_k)
+           for c in cpu_layers]
+    x = synth.activations(wl, n_tokens, seed=4242)
+    t0 = time.perf_counter()
+    for t in range(n_tokens):
+        oracle.decode_stack(ors, x[t].double().numpy(), 1)
+    dt = time.perf_counter() - t0
+    per_token_full = dt / n_tokens * wl.n_layers / len(ors)
+    return dict(value=1.0 / per_token_full, unit="tok/s", cores=1, kind="oracle",
+                sample="%d tokens through %d of the %d layers (fp64 truth mode, one thread), "
+                       "%.1f s; rate scaled to %d layers" % (n_tokens, len(ors), wl.n_layers, dt,
+                                                             wl.n_layers))
+
+
+def run_stack(args):
+    wl = synth.STACK24_B1
+    n_cpu_layers = 0 if args.no_cpu_baseline else 3
+    layers, cpu_layers = [], []
+    for l in range(wl.n_layers):
+        layer, cpu = build_layer(wl, l, keep_cpu=l < n_cpu_layers)
+        layers.append(layer)
+        if cpu is not None:
+            cpu_layers.append(cpu)
+    torch.cuda.synchronize()
+    assert all(int(l.bad_count.item()) == 0 for l in layers)
+    x0 = synth.activations(wl, 1, device="cuda")[0]
+    bufs = [x0.clone(), torch.empty_like(x0)]
+    ws = torch.empty(tw.decode_workspace_bytes(layers), dtype=torch.uint8, device="cuda")
+
+    def step(t):
+        tw.ternary_moe_ffn_decode(layers, bufs[t % 2], out=bufs[(t + 1) % 2], workspace=ws)
+
+    G = args.graph_steps
+    total, per = time_graph(step, G, args.warmup, args.steps)
+    ms_per_step = total / args.steps * 1e3
+    bytes_per_step = accounting.stack_bytes_per_token(wl)
+    tok_s = args.steps / total
+    achieved = bytes_per_step / (total / args.steps) / 1e9
+    per_tok_us = sorted(p / G * 1e6 for p in per)
+    log("stack24_b1: %.2f us/token median over %d replays of %d steps (min %.2f, p90 %.2f)" % (
+        per_tok_us[len(per_tok_us) // 2], len(per), G, per_tok_us[0],
+        per_tok_us[int(0.9 * (len(per_tok_us) - 1))]))
+    cpu = cpu_baseline_stack(cpu_layers, wl, args.cpu_tokens) if cpu_layers else None
+    traffic = traffic_from_profiles("stack24_b1")
+    return dict(
+        metric=METRIC, value=tok_s, unit="tok/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=ms_per_step, higher_is_better=True, scaling="weak",
+        vs_baseline=None, dtype="int8xint8->int32, fp32 (bf16 I/O)", data="synthetic",
+        config=dict(workload="stack24_b1", layers=wl.n_layers, d_model=wl.d_model,
+                    n_experts=wl.n_experts, d_ff=wl.d_ff, top_k=wl.top_k, batch=1,
+                    graph_steps=G, bytes_per_token=bytes_per_step,
+                    us_per_token_median=per_tok_us[len(per_tok_us) // 2],
+                    us_per_token_min=per_tok_us[0]),
+        roofline=dict(bound="hbm", achieved=achieved, peak=accounting.HBM_PEAK_BPS / 1e9,
+                      unit="GB/s", frac=achieved * 1e9 / accounting.HBM_PEAK_BPS,
+                      traffic=traffic, kernel="decode step (24 layers)"),
+        cpu_baseline=cpu,
+    )
+
+
+def run_single_layer(args, name):
+    wl = synth.WORKLOADS[name]
+    n_copies = 8
+    T = wl.batch
+    act = wl.act
+    layers = []
+    for c in range(n_copies):
+        layer, _ = build_layer(wl, c)
+        layers.append(layer)
+    xs = [synth.activations(wl, T, device="cuda", stream=c) for c in range(n_copies)]
+    outs = [torch.empty((T, wl.d_model), dtype=torch.bfloat16 if wl.out_dtype == "bf16"
+                        else torch.float32, device="cuda") for _ in range(n_copies)]
+    # distinct experts per copy, from the routing the call itself will compute
+    distinct = []
+    for c in range(n_copies):
+        _, ids, _ = tw.moe_route_topk(xs[c], layers[c].w_router, wl.top_k)
+        distinct.append(int(torch.unique(ids).numel()))
+    if T == 1:
+        ws = torch.empty(tw.decode_workspace_bytes([layers[0]]), dtype=torch.uint8, device="cuda")
+
+        def step(t):
+            c = t % n_copies
+            tw.ternary_moe_ffn_decode([layers[c]], xs[c][0], out=outs[c][0], workspace=ws)
+    else:
+        ws = torch.empty(tw.batched_workspace_bytes(layers[0], T, act), dtype=torch.uint8,
+                         device="cuda")
+
+        def step(t):
+            c = t % n_copies
+            tw.ternary_moe_ffn_batched(layers[c], xs[c], act=act, out=outs[c], workspace=ws)
+
+    G = args.graph_steps
+    total, per = time_graph(step, G, args.warmup, args.steps)
+    bytes_per_step = sum(accounting.layer_bytes(wl, T, distinct[t % n_copies])
+                         for t in range(G)) / G
+    achieved = bytes_per_step / (total / args.steps) / 1e9
+    return dict(
+        metric="%s tokens/s (one layer, %d tokens per call)" % (name, T), value=T * args.steps / total,
+        unit="tok/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=total / args.steps * 1e3, higher_is_better=True, scaling="weak",
+        vs_baseline=None, dtype="int8xint8->int32, fp32", data="synthetic",
+        config=dict(workload=name, batch=T, act=act, layer_copies=n_copies,
+                    distinct_experts=distinct, bytes_per_step=bytes_per_step),
+        roofline=dict(bound="hbm", achieved=achieved, peak=accounting.HBM_PEAK_BPS / 1e9,
+                      unit="GB/s", frac=achieved * 1e9 / accounting.HBM_PEAK_BPS,
+                      traffic=traffic_from_profiles(name), kernel="one call"),
+        cpu_baseline=None,
+    )
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2560)
+    ap.add_argument("--warmup", type=int, default=512)
+    ap.add_argument("--graph-steps", type=int, default=256)
+    ap.add_argument("--workload", default="stack24_b1",
+                    choices=["stack24_b1", "layer_b1", "batched_b64", "batched_b64_int8"])
+    ap.add_argument("--cpu-tokens", type=int, default=12)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.steps % args.graph_steps:
+        args.steps = max(1, round(args.steps / args.graph_steps)) * args.graph_steps
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    tw.lib()
+    if args.workload == "stack24_b1":
+        res = run_stack(args)
+    else:
+        res = run_single_layer(args, args.workload)
+    res["device"] = torch.cuda.get_device_properties(0).gcnArchName
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,173 @@
+/*
+ * ternary_moe.h -- C ABI of libternary_moe.so: the decode-time ternary mixture-of-experts FFN on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (titles as printed):
+ *   [MacMini]   "A 20B AI Model Trained in Ternary Just Hit 218 Tokens/Second on a $599 Mac Mini"
+ *   [iPhone20B] "How a 20B Model Hits 120 tok/s on an iPhone"
+ *   [Hub]       "iPhone Runs a 20B Model at 120 tok/s"
+ *
+ * What one layer computes, per token x (d_model values):
+ *   router logits  l = W_r xn            W_r [E][d], no bias; xn = x, or x / sqrt(mean(x^2)+1e-6)
+ *                                         when the layer has a pre-RMSNorm (unit weight)
+ *   routing        ids = the top_k experts by (l descending, expert id ascending);
+ *                  g_j = softmax over the top_k selected logits  (router choosing a few experts
+ *                  per token: [Hub] "MoE Is the Other Half of the Story Behind the 20B Figure";
+ *                  8 of 256: [MacMini] "The Architecture: Designed for the Hardware")
+ *   per expert e = ids_j:
+ *                  gate = s_g[e] * (T_g[e] xn),  up = s_u[e] * (T_u[e] xn)   (ternary GEMV)
+ *                  h    = SiLU(gate) * up,        SiLU(z) = z / (1 + e^-z)
+ *                  y_j  = s_d[e] * (T_d[e] h)                                  (ternary GEMV)
+ *   output         out = x + sum_j g_j y_j  (j in selection order)
+ * Every weight is -1, 0 or +1, so each product is a pass-through, a negation or a skip, and sums
+ * accumulate without any dequantised weight matrix in memory ([MacMini] "What Ternary Actually
+ * Means" and "The Architecture: Designed for the Hardware").  The pages leave the expert's form,
+ * the gating function and the scale granularity open; the reading above (SiLU-gated expert, softmax
+ * over the selected logits, one fp32 scale per output row) is the one this library implements.
+ *
+ * Packed ternary layout (four weights per byte, [MacMini] "What Ternary Actually Means"):
+ *   code 00 = 0, 01 = +1, 10 = -1 (11 never written; read as 0); weight 4b+j of a row in bits
+ *   2j..2j+1 of byte b; a row is one output channel with its inputs contiguous; row stride
+ *   ceil(cols/4) bytes; expert-major: T_g, T_u [E][F][d/4], T_d [E][d][F/4].
+ *
+ * Conventions for every entry point:
+ *   - Every pointer argument except `layers`/`layer` themselves is a DEVICE pointer (memory from
+ *     hipMalloc or torch CUDA tensors).  The tw_moe_layer structs live in HOST memory; they are read
+ *     during the call only, and their values are copied into kernel arguments.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream).  They never
+ *     synchronize, allocate, free or read device memory on the host, so they can be captured into
+ *     a hipGraph.  The caller owns every buffer; the library keeps no pointer after the call returns
+ *     (kernels already queued still use them).
+ *   - Arguments are checked on the host before any HIP call; a failed check returns an error code
+ *     and launches nothing.  Launch failures return TW_E_HIP.  Nothing throws across the ABI.
+ *   - A workspace belongs to one in-flight call at a time; two calls in flight on different
+ *     streams must use different workspaces.  Its contents need no initialisation.
+ *   - Supported shapes: d_model and d_ff powers of two in [64, 4096]; 1 <= top_k <= min(E, 32);
+ *     n_experts in [1, 1024].  Others return TW_E_UNSUPPORTED.
+ */
+#ifndef TERNARY_MOE_H
+#define TERNARY_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TW_OK = 0,
+    TW_E_NULL = -1,         /* a required pointer is NULL */
+    TW_E_SHAPE = -2,        /* negative or inconsistent sizes */
+    TW_E_DTYPE = -3,        /* unknown dtype / activation mode */
+    TW_E_WORKSPACE = -4,    /* workspace smaller than the *_workspace_bytes query */
+    TW_E_ALIAS = -5,        /* output overlaps an input it must not overlap */
+    TW_E_UNSUPPORTED = -6,  /* valid but outside what the kernels implement */
+    TW_E_HIP = -7           /* a HIP launch reported an error */
+} tw_status;
+
+typedef enum { TW_F32 = 0, TW_BF16 = 1 } tw_float;      /* element types of float tensors */
+typedef enum { TW_ACT_FLOAT = 0, TW_ACT_INT8 = 1 } tw_act;
+
+/* One layer's parameters.  All pointers are device pointers. */
+typedef struct {
+    int32_t d_model;        /* d */
+    int32_t d_ff;           /* F, width of one expert */
+    int32_t n_experts;      /* E */
+    int32_t top_k;          /* k */
+    int32_t router_dtype;   /* tw_float of w_router */
+    int32_t pre_rmsnorm;    /* 1: the FFN input is x / sqrt(mean(x^2) + 1e-6); residual un-normed */
+    const void *w_router;   /* [E][d] router_dtype, row-major */
+    const uint8_t *w_gate;  /* [E][F][d/4] packed codes */
+    const uint8_t *w_up;    /* [E][F][d/4] packed codes */
+    const uint8_t *w_down;  /* [E][d][F/4] packed codes */
+    const float *s_gate;    /* [E][F] per-row scales */
+    const float *s_up;      /* [E][F] */
+    const float *s_down;    /* [E][d] */
+} tw_moe_layer;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *tw_status_str(tw_status status);
+
+/*
+ * ternary_pack -- pack int8 weights with values in {-1, 0, +1} into the 2-bit layout above.
+ *   w         [rows][cols] int8, device, row-major.
+ *   packed    [rows][ceil(cols/4)] uint8, device, written in full (padding weights get code 00).
+ *   bad_count nullable device int32: incremented (atomically) by the number of inputs outside
+ *             {-1,0,1}; each such input is packed as 0.  Not cleared by the call.
+ *   Errors: TW_E_NULL (w or packed NULL with rows*cols > 0), TW_E_SHAPE (rows or cols < 0),
+ *   TW_E_ALIAS (packed overlaps w).  rows == 0 or cols == 0 is a no-op.
+ *   Source: four weights per byte, [MacMini] "What Ternary Actually Means".
+ */
+tw_status ternary_pack(const int8_t *w, int64_t rows, int64_t cols, uint8_t *packed,
+                       int32_t *bad_count, void *stream);
+
+/*
+ * moe_route_topk -- router logits, top-k selection and softmax gates for n_tokens tokens.
+ *   x          [T][d] in x_dtype (TW_F32 or TW_BF16).
+ *   w_router   [E][d] in w_dtype.
+ *   pre_rmsnorm  1: logits of x / sqrt(mean(x^2) + 1e-6).
+ *   logits     [T][E] fp32 output (the logits the selection used).
+ *   expert_ids [T][k] int32 output, in selection order (descending logit, ties to the lower id).
+ *   gate_w     [T][k] fp32 output, softmax over the k selected logits (sums to 1).
+ *   Sums accumulate in fp32.  Errors: TW_E_NULL, TW_E_SHAPE (T < 0, k > E, k < 1), TW_E_DTYPE,
+ *   TW_E_UNSUPPORTED (shape limits above), TW_E_ALIAS (an output overlapping another output).
+ *   Source: routing of a token to a few experts, [Hub] "MoE Is the Other Half of the Story Behind
+ *   the 20B Figure"; 8 of 256 experts per token, [MacMini] "The Architecture: Designed for the
+ *   Hardware".
+ */
+tw_status moe_route_topk(const void *x, int32_t x_dtype, const void *w_router, int32_t w_dtype,
+                         int64_t n_tokens, int32_t d_model, int32_t n_experts, int32_t top_k,
+                         int32_t pre_rmsnorm, float *logits, int32_t *expert_ids, float *gate_w,
+                         void *stream);
+
+/*
+ * ternary_moe_ffn_decode -- batch-1 decode through n_layers consecutive layers (the layer above,
+ * applied n_layers times; layer i's output is layer i+1's input).
+ *   layers     host array of n_layers descriptors (1 <= n_layers <= 64), equal shapes and dtypes.
+ *   x_in       [d] in io_dtype; x_out [d] in io_dtype, must not overlap x_in.
+ *   io_dtype   TW_F32 or TW_BF16; between layers the residual is rounded to io_dtype, exactly as if
+ *              the layers were called one at a time.
+ *   workspace  device memory of at least ternary_moe_decode_workspace_bytes(layers, n_layers).
+ *   Float arithmetic: ternary sums are exact integer sums of the activations split into int8
+ *   digits under a power-of-two scale (2 digits for bf16 I/O, 3 for fp32 I/O), then scaled in
+ *   fp32; everything else is fp32.  Errors: as moe_route_topk, plus TW_E_WORKSPACE, TW_E_ALIAS.
+ *   Source: one decode step is a sequence of matrix-vector products that stream the active
+ *   weights, [MacMini] "What Ternary Actually Means"; 24 layers, [iPhone20B] opening section.
+ */
+tw_status ternary_moe_ffn_decode(const tw_moe_layer *layers, int32_t n_layers, const void *x_in,
+                                 void *x_out, int32_t io_dtype, void *workspace, size_t ws_bytes,
+                                 void *stream);
+size_t ternary_moe_decode_workspace_bytes(const tw_moe_layer *layers, int32_t n_layers);
+
+/*
+ * ternary_moe_ffn_batched -- one layer for n_tokens independent tokens, each expert's weights read
+ * once per call: (token, slot) pairs are grouped by expert and each expert's rows are applied to
+ * all of its tokens.
+ *   x_in       [T][d] in in_dtype; x_out [T][d] in out_dtype (must not overlap x_in).
+ *   act        TW_ACT_FLOAT: as the decode call.  TW_ACT_INT8: per-token absmax quantisation of x
+ *              to int8 in [-127,127] (scale amax/127), int32 sums, h re-quantised the same way per
+ *              (token, expert), then the fixed fp32 sequence gate = (acc*s_x)*s_g, h =
+ *              (gate/(1+exp(-gate)))*up, y = (acc*s_h)*s_d, out = ((x + g_0 y_0) + g_1 y_1) + ...,
+ *              with one rounding per operation and a fixed exp: the result is bit-exact and does
+ *              not depend on grouping or launch shape.  int8 with pre_rmsnorm is unsupported.
+ *   expert_ids, gate_w  nullable [T][k]: when given, this routing is used as is (both or
+ *              neither; a slot whose id is outside [0, E) contributes nothing); when NULL the call
+ *              routes itself as moe_route_topk does.
+ *   workspace  at least ternary_moe_batched_workspace_bytes(layer, n_tokens, act).
+ *   n_tokens == 0 is a no-op.  Errors: as above.
+ *   Source: expert layout and scheduling co-designed against scattered reads, [Hub] "MoE Is the
+ *   Other Half of the Story Behind the 20B Figure"; prefill versus decode, [Hub] "What Makes
+ *   120 tok/s So Fast?".
+ */
+tw_status ternary_moe_ffn_batched(const tw_moe_layer *layer, int64_t n_tokens, const void *x_in,
+                                  int32_t in_dtype, void *x_out, int32_t out_dtype, int32_t act,
+                                  const int32_t *expert_ids, const float *gate_w, void *workspace,
+                                  size_t ws_bytes, void *stream);
+size_t ternary_moe_batched_workspace_bytes(const tw_moe_layer *layer, int64_t n_tokens,
+                                           int32_t act);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

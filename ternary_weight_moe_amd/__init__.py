@@ -1,0 +1,209 @@
+"""Python binding of libternary_moe.so: the decode-time ternary MoE FFN on MI355X (gfx950).
+
+Thin argument marshalling over the C ABI declared in include/ternary_moe.h: every step of the
+computation runs in the library's HIP kernels.  PyTorch provides device memory and the current
+stream only.  If the library is not built, every call raises (there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libternary_moe.so")
+
+TW_F32, TW_BF16 = 0, 1
+ACT_FLOAT, ACT_INT8 = 0, 1
+_DT = {torch.float32: TW_F32, torch.bfloat16: TW_BF16}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class TwError(RuntimeError):
+    """A non-zero tw_status returned by the library."""
+
+    def __init__(self, what: str, status: int, text: str):
+        super().__init__("%s: %s (status %d)" % (what, text, status))
+        self.status = status
+
+
+class TwLayer(C.Structure):
+    """Mirror of tw_moe_layer (include/ternary_moe.h)."""
+    _fields_ = [("d_model", C.c_int32), ("d_ff", C.c_int32), ("n_experts", C.c_int32),
+                ("top_k", C.c_int32), ("router_dtype", C.c_int32), ("pre_rmsnorm", C.c_int32),
+                ("w_router", C.c_void_p), ("w_gate", C.c_void_p), ("w_up", C.c_void_p),
+                ("w_down", C.c_void_p), ("s_gate", C.c_void_p), ("s_up", C.c_void_p),
+                ("s_down", C.c_void_p)]
+
+
+EXPORTS = ("tw_status_str", "ternary_pack", "moe_route_topk", "ternary_moe_ffn_decode",
+           "ternary_moe_decode_workspace_bytes", "ternary_moe_ffn_batched",
+           "ternary_moe_batched_workspace_bytes")
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError("libternary_moe.so is not built (python -m "
+                                   "ternary_weight_moe_amd.build); there is no fallback path")
+            L = C.CDLL(LIB_PATH)
+            i32, i64, vp, sz = C.c_int32, C.c_int64, C.c_void_p, C.c_size_t
+            LP = C.POINTER(TwLayer)
+            sig = {
+                "tw_status_str": (C.c_char_p, [i32]),
+                "ternary_pack": (i32, [vp, i64, i64, vp, vp, vp]),
+                "moe_route_topk": (i32, [vp, i32, vp, i32, i64, i32, i32, i32, i32, vp, vp, vp,
+                                         vp]),
+                "ternary_moe_ffn_decode": (i32, [LP, i32, vp, vp, i32, vp, sz, vp]),
+                "ternary_moe_decode_workspace_bytes": (sz, [LP, i32]),
+                "ternary_moe_ffn_batched": (i32, [LP, i64, vp, i32, vp, i32, i32, vp, vp, vp, sz,
+                                                  vp]),
+                "ternary_moe_batched_workspace_bytes": (sz, [LP, i64, i32]),
+            }
+            for name, (res, args) in sig.items():
+                f = getattr(L, name)
+                f.restype = res
+                f.argtypes = args
+            _lib = L
+        return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise TwError(what, status, lib().tw_status_str(status).decode())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("expected contiguous CUDA tensors")
+
+
+# ---- ternary_pack --------------------------------------------------------------------------------
+
+def ternary_pack(w: torch.Tensor, bad_count: torch.Tensor | None = None, out=None,
+                 stream=None) -> torch.Tensor:
+    """int8 [..., cols] with values in {-1,0,1} -> packed uint8 [..., ceil(cols/4)]."""
+    _need_cuda(w, bad_count, out)
+    if w.dtype != torch.int8:
+        raise ValueError("ternary_pack expects int8")
+    cols = w.shape[-1]
+    rows = w.numel() // cols if cols else 0
+    if out is None:
+        out = torch.empty(w.shape[:-1] + ((cols + 3) // 4,), dtype=torch.uint8, device=w.device)
+    _check(lib().ternary_pack(_ptr(w), rows, cols, _ptr(out), _ptr(bad_count), _stream(stream)),
+           "ternary_pack")
+    return out
+
+
+# ---- routing -------------------------------------------------------------------------------------
+
+def moe_route_topk(x: torch.Tensor, w_router: torch.Tensor, top_k: int, pre_rmsnorm: bool = False,
+                   stream=None):
+    """Router logits [T][E] fp32, expert ids [T][k] int32 and gates [T][k] fp32."""
+    _need_cuda(x, w_router)
+    x2 = x.reshape(-1, x.shape[-1])
+    T, d = x2.shape
+    E = w_router.shape[0]
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=x.device)
+    gates = torch.empty((T, top_k), dtype=torch.float32, device=x.device)
+    _check(lib().moe_route_topk(_ptr(x2), _DT[x.dtype], _ptr(w_router), _DT[w_router.dtype], T,
+                                d, E, top_k, int(pre_rmsnorm), _ptr(logits), _ptr(ids),
+                                _ptr(gates), _stream(stream)), "moe_route_topk")
+    return logits, ids, gates
+
+
+# ---- layers --------------------------------------------------------------------------------------
+
+class MoELayer:
+    """One layer's device tensors (packed ternary weights, fp32 scales, router) and its
+    tw_moe_layer descriptor."""
+
+    def __init__(self, w_router, p_gate, p_up, p_down, s_gate, s_up, s_down, top_k: int,
+                 pre_rmsnorm: bool = False):
+        _need_cuda(w_router, p_gate, p_up, p_down, s_gate, s_up, s_down)
+        self.w_router, self.p_gate, self.p_up, self.p_down = w_router, p_gate, p_up, p_down
+        self.s_gate, self.s_up, self.s_down = s_gate, s_up, s_down
+        E, d = w_router.shape
+        F = p_gate.shape[1]
+        self.d, self.F, self.E, self.k = d, F, E, int(top_k)
+        self.pre_rmsnorm = bool(pre_rmsnorm)
+        self.c = TwLayer(d, F, E, self.k, _DT[w_router.dtype], int(pre_rmsnorm),
+                         w_router.data_ptr(), p_gate.data_ptr(), p_up.data_ptr(),
+                         p_down.data_ptr(), s_gate.data_ptr(), s_up.data_ptr(), s_down.data_ptr())
+
+    @classmethod
+    def from_ternary(cls, w_router, t_gate, t_up, t_down, s_gate, s_up, s_down, top_k: int,
+                     pre_rmsnorm: bool = False, stream=None):
+        """Packs int8 ternary weights with ternary_pack (on the device) and keeps the result."""
+        dev = w_router.device
+        bad = torch.zeros(1, dtype=torch.int32, device=dev)
+        p = [ternary_pack(t.to(dev).contiguous(), bad, stream=stream) for t in (t_gate, t_up, t_down)]
+        layer = cls(w_router.to(dev).contiguous(), p[0], p[1], p[2], s_gate.to(dev).contiguous(),
+                    s_up.to(dev).contiguous(), s_down.to(dev).contiguous(), top_k, pre_rmsnorm)
+        layer.bad_count = bad
+        return layer
+
+
+def decode_workspace_bytes(layers) -> int:
+    arr = (TwLayer * len(layers))(*[l.c for l in layers])
+    return int(lib().ternary_moe_decode_workspace_bytes(arr, len(layers)))
+
+
+def batched_workspace_bytes(layer: MoELayer, n_tokens: int, act: str = "float") -> int:
+    return int(lib().ternary_moe_batched_workspace_bytes(C.byref(layer.c), n_tokens,
+                                                         ACT_INT8 if act == "int8" else ACT_FLOAT))
+
+
+def ternary_moe_ffn_decode(layers, x: torch.Tensor, out: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Batch-1 decode of x [d] (fp32 or bf16) through the given layers; returns out [d]."""
+    layers = list(layers)
+    _need_cuda(x, out, workspace)
+    arr = (TwLayer * len(layers))(*[l.c for l in layers])
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = torch.empty(decode_workspace_bytes(layers), dtype=torch.uint8, device=x.device)
+    _check(lib().ternary_moe_ffn_decode(arr, len(layers), _ptr(x), _ptr(out), _DT[x.dtype],
+                                        _ptr(workspace), workspace.numel(), _stream(stream)),
+           "ternary_moe_ffn_decode")
+    return out
+
+
+def ternary_moe_ffn_batched(layer: MoELayer, x: torch.Tensor, act: str = "float",
+                            out_dtype: torch.dtype | None = None, expert_ids=None, gate_w=None,
+                            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                            stream=None) -> torch.Tensor:
+    """One layer for T tokens x [T][d]; act "float" or "int8"; optional routing passed in."""
+    _need_cuda(x, expert_ids, gate_w, out, workspace)
+    T = x.shape[0]
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((T, x.shape[1]), dtype=out_dtype, device=x.device)
+    a = ACT_INT8 if act == "int8" else ACT_FLOAT
+    if workspace is None:
+        workspace = torch.empty(max(1, batched_workspace_bytes(layer, T, act)), dtype=torch.uint8,
+                                device=x.device)
+    _check(lib().ternary_moe_ffn_batched(C.byref(layer.c), T, _ptr(x), _DT[x.dtype], _ptr(out),
+                                         _DT[out.dtype], a, _ptr(expert_ids), _ptr(gate_w),
+                                         _ptr(workspace), workspace.numel(), _stream(stream)),
+           "ternary_moe_ffn_batched")
+    return out

@@ -1,0 +1,54 @@
+"""Builds libternary_moe.so in-tree for gfx950 (hipcc).  ``python -m ternary_weight_moe_amd.build``.
+
+The host-side argument checks (tw_host.cpp) are compiled by the host compiler as plain C++; the
+kernels (tw_kernels.hip) by hipcc for gfx950 only.  Flags that matter for the numerics:
+-ffp-contract=off (no fused multiply-add: every fp32 step of the int8 path is one rounding) and
+correctly rounded fp32 division and square root.  Packed-fp32 instructions are disabled.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+LIB = os.path.join(HERE, "libternary_moe.so")
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
+    "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-rdc",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", "-I" + INCLUDE,
+]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("build step failed: " + " ".join(cmd))
+    return r
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    bdir = os.path.join(HERE, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    host_o = os.path.join(bdir, "tw_host.o")
+    kern_o = os.path.join(bdir, "tw_kernels.o")
+    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-c",
+          os.path.join(CSRC, "tw_host.cpp"), "-o", host_o])
+    _run([hipcc] + HIP_FLAGS + ["-c", os.path.join(CSRC, "tw_kernels.hip"), "-o", kern_o])
+    tmp = LIB + ".tmp%d" % os.getpid()
+    _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", host_o, kern_o, "-o", tmp])
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

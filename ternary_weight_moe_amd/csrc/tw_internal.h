@@ -1,0 +1,85 @@
+// tw_internal.h -- internal interface between the host-side argument checks (tw_host.cpp, no HIP
+// headers) and the HIP kernels and launchers (tw_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tw {
+
+// A layer as the kernels see it (device pointers only).
+struct LayerPtrs {
+    const void *w_router;
+    const uint8_t *w_gate, *w_up, *w_down;
+    const float *s_gate, *s_up, *s_down;
+};
+
+struct Dims {
+    int32_t d, F, E, k;
+    int32_t router_bf16;   // 1: router weights are bf16, 0: fp32
+    int32_t pre_norm;      // 1: pre-RMSNorm on the FFN input
+};
+
+constexpr int kMaxLayers = 64;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxExperts = 1024;
+
+// Number of int8 digit planes the float path splits an activation vector into.
+inline int float_planes(int io_bf16) { return io_bf16 ? 2 : 3; }
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// ---- decode (batch 1) workspace -------------------------------------------------------------
+struct DecodeWs {
+    size_t ctrl, logits, ids, gates, xinfo, xdig, h, xbuf, total;
+};
+inline DecodeWs decode_ws_layout(const Dims &dm) {
+    DecodeWs w{};
+    size_t o = 0;
+    w.ctrl = o;   o += align256(256);
+    w.logits = o; o += align256(sizeof(float) * dm.E);
+    w.ids = o;    o += align256(sizeof(int32_t) * kMaxTopK);
+    w.gates = o;  o += align256(sizeof(float) * kMaxTopK);
+    w.xinfo = o;  o += align256(64);
+    w.xdig = o;   o += align256(size_t(3) * dm.d);
+    w.h = o;      o += align256(sizeof(float) * size_t(dm.k) * dm.F);
+    w.xbuf = o;   o += align256(sizeof(float) * 2 * size_t(dm.d));
+    w.total = o;
+    return w;
+}
+
+// ---- batched workspace ------------------------------------------------------------------------
+struct BatchedWs {
+    size_t ctrl, logits, ids, gates, tinfo, xdig, counts, offsets, pairs, h, y, total;
+};
+inline BatchedWs batched_ws_layout(const Dims &dm, int64_t T, int planes) {
+    BatchedWs w{};
+    size_t o = 0;
+    size_t pairs = size_t(T) * dm.k;
+    w.ctrl = o;    o += align256(256);
+    w.logits = o;  o += align256(sizeof(float) * size_t(T) * dm.E);
+    w.ids = o;     o += align256(sizeof(int32_t) * pairs);
+    w.gates = o;   o += align256(sizeof(float) * pairs);
+    w.tinfo = o;   o += align256(sizeof(float) * 2 * size_t(T));
+    w.xdig = o;    o += align256(size_t(planes) * size_t(T) * dm.d);
+    w.counts = o;  o += align256(sizeof(int32_t) * (dm.E + 1));
+    w.offsets = o; o += align256(sizeof(int32_t) * (dm.E + 1));
+    w.pairs = o;   o += align256(sizeof(int32_t) * pairs);
+    w.h = o;       o += align256(sizeof(float) * pairs * dm.F);
+    w.y = o;       o += align256(sizeof(float) * pairs * dm.d);
+    w.total = o;
+    return w;
+}
+
+// ---- launchers (tw_kernels.hip); each returns 0 or a hipError_t value --------------------------
+int launch_pack(const int8_t *w, int64_t rows, int64_t cols, uint8_t *packed, int32_t *bad,
+                void *stream);
+int launch_route(const void *x, int x_bf16, const void *w_router, int w_bf16, int64_t T,
+                 const Dims &dm, float *logits, int32_t *ids, float *gates, void *stream);
+int launch_decode(const Dims &dm, const LayerPtrs *layers, int n_layers, const void *x_in,
+                  void *x_out, int io_bf16, void *ws, void *stream);
+int launch_batched(const Dims &dm, const LayerPtrs &layer, int64_t T, const void *x_in,
+                   int in_bf16, void *x_out, int out_bf16, int int8_act, const int32_t *ids,
+                   const float *gates, void *ws, void *stream);
+
+}  // namespace tw

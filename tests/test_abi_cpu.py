@@ -1,0 +1,140 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/ternary_moe.h
+declares, and rejects bad arguments on the host before any HIP call (fake, never-dereferenced
+device addresses are used; no kernel is launched)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import ternary_weight_moe_amd as tw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ternary_moe.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_WS, E_ALIAS, E_UNSUP, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7
+
+# Fake device addresses, 256-byte aligned and far apart (never dereferenced: every call below fails
+# its host-side checks before any HIP call).
+A = [0x10000000 * (i + 1) for i in range(16)]
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(tw.LIB_PATH):
+        from ternary_weight_moe_amd import build
+        build.build()
+    return tw.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert set(names) == set(tw.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n)
+
+
+def test_status_strings(L):
+    for s in (OK, E_NULL, E_SHAPE, E_DTYPE, E_WS, E_ALIAS, E_UNSUP, E_HIP):
+        assert L.tw_status_str(s) and L.tw_status_str(s) != b"unknown status"
+    assert L.tw_status_str(12345) == b"unknown status"
+
+
+def layer(d=2048, F=512, E=256, k=8, rdt=1, pre=0, base=0):
+    return tw.TwLayer(d, F, E, k, rdt, pre, A[base], A[base + 1], A[base + 2], A[base + 3],
+                      A[base + 4], A[base + 5], A[base + 6])
+
+
+def test_pack_errors(L):
+    s = C.c_void_p(0)
+    assert L.ternary_pack(A[0], -1, 4, A[1], None, s) == E_SHAPE
+    assert L.ternary_pack(A[0], 4, -1, A[1], None, s) == E_SHAPE
+    assert L.ternary_pack(None, 4, 4, A[1], None, s) == E_NULL
+    assert L.ternary_pack(A[0], 4, 4, None, None, s) == E_NULL
+    assert L.ternary_pack(None, 0, 4, None, None, s) == OK        # empty: no-op
+    assert L.ternary_pack(A[0], 4, 64, A[0] + 16, None, s) == E_ALIAS
+    assert L.ternary_pack(A[0], 4, 64, A[1], A[1] + 4, s) == E_ALIAS
+
+
+def test_route_errors(L):
+    s = C.c_void_p(0)
+    args = lambda **kw: [kw.get("x", A[0]), kw.get("xdt", 1), kw.get("w", A[1]), kw.get("wdt", 1),
+                         kw.get("T", 4), kw.get("d", 2048), kw.get("E", 256), kw.get("k", 8),
+                         kw.get("pre", 0), kw.get("lg", A[2]), kw.get("ids", A[3]),
+                         kw.get("g", A[4]), s]
+    assert L.moe_route_topk(*args(T=-1)) == E_SHAPE
+    assert L.moe_route_topk(*args(k=0)) == E_SHAPE
+    assert L.moe_route_topk(*args(k=9, E=8)) == E_SHAPE            # k > E
+    assert L.moe_route_topk(*args(k=33, E=64)) == E_UNSUP          # k above 32
+    assert L.moe_route_topk(*args(d=1000)) == E_UNSUP              # not a power of two
+    assert L.moe_route_topk(*args(d=8192)) == E_UNSUP
+    assert L.moe_route_topk(*args(E=2048)) == E_UNSUP
+    assert L.moe_route_topk(*args(xdt=7)) == E_DTYPE
+    assert L.moe_route_topk(*args(wdt=-1)) == E_DTYPE
+    assert L.moe_route_topk(*args(pre=3)) == E_SHAPE
+    assert L.moe_route_topk(*args(x=None)) == E_NULL
+    assert L.moe_route_topk(*args(lg=None)) == E_NULL
+    assert L.moe_route_topk(*args(ids=A[2] + 8)) == E_ALIAS        # ids inside logits
+    assert L.moe_route_topk(*args(T=0, x=None)) == OK              # empty: no-op
+
+
+def test_decode_errors(L):
+    s = C.c_void_p(0)
+    one = (tw.TwLayer * 1)(layer())
+    need = L.ternary_moe_decode_workspace_bytes(one, 1)
+    assert need > 0
+    call = lambda ls, n=1, xi=A[8], xo=A[9], dt=1, ws=A[10], wsb=need: L.ternary_moe_ffn_decode(
+        ls, n, xi, xo, dt, ws, wsb, s)
+    assert call(None) == E_NULL
+    assert call(one, n=0) == E_SHAPE
+    assert call(one, n=65) == E_UNSUP
+    assert call(one, xi=None) == E_NULL
+    assert call(one, ws=None) == E_NULL
+    assert call(one, dt=5) == E_DTYPE
+    assert call(one, wsb=need - 1) == E_WS
+    assert call(one, xo=A[8] + 2) == E_ALIAS
+    assert call(one, ws=A[8] - 256, wsb=need + 4096) == E_ALIAS      # workspace over x_in
+    bad = (tw.TwLayer * 1)(layer(d=1000))
+    assert call(bad) == E_UNSUP
+    bad = (tw.TwLayer * 1)(layer(k=300))
+    assert call(bad) == E_SHAPE
+    bad = (tw.TwLayer * 1)(layer(rdt=9))
+    assert call(bad) == E_DTYPE
+    l0 = layer()
+    l0.w_up = None
+    assert call((tw.TwLayer * 1)(l0)) == E_NULL
+    l0 = layer()
+    l0.w_down = A[3] + 8                                             # packed rows need 16-B alignment
+    assert call((tw.TwLayer * 1)(l0)) == E_UNSUP
+    two = (tw.TwLayer * 2)(layer(), layer(F=256))
+    assert call(two, n=2) == E_SHAPE                                  # layers must match
+    two = (tw.TwLayer * 2)(layer(), layer(pre=1))
+    assert call(two, n=2) == E_SHAPE
+
+
+def test_batched_errors(L):
+    s = C.c_void_p(0)
+    l = layer()
+    need = L.ternary_moe_batched_workspace_bytes(C.byref(l), 64, 0)
+    need8 = L.ternary_moe_batched_workspace_bytes(C.byref(l), 64, 1)
+    assert need > need8 > 0
+    assert L.ternary_moe_batched_workspace_bytes(C.byref(l), 64, 7) == 0
+    call = lambda T=64, xi=A[8], idt=1, xo=A[9], odt=1, act=0, ids=None, g=None, ws=A[10], wsb=need, ll=None: \
+        L.ternary_moe_ffn_batched(C.byref(ll if ll is not None else l), T, xi, idt, xo, odt, act,
+                                  ids, g, ws, wsb, s)
+    assert call(T=-1) == E_SHAPE
+    assert call(idt=3) == E_DTYPE
+    assert call(act=2) == E_DTYPE
+    assert call(ids=A[11]) == E_NULL                                  # ids without gates
+    assert call(xi=None) == E_NULL
+    assert call(wsb=need - 1) == E_WS
+    assert call(xo=A[8] + 64) == E_ALIAS
+    assert call(T=0, xi=None, xo=None, ws=None) == OK
+    assert call(act=1, ll=layer(pre=1), wsb=need8) == E_UNSUP         # int8 with pre-norm
+    assert L.ternary_moe_ffn_batched(None, 4, A[8], 1, A[9], 1, 0, None, None, A[10], need, s) == E_NULL

@@ -1,0 +1,302 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, element by element, on seeded
+synthetic inputs.  Bars: bit-exact for packing and for the int8-activation path; for float outputs
+the normwise error max|gpu - oracle| / max|oracle| <= 1e-4 (fp32 I/O) or <= 2e-2 (bf16 I/O), and
+in addition every bf16 element within one bf16 ulp of the exact value (plus 1e-3 of the vector's
+maximum).  Routing: equal ids, except across near-ties of the oracle's logits (< 1e-5), where any
+choice consistent with the oracle's logits is accepted and the output is compared against the
+oracle's output for that choice."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import ternary_weight_moe_amd as tw
+from parity_util import (TAU, LayerPair, bf16_ulp, check_routing, make_pair, normwise,
+                         require_gpu, routing_alternatives, step, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+@pytest.fixture(scope="module")
+def small():
+    step("build small_layer_b1 layer pair")
+    return make_pair(synth.SMALL_LAYER_B1)
+
+
+@pytest.fixture(scope="module")
+def full():
+    step("build layer_b1 layer pair (full size)")
+    return make_pair(synth.LAYER_B1)
+
+
+def assert_bf16_close(gpu, exact, what="", ulps=1):
+    gpu = np.asarray(gpu, np.float64)
+    exact = np.asarray(exact, np.float64)
+    assert normwise(gpu, exact) <= 2e-2, what
+    # the float path's 2-digit activation split has relative error ~1e-4; one bf16 ulp of rounding
+    # plus 1e-3 of the vector's maximum covers both and is still 20x inside the 2e-2 bar.  Through
+    # a chain of L layers each bf16 rounding may differ by an ulp and the residual carries it on.
+    tol = ulps * bf16_ulp(exact) + 1e-3 * np.max(np.abs(exact))
+    bad = np.abs(gpu - exact) > tol
+    assert not bad.any(), (what, int(bad.sum()), np.max(np.abs(gpu - exact) - tol))
+
+
+# ---- ternary_pack ----------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,cols", [(64, 2048), (5, 7), (3, 33), (17, 64), (1, 1)])
+def test_pack_bit_exact(rows, cols):
+    step("ternary_pack %dx%d" % (rows, cols))
+    g = torch.Generator().manual_seed(rows * 1000 + cols)
+    w = torch.randint(-1, 2, (rows, cols), dtype=torch.int8, generator=g)
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    p = tw.ternary_pack(w.cuda(), bad)
+    torch.cuda.synchronize()
+    ref, nbad = oracle.pack(w)
+    assert nbad == 0 and int(bad.item()) == 0
+    assert np.array_equal(p.cpu().numpy(), ref)
+
+
+def test_pack_counts_invalid_values():
+    step("ternary_pack invalid values")
+    w = torch.randint(-1, 2, (8, 128), dtype=torch.int8)
+    w[0, 5], w[3, 100], w[7, 127] = 2, -3, 127
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    p = tw.ternary_pack(w.cuda(), bad)
+    torch.cuda.synchronize()
+    ref, nbad = oracle.pack(w)
+    assert nbad == 3 and int(bad.item()) == 3
+    assert np.array_equal(p.cpu().numpy(), ref)
+
+
+def test_pack_full_layer_matches_oracle(full):
+    # the full-size layer pair was packed on both sides: every byte must agree
+    step("compare packed full layer")
+    for a, b in ((full.gpu.p_gate, full.ora.p_gate), (full.gpu.p_up, full.ora.p_up),
+                 (full.gpu.p_down, full.ora.p_down)):
+        assert np.array_equal(a.cpu().numpy(), b)
+
+
+# ---- routing -------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("which,T,pre", [("small", 37, False), ("full", 64, False), ("full", 19, True)])
+def test_route_topk(which, T, pre, small, full):
+    lp = small if which == "small" else full
+    wl = synth.SMALL_LAYER_B1 if which == "small" else synth.LAYER_B1
+    x = synth.activations(wl, T, seed=77 + T)
+    step("moe_route_topk %s T=%d pre=%s" % (which, T, pre))
+    lg, ids, g = tw.moe_route_topk(x.cuda(), lp.gpu.w_router, lp.gpu.k, pre_rmsnorm=pre)
+    torch.cuda.synchronize()
+    L = lp.ora
+    L2 = oracle.Layer(L.w_router, L.p_gate, L.p_up, L.p_down, L.s_gate, L.s_up, L.s_down,
+                      pre_rmsnorm=pre, top_k=L.k, packed=True)
+    oids, og, olg = oracle.route(L2, x, n_threads=4)
+    assert np.max(np.abs(lg.cpu().numpy() - olg)) <= 1e-5 * max(1.0, np.max(np.abs(olg)))
+    ties = check_routing(ids.cpu().numpy(), g.cpu().numpy(), olg, oids, og, L.k)
+    assert ties <= max(1, T // 100)
+    assert np.allclose(g.sum(1).cpu().numpy(), 1.0, atol=L.k * 2.0 ** -23)
+
+
+def test_route_zero_input_goes_to_lowest_ids(full):
+    step("moe_route_topk zero input")
+    x = torch.zeros((3, 2048), dtype=torch.bfloat16, device="cuda")
+    lg, ids, g = tw.moe_route_topk(x, full.gpu.w_router, 8)
+    torch.cuda.synchronize()
+    assert np.all(ids.cpu().numpy() == np.arange(8)[None])
+    assert np.all(g.cpu().numpy() == np.float32(1 / 8))
+
+
+# ---- batch-1 decode ------------------------------------------------------------------------------
+
+def oracle_decode_expect(L, x_row, tau=TAU):
+    """Oracle outputs (double) of one token for its routing and any near-tie alternative."""
+    out, ids, g, lg = oracle.moe_layer(L, x_row[None])
+    alts = routing_alternatives(lg[0], ids[0], L.k, tau)
+    res = [out[0]]
+    for sel, gg in alts[1:]:
+        res.append(oracle.ffn_token(L, x_row, sel, gg))
+    return res
+
+
+def test_decode_small_layer_fp32(small):
+    x = synth.activations(synth.SMALL_LAYER_B1, 16, seed=5)
+    ws = torch.empty(tw.decode_workspace_bytes([small.gpu]), dtype=torch.uint8, device="cuda")
+    for t in range(16):
+        step("decode small_layer_b1 token %d" % t)
+        out = tw.ternary_moe_ffn_decode([small.gpu], x[t].cuda(), workspace=ws)
+        torch.cuda.synchronize()
+        got = to_np(out)
+        xr = x[t].double().numpy()
+        cands = oracle_decode_expect(small.ora, xr)
+        errs = [normwise(got, c) for c in cands]
+        i = int(np.argmin(errs))
+        assert errs[i] <= 1e-4, (t, errs)
+        assert normwise(got - xr, cands[i] - xr) <= 1e-3, t
+
+
+def test_decode_full_layer_bf16(full):
+    x = synth.activations(synth.LAYER_B1, 8, seed=11)
+    ws = torch.empty(tw.decode_workspace_bytes([full.gpu]), dtype=torch.uint8, device="cuda")
+    for t in range(8):
+        step("decode layer_b1 token %d" % t)
+        out = tw.ternary_moe_ffn_decode([full.gpu], x[t].cuda(), workspace=ws)
+        torch.cuda.synchronize()
+        got = to_np(out)
+        cands = oracle_decode_expect(full.ora, x[t].double().numpy())
+        errs = [normwise(got, c) for c in cands]
+        i = int(np.argmin(errs))
+        assert_bf16_close(got, cands[i], "token %d" % t)
+
+
+def test_decode_is_deterministic(full):
+    x = synth.activations(synth.LAYER_B1, 1, seed=3)[0].cuda()
+    step("decode determinism")
+    a = tw.ternary_moe_ffn_decode([full.gpu], x)
+    b = tw.ternary_moe_ffn_decode([full.gpu], x)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_decode_zero_input_and_zero_weights(small):
+    step("decode zero input")
+    z = torch.zeros(256, dtype=torch.float32, device="cuda")
+    out = tw.ternary_moe_ffn_decode([small.gpu], z)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+    step("decode all-zero codes")
+    w = synth.layer_weights(synth.SMALL_LAYER_B1, 0)
+    for key in ("t_gate", "t_up", "t_down"):
+        w[key] = torch.zeros_like(w[key])
+    zl = LayerPair(w, 2, False)
+    x = synth.activations(synth.SMALL_LAYER_B1, 1, seed=9)[0].cuda()
+    out = tw.ternary_moe_ffn_decode([zl.gpu], x)
+    torch.cuda.synchronize()
+    assert torch.equal(out, x)
+
+
+@pytest.fixture(scope="module")
+def stack3():
+    layers = []
+    for l in range(3):
+        step("build stack layer %d" % l)
+        layers.append(make_pair(synth.STACK24_B1, layer=l))
+    return layers
+
+
+def test_decode_stack_teacher_forced_and_chained(stack3):
+    x0 = synth.activations(synth.STACK24_B1, 1, seed=21)[0]
+    ors = [p.ora for p in stack3]
+    li, oout, oids, og, olg = oracle.decode_stack(ors, x0.double().numpy(), 2)
+    # (a) every layer, fed the oracle's own input for it, matches the oracle's output
+    for s in range(2):
+        for l in range(3):
+            step("stack teacher-forced step %d layer %d" % (s, l))
+            xin = torch.from_numpy(li[s, l]).to(torch.bfloat16).cuda()
+            got = to_np(tw.ternary_moe_ffn_decode([stack3[l].gpu], xin))
+            cands = oracle_decode_expect(ors[l], li[s, l])
+            errs = [normwise(got, c) for c in cands]
+            assert_bf16_close(got, cands[int(np.argmin(errs))], "step %d layer %d" % (s, l))
+    # (b) one 3-layer call equals three chained 1-layer calls, bit for bit
+    step("stack fused call vs chained calls")
+    xg = x0.cuda()
+    fused = tw.ternary_moe_ffn_decode([p.gpu for p in stack3], xg)
+    cur = xg
+    for p in stack3:
+        cur = tw.ternary_moe_ffn_decode([p.gpu], cur)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), cur.view(torch.int16))
+    # (c) end to end against the oracle when no layer sits near a routing tie
+    srt = np.sort(olg[0], axis=1)[:, ::-1]
+    margin = np.min(srt[:, 7] - srt[:, 8])
+    if margin > 1e-3:
+        assert_bf16_close(to_np(fused), oout[0], "end to end", ulps=len(stack3) + 1)
+
+
+# ---- batched -------------------------------------------------------------------------------------
+
+def test_batched_float_matches_oracle_and_decode(full):
+    T = 64
+    x = synth.activations(synth.BATCHED_B64, T)
+    step("batched float T=64")
+    out = tw.ternary_moe_ffn_batched(full.gpu, x.cuda())
+    torch.cuda.synchronize()
+    got = to_np(out)
+    oout, oids, og, olg = oracle.moe_layer(full.ora, x, n_threads=8)
+    ws = torch.empty(tw.decode_workspace_bytes([full.gpu]), dtype=torch.uint8, device="cuda")
+    for t in range(T):
+        cands = [oout[t]] + [oracle.ffn_token(full.ora, x[t].double().numpy(), s, g)
+                             for s, g in routing_alternatives(olg[t], oids[t], 8)[1:]]
+        errs = [normwise(got[t], c) for c in cands]
+        assert_bf16_close(got[t], cands[int(np.argmin(errs))], "token %d" % t)
+    # the batched path computes exactly what batch-1 decode computes, token by token
+    for t in range(0, T, 9):
+        step("batched vs decode token %d" % t)
+        d1 = tw.ternary_moe_ffn_decode([full.gpu], x[t].cuda(), workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(d1.view(torch.int16), out[t].view(torch.int16)), t
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_batched_int8_bit_exact(full, out_dtype):
+    T = 64
+    x = synth.activations(synth.BATCHED_B64_INT8, T, seed=31)
+    oids, og, _ = oracle.route(full.ora, x, n_threads=8)
+    ids = torch.from_numpy(oids).cuda()
+    gates = torch.from_numpy(og.astype(np.float32)).cuda()
+    step("batched int8 T=64 out=%s" % out_dtype)
+    out = tw.ternary_moe_ffn_batched(full.gpu, x.cuda(), act="int8", out_dtype=out_dtype,
+                                     expert_ids=ids, gate_w=gates)
+    torch.cuda.synchronize()
+    ref = oracle.ffn_batch_i8(full.ora, x, oids, og.astype(np.float32), n_threads=8)
+    if out_dtype == torch.float32:
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    else:
+        ref16 = oracle.round_bf16_bits(ref.astype(np.float64))
+        assert np.array_equal(out.cpu().view(torch.int16).numpy().view(np.uint16), ref16)
+
+
+def test_batched_int8_internal_routing_close(full):
+    T = 16
+    x = synth.activations(synth.BATCHED_B64_INT8, T, seed=41)
+    step("batched int8 internal routing")
+    out = tw.ternary_moe_ffn_batched(full.gpu, x.cuda(), act="int8", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    oids, og, olg = oracle.route(full.ora, x, n_threads=8)
+    ref = oracle.ffn_batch_i8(full.ora, x, oids, og.astype(np.float32), n_threads=8)
+    for t in range(T):
+        assert normwise(out[t].cpu().numpy(), ref[t]) <= 1e-4, t
+
+
+def test_batched_int8_all_tokens_one_expert(full):
+    # adversarial grouping: every token sends all k slots to the same 8 experts
+    T = 40
+    x = synth.activations(synth.BATCHED_B64_INT8, T, seed=51)
+    ids = np.tile(np.array([7, 3, 200, 5, 6, 9, 100, 255], np.int32), (T, 1))
+    g = np.full((T, 8), 0.125, np.float32)
+    step("batched int8 adversarial routing T=40")
+    out = tw.ternary_moe_ffn_batched(full.gpu, x.cuda(), act="int8", out_dtype=torch.float32,
+                                     expert_ids=torch.from_numpy(ids).cuda(),
+                                     gate_w=torch.from_numpy(g).cuda())
+    torch.cuda.synchronize()
+    ref = oracle.ffn_batch_i8(full.ora, x, ids, g, n_threads=8)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def test_batched_ragged_and_empty(small):
+    for T in (0, 1, 5):
+        x = synth.activations(synth.SMALL_LAYER_B1, max(T, 1), seed=61)[:T]
+        step("batched small T=%d" % T)
+        out = tw.ternary_moe_ffn_batched(small.gpu, x.cuda())
+        torch.cuda.synchronize()
+        if T == 0:
+            assert out.shape == (0, 256)
+            continue
+        got = to_np(out)
+        oout, oids, og, olg = oracle.moe_layer(small.ora, x)
+        for t in range(T):
+            assert normwise(got[t], oout[t]) <= 1e-4, (T, t)
