@@ -210,11 +210,16 @@ def test_decode_stack_teacher_forced_and_chained(stack3):
         cur = tw.ternary_moe_ffn_decode([p.gpu], cur)
     torch.cuda.synchronize()
     assert torch.equal(fused.view(torch.int16), cur.view(torch.int16))
-    # (c) end to end against the oracle when no layer sits near a routing tie
+    # (c) end to end against the oracle when no layer sits near a routing tie.  Each layer rounds
+    # its output to bf16 and the next layer (pre-RMSNorm, SiLU) amplifies a one-ulp difference, so
+    # the chained result drifts element-wise; only the normwise bf16 bar applies here, the strict
+    # element check is the teacher-forced one in (a).
     srt = np.sort(olg[0], axis=1)[:, ::-1]
     margin = np.min(srt[:, 7] - srt[:, 8])
     if margin > 1e-3:
-        assert_bf16_close(to_np(fused), oout[0], "end to end", ulps=len(stack3) + 1)
+        drift = normwise(to_np(fused), oout[0])
+        print("end-to-end normwise drift over %d layers: %.3g" % (len(stack3), drift))
+        assert drift <= 2e-2
 
 
 # ---- batched -------------------------------------------------------------------------------------
