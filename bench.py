@@ -154,7 +154,11 @@ def run_stack(args):
                     us_per_token_min=per_tok_us[0]),
         roofline=dict(bound="hbm", achieved=achieved, peak=accounting.HBM_PEAK_BPS / 1e9,
                       unit="GB/s", frac=achieved * 1e9 / accounting.HBM_PEAK_BPS,
-                      traffic=traffic, kernel="decode step (24 layers)"),
+                      traffic=traffic,
+                      kernel="k_persist<2048,512,8>: one launch per step runs all 24 layers "
+                             "(plus its 2 us word-clearing kernel)",
+                      bytes_per_launch=bytes_per_step,
+                      us_per_launch=total / args.steps * 1e6),
         cpu_baseline=cpu,
     )
 

@@ -57,8 +57,14 @@ BATCHED_B64_INT8 = dataclasses.replace(BATCHED_B64, name="batched_b64_int8", act
 PREFILL_4096 = Workload("prefill_4096", 2048, 256, 512, 8, "bf16", "bf16", "f32", batch=4096,
                         act="int8", seed=1004)
 
+# test-only shapes: a mid-size stack (a second shape of the one-launch stacked decode) and a
+# narrow bf16 layer that the stacked decode does not serve (per-layer kernels)
+MID_STACK_B1 = Workload("mid_stack_b1", 1024, 64, 256, 4, "bf16", "bf16", "bf16", n_layers=3,
+                        pre_rmsnorm=True, seed=1005)
+NARROW_LAYER_B1 = Workload("narrow_layer_b1", 512, 16, 128, 2, "bf16", "bf16", "bf16", seed=1006)
+
 WORKLOADS = {w.name: w for w in (SMALL_LAYER_B1, LAYER_B1, STACK24_B1, BATCHED_B64,
-                                 BATCHED_B64_INT8, PREFILL_4096)}
+                                 BATCHED_B64_INT8, PREFILL_4096, MID_STACK_B1, NARROW_LAYER_B1)}
 
 _KINDS = {"router": 1, "gate": 2, "up": 3, "down": 4, "s_gate": 5, "s_up": 6, "s_down": 7,
           "x": 8}

@@ -16,6 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libternary_moe.so")
 ARCH = "gfx950"
+HIP_SOURCES = ("tw_kernels.hip", "tw_persist.hip")
 
 HIP_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
@@ -38,12 +39,15 @@ def build(verbose: bool = False) -> str:
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
     host_o = os.path.join(bdir, "tw_host.o")
-    kern_o = os.path.join(bdir, "tw_kernels.o")
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-c",
           os.path.join(CSRC, "tw_host.cpp"), "-o", host_o])
-    _run([hipcc] + HIP_FLAGS + ["-c", os.path.join(CSRC, "tw_kernels.hip"), "-o", kern_o])
+    objs = [host_o]
+    for src in HIP_SOURCES:
+        o = os.path.join(bdir, src.replace(".hip", ".o"))
+        _run([hipcc] + HIP_FLAGS + ["-c", os.path.join(CSRC, src), "-o", o])
+        objs.append(o)
     tmp = LIB + ".tmp%d" % os.getpid()
-    _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", host_o, kern_o, "-o", tmp])
+    _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp])
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

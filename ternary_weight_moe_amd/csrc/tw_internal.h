@@ -21,6 +21,7 @@ struct Dims {
 };
 
 constexpr int kMaxLayers = 64;
+constexpr int kMaxPersistLayers = 32;   // layers per launch of the one-launch stacked decode
 constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 1024;
 
@@ -31,8 +32,11 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // ---- decode (batch 1) workspace -------------------------------------------------------------
 struct DecodeWs {
-    size_t ctrl, logits, ids, gates, xinfo, xdig, h, xbuf, total;
+    size_t ctrl, logits, ids, gates, xinfo, xdig, h, xbuf, ll, err, total;
 };
+// Tagged words of the one-launch stacked decode: two parities of (E logits, k*F fp32 h values,
+// d/2 packed bf16 residual pairs).
+inline size_t persist_words(const Dims &dm) { return 2 * (size_t(dm.E) + size_t(dm.k) * dm.F + dm.d / 2); }
 inline DecodeWs decode_ws_layout(const Dims &dm) {
     DecodeWs w{};
     size_t o = 0;
@@ -44,6 +48,8 @@ inline DecodeWs decode_ws_layout(const Dims &dm) {
     w.xdig = o;   o += align256(size_t(3) * dm.d);
     w.h = o;      o += align256(sizeof(float) * size_t(dm.k) * dm.F);
     w.xbuf = o;   o += align256(sizeof(float) * 2 * size_t(dm.d));
+    w.ll = o;     o += align256(sizeof(uint64_t) * persist_words(dm));
+    w.err = o;    o += align256(sizeof(uint32_t) * 4);
     w.total = o;
     return w;
 }
@@ -76,6 +82,10 @@ int launch_pack(const int8_t *w, int64_t rows, int64_t cols, uint8_t *packed, in
                 void *stream);
 int launch_route(const void *x, int x_bf16, const void *w_router, int w_bf16, int64_t T,
                  const Dims &dm, float *logits, int32_t *ids, float *gates, void *stream);
+// One launch per (up to kMaxPersistLayers) layers; returns -1 when the shape or device is not
+// served by that path (the caller then uses launch_decode).
+int launch_decode_persist(const Dims &dm, const LayerPtrs *layers, int n_layers, const void *x_in,
+                          void *x_out, int io_bf16, void *ws, void *stream);
 int launch_decode(const Dims &dm, const LayerPtrs *layers, int n_layers, const void *x_in,
                   void *x_out, int io_bf16, void *ws, void *stream);
 int launch_batched(const Dims &dm, const LayerPtrs &layer, int64_t T, const void *x_in,

@@ -1,242 +1,14 @@
-// tw_kernels.hip -- HIP kernels for the ternary MoE FFN on gfx950 (MI355X), and their launchers.
-//
-// Pages cited (titles as printed):
-//   [MacMini] "A 20B AI Model Trained in Ternary Just Hit 218 Tokens/Second on a $599 Mac Mini"
-//   [Hub]     "iPhone Runs a 20B Model at 120 tok/s"
-//
-// The ternary dot product.  The pages' kernel masks each 2-bit code and adds, subtracts or skips
-// the activation, accumulating in FP32 ([MacMini] "What Ternary Actually Means", "The
-// Architecture: Designed for the Hardware").  On gfx950 the cheapest add/subtract/skip is an int8
-// dot: one v_perm_b32 turns four 2-bit codes into four int8 weights in {-1,0,+1} (a byte lookup
-// with the codes as selectors), and one v_dot4_i32_i8 applies four of them to four int8
-// activations with an exact int32 sum.  Activations are therefore split into int8 "digit planes":
-//   - int8 activation mode: one plane, q = clamp(rint(v * (127/amax)), +-127), scale amax/127;
-//   - float mode: P planes (P = 2 for bf16 I/O, 3 for fp32 I/O) of a fixed-point image
-//     X = rint(v * 2^sh) with |X| < 2^(7P), digits of |X| in base 128 carrying the sign of X.
-//     The dot is sum_k 128^(P-1-k) acc_k * 2^-sh; its error is the fixed-point rounding of the
-//     activations (<= amax * 2^-(7P) per element), far below the bf16 output rounding for P = 2 and
-//     of the order of fp32 accumulation error for P = 3.
-// Code word layout: a 32-bit word holds weights 0..15 of a 16-weight group (weight i in bits
-// 2i..2i+1).  Decoding gives four int8x4 words W_m whose byte b is weight 4b+m; the matching
-// activation digits are stored with the same 4x4 transpose inside every group of 16, so that
-// W_m lines up with the activation word A_m without any shuffling at run time.
+// tw_kernels.hip -- HIP kernels for the ternary MoE FFN on gfx950 (MI355X), and their launchers:
+// packing, routing, the per-layer batch-1 decode kernels and the expert-grouped batched path.
+// The ternary dot product and the activation digit planes are described in tw_device.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tw_device.h"
 #include "tw_internal.h"
 
 namespace tw {
 namespace {
-
-constexpr uint32_t kCodeMask = 0x03030303u;
-// Byte c of this word is the int8 weight of code c: 00 -> 0, 01 -> +1, 10 -> -1, 11 -> 0.
-constexpr uint32_t kCodeLut = 0x00FF0100u;
-
-// ------------------------------------------------------------------------------------------------
-// scalar helpers
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
-
-__device__ __forceinline__ uint16_t f32_to_bf16(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;   // NaN
-    u += 0x7fffu + ((u >> 16) & 1u);                       // round to nearest, ties to even
-    return uint16_t(u >> 16);
-}
-
-__device__ __forceinline__ float load_act(const void *p, int64_t i, int bf16)
-{
-    return bf16 ? bf16_to_f32(static_cast<const uint16_t *>(p)[i]) : static_cast<const float *>(p)[i];
-}
-
-__device__ __forceinline__ void store_act(void *p, int64_t i, float v, int bf16)
-{
-    if (bf16)
-        static_cast<uint16_t *>(p)[i] = f32_to_bf16(v);
-    else
-        static_cast<float *>(p)[i] = v;
-}
-
-__device__ __forceinline__ float wave_sum(float v)
-{
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
-__device__ __forceinline__ float wave_max(float v)
-{
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-
-// exp used by SiLU and the softmax gates: Cody-Waite reduction z = n ln2 + r with ln2 split in a
-// high part whose 12 low significand bits are zero (so n * hi is exact) and a low part, a degree-7
-// Taylor polynomial of e^r in Horner form (coefficients 1/m! rounded to fp32), then a scaling by
-// 2^n.  Arguments above 80 give +inf and below -80 give 0, so no result is subnormal.  Compiled
-// with -ffp-contract=off: every step is one rounded fp32 operation.
-__device__ __forceinline__ float tw_exp(float z)
-{
-    if (z > 80.0f) return __builtin_inff();
-    if (z < -80.0f) return 0.0f;
-    const float kLog2e = 1.44269504088896340736f;
-    const float kLn2Hi = 0.693145751953125f;
-    const float kLn2Lo = 1.42860682030941723212e-6f;
-    float n = __builtin_rintf(z * kLog2e);
-    float r = z - n * kLn2Hi;
-    r = r - n * kLn2Lo;
-    float p = 1.98412698412698412698e-4f;    // 1/7!
-    p = p * r + 1.38888888888888888889e-3f;  // 1/6!
-    p = p * r + 8.33333333333333333333e-3f;  // 1/5!
-    p = p * r + 4.16666666666666666667e-2f;  // 1/4!
-    p = p * r + 1.66666666666666666667e-1f;  // 1/3!
-    p = p * r + 0.5f;
-    p = p * r + 1.0f;
-    p = p * r + 1.0f;
-    return __builtin_ldexpf(p, int(n));
-}
-
-// SiLU(z) = z / (1 + e^-z), as the division of z by one rounded denominator.
-__device__ __forceinline__ float tw_silu(float z) { return z / (1.0f + tw_exp(-z)); }
-
-// Position of element i in the digit-plane layout (4x4 transpose inside every group of 16).
-__device__ __forceinline__ int perm16(int i) { return (i & ~15) | ((i & 3) << 2) | ((i >> 2) & 3); }
-
-// ---- digit planes ---------------------------------------------------------------------------
-
-// Shift sh with |v| * 2^sh < 2^(7P) for every |v| <= amax.
-__device__ __forceinline__ int float_digit_shift(float amax, int P)
-{
-    if (!(amax > 0.0f)) return 0;
-    int e;
-    frexpf(amax, &e);   // amax = f 2^e, f in [0.5, 1)
-    return 7 * P - e;
-}
-
-template <int P>
-__device__ __forceinline__ void float_digits(float v, int sh, int8_t (&dg)[P])
-{
-    float X = __builtin_rintf(__builtin_ldexpf(v, sh));
-    int a = int(fminf(fabsf(X), float((1 << (7 * P)) - 1)));
-#pragma unroll
-    for (int k = 0; k < P; k++) {
-        int dk = (a >> (7 * (P - 1 - k))) & 127;
-        dg[k] = int8_t(X < 0.0f ? -dk : dk);
-    }
-}
-
-// int8 activation mode: q = clamp(rint(v * inv), -127, 127) with inv = 127 / amax.
-__device__ __forceinline__ int8_t int8_quant(float v, float inv)
-{
-    float t = __builtin_rintf(v * inv);
-    t = fminf(fmaxf(t, -127.0f), 127.0f);
-    return int8_t(int(t));
-}
-
-// ---- the ternary dot on one 16-byte chunk of codes (64 weights) -------------------------------
-
-__device__ __forceinline__ int32_t lut4(uint32_t sel)
-{
-    return int32_t(__builtin_amdgcn_perm(0u, kCodeLut, sel));
-}
-
-template <int P>
-__device__ __forceinline__ void chunk_dot(const int4 code, const int4 (&dg)[P][4], int32_t (&acc)[P])
-{
-    const uint32_t w[4] = {uint32_t(code.x), uint32_t(code.y), uint32_t(code.z), uint32_t(code.w)};
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-        const int32_t t0 = lut4(w[q] & kCodeMask);
-        const int32_t t1 = lut4((w[q] >> 2) & kCodeMask);
-        const int32_t t2 = lut4((w[q] >> 4) & kCodeMask);
-        const int32_t t3 = lut4((w[q] >> 6) & kCodeMask);
-#pragma unroll
-        for (int p = 0; p < P; p++) {
-            acc[p] = __builtin_amdgcn_sdot4(t0, dg[p][q].x, acc[p], false);
-            acc[p] = __builtin_amdgcn_sdot4(t1, dg[p][q].y, acc[p], false);
-            acc[p] = __builtin_amdgcn_sdot4(t2, dg[p][q].z, acc[p], false);
-            acc[p] = __builtin_amdgcn_sdot4(t3, dg[p][q].w, acc[p], false);
-        }
-    }
-}
-
-// Sum over the `lanes` consecutive lanes that share one row (lanes is a power of two <= 64).
-template <int P>
-__device__ __forceinline__ void group_reduce(int32_t (&acc)[P], int lanes)
-{
-    for (int o = lanes >> 1; o > 0; o >>= 1) {
-#pragma unroll
-        for (int p = 0; p < P; p++) acc[p] += __shfl_xor(acc[p], o);
-    }
-}
-
-// Float-mode value of a row: sum_k 128^(P-1-k) acc_k, scaled by 2^-sh.
-template <int P>
-__device__ __forceinline__ float float_value(const int32_t (&acc)[P], int sh)
-{
-    float v = float(acc[0]);
-#pragma unroll
-    for (int p = 1; p < P; p++) v = v * 128.0f + float(acc[p]);
-    return __builtin_ldexpf(v, -sh);
-}
-
-// ---- top-k + softmax by one wave ------------------------------------------------------------
-// Selection order: larger logit first; equal logits -> lower expert id first.
-__device__ void topk_softmax_wave(const float *logits, int E, int k, int32_t *ids_out,
-                                  float *gates_out, int lane)
-{
-    constexpr int kPer = kMaxExperts / 64;
-    float v[kPer];
-    uint32_t taken = 0;
-#pragma unroll
-    for (int s = 0; s < kPer; s++) {
-        int e = lane + 64 * s;
-        v[s] = e < E ? logits[e] : -__builtin_inff();
-        if (e >= E) taken |= 1u << s;
-    }
-    float sel_v[kMaxTopK];
-    int32_t sel_i[kMaxTopK];
-    for (int j = 0; j < k; j++) {
-        float bv = -__builtin_inff();
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int s = 0; s < kPer; s++) {
-            int e = lane + 64 * s;
-            bool free_ = !((taken >> s) & 1u);
-            // the first free entry is always taken, so the id is valid even for NaN logits
-            if (free_ && (bi == 0x7fffffff || v[s] > bv || (v[s] == bv && e < bi))) {
-                bv = v[s];
-                bi = e;
-            }
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            float ov = __shfl_xor(bv, o);
-            int oi = __shfl_xor(bi, o);
-            if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-        sel_v[j] = bv;
-        sel_i[j] = bi;
-    }
-    if (lane == 0) {
-        float ex[kMaxTopK];
-        float den = 0.0f;
-        for (int j = 0; j < k; j++) {
-            ex[j] = tw_exp(sel_v[j] - sel_v[0]);
-            den = den + ex[j];
-        }
-        for (int j = 0; j < k; j++) {
-            ids_out[j] = sel_i[j];
-            gates_out[j] = ex[j] / den;
-        }
-    }
-}
 
 // ------------------------------------------------------------------------------------------------
 // ternary_pack
@@ -308,18 +80,9 @@ __global__ __launch_bounds__(256) void k_router_logits(const void *__restrict__ 
     const int64_t t = gw / E;
     const int e = int(gw % E);
     const int64_t xo = t * d;
-    float acc = 0.0f, ss = 0.0f;
-    for (int i = lane; i < d; i += 64) {
-        const float xv = load_act(x, xo + i, x_bf16);
-        const float wv = load_act(wr, int64_t(e) * d + i, w_bf16);
-        acc += wv * xv;
-        ss += xv * xv;
-    }
-    acc = wave_sum(acc);
-    if (pre_norm) {
-        ss = wave_sum(ss);
-        acc = acc * (1.0f / sqrtf(ss / float(d) + 1e-6f));
-    }
+    auto xv = [&](int i) { return load_act(x, xo + i, x_bf16); };
+    float acc = canon_dot(d, lane, [&](int i) { return load_act(wr, int64_t(e) * d + i, w_bf16); }, xv);
+    if (pre_norm) acc = acc * inv_rms_of(canon_dot(d, lane, xv, xv), d);
     if (lane == 0) logits[t * E + e] = acc;
 }
 
@@ -357,20 +120,13 @@ __global__ __launch_bounds__(256) void k_dec_route(DecodeArgs a, const void *__r
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int d = a.dm.d, E = a.dm.E;
     float *logits = reinterpret_cast<float *>(ws + a.L.logits);
-    float ss = 0.0f;
-    for (int i = lane; i < d; i += 64) {
-        const float v = load_act(x, i, a.io_bf16);
-        ss += v * v;
-    }
-    ss = wave_sum(ss);
-    const float inv_rms = a.dm.pre_norm ? 1.0f / sqrtf(ss / float(d) + 1e-6f) : 1.0f;
+    auto xv = [&](int i) { return load_act(x, i, a.io_bf16); };
+    const float inv_rms = a.dm.pre_norm ? inv_rms_of(canon_dot(d, lane, xv, xv), d) : 1.0f;
     const int e = blockIdx.x * 4 + wave;
     if (e < E) {
-        float acc = 0.0f;
-        for (int i = lane; i < d; i += 64)
-            acc += load_act(wr, int64_t(e) * d + i, a.dm.router_bf16) * load_act(x, i, a.io_bf16);
-        acc = wave_sum(acc);
-        if (lane == 0) logits[e] = acc * inv_rms;
+        float acc = canon_dot(d, lane, [&](int i) { return load_act(wr, int64_t(e) * d + i, a.dm.router_bf16); }, xv);
+        if (a.dm.pre_norm) acc = acc * inv_rms;
+        if (lane == 0) logits[e] = acc;
     }
     if (blockIdx.x == 0 && wave == 0) {
         float am = 0.0f;
@@ -559,7 +315,12 @@ __global__ __launch_bounds__(64) void k_bat_quant_x(BatchedArgs a, const void *_
 #pragma unroll
             for (int p = 0; p < P; p++) xd[p * d + perm16(i)] = dg[p];
         }
-        if (lane == 0) reinterpret_cast<int32_t *>(ti)[0] = sh;
+        auto xv = [&](int i) { return load_act(x, xo + i, x_bf16); };
+        const float inv = a.dm.pre_norm ? inv_rms_of(canon_dot(d, lane, xv, xv), d) : 1.0f;
+        if (lane == 0) {
+            reinterpret_cast<int32_t *>(ti)[0] = sh;
+            ti[1] = inv;
+        }
     }
 }
 
@@ -644,7 +405,8 @@ __global__ __launch_bounds__(256) void k_bat_gateup(BatchedArgs a, LayerPtrs lp,
                 if (INT8)
                     v = (float(acc[0]) * tinfo[2 * t]) * s;
                 else
-                    v = float_value<P>(acc, reinterpret_cast<const int32_t *>(tinfo)[2 * t]) * s;
+                    v = float_value<P>(acc, reinterpret_cast<const int32_t *>(tinfo)[2 * t]) * s *
+                        tinfo[2 * t + 1];
                 sums[job] = v;
             }
         }
@@ -843,6 +605,8 @@ int launch_route(const void *x, int x_bf16, const void *w_router, int w_bf16, in
 int launch_decode(const Dims &dm, const LayerPtrs *layers, int n_layers, const void *x_in,
                   void *x_out, int io_bf16, void *ws, void *stream)
 {
+    const int r = launch_decode_persist(dm, layers, n_layers, x_in, x_out, io_bf16, ws, stream);
+    if (r >= 0) return r;
     if (io_bf16) return decode_p<2>(dm, layers, n_layers, x_in, x_out, io_bf16, ws, stream);
     return decode_p<3>(dm, layers, n_layers, x_in, x_out, io_bf16, ws, stream);
 }

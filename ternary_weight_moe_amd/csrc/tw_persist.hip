@@ -1,0 +1,456 @@
+// tw_persist.hip -- batch-1 decode through a stack of layers in ONE launch (gfx950, bf16 I/O).
+//
+// Why one launch.  A decode step is latency-bound: each layer is a chain of all-to-all
+// dependencies (residual -> router logits -> top-k -> gate/up rows -> h -> down rows -> residual),
+// and a kernel boundary inside a hipGraph costs about 1.5 us on MI355X, three per layer.  Here
+// 256 workgroups of 1024 threads (one per compute unit) stay resident for the whole stack and hand each other the
+// three small vectors of every layer through tagged 64-bit words (tw_device.h): each word is one
+// device-scope atomic store of (tag, data) and is read by polling, so a hand-off costs one memory
+// round trip and needs no grid barrier, no fence and no atomic read-modify-write.
+//
+// Per layer, workgroup b (of 256) does:
+//   1. input   x: layer 0 reads x_in; later layers gather the d/2 words of packed bf16 pairs that
+//              the previous layer published (every workgroup needs all of x).
+//   2. router  the workgroup computes the logits of experts b + 256 m (router rows prefetched
+//              during the previous layer, one 16-byte chunk per thread) and publishes them; the
+//              pre-RMSNorm is a scalar on the logits and on the gate/up sums.
+//   3. top-k   every workgroup gathers all E logits and selects the same top-k (same values, same
+//              deterministic selection), so nothing else has to be broadcast.
+//   4. loads   all of this workgroup's expert bytes for the layer are requested at once: its share
+//              of gate/up rows (2 x k*F/256 rows of d/4 bytes) and of down rows (k experts x
+//              d/256 output rows of F/4 bytes), with their scales; then the next layer's router
+//              row.  Little's law wants megabytes in flight across the chip; issuing everything
+//              before the first use gives ~6 MB for the 2048/512/top-8 layer.
+//   5. gate/up the ternary dots (tw_device.h) against the digit planes of x, h = SiLU(gate)*up
+//              in fp32, published one value per word.
+//   6. down    gather all k*F values of h, digit planes per expert, the down dots for the
+//              workgroup's output rows, out = x + sum_j g_j y_j in selection order, rounded to
+//              bf16 and published (or stored to x_out after the last layer).
+// Tags are the layer index + 1 and the words alternate between two parities by layer, so a word
+// is never overwritten while a reader may still need its previous value (a workgroup can be at
+// most one hand-off ahead of any other).  A small kernel zeroes the words before each launch.
+//
+// Every wait is bounded: a wait that exceeds the spin limit marks the workgroup aborted (its
+// remaining waits return at once) and sets a word in the workspace error slot, so the launch
+// always ends.  The arithmetic is that of the per-layer kernels (same digit planes, same canonical
+// router order, same rounding points), so results equal a chain of single-layer calls bit for bit.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "tw_device.h"
+#include "tw_internal.h"
+
+namespace tw {
+namespace {
+
+constexpr int kPB = 256;               // workgroups of a launch (one per compute unit)
+constexpr int kPT = 1024;              // threads per workgroup (16 waves)
+constexpr int kNW = kPT / 64;          // waves per workgroup
+constexpr int kCT = 256;               // threads of the canonical router order (4 waves)
+constexpr uint32_t kSpinLimit = 1u << 21;
+constexpr int kEM = 1;                 // router rows per workgroup: expert b (E <= 256)
+
+struct PLayer {
+    const uint16_t *w_router;
+    const uint8_t *w_gate, *w_up, *w_down;
+    const float *s_gate, *s_up, *s_down;
+};
+
+struct PArgs {
+    const uint16_t *x_in;
+    uint16_t *x_out;
+    uint64_t *ll;      // tagged words (2 parities)
+    uint32_t *err;     // error slot: nonzero after a wait timed out
+    int E, n_layers, pre_norm;
+    PLayer L[kMaxPersistLayers];
+};
+
+template <int D, int F, int K>
+struct PC {
+    static constexpr int Q = K * F / kPB;                    // h rows per workgroup
+    static constexpr int LPR = D / 64;                       // lanes per gate/up row (16 B each)
+    static constexpr int RPP = kPT / LPR;                    // gate/up rows per pass
+    static constexpr int PGU = (2 * Q + RPP - 1) / RPP;      // gate/up passes
+    static constexpr int RD = D / kPB;                       // output rows per workgroup
+    static constexpr int LPRD = F / 64;                      // lanes per down row
+    static constexpr int RPPD = kPT / LPRD;                  // down rows per pass
+    static constexpr int PD = (K * RD + RPPD - 1) / RPPD;    // down passes
+    static constexpr int XW = D / 2;                         // residual words (bf16 pairs)
+    static constexpr int HW = K * F;                         // h words (fp32)
+    static constexpr int NRC = (D / 8 + kCT - 1) / kCT;      // 8-element chunks per router thread
+    static_assert(Q >= 1, "k*F must be a multiple of 256");
+    static_assert(RD >= 2 && RD % 2 == 0, "d must be a multiple of 512");
+    static_assert(LPR >= 1 && LPR <= 64 && LPRD >= 1 && LPRD <= 64, "row widths 64..4096");
+    static_assert(K <= kMaxTopK && K <= 16, "top-k");
+    static_assert(HW % kPT == 0 && F % 64 == 0, "k*F a multiple of 1024");
+    static_assert(XW % 64 == 0, "d a multiple of 128");
+};
+
+// Waits until the words base[t + kPT*n] (n < N, index < W) carry `tag`; v receives them.
+template <int N>
+__device__ __forceinline__ void wait_words(const uint64_t *base, int W, uint32_t tag, uint64_t (&v)[N],
+                                           volatile int *s_abort, uint32_t *err)
+{
+    const int t = threadIdx.x;
+    uint32_t pend = 0;
+#pragma unroll
+    for (int n = 0; n < N; n++)
+        if (t + kPT * n < W) pend |= 1u << n;
+    for (uint32_t it = 0; pend; ++it) {
+#pragma unroll
+        for (int n = 0; n < N; n++)
+            if ((pend >> n) & 1u) v[n] = ld_tagged(base + t + kPT * n);
+#pragma unroll
+        for (int n = 0; n < N; n++)
+            if (((pend >> n) & 1u) && uint32_t(v[n] >> 32) == tag) pend &= ~(1u << n);
+        if (pend && (it > kSpinLimit || *s_abort)) {
+            *s_abort = 1;
+            atomicOr(err, 1u);
+            break;
+        }
+    }
+}
+
+// Router rows of the experts b + kPB*m (m < kEM) of this workgroup: router thread t (< kCT)
+// holds the 16-byte chunks t + kCT*n (8 bf16 each) of each row.
+template <int NRC>
+__device__ __forceinline__ void load_router(int4 (&rw)[kEM][NRC], const uint16_t *wr, int b, int E,
+                                            int d)
+{
+#pragma unroll
+    for (int m = 0; m < kEM; m++)
+#pragma unroll
+        for (int n = 0; n < NRC; n++) {
+            const int c = threadIdx.x + kCT * n, e = b + kPB * m;
+            rw[m][n] = (threadIdx.x < kCT && e < E && c < (d >> 3))
+                           ? reinterpret_cast<const int4 *>(wr + size_t(e) * d)[c]
+                           : make_int4(0, 0, 0, 0);
+        }
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return bf16_to_f32(uint16_t(w & 0xffffu)); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return bf16_to_f32(uint16_t(w >> 16)); }
+
+template <int D, int F, int K>
+__global__ __launch_bounds__(kPT) void k_persist(PArgs a)
+{
+    using C = PC<D, F, K>;
+    const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int E = a.E;
+    __shared__ float xs[D];                                      // layer input x
+    __shared__ __attribute__((aligned(16))) int8_t xd[2 * D];    // its digit planes
+    __shared__ __attribute__((aligned(16))) int8_t hd[K * 2 * F];// digit planes of h, per expert
+    __shared__ float lg[kPB];
+    __shared__ float sums[2 * C::Q];
+    __shared__ float ys[K * C::RD];
+    __shared__ float red[4][2 + kEM];
+    __shared__ int32_t s_hmax[K];                                // per-expert max |h| (float bits)
+    __shared__ int32_t s_ids[kMaxTopK];
+    __shared__ float s_gates[kMaxTopK];
+    __shared__ int s_hsh[K];
+    __shared__ int s_xsh;
+    __shared__ float s_inv;
+    __shared__ int s_abort;
+    if (t == 0) s_abort = 0;
+
+    int4 rw[kEM][C::NRC];
+    load_router<C::NRC>(rw, a.L[0].w_router, b, E, D);
+    const size_t lls = size_t(E) + C::HW + C::XW;
+    const int c_gu = t % C::LPR, c_d = t % C::LPRD;
+    __syncthreads();
+
+    for (int l = 0; l < a.n_layers; l++) {
+        const PLayer &P = a.L[l];
+        const uint32_t tag = uint32_t(l + 1);
+        uint64_t *lgw = a.ll + size_t(l & 1) * lls, *hw = lgw + E, *xw = hw + C::HW;
+
+        // 1. layer input
+        if (l == 0) {
+            for (int i = t; i < D; i += kPT) xs[i] = bf16_to_f32(a.x_in[i]);
+        } else {
+            const uint64_t *xprev = a.ll + size_t((l - 1) & 1) * lls + E + C::HW;
+            constexpr int N = (C::XW + kPT - 1) / kPT;
+            uint64_t v[N];
+            wait_words<N>(xprev, C::XW, tag - 1, v, &s_abort, a.err);
+#pragma unroll
+            for (int n = 0; n < N; n++) {
+                const int i = t + kPT * n;
+                if (i < C::XW) {
+                    xs[2 * i] = bf16_lo(uint32_t(v[n]));
+                    xs[2 * i + 1] = bf16_hi(uint32_t(v[n]));
+                }
+            }
+        }
+        if (t < K) s_hmax[t] = 0;
+        __syncthreads();
+
+        // 2. router threads: their 8-element chunks of x (amax, sum of squares, router partials in
+        //    the canonical order), wave reductions, then block totals, logits and digit planes
+        if (t < kCT) {
+            float am = 0.0f, ss = 0.0f, rp[kEM];
+#pragma unroll
+            for (int m = 0; m < kEM; m++) rp[m] = 0.0f;
+#pragma unroll
+            for (int n = 0; n < C::NRC; n++) {
+                const int c = t + kCT * n;
+                if (c < (D >> 3)) {
+                    float xv[8];
+#pragma unroll
+                    for (int j = 0; j < 8; j++) {
+                        xv[j] = xs[8 * c + j];
+                        am = fmaxf(am, fabsf(xv[j]));
+                        ss = ss + xv[j] * xv[j];
+                    }
+#pragma unroll
+                    for (int m = 0; m < kEM; m++) {
+                        const uint32_t w4[4] = {uint32_t(rw[m][n].x), uint32_t(rw[m][n].y),
+                                                uint32_t(rw[m][n].z), uint32_t(rw[m][n].w)};
+#pragma unroll
+                        for (int j = 0; j < 8; j++) {
+                            const float wv = (j & 1) ? bf16_hi(w4[j >> 1]) : bf16_lo(w4[j >> 1]);
+                            rp[m] = rp[m] + wv * xv[j];
+                        }
+                    }
+                }
+            }
+            am = wave_max(am);
+            ss = wave_sum(ss);
+#pragma unroll
+            for (int m = 0; m < kEM; m++) rp[m] = wave_sum(rp[m]);
+            if (lane == 0) {
+                red[wave][0] = am;
+                red[wave][1] = ss;
+#pragma unroll
+                for (int m = 0; m < kEM; m++) red[wave][2 + m] = rp[m];
+            }
+        }
+        __syncthreads();
+        {
+            const float am = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
+            const float ss = (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]);
+            const float inv = a.pre_norm ? inv_rms_of(ss, D) : 1.0f;
+            const int sh = float_digit_shift(am, 2);
+            if (t < kEM && b + kPB * t < E) {
+                float lgt = (red[0][2 + t] + red[1][2 + t]) + (red[2][2 + t] + red[3][2 + t]);
+                if (a.pre_norm) lgt = lgt * inv;
+                st_tagged(lgw + b + kPB * t, tag, __float_as_uint(lgt));
+            }
+            if (t == 0) {
+                s_xsh = sh;
+                s_inv = inv;
+            }
+            for (int i = t; i < D; i += kPT) {
+                int8_t dg[2];
+                float_digits<2>(xs[i], sh, dg);
+                xd[perm16(i)] = dg[0];
+                xd[D + perm16(i)] = dg[1];
+            }
+        }
+
+        // 3. routing: every workgroup gathers all logits and selects the same experts
+        {
+            constexpr int N = (kPB + kPT - 1) / kPT;
+            uint64_t v[N];
+            wait_words<N>(lgw, E, tag, v, &s_abort, a.err);
+#pragma unroll
+            for (int n = 0; n < N; n++)
+                if (t + kPT * n < E) lg[t + kPT * n] = __uint_as_float(uint32_t(v[n]));
+        }
+        __syncthreads();
+        if (wave == 0) topk_softmax_wave_t<kPB / 64>(lg, E, K, s_ids, s_gates, lane);
+        __syncthreads();
+
+        // 4. request every expert byte of this workgroup's share at once
+        int4 cg[C::PGU];
+        float sg[C::PGU];
+#pragma unroll
+        for (int p = 0; p < C::PGU; p++) {
+            const int jb = p * C::RPP + t / C::LPR;
+            const bool valid = jb < 2 * C::Q;
+            const int i = valid ? (jb >> 1) : 0, kind = jb & 1;
+            const int q = b * C::Q + i, j = q / F, r = q % F;
+            const int e = min(max(s_ids[j], 0), E - 1);
+            const uint8_t *row = (kind ? P.w_up : P.w_gate) + (size_t(e) * F + r) * (D / 4);
+            cg[p] = valid ? reinterpret_cast<const int4 *>(row)[c_gu] : make_int4(0, 0, 0, 0);
+            sg[p] = (valid && c_gu == 0) ? (kind ? P.s_up : P.s_gate)[size_t(e) * F + r] : 0.0f;
+        }
+        int4 cd[C::PD];
+        float sd[C::PD];
+#pragma unroll
+        for (int p = 0; p < C::PD; p++) {
+            const int jd = p * C::RPPD + t / C::LPRD;
+            const bool valid = jd < K * C::RD;
+            const int j = valid ? jd / C::RD : 0, rl = jd % C::RD;
+            const int R = b * C::RD + rl;
+            const int e = min(max(s_ids[j], 0), E - 1);
+            const uint8_t *row = P.w_down + (size_t(e) * D + R) * (F / 4);
+            cd[p] = valid ? reinterpret_cast<const int4 *>(row)[c_d] : make_int4(0, 0, 0, 0);
+            sd[p] = (valid && c_d == 0) ? P.s_down[size_t(e) * D + R] : 0.0f;
+        }
+        if (l + 1 < a.n_layers) load_router<C::NRC>(rw, a.L[l + 1].w_router, b, E, D);
+
+        // 5. gate/up dots, h = SiLU(gate) * up in fp32, published one value per word
+        {
+            int4 dg[2][4];
+#pragma unroll
+            for (int pl = 0; pl < 2; pl++)
+#pragma unroll
+                for (int qq = 0; qq < 4; qq++)
+                    dg[pl][qq] = reinterpret_cast<const int4 *>(xd + pl * D + c_gu * 64)[qq];
+#pragma unroll
+            for (int p = 0; p < C::PGU; p++) {
+                const int jb = p * C::RPP + t / C::LPR;
+                int32_t acc[2] = {0, 0};
+                chunk_dot<2>(cg[p], dg, acc);
+                group_reduce<2>(acc, C::LPR);
+                if (c_gu == 0 && jb < 2 * C::Q) sums[jb] = float_value<2>(acc, s_xsh) * sg[p] * s_inv;
+            }
+        }
+        __syncthreads();
+        if (t < C::Q) {
+            const float h = tw_silu(sums[2 * t]) * sums[2 * t + 1];
+            st_tagged(hw + b * C::Q + t, tag, __float_as_uint(h));
+        }
+
+        // 6. gather h (word w = t + kPT n: expert w / F, element w % F; a wave's 64 words share
+        //    one expert), per-expert max |h|, digit planes, down dots, combine
+        {
+            constexpr int N = C::HW / kPT;
+            uint64_t v[N];
+            wait_words<N>(hw, C::HW, tag, v, &s_abort, a.err);
+#pragma unroll
+            for (int n = 0; n < N; n++) {
+                const float am = wave_max(fabsf(__uint_as_float(uint32_t(v[n]))));
+                if (lane == 0) atomicMax(&s_hmax[(t + kPT * n) / F], __float_as_int(am));
+            }
+            __syncthreads();
+#pragma unroll
+            for (int n = 0; n < N; n++) {
+                const int w = t + kPT * n, j = w / F, i = w % F;
+                const int sh = float_digit_shift(__int_as_float(s_hmax[j]), 2);
+                if (i == 0) s_hsh[j] = sh;
+                int8_t dg[2];
+                float_digits<2>(__uint_as_float(uint32_t(v[n])), sh, dg);
+                hd[(j * 2) * F + perm16(i)] = dg[0];
+                hd[(j * 2 + 1) * F + perm16(i)] = dg[1];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < C::PD; p++) {
+            const int jd = p * C::RPPD + t / C::LPRD;
+            const bool valid = jd < K * C::RD;
+            const int j = valid ? jd / C::RD : 0, rl = jd % C::RD;
+            int4 dh[2][4];
+#pragma unroll
+            for (int pl = 0; pl < 2; pl++)
+#pragma unroll
+                for (int qq = 0; qq < 4; qq++)
+                    dh[pl][qq] = reinterpret_cast<const int4 *>(hd + (j * 2 + pl) * F + c_d * 64)[qq];
+            int32_t acc[2] = {0, 0};
+            chunk_dot<2>(cd[p], dh, acc);
+            group_reduce<2>(acc, C::LPRD);
+            if (c_d == 0 && valid) ys[j * C::RD + rl] = float_value<2>(acc, s_hsh[j]) * sd[p];
+        }
+        __syncthreads();
+        if (t < C::RD / 2) {
+            const int R0 = b * C::RD + 2 * t;
+            float o0 = xs[R0], o1 = xs[R0 + 1];
+            for (int j = 0; j < K; j++) {
+                o0 = o0 + s_gates[j] * ys[j * C::RD + 2 * t];
+                o1 = o1 + s_gates[j] * ys[j * C::RD + 2 * t + 1];
+            }
+            if (l == a.n_layers - 1) {
+                a.x_out[R0] = f32_to_bf16(o0);
+                a.x_out[R0 + 1] = f32_to_bf16(o1);
+            } else {
+                st_tagged(xw + (b * C::RD) / 2 + t, tag, pack_bf16x2(o0, o1));
+            }
+        }
+        __syncthreads();
+    }
+}
+
+__global__ void k_persist_zero(uint64_t *ll, int64_t n, uint32_t *err)
+{
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += int64_t(gridDim.x) * blockDim.x)
+        ll[i] = 0;
+    if (blockIdx.x == 0 && threadIdx.x < 4) err[threadIdx.x] = 0;
+}
+
+// Whether all kPB workgroups of an instantiation fit on the current device at once (cached).
+template <int D, int F, int K>
+bool fits_device()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        int cus = 0, per_cu = 0;
+        bool ok = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                  hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_persist<D, F, K>, kPT, 0) ==
+                      hipSuccess &&
+                  int64_t(cus) * per_cu >= kPB;
+        c = ok ? 1 : -1;
+        cache[dev].store(c, std::memory_order_relaxed);
+    }
+    return c > 0;
+}
+
+template <int D, int F, int K>
+int persist_run(const Dims &dm, const LayerPtrs *layers, int n, const void *x_in, void *x_out,
+                void *ws, void *stream)
+{
+    for (int i = 0; i < n; i++)   // router rows are read 16 bytes at a time
+        if (reinterpret_cast<uintptr_t>(layers[i].w_router) & 15) return -1;
+    if (!fits_device<D, F, K>()) return -1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const DecodeWs L = decode_ws_layout(dm);
+    uint8_t *w = static_cast<uint8_t *>(ws);
+    uint64_t *ll = reinterpret_cast<uint64_t *>(w + L.ll);
+    uint32_t *err = reinterpret_cast<uint32_t *>(w + L.err);
+    uint16_t *xb[2] = {reinterpret_cast<uint16_t *>(w + L.xbuf),
+                       reinterpret_cast<uint16_t *>(w + L.xbuf) + dm.d};
+    const int64_t nw = int64_t(persist_words(dm));
+    int done = 0, chunk = 0;
+    while (done < n) {
+        const int m = n - done < kMaxPersistLayers ? n - done : kMaxPersistLayers;
+        PArgs a{};
+        a.x_in = done == 0 ? static_cast<const uint16_t *>(x_in) : xb[(chunk - 1) & 1];
+        a.x_out = done + m == n ? static_cast<uint16_t *>(x_out) : xb[chunk & 1];
+        a.ll = ll;
+        a.err = err;
+        a.E = dm.E;
+        a.n_layers = m;
+        a.pre_norm = dm.pre_norm;
+        for (int i = 0; i < m; i++) {
+            const LayerPtrs &p = layers[done + i];
+            a.L[i] = PLayer{static_cast<const uint16_t *>(p.w_router), p.w_gate, p.w_up, p.w_down,
+                            p.s_gate, p.s_up, p.s_down};
+        }
+        k_persist_zero<<<16, 256, 0, s>>>(ll, nw, err);
+        k_persist<D, F, K><<<kPB, kPT, 0, s>>>(a);
+        done += m;
+        chunk++;
+    }
+    return int(hipGetLastError());
+}
+
+}  // namespace
+
+int launch_decode_persist(const Dims &dm, const LayerPtrs *layers, int n_layers, const void *x_in,
+                          void *x_out, int io_bf16, void *ws, void *stream)
+{
+    if (!io_bf16 || !dm.router_bf16 || dm.E > kPB || dm.E < dm.k) return -1;
+    if (dm.d == 2048 && dm.F == 512 && dm.k == 8)
+        return persist_run<2048, 512, 8>(dm, layers, n_layers, x_in, x_out, ws, stream);
+    if (dm.d == 1024 && dm.F == 256 && dm.k == 4)
+        return persist_run<1024, 256, 4>(dm, layers, n_layers, x_in, x_out, ws, stream);
+    return -1;
+}
+
+}  // namespace tw

@@ -222,6 +222,72 @@ def test_decode_stack_teacher_forced_and_chained(stack3):
         assert drift <= 2e-2
 
 
+@pytest.fixture(scope="module")
+def mid3():
+    layers = []
+    for l in range(3):
+        step("build mid stack layer %d" % l)
+        layers.append(make_pair(synth.MID_STACK_B1, layer=l))
+    return layers
+
+
+def test_decode_mid_stack_second_shape(mid3):
+    # d=1024, 64 experts, F=256, top-4, pre-RMSNorm: the second shape of the one-launch decode
+    x0 = synth.activations(synth.MID_STACK_B1, 1, seed=23)[0]
+    ors = [p.ora for p in mid3]
+    li, oout, oids, og, olg = oracle.decode_stack(ors, x0.double().numpy(), 2)
+    for s in range(2):
+        for l in range(3):
+            step("mid stack teacher-forced step %d layer %d" % (s, l))
+            xin = torch.from_numpy(li[s, l]).to(torch.bfloat16).cuda()
+            got = to_np(tw.ternary_moe_ffn_decode([mid3[l].gpu], xin))
+            cands = oracle_decode_expect(ors[l], li[s, l])
+            errs = [normwise(got, c) for c in cands]
+            assert_bf16_close(got, cands[int(np.argmin(errs))], "step %d layer %d" % (s, l))
+    step("mid stack fused vs chained")
+    xg = x0.cuda()
+    fused = tw.ternary_moe_ffn_decode([p.gpu for p in mid3], xg)
+    cur = xg
+    for p in mid3:
+        cur = tw.ternary_moe_ffn_decode([p.gpu], cur)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), cur.view(torch.int16))
+
+
+def test_decode_more_layers_than_one_launch_holds(mid3):
+    # 36 layers (the three layers repeated) exceed one launch's 32-layer table: the call is split
+    # into launches chained through the workspace and must equal 36 single-layer calls
+    seq = [p.gpu for p in mid3] * 12
+    x0 = synth.activations(synth.MID_STACK_B1, 1, seed=29)[0].cuda()
+    step("decode 36 layers fused")
+    fused = tw.ternary_moe_ffn_decode(seq, x0)
+    step("decode 36 layers chained")
+    cur = x0
+    for layer in seq:
+        cur = tw.ternary_moe_ffn_decode([layer], cur)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), cur.view(torch.int16))
+    assert torch.isfinite(fused.float()).all()
+
+
+def test_decode_bf16_shape_served_by_per_layer_kernels():
+    # a bf16 shape outside the one-launch decode's instantiations runs the per-layer kernels
+    wl = synth.NARROW_LAYER_B1
+    pair = make_pair(wl)
+    x = synth.activations(wl, 6, seed=13)
+    for t in range(6):
+        step("decode narrow_layer_b1 token %d" % t)
+        got = to_np(tw.ternary_moe_ffn_decode([pair.gpu], x[t].cuda()))
+        cands = oracle_decode_expect(pair.ora, x[t].double().numpy())
+        errs = [normwise(got, c) for c in cands]
+        assert_bf16_close(got, cands[int(np.argmin(errs))], "token %d" % t)
+    step("narrow two-layer fused vs chained")
+    fused = tw.ternary_moe_ffn_decode([pair.gpu, pair.gpu], x[0].cuda())
+    chained = tw.ternary_moe_ffn_decode([pair.gpu], tw.ternary_moe_ffn_decode([pair.gpu], x[0].cuda()))
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), chained.view(torch.int16))
+
+
 # ---- batched -------------------------------------------------------------------------------------
 
 def test_batched_float_matches_oracle_and_decode(full):
