@@ -11,8 +11,9 @@ bytes per step / measured time per step against the 8 TB/s HBM peak) and the CPU
 bounded sample of the same workload.
 
 Other workloads (--workload): layer_b1 (one layer, batch 1), batched_b64 / batched_b64_int8 (one
-layer, 64 tokens grouped by expert); single-layer workloads rotate 8 independently seeded layer
-copies so that the 256 MB last-level cache never holds the layer being timed.
+layer, 64 tokens grouped by expert), prefill_4096 (one layer, 4096 tokens, int8 activations, routing
+passed in; reported as int8 MFMA throughput); single-layer workloads rotate 8 independently seeded
+layer copies so that the 256 MB last-level cache never holds the layer being timed.
 """
 from __future__ import annotations
 
@@ -175,11 +176,13 @@ def run_single_layer(args, name):
     xs = [synth.activations(wl, T, device="cuda", stream=c) for c in range(n_copies)]
     outs = [torch.empty((T, wl.d_model), dtype=torch.bfloat16 if wl.out_dtype == "bf16"
                         else torch.float32, device="cuda") for _ in range(n_copies)]
-    # distinct experts per copy, from the routing the call itself will compute
-    distinct = []
+    # distinct experts per copy, from the routing the call itself will compute; the int8
+    # prefill-shaped workload takes its routing as an input (computed here, outside the timing)
+    distinct, routing = [], []
     for c in range(n_copies):
-        _, ids, _ = tw.moe_route_topk(xs[c], layers[c].w_router, wl.top_k)
+        _, ids, gates = tw.moe_route_topk(xs[c], layers[c].w_router, wl.top_k)
         distinct.append(int(torch.unique(ids).numel()))
+        routing.append((ids, gates) if name == "prefill_4096" else (None, None))
     if T == 1:
         ws = torch.empty(tw.decode_workspace_bytes([layers[0]]), dtype=torch.uint8, device="cuda")
 
@@ -192,13 +195,25 @@ def run_single_layer(args, name):
 
         def step(t):
             c = t % n_copies
-            tw.ternary_moe_ffn_batched(layers[c], xs[c], act=act, out=outs[c], workspace=ws)
+            tw.ternary_moe_ffn_batched(layers[c], xs[c], act=act, out=outs[c], workspace=ws,
+                                       expert_ids=routing[c][0], gate_w=routing[c][1])
 
     G = args.graph_steps
     total, per = time_graph(step, G, args.warmup, args.steps)
     bytes_per_step = sum(accounting.layer_bytes(wl, T, distinct[t % n_copies])
                          for t in range(G)) / G
     achieved = bytes_per_step / (total / args.steps) / 1e9
+    if name == "prefill_4096":
+        ops = accounting.int8_ops(wl, T * wl.top_k)
+        tops = ops / (total / args.steps) / 1e12
+        roof = dict(bound="mfma", achieved=tops, peak=accounting.INT8_MFMA_PEAK_OPS / 1e12,
+                    unit="TOP/s", frac=tops * 1e12 / accounting.INT8_MFMA_PEAK_OPS, traffic=None,
+                    kernel="one call: quantise x, group, k_pf_ffn<2048,512>, combine",
+                    ops_per_call=ops, hbm_gb_s=achieved)
+    else:
+        roof = dict(bound="hbm", achieved=achieved, peak=accounting.HBM_PEAK_BPS / 1e9,
+                    unit="GB/s", frac=achieved * 1e9 / accounting.HBM_PEAK_BPS,
+                    traffic=traffic_from_profiles(name), kernel="one call")
     return dict(
         metric="%s tokens/s (one layer, %d tokens per call)" % (name, T), value=T * args.steps / total,
         unit="tok/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
@@ -206,9 +221,7 @@ def run_single_layer(args, name):
         vs_baseline=None, dtype="int8xint8->int32, fp32", data="synthetic",
         config=dict(workload=name, batch=T, act=act, layer_copies=n_copies,
                     distinct_experts=distinct, bytes_per_step=bytes_per_step),
-        roofline=dict(bound="hbm", achieved=achieved, peak=accounting.HBM_PEAK_BPS / 1e9,
-                      unit="GB/s", frac=achieved * 1e9 / accounting.HBM_PEAK_BPS,
-                      traffic=traffic_from_profiles(name), kernel="one call"),
+        roofline=roof,
         cpu_baseline=None,
     )
 
@@ -220,7 +233,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=512)
     ap.add_argument("--graph-steps", type=int, default=256)
     ap.add_argument("--workload", default="stack24_b1",
-                    choices=["stack24_b1", "layer_b1", "batched_b64", "batched_b64_int8"])
+                    choices=["stack24_b1", "layer_b1", "batched_b64", "batched_b64_int8",
+                             "prefill_4096"])
     ap.add_argument("--cpu-tokens", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()

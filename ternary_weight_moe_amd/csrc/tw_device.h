@@ -196,6 +196,32 @@ __device__ __forceinline__ void chunk_dot(const int4 code, const int4 (&dg)[P][4
     }
 }
 
+// The same dot with the 16-byte chunk decoded once (wd[4q+m] = the int8x4 word W_m of code word q),
+// for chunks applied to several activation vectors.
+__device__ __forceinline__ void decode_chunk(const int4 code, int32_t (&wd)[16])
+{
+    const uint32_t w[4] = {uint32_t(code.x), uint32_t(code.y), uint32_t(code.z), uint32_t(code.w)};
+#pragma unroll
+    for (int q = 0; q < 4; q++)
+#pragma unroll
+        for (int m = 0; m < 4; m++) wd[4 * q + m] = lut4((w[q] >> (2 * m)) & kCodeMask);
+}
+
+template <int P>
+__device__ __forceinline__ void dec_dot(const int32_t (&wd)[16], const int4 (&dg)[P][4], int32_t (&acc)[P])
+{
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+            acc[p] = __builtin_amdgcn_sdot4(wd[4 * q + 0], dg[p][q].x, acc[p], false);
+            acc[p] = __builtin_amdgcn_sdot4(wd[4 * q + 1], dg[p][q].y, acc[p], false);
+            acc[p] = __builtin_amdgcn_sdot4(wd[4 * q + 2], dg[p][q].z, acc[p], false);
+            acc[p] = __builtin_amdgcn_sdot4(wd[4 * q + 3], dg[p][q].w, acc[p], false);
+        }
+    }
+}
+
 // Integer sum over the `lanes` consecutive lanes that share one row of weights (lanes a power of
 // two <= 64); every lane of the group receives the total (integer sums: any order is exact).
 template <int P>

@@ -45,8 +45,8 @@ tw_status check_layer(const tw_moe_layer *L)
     if (!L->w_router || !L->w_gate || !L->w_up || !L->w_down || !L->s_gate || !L->s_up ||
         !L->s_down)
         return TW_E_NULL;
-    // packed rows are read 16 bytes at a time
-    if (((uintptr_t)L->w_gate | (uintptr_t)L->w_up | (uintptr_t)L->w_down) & 15)
+    // packed rows and router rows are read 16 bytes at a time
+    if (((uintptr_t)L->w_gate | (uintptr_t)L->w_up | (uintptr_t)L->w_down | (uintptr_t)L->w_router) & 15)
         return TW_E_UNSUPPORTED;
     return TW_OK;
 }
@@ -122,6 +122,7 @@ tw_status moe_route_topk(const void *x, int32_t x_dtype, const void *w_router, i
     if (pre_rmsnorm != 0 && pre_rmsnorm != 1) return TW_E_SHAPE;
     if (n_tokens == 0) return TW_OK;
     if (!x || !w_router || !logits || !expert_ids || !gate_w) return TW_E_NULL;
+    if (((uintptr_t)x | (uintptr_t)w_router) & 15) return TW_E_UNSUPPORTED;   // 16-byte loads
     size_t T = size_t(n_tokens);
     size_t nl = T * n_experts * 4, nk = T * top_k * 4;
     if (overlap(logits, nl, expert_ids, nk) || overlap(logits, nl, gate_w, nk) ||
@@ -201,6 +202,7 @@ tw_status ternary_moe_ffn_batched(const tw_moe_layer *layer, int64_t n_tokens, c
     if (n_tokens > (int64_t(1) << 24)) return TW_E_UNSUPPORTED;
     if (n_tokens == 0) return TW_OK;
     if (!x_in || !x_out || !workspace) return TW_E_NULL;
+    if ((uintptr_t)x_in & 15) return TW_E_UNSUPPORTED;   // the router reads 16-byte chunks
     tw::Dims dm = dims_of(layer);
     int planes = act == TW_ACT_INT8 ? 1 : 3;
     size_t need = tw::batched_ws_layout(dm, n_tokens, planes).total;

@@ -56,8 +56,17 @@ inline DecodeWs decode_ws_layout(const Dims &dm) {
 
 // ---- batched workspace ------------------------------------------------------------------------
 struct BatchedWs {
-    size_t ctrl, logits, ids, gates, tinfo, xdig, counts, offsets, pairs, h, y, total;
+    size_t ctrl, logits, ids, gates, tinfo, xdig, counts, offsets, pairs, tiles, h, y, total;
 };
+constexpr int kTileTokens = 64;     // tokens per tile: large tiles (many tokens per expert)
+constexpr int kSmallTile = 16;      // tokens per tile: small tiles (few tokens per expert)
+// Upper bound on the (expert, tile) work items of T tokens in tiles of `tt` tokens, rounded up to a
+// multiple of 8.
+inline int64_t max_tiles(const Dims &dm, int64_t T, int tt)
+{
+    const int64_t n = (T * dm.k + tt - 1) / tt + dm.E;
+    return (n + 7) / 8 * 8;
+}
 inline BatchedWs batched_ws_layout(const Dims &dm, int64_t T, int planes) {
     BatchedWs w{};
     size_t o = 0;
@@ -71,6 +80,7 @@ inline BatchedWs batched_ws_layout(const Dims &dm, int64_t T, int planes) {
     w.counts = o;  o += align256(sizeof(int32_t) * (dm.E + 1));
     w.offsets = o; o += align256(sizeof(int32_t) * (dm.E + 1));
     w.pairs = o;   o += align256(sizeof(int32_t) * pairs);
+    w.tiles = o;   o += align256(sizeof(int32_t) * size_t(max_tiles(dm, T, kSmallTile) + 16));
     w.h = o;       o += align256(sizeof(float) * pairs * dm.F);
     w.y = o;       o += align256(sizeof(float) * pairs * dm.d);
     w.total = o;
@@ -88,6 +98,12 @@ int launch_decode_persist(const Dims &dm, const LayerPtrs *layers, int n_layers,
                           void *x_out, int io_bf16, void *ws, void *stream);
 int launch_decode(const Dims &dm, const LayerPtrs *layers, int n_layers, const void *x_in,
                   void *x_out, int io_bf16, void *ws, void *stream);
+// Grouped MFMA path of the batched FFN (after quantisation/digit planes and grouping into tiles of
+// `tile` tokens): planes = 1 (int8 activations) or 2, 3 (float digit planes).
+int launch_grouped_mfma(const Dims &dm, const LayerPtrs &layer, int64_t T, int planes, int tile,
+                        const BatchedWs &L, uint8_t *ws, void *stream);
+// Whether that path serves this shape; *tile receives the tile size to group with.
+bool grouped_mfma_serves(const Dims &dm, int64_t T, int planes, int *tile);
 int launch_batched(const Dims &dm, const LayerPtrs &layer, int64_t T, const void *x_in,
                    int in_bf16, void *x_out, int out_bf16, int int8_act, const int32_t *ids,
                    const float *gates, void *ws, void *stream);

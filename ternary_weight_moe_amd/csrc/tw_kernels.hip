@@ -66,24 +66,86 @@ __global__ void k_pack_any(const int8_t *__restrict__ w, int64_t rows, int64_t c
 }
 
 // ------------------------------------------------------------------------------------------------
-// Router logits for T tokens: one wave per (token, expert), fp32 sums.  Also the pre-RMSNorm
-// factor of the token, folded in as a scalar: W_r (x / rms) = (W_r x) / rms.
+// Router logits for T tokens: one workgroup of 256 threads per expert.  Thread t holds the expert's
+// router chunks t, t+256 (8 elements each) in registers and, for each token, adds its chunks'
+// products in order; the 256 partials are summed by wave_sum per wave and then (w0+w1)+(w2+w3): the
+// canonical order of canon_dot.  The pre-RMSNorm factor comes from the token's sum of squares in
+// the same order, folded in as a scalar: W_r (x / rms) = (W_r x) / rms.
+constexpr int kRouteTok = 8;   // tokens per workgroup of the router
 
-__global__ __launch_bounds__(256) void k_router_logits(const void *__restrict__ x, int x_bf16,
+// The 8 activations of chunk c of row `row` (bf16 or fp32), as fp32.
+__device__ __forceinline__ void load_chunk8(const void *x, int64_t row, int d, int c, int bf16, float (&v)[8])
+{
+    if (bf16) {
+        const int4 q = reinterpret_cast<const int4 *>(static_cast<const uint16_t *>(x) + row * d)[c];
+        const uint32_t w[4] = {uint32_t(q.x), uint32_t(q.y), uint32_t(q.z), uint32_t(q.w)};
+#pragma unroll
+        for (int j = 0; j < 8; j++) v[j] = bf16_to_f32(uint16_t(w[j >> 1] >> (16 * (j & 1))));
+    } else {
+        const int4 *p = reinterpret_cast<const int4 *>(static_cast<const float *>(x) + row * d) + 2 * c;
+        const int4 a = p[0], b = p[1];
+        v[0] = __int_as_float(a.x); v[1] = __int_as_float(a.y); v[2] = __int_as_float(a.z); v[3] = __int_as_float(a.w);
+        v[4] = __int_as_float(b.x); v[5] = __int_as_float(b.y); v[6] = __int_as_float(b.z); v[7] = __int_as_float(b.w);
+    }
+}
+
+// Workgroup (expert e, tokens 8 g .. 8 g + 7): all loads of the workgroup are issued at once.
+__global__ __launch_bounds__(256) void k_route_experts(const void *__restrict__ x, int x_bf16,
                                                        const void *__restrict__ wr, int w_bf16,
                                                        int64_t T, int d, int E, int pre_norm,
                                                        float *__restrict__ logits)
 {
-    const int lane = threadIdx.x & 63;
-    const int64_t gw = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (gw >= T * E) return;
-    const int64_t t = gw / E;
-    const int e = int(gw % E);
-    const int64_t xo = t * d;
-    auto xv = [&](int i) { return load_act(x, xo + i, x_bf16); };
-    float acc = canon_dot(d, lane, [&](int i) { return load_act(wr, int64_t(e) * d + i, w_bf16); }, xv);
-    if (pre_norm) acc = acc * inv_rms_of(canon_dot(d, lane, xv, xv), d);
-    if (lane == 0) logits[t * E + e] = acc;
+    const int e = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t tb = int64_t(blockIdx.y) * kRouteTok;
+    const int nt = int(T - tb < kRouteTok ? T - tb : kRouteTok);
+    const int nch = d >> 3;
+    float wv[2][8], xv[kRouteTok][2][8];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int c = t + 256 * i;
+        if (c < nch) {
+            load_chunk8(wr, e, d, c, w_bf16, wv[i]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; j++) wv[i][j] = 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kRouteTok; u++) {
+            if (u < nt && c < nch) {
+                load_chunk8(x, tb + u, d, c, x_bf16, xv[u][i]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; q++) xv[u][i][q] = 0.0f;
+            }
+        }
+    }
+    __shared__ float red[4][2][kRouteTok];
+#pragma unroll
+    for (int u = 0; u < kRouteTok; u++) {
+        float dot = 0.0f, ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            if (t + 256 * i < nch) {
+#pragma unroll
+                for (int q = 0; q < 8; q++) {
+                    dot = dot + wv[i][q] * xv[u][i][q];
+                    ss = ss + xv[u][i][q] * xv[u][i][q];
+                }
+            }
+        }
+        dot = wave_sum(dot);
+        if (pre_norm) ss = wave_sum(ss);
+        if (lane == 0) {
+            red[wave][0][u] = dot;
+            red[wave][1][u] = ss;
+        }
+    }
+    __syncthreads();
+    if (t < nt) {
+        float v = (red[0][0][t] + red[1][0][t]) + (red[2][0][t] + red[3][0][t]);
+        if (pre_norm) v = v * inv_rms_of((red[0][1][t] + red[1][1][t]) + (red[2][1][t] + red[3][1][t]), d);
+        logits[(tb + t) * E + e] = v;
+    }
 }
 
 __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, int64_t T, int E,
@@ -324,173 +386,334 @@ __global__ __launch_bounds__(64) void k_bat_quant_x(BatchedArgs a, const void *_
     }
 }
 
-// Counting sort of the T*k (token, slot) pairs by expert, stable in pair index: one block, one
-// thread per expert scanning all pairs in order.
+// Groups the T*k (token, slot) pairs by expert: counts[e], offsets[E+1] and pairs[] (the pairs of
+// expert e at offsets[e]..offsets[e+1]; their order inside a group is not fixed, and no result
+// depends on it: every pair is computed on its own), plus the list of (expert, tile of tt tokens)
+// work items: tiles[0] = their number, tiles[1 + i] = e | (tile << 10).
+// One workgroup of 1024 threads; counts and placement use LDS atomics.
 __global__ __launch_bounds__(1024) void k_group(BatchedArgs a, const int32_t *__restrict__ ids,
-                                                uint8_t *__restrict__ ws)
+                                                uint8_t *__restrict__ ws, int tt)
 {
-    const int E = a.dm.E;
+    const int E = a.dm.E, t = threadIdx.x;
     const int64_t npairs = a.T * a.dm.k;
     int32_t *counts = reinterpret_cast<int32_t *>(ws + a.L.counts);
     int32_t *offsets = reinterpret_cast<int32_t *>(ws + a.L.offsets);
     int32_t *pairs = reinterpret_cast<int32_t *>(ws + a.L.pairs);
-    __shared__ int32_t cnt[kMaxExperts + 1];
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        int32_t c = 0;
-        for (int64_t p = 0; p < npairs; p++) c += ids[p] == e;
-        cnt[e] = c;
+    int32_t *tiles = reinterpret_cast<int32_t *>(ws + a.L.tiles);
+    __shared__ int32_t cnt[kMaxExperts], cur[kMaxExperts], scan[1024], tscan[1024];
+    for (int e = t; e < E; e += 1024) cnt[e] = 0;
+    __syncthreads();
+    for (int64_t p = t; p < npairs; p += 1024) {
+        const int id = ids[p];
+        if (id >= 0 && id < E) atomicAdd(&cnt[id], 1);
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int32_t run = 0;
-        for (int e = 0; e < E; e++) {
-            offsets[e] = run;
-            counts[e] = cnt[e];
-            run += cnt[e];
-        }
-        offsets[E] = run;
+    const int c = t < E ? cnt[t] : 0;
+    const int nt = (c + tt - 1) / tt;
+    scan[t] = c;
+    tscan[t] = nt;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {   // inclusive scans (Hillis-Steele)
+        const int x = t >= off ? scan[t - off] : 0, y = t >= off ? tscan[t - off] : 0;
+        __syncthreads();
+        scan[t] += x;
+        tscan[t] += y;
+        __syncthreads();
+    }
+    const int off_e = scan[t] - c, tile0 = tscan[t] - nt;
+    if (t < E) {
+        counts[t] = c;
+        offsets[t] = off_e;
+        cur[t] = off_e;
+        for (int i = 0; i < nt; i++) tiles[1 + tile0 + i] = t | (i << 10);
+    }
+    if (t == 1023) {
+        offsets[E] = scan[1023];
+        tiles[0] = tscan[1023];
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        int32_t pos = offsets[e];
-        for (int64_t p = 0; p < npairs; p++)
-            if (ids[p] == e) pairs[pos++] = int32_t(p);
+    for (int64_t p = t; p < npairs; p += 1024) {
+        const int id = ids[p];
+        if (id >= 0 && id < E) pairs[atomicAdd(&cur[id], 1)] = int32_t(p);
     }
 }
 
-// Gate/up rows of one expert for all its tokens: block = (expert, block of 16 rows).
-template <int P, bool INT8>
-__global__ __launch_bounds__(256) void k_bat_gateup(BatchedArgs a, LayerPtrs lp,
-                                                    uint8_t *__restrict__ ws)
+// Batched gate/up and down.  Work items are (expert tile, row block) -- a tile is up to 64 of an
+// expert's tokens (k_group) and a row block is 16 h rows (gate/up: 32 code rows of d/4 bytes) or
+// 64 output rows (down: 64 code rows of F/4 bytes).  A grid of kBatG workgroups walks the items
+// in expert-major order, each workgroup a contiguous range: the code rows of its next item are
+// requested before the current item is computed (latency hidden behind the dots), and the
+// activation digits of a tile are staged in LDS once for all of the tile's row blocks.  Each code
+// byte is read once per call.
+constexpr int kBatTok = 16;    // at most this many tokens staged per round
+constexpr int kBatG = 512;     // workgroups of the gate/up and down grids
+// Tokens per round such that their staged digit planes fit in 64 KiB of LDS.
+inline int tokens_per_round(int bytes_per_token)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = 65536 / bytes_per_token;
+    return n < 1 ? 1 : (n > kBatTok ? kBatTok : n);
+}
+
+// Item metadata of a tile: expert, its tokens in the tile, first pair position.
+struct BatTile {
+    int e, ntok, p0;
+};
+
+__device__ __forceinline__ BatTile bat_tile(const int32_t *tiles, const int32_t *counts,
+                                            const int32_t *offsets, int ti)
+{
+    const int tl = tiles[1 + ti], e = tl & 1023, mt = tl >> 10;
+    const int n = counts[e] - mt * kTileTokens;
+    return BatTile{e, n < kTileTokens ? n : kTileTokens, offsets[e] + mt * kTileTokens};
+}
+
+// NP: passes of code rows per item (>= rows * (cols / 64) / 256).
+template <int P, bool INT8, int NP>
+__global__ __launch_bounds__(256) void k_bat_gu(BatchedArgs a, LayerPtrs lp, uint8_t *__restrict__ ws,
+                                                int tpr)
+{
+    extern __shared__ __attribute__((aligned(16))) int8_t smem[];   // [tpr][P][d]
+    __shared__ float sums[kBatTok][32];
+    __shared__ int32_t s_pair[kBatTok];
+    __shared__ float s_tok[kBatTok][2];   // per token: s_x (int8) or digit shift bits, 1/rms
+    const int t = threadIdx.x;
     const int d = a.dm.d, F = a.dm.F, k = a.dm.k;
-    const int nrb = F / kDecRowsGU;
-    const int e = blockIdx.x / nrb, rb = blockIdx.x % nrb;
+    const int nrb = F / 16;
+    const int32_t *tiles = reinterpret_cast<const int32_t *>(ws + a.L.tiles);
+    const int32_t *counts = reinterpret_cast<const int32_t *>(ws + a.L.counts);
     const int32_t *offsets = reinterpret_cast<const int32_t *>(ws + a.L.offsets);
     const int32_t *pairs = reinterpret_cast<const int32_t *>(ws + a.L.pairs);
-    const int p0 = offsets[e], p1 = offsets[e + 1];
-    if (p0 == p1) return;
-    const int lpr = d >> 6, rpp = 64 / lpr;
-    const int sub = lane / lpr, c = lane % lpr;
-    const int njobs = 2 * kDecRowsGU;
-    const int64_t rstride = d / 4;
     const int8_t *xdig = reinterpret_cast<const int8_t *>(ws + a.L.xdig);
     const float *tinfo = reinterpret_cast<const float *>(ws + a.L.tinfo);
     float *hbuf = reinterpret_cast<float *>(ws + a.L.h);
-    __shared__ float sums[2 * kDecRowsGU];
-    for (int pi = p0; pi < p1; pi++) {
-        const int pair = pairs[pi];
-        const int64_t t = pair / k;
-        const int8_t *xd = xdig + t * int64_t(P) * d;
-        int4 dg[P][4];
+    const int nitems = tiles[0] * nrb;
+    const int i0 = int(int64_t(blockIdx.x) * nitems / gridDim.x);
+    const int i1 = int(int64_t(blockIdx.x + 1) * nitems / gridDim.x);
+    if (i0 >= i1) return;
+    const int lpr = d >> 6, rpp = 256 / lpr, c = t % lpr;
+    const int npass = (32 + rpp - 1) / rpp;
+    // code rows of item `it` (clamped into the block's range: loads are unconditional, so the
+    // compiler can count them and wait only for the ones it needs)
+    int ld_ti = -1, ld_e = 0;
+    auto load = [&](int it, int4 (&code)[NP], float (&sc)[NP]) {
+        it = it < i1 ? it : i1 - 1;
+        const int ti = it / nrb;
+        if (ti != ld_ti) {
+            ld_ti = ti;
+            ld_e = tiles[1 + ti] & 1023;
+        }
+        const int r0 = (it % nrb) * 16;
 #pragma unroll
-        for (int p = 0; p < P; p++)
+        for (int p = 0; p < NP; p++) {
+            const int jb = p * rpp + t / lpr;
+            const bool valid = p < npass && jb < 32;
+            const int i = valid ? (jb >> 1) : 0, kind = jb & 1;
+            const int64_t row = int64_t(ld_e) * F + r0 + i;
+            const int4 v = reinterpret_cast<const int4 *>((kind ? lp.w_up : lp.w_gate) + row * (d / 4))[c];
+            const float sv = (kind ? lp.s_up : lp.s_gate)[row];
+            code[p] = valid ? v : make_int4(0, 0, 0, 0);
+            sc[p] = valid ? sv : 0.0f;
+        }
+    };
+    int cur_ti = -1, staged = -1;
+    BatTile tl{0, 0, 0};
+    auto process = [&](int it, const int4 (&code)[NP], const float (&sc)[NP]) {
+        const int ti = it / nrb, r0 = (it % nrb) * 16;
+        if (ti != cur_ti) {
+            cur_ti = ti;
+            tl = bat_tile(tiles, counts, offsets, ti);
+        }
+        int32_t wd[NP][16];
 #pragma unroll
-            for (int q = 0; q < 4; q++) dg[p][q] = reinterpret_cast<const int4 *>(xd + p * d + c * 64)[q];
-        for (int base = wave * rpp; base < njobs; base += 4 * rpp) {
-            const int job = base + sub;
-            const bool valid = job < njobs;
-            const int rl = job % kDecRowsGU;
-            const bool up = job >= kDecRowsGU;
-            const int r = rb * kDecRowsGU + rl;
-            const uint8_t *row = (up ? lp.w_up : lp.w_gate) + (int64_t(e) * F + r) * rstride;
-            const int4 code = valid ? reinterpret_cast<const int4 *>(row)[c] : make_int4(0, 0, 0, 0);
-            int32_t acc[P] = {};
-            chunk_dot<P>(code, dg, acc);
-            group_reduce<P>(acc, lpr);
-            if (c == 0 && valid) {
-                const float s = (up ? lp.s_up : lp.s_gate)[int64_t(e) * F + r];
-                float v;
-                if (INT8)
-                    v = (float(acc[0]) * tinfo[2 * t]) * s;
-                else
-                    v = float_value<P>(acc, reinterpret_cast<const int32_t *>(tinfo)[2 * t]) * s *
-                        tinfo[2 * t + 1];
-                sums[job] = v;
+        for (int p = 0; p < NP; p++) decode_chunk(code[p], wd[p]);
+        for (int tb = 0; tb < tl.ntok; tb += tpr) {
+            const int nt = tl.ntok - tb < tpr ? tl.ntok - tb : tpr;
+            if (!(staged == ti && tb == 0)) {
+                __syncthreads();
+                if (t < nt) {
+                    const int pr = pairs[tl.p0 + tb + t];
+                    s_pair[t] = pr;
+                    s_tok[t][0] = tinfo[2 * (pr / k)];
+                    s_tok[t][1] = tinfo[2 * (pr / k) + 1];
+                }
+                __syncthreads();
+                const int cpt = P * d / 16;   // 16-byte chunks per token
+                for (int idx = t; idx < nt * cpt; idx += 256) {
+                    const int j = idx / cpt, r = idx % cpt;
+                    const int64_t tok = s_pair[j] / k;
+                    reinterpret_cast<int4 *>(smem + j * P * d)[r] =
+                        reinterpret_cast<const int4 *>(xdig + tok * P * d)[r];
+                }
+                __syncthreads();
+                staged = tl.ntok <= tpr ? ti : -1;
             }
+            for (int j = 0; j < nt; j++) {
+                int4 dg[P][4];
+#pragma unroll
+                for (int pl = 0; pl < P; pl++)
+#pragma unroll
+                    for (int q = 0; q < 4; q++)
+                        dg[pl][q] = reinterpret_cast<const int4 *>(smem + (j * P + pl) * d + c * 64)[q];
+#pragma unroll
+                for (int p = 0; p < NP; p++) {
+                    if (p < npass) {
+                        const int jb = p * rpp + t / lpr;
+                        int32_t acc[P] = {};
+                        dec_dot<P>(wd[p], dg, acc);
+                        group_reduce<P>(acc, lpr);
+                        if (c == 0 && jb < 32) {
+                            float v;
+                            if (INT8)
+                                v = (float(acc[0]) * s_tok[j][0]) * sc[p];
+                            else
+                                v = float_value<P>(acc, __float_as_int(s_tok[j][0])) * sc[p] * s_tok[j][1];
+                            sums[j][jb] = v;
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            for (int idx = t; idx < nt * 16; idx += 256) {
+                const int j = idx >> 4, i = idx & 15;
+                hbuf[int64_t(s_pair[j]) * F + r0 + i] = tw_silu(sums[j][2 * i]) * sums[j][2 * i + 1];
+            }
+            __syncthreads();
         }
-        __syncthreads();
-        if (threadIdx.x < kDecRowsGU) {
-            const int tt = threadIdx.x;
-            const float g = sums[tt], u = sums[kDecRowsGU + tt];
-            hbuf[int64_t(pair) * F + rb * kDecRowsGU + tt] = tw_silu(g) * u;
-        }
-        __syncthreads();
+    };
+    int4 ca[NP], cb[NP];
+    float sa[NP], sb[NP];
+    load(i0, ca, sa);
+    for (int it = i0; it < i1; it += 2) {
+        load(it + 1, cb, sb);
+        process(it, ca, sa);
+        if (it + 1 >= i1) break;
+        load(it + 2, ca, sa);
+        process(it + 1, cb, sb);
     }
 }
 
-// Down rows of one expert for all its tokens (block = expert, block of 8 rows); h of each pair is
-// turned into digit planes in shared memory first (int8 mode: per (token, expert) absmax).
-template <int P, bool INT8>
-__global__ __launch_bounds__(256) void k_bat_down(BatchedArgs a, LayerPtrs lp,
-                                                  uint8_t *__restrict__ ws)
+// Down: item = (expert tile, 64 output rows); per token round, the tokens' h vectors become digit
+// planes in LDS (per (token, expert) maximum: int8 absmax, or the float fixed-point shift) once
+// per tile when all of its tokens fit, then every token's dots run against the item's codes.
+template <int P, bool INT8, int NP>
+__global__ __launch_bounds__(256) void k_bat_dn(BatchedArgs a, LayerPtrs lp, uint8_t *__restrict__ ws,
+                                                int tpr)
 {
-    extern __shared__ __attribute__((aligned(16))) int8_t smem[];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    extern __shared__ __attribute__((aligned(16))) int8_t smem[];   // [tpr][P][F] digits
+    __shared__ int32_t s_pair[kBatTok];
+    __shared__ float s_hs[kBatTok];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int d = a.dm.d, F = a.dm.F;
-    const int nrb = d / kDecRowsDown;
-    const int e = blockIdx.x / nrb, rb = blockIdx.x % nrb;
+    const int nrb = d / 64;
+    const int32_t *tiles = reinterpret_cast<const int32_t *>(ws + a.L.tiles);
+    const int32_t *counts = reinterpret_cast<const int32_t *>(ws + a.L.counts);
     const int32_t *offsets = reinterpret_cast<const int32_t *>(ws + a.L.offsets);
     const int32_t *pairs = reinterpret_cast<const int32_t *>(ws + a.L.pairs);
-    const int p0 = offsets[e], p1 = offsets[e + 1];
-    if (p0 == p1) return;
     const float *hbuf = reinterpret_cast<const float *>(ws + a.L.h);
     float *ybuf = reinterpret_cast<float *>(ws + a.L.y);
-    int8_t *hd = smem;                                          // [P][F]
-    float *hs = reinterpret_cast<float *>(smem + P * F);        // [1] scale / shift
-    const int lpr = F >> 6, rpp = 64 / lpr;
-    const int sub = lane / lpr, c = lane % lpr;
-    const int njobs = kDecRowsDown;
-    const int64_t rstride = F / 4;
-    for (int pi = p0; pi < p1; pi++) {
-        const int pair = pairs[pi];
-        const float *h = hbuf + int64_t(pair) * F;
-        if (wave == 0) {
-            float am = 0.0f;
-            for (int i = lane; i < F; i += 64) am = fmaxf(am, fabsf(h[i]));
-            am = wave_max(am);
-            if (INT8) {
-                const float inv = am > 0.0f ? 127.0f / am : 0.0f;
-                for (int i = lane; i < F; i += 64) hd[perm16(i)] = am > 0.0f ? int8_quant(h[i], inv) : int8_t(0);
-                if (lane == 0) hs[0] = am > 0.0f ? am / 127.0f : 0.0f;
-            } else {
-                const int sh = float_digit_shift(am, P);
-                for (int i = lane; i < F; i += 64) {
-                    int8_t dg[P];
-                    float_digits<P>(h[i], sh, dg);
+    const int nitems = tiles[0] * nrb;
+    const int i0 = int(int64_t(blockIdx.x) * nitems / gridDim.x);
+    const int i1 = int(int64_t(blockIdx.x + 1) * nitems / gridDim.x);
+    if (i0 >= i1) return;
+    const int lpr = F >> 6, rpp = 256 / lpr, c = t % lpr;
+    const int npass = (64 + rpp - 1) / rpp;
+    int ld_ti = -1, ld_e = 0;
+    auto load = [&](int it, int4 (&code)[NP], float (&sc)[NP]) {
+        it = it < i1 ? it : i1 - 1;
+        const int ti = it / nrb;
+        if (ti != ld_ti) {
+            ld_ti = ti;
+            ld_e = tiles[1 + ti] & 1023;
+        }
+        const int r0 = (it % nrb) * 64;
 #pragma unroll
-                    for (int p = 0; p < P; p++) hd[p * F + perm16(i)] = dg[p];
+        for (int p = 0; p < NP; p++) {
+            const int jd = p * rpp + t / lpr;
+            const bool valid = p < npass && jd < 64;
+            const int64_t row = int64_t(ld_e) * d + r0 + (valid ? jd : 0);
+            const int4 v = reinterpret_cast<const int4 *>(lp.w_down + row * (F / 4))[c];
+            const float sv = lp.s_down[row];
+            code[p] = valid ? v : make_int4(0, 0, 0, 0);
+            sc[p] = valid ? sv : 0.0f;
+        }
+    };
+    int cur_ti = -1, staged = -1;
+    BatTile tl{0, 0, 0};
+    auto process = [&](int it, const int4 (&code)[NP], const float (&sc)[NP]) {
+        const int ti = it / nrb, r0 = (it % nrb) * 64;
+        if (ti != cur_ti) {
+            cur_ti = ti;
+            tl = bat_tile(tiles, counts, offsets, ti);
+        }
+        int32_t wd[NP][16];
+#pragma unroll
+        for (int p = 0; p < NP; p++) decode_chunk(code[p], wd[p]);
+        for (int tb = 0; tb < tl.ntok; tb += tpr) {
+            const int nt = tl.ntok - tb < tpr ? tl.ntok - tb : tpr;
+            if (!(staged == ti && tb == 0)) {
+                __syncthreads();
+                if (t < nt) s_pair[t] = pairs[tl.p0 + tb + t];
+                __syncthreads();
+                for (int j = wave; j < nt; j += 4) {
+                    const float *h = hbuf + int64_t(s_pair[j]) * F;
+                    float am = 0.0f;
+                    for (int i = lane; i < F; i += 64) am = fmaxf(am, fabsf(h[i]));
+                    am = wave_max(am);
+                    int8_t *hd = smem + j * P * F;
+                    if (INT8) {
+                        const float inv = am > 0.0f ? 127.0f / am : 0.0f;
+                        for (int i = lane; i < F; i += 64) hd[perm16(i)] = am > 0.0f ? int8_quant(h[i], inv) : int8_t(0);
+                        if (lane == 0) s_hs[j] = am > 0.0f ? am / 127.0f : 0.0f;
+                    } else {
+                        const int sh = float_digit_shift(am, P);
+                        for (int i = lane; i < F; i += 64) {
+                            int8_t dg[P];
+                            float_digits<P>(h[i], sh, dg);
+#pragma unroll
+                            for (int pl = 0; pl < P; pl++) hd[pl * F + perm16(i)] = dg[pl];
+                        }
+                        if (lane == 0) reinterpret_cast<int32_t *>(s_hs)[j] = sh;
+                    }
                 }
-                if (lane == 0) reinterpret_cast<int32_t *>(hs)[0] = sh;
+                __syncthreads();
+                staged = tl.ntok <= tpr ? ti : -1;
+            }
+            for (int j = 0; j < nt; j++) {
+                int4 dh[P][4];
+#pragma unroll
+                for (int pl = 0; pl < P; pl++)
+#pragma unroll
+                    for (int q = 0; q < 4; q++)
+                        dh[pl][q] = reinterpret_cast<const int4 *>(smem + (j * P + pl) * F + c * 64)[q];
+#pragma unroll
+                for (int p = 0; p < NP; p++) {
+                    if (p < npass) {
+                        const int jd = p * rpp + t / lpr;
+                        int32_t acc[P] = {};
+                        dec_dot<P>(wd[p], dh, acc);
+                        group_reduce<P>(acc, lpr);
+                        if (c == 0 && jd < 64) {
+                            float v;
+                            if (INT8)
+                                v = (float(acc[0]) * s_hs[j]) * sc[p];
+                            else
+                                v = float_value<P>(acc, reinterpret_cast<const int32_t *>(s_hs)[j]) * sc[p];
+                            ybuf[int64_t(s_pair[j]) * d + r0 + jd] = v;
+                        }
+                    }
+                }
             }
         }
-        __syncthreads();
-        for (int base = wave * rpp; base < njobs; base += 4 * rpp) {
-            const int job = base + sub;
-            const bool valid = job < njobs;
-            const int r = rb * kDecRowsDown + (valid ? job : 0);
-            const uint8_t *row = lp.w_down + (int64_t(e) * d + r) * rstride;
-            const int4 code = valid ? reinterpret_cast<const int4 *>(row)[c] : make_int4(0, 0, 0, 0);
-            int4 dg[P][4];
-#pragma unroll
-            for (int p = 0; p < P; p++)
-#pragma unroll
-                for (int q = 0; q < 4; q++) dg[p][q] = reinterpret_cast<const int4 *>(hd + p * F + c * 64)[q];
-            int32_t acc[P] = {};
-            chunk_dot<P>(code, dg, acc);
-            group_reduce<P>(acc, lpr);
-            if (c == 0 && valid) {
-                const float s = lp.s_down[int64_t(e) * d + r];
-                float v;
-                if (INT8)
-                    v = (float(acc[0]) * hs[0]) * s;
-                else
-                    v = float_value<P>(acc, reinterpret_cast<const int32_t *>(hs)[0]) * s;
-                ybuf[int64_t(pair) * d + r] = v;
-            }
-        }
-        __syncthreads();
+    };
+    int4 ca[NP], cb[NP];
+    float sa[NP], sb[NP];
+    load(i0, ca, sa);
+    for (int it = i0; it < i1; it += 2) {
+        load(it + 1, cb, sb);
+        process(it, ca, sa);
+        if (it + 1 >= i1) break;
+        load(it + 2, ca, sa);
+        process(it + 1, cb, sb);
     }
 }
 
@@ -556,18 +779,34 @@ int batched_p(const Dims &dm, const LayerPtrs &lp, int64_t T, const void *x_in, 
         float *logits = reinterpret_cast<float *>(w + a.L.logits);
         int32_t *wid = reinterpret_cast<int32_t *>(w + a.L.ids);
         float *wg = reinterpret_cast<float *>(w + a.L.gates);
-        const int64_t waves = T * dm.E;
-        k_router_logits<<<unsigned((waves + 3) / 4), 256, 0, S(stream)>>>(
-            x_in, in_bf16, lp.w_router, dm.router_bf16, T, dm.d, dm.E, dm.pre_norm, logits);
+        k_route_experts<<<dim3(unsigned(dm.E), unsigned((T + kRouteTok - 1) / kRouteTok)), 256, 0,
+                          S(stream)>>>(x_in, in_bf16, lp.w_router, dm.router_bf16, T, dm.d, dm.E,
+                                       dm.pre_norm, logits);
         k_topk<<<unsigned((T + 3) / 4), 256, 0, S(stream)>>>(logits, T, dm.E, dm.k, wid, wg);
         ids = wid;
         gates = wg;
     }
     k_bat_quant_x<P, INT8><<<unsigned(T), 64, 0, S(stream)>>>(a, x_in, in_bf16, w);
-    k_group<<<1, 1024, 0, S(stream)>>>(a, ids, w);
-    k_bat_gateup<P, INT8><<<dm.E * (dm.F / kDecRowsGU), 256, 0, S(stream)>>>(a, lp, w);
-    const size_t smem_down = size_t(P) * dm.F + 16;
-    k_bat_down<P, INT8><<<dm.E * (dm.d / kDecRowsDown), 256, smem_down, S(stream)>>>(a, lp, w);
+    int tile = kTileTokens;
+    if (grouped_mfma_serves(dm, T, P, &tile)) {
+        k_group<<<1, 1024, 0, S(stream)>>>(a, ids, w, tile);
+        const int r = launch_grouped_mfma(dm, lp, T, P, tile, a.L, w, stream);
+        if (r != 0) return r;
+        const int64_t n = T * dm.d;
+        const unsigned nb = unsigned(n / 256 + 1 < 65536 ? n / 256 + 1 : 65536);
+        k_bat_combine<<<nb, 256, 0, S(stream)>>>(a, x_in, in_bf16, x_out, out_bf16, ids, gates, w);
+        return last_error();
+    }
+    k_group<<<1, 1024, 0, S(stream)>>>(a, ids, w, kTileTokens);
+    const int tg = tokens_per_round(P * dm.d), td = tokens_per_round(P * dm.F);
+    if (dm.d <= 2048)
+        k_bat_gu<P, INT8, 4><<<kBatG, 256, size_t(tg) * P * dm.d, S(stream)>>>(a, lp, w, tg);
+    else
+        k_bat_gu<P, INT8, 8><<<kBatG, 256, size_t(tg) * P * dm.d, S(stream)>>>(a, lp, w, tg);
+    if (dm.F <= 512)
+        k_bat_dn<P, INT8, 2><<<kBatG, 256, size_t(td) * P * dm.F, S(stream)>>>(a, lp, w, td);
+    else
+        k_bat_dn<P, INT8, 16><<<kBatG, 256, size_t(td) * P * dm.F, S(stream)>>>(a, lp, w, td);
     const int64_t n = T * dm.d;
     const unsigned nb = unsigned(n / 256 + 1 < 65536 ? n / 256 + 1 : 65536);
     k_bat_combine<<<nb, 256, 0, S(stream)>>>(a, x_in, in_bf16, x_out, out_bf16, ids, gates, w);
@@ -595,9 +834,8 @@ int launch_pack(const int8_t *w, int64_t rows, int64_t cols, uint8_t *packed, in
 int launch_route(const void *x, int x_bf16, const void *w_router, int w_bf16, int64_t T,
                  const Dims &dm, float *logits, int32_t *ids, float *gates, void *stream)
 {
-    const int64_t waves = T * dm.E;
-    k_router_logits<<<unsigned((waves + 3) / 4), 256, 0, S(stream)>>>(
-        x, x_bf16, w_router, w_bf16, T, dm.d, dm.E, dm.pre_norm, logits);
+    k_route_experts<<<dim3(unsigned(dm.E), unsigned((T + kRouteTok - 1) / kRouteTok)), 256, 0,
+                      S(stream)>>>(x, x_bf16, w_router, w_bf16, T, dm.d, dm.E, dm.pre_norm, logits);
     k_topk<<<unsigned((T + 3) / 4), 256, 0, S(stream)>>>(logits, T, dm.E, dm.k, ids, gates);
     return last_error();
 }

@@ -371,3 +371,30 @@ def test_batched_ragged_and_empty(small):
         oout, oids, og, olg = oracle.moe_layer(small.ora, x)
         for t in range(T):
             assert normwise(got[t], oout[t]) <= 1e-4, (T, t)
+
+
+def test_batched_shape_served_by_dot4_kernels():
+    # d=512, F=128 is not an instantiation of the grouped MFMA kernel: the per-pair v_dot4 kernels
+    # serve it (float and int8), checked against the oracle
+    wl = synth.NARROW_LAYER_B1
+    pair = make_pair(wl)
+    T = 40
+    x = synth.activations(wl, T, seed=83)
+    step("batched narrow float T=%d" % T)
+    out = tw.ternary_moe_ffn_batched(pair.gpu, x.cuda())
+    torch.cuda.synchronize()
+    got = to_np(out)
+    oout, oids, og, olg = oracle.moe_layer(pair.ora, x)
+    for t in range(T):
+        cands = [oout[t]] + [oracle.ffn_token(pair.ora, x[t].double().numpy(), sl, g)
+                             for sl, g in routing_alternatives(olg[t], oids[t], wl.top_k)[1:]]
+        errs = [normwise(got[t], c) for c in cands]
+        assert_bf16_close(got[t], cands[int(np.argmin(errs))], "token %d" % t)
+    step("batched narrow int8 T=%d" % T)
+    ids = torch.from_numpy(oids).cuda()
+    gates = torch.from_numpy(og.astype(np.float32)).cuda()
+    out8 = tw.ternary_moe_ffn_batched(pair.gpu, x.cuda(), act="int8", out_dtype=torch.float32,
+                                      expert_ids=ids, gate_w=gates)
+    torch.cuda.synchronize()
+    ref = oracle.ffn_batch_i8(pair.ora, x, oids, og.astype(np.float32), n_threads=8)
+    assert np.array_equal(out8.cpu().numpy().view(np.uint32), ref.view(np.uint32))

@@ -1,0 +1,114 @@
+"""Parity of the grouped int8 MFMA path (many tokens per expert, prefill-shaped) with the CPU
+oracle's int8 specification and with the per-pair v_dot4 path, bit for bit.  The int8 path is
+exact, so the three must agree in every bit of the fp32 output.  Routing is an input (computed by
+moe_route_topk on the GPU and handed to both sides)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import ternary_weight_moe_amd as tw
+from parity_util import make_pair, require_gpu, step
+
+pytestmark = pytest.mark.gpu
+
+NTH = min(16, os.cpu_count() or 1)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+@pytest.fixture(scope="module")
+def full():
+    step("build layer_b1 layer pair (full size) for the prefill tests")
+    return make_pair(synth.LAYER_B1)
+
+
+def run_int8(layer, x, ids, gates):
+    out = tw.ternary_moe_ffn_batched(layer, x, act="int8", out_dtype=torch.float32,
+                                     expert_ids=ids, gate_w=gates)
+    torch.cuda.synchronize()
+    return out
+
+
+def dot_path_in_chunks(layer, x, ids, gates, chunk=64):
+    """The same tokens through calls small enough to take the per-pair v_dot4 path."""
+    outs = [run_int8(layer, x[i:i + chunk].contiguous(), ids[i:i + chunk].contiguous(),
+                     gates[i:i + chunk].contiguous()) for i in range(0, x.shape[0], chunk)]
+    return torch.cat(outs)
+
+
+def bits(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def test_prefill_int8_matches_oracle_and_dot_path(full):
+    T = 256   # T*k = 8*E: the grouped MFMA path
+    x = synth.activations(synth.PREFILL_4096, T, seed=71).cuda()
+    _, ids, gates = tw.moe_route_topk(x, full.gpu.w_router, 8)
+    step("prefill int8 T=%d (MFMA path)" % T)
+    out = run_int8(full.gpu, x, ids, gates)
+    step("same tokens through the dot4 path")
+    ref_dot = dot_path_in_chunks(full.gpu, x, ids, gates)
+    assert np.array_equal(bits(out), bits(ref_dot))
+    step("oracle int8 spec, %d tokens, %d threads" % (T, NTH))
+    ref = oracle.ffn_batch_i8(full.ora, x.cpu(), ids.cpu().numpy(), gates.cpu().numpy(),
+                              n_threads=NTH)
+    assert np.array_equal(bits(out), ref.view(np.uint32))
+
+
+def test_prefill_int8_full_size(full):
+    # 4096 tokens, top-8 of 256 experts (~128 per expert): every output against the dot4 path,
+    # a sample of tokens against the oracle
+    T = 4096
+    x = synth.activations(synth.PREFILL_4096, T).cuda()
+    _, ids, gates = tw.moe_route_topk(x, full.gpu.w_router, 8)
+    step("prefill int8 T=4096 (MFMA path)")
+    out = run_int8(full.gpu, x, ids, gates)
+    step("4096 tokens through the dot4 path in 64-token calls")
+    ref_dot = dot_path_in_chunks(full.gpu, x, ids, gates)
+    assert np.array_equal(bits(out), bits(ref_dot))
+    sample = np.unique(np.concatenate([np.arange(0, T, 97), [1, 63, 64, T - 2, T - 1]]))
+    step("oracle int8 spec on %d sampled tokens" % len(sample))
+    ref = oracle.ffn_batch_i8(full.ora, x.cpu()[sample], ids.cpu().numpy()[sample],
+                              gates.cpu().numpy()[sample], n_threads=NTH)
+    assert np.array_equal(bits(out)[sample], ref.view(np.uint32))
+
+
+def test_prefill_int8_one_hot_experts_ragged_tiles(full):
+    # every token sends its 8 slots to the same 8 experts: 1000 tokens per expert, 15 full tiles
+    # of 64 and a 40-token tail each
+    T = 1000
+    x = synth.activations(synth.PREFILL_4096, T, seed=73).cuda()
+    ids = torch.tensor([3, 250, 17, 0, 128, 255, 64, 9], dtype=torch.int32).repeat(T, 1).cuda()
+    g = torch.rand((T, 8), generator=torch.Generator().manual_seed(5)) + 0.05
+    gates = (g / g.sum(1, keepdim=True)).float().contiguous().cuda()
+    step("prefill int8 adversarial routing T=1000")
+    out = run_int8(full.gpu, x, ids, gates)
+    ref_dot = dot_path_in_chunks(full.gpu, x, ids, gates)
+    assert np.array_equal(bits(out), bits(ref_dot))
+    sample = np.array([0, 1, 959, 960, 999])
+    ref = oracle.ffn_batch_i8(full.ora, x.cpu()[sample], ids.cpu().numpy()[sample],
+                              gates.cpu().numpy()[sample], n_threads=NTH)
+    assert np.array_equal(bits(out)[sample], ref.view(np.uint32))
+
+
+def test_prefill_int8_second_shape():
+    # d=1024, 64 experts, F=256, top-4: the second instantiation of the MFMA path
+    wl = synth.MID_STACK_B1
+    pair = make_pair(wl, pre=False)
+    T = 256
+    x = synth.activations(wl, T, seed=75).cuda()
+    _, ids, gates = tw.moe_route_topk(x, pair.gpu.w_router, wl.top_k)
+    step("prefill int8 mid shape T=%d" % T)
+    out = run_int8(pair.gpu, x, ids, gates)
+    ref = oracle.ffn_batch_i8(pair.ora, x.cpu(), ids.cpu().numpy(), gates.cpu().numpy(),
+                              n_threads=NTH)
+    assert np.array_equal(bits(out), ref.view(np.uint32))
+    ref_dot = dot_path_in_chunks(pair.gpu, x, ids, gates)
+    assert np.array_equal(bits(out), bits(ref_dot))
