@@ -34,7 +34,9 @@ import ternary_weight_moe_amd as tw  # noqa: E402
 from ternary_weight_moe_amd import accounting  # noqa: E402
 
 METRIC = "decode tok/s, 24-layer ternary MoE FFN stack, B=1; achieved HBM GB/s vs peak"
-KERNEL_SRC = os.path.join(ROOT, "ternary_weight_moe_amd", "csrc", "tw_kernels.hip")
+# sources of the kernel whose traffic counters are committed (the one-launch stacked decode)
+KERNEL_SRCS = [os.path.join(ROOT, "ternary_weight_moe_amd", "csrc", f)
+               for f in ("tw_persist.hip", "tw_device.h", "tw_internal.h")]
 
 
 def log(*a):
@@ -42,7 +44,10 @@ def log(*a):
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(workload: str):
@@ -226,6 +231,26 @@ def run_single_layer(args, name):
     )
 
 
+def run_copy_calib(args):
+    """A plain device-to-device copy of a known size (4 x 1 GiB), for scaling the FETCH_SIZE and
+    WRITE_SIZE hardware counters of the measured kernels."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    reps = 4
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    return dict(metric="device copy GB/s (read + write)", value=2 * n * reps / dt / 1e9, unit="GB/s",
+                n_gpus=1, steps=reps, warmup=0, ms_per_step=dt / reps * 1e3,
+                higher_is_better=True, scaling="weak", vs_baseline=None, dtype="u8",
+                data="synthetic", config=dict(workload="copy_calib", bytes_per_copy=n),
+                roofline=None, cpu_baseline=None)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,7 +259,7 @@ def main():
     ap.add_argument("--graph-steps", type=int, default=256)
     ap.add_argument("--workload", default="stack24_b1",
                     choices=["stack24_b1", "layer_b1", "batched_b64", "batched_b64_int8",
-                             "prefill_4096"])
+                             "prefill_4096", "copy_calib"])
     ap.add_argument("--cpu-tokens", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -250,6 +275,8 @@ def main():
     tw.lib()
     if args.workload == "stack24_b1":
         res = run_stack(args)
+    elif args.workload == "copy_calib":
+        res = run_copy_calib(args)
     else:
         res = run_single_layer(args, args.workload)
     res["device"] = torch.cuda.get_device_properties(0).gcnArchName
