@@ -202,7 +202,7 @@ tw_status ternary_moe_ffn_batched(const tw_moe_layer *layer, int64_t n_tokens, c
     if (n_tokens > (int64_t(1) << 24)) return TW_E_UNSUPPORTED;
     if (n_tokens == 0) return TW_OK;
     if (!x_in || !x_out || !workspace) return TW_E_NULL;
-    if ((uintptr_t)x_in & 15) return TW_E_UNSUPPORTED;   // the router reads 16-byte chunks
+    if (((uintptr_t)x_in | (uintptr_t)x_out) & 15) return TW_E_UNSUPPORTED;   // 16-byte accesses
     tw::Dims dm = dims_of(layer);
     int planes = act == TW_ACT_INT8 ? 1 : 3;
     size_t need = tw::batched_ws_layout(dm, n_tokens, planes).total;

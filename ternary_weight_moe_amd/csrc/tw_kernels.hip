@@ -89,28 +89,64 @@ __device__ __forceinline__ void load_chunk8(const void *x, int64_t row, int d, i
     }
 }
 
-// Workgroup (expert e, tokens 8 g .. 8 g + 7): all loads of the workgroup are issued at once.
+// The canonical sum of 256 partials (tw_device.h: wave_sum per 64, then (w0+w1)+(w2+w3)) is a
+// balanced binary tree over the partials in natural order; a single lane can form it from LDS.
+__device__ __forceinline__ float tree16(const float *p)
+{
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const float4 f = reinterpret_cast<const float4 *>(p)[q];
+        v[4 * q] = f.x;
+        v[4 * q + 1] = f.y;
+        v[4 * q + 2] = f.z;
+        v[4 * q + 3] = f.w;
+    }
+#pragma unroll
+    for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2 * w) v[i] = v[i] + v[i + w];
+    return v[0];
+}
+
+__device__ __forceinline__ float tree256(const float *p)
+{
+    float g[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) g[i] = tree16(p + 16 * i);
+#pragma unroll
+    for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2 * w) g[i] = g[i] + g[i + w];
+    return g[0];
+}
+
+// Workgroup (experts 4 f .. 4 f + 3, tokens 8 g .. 8 g + 7): thread t forms the canonical partial of
+// its chunks for every (expert, token) pair and for every token's sum of squares; the partials go
+// to LDS and one lane per pair adds them in the canonical tree.  All loads are issued at once.
+// NCH: 8-element chunks per thread (1 for d <= 2048, 2 for d <= 4096).
+constexpr int kRouteExp = 4;
+
+template <int NCH>
 __global__ __launch_bounds__(256) void k_route_experts(const void *__restrict__ x, int x_bf16,
                                                        const void *__restrict__ wr, int w_bf16,
                                                        int64_t T, int d, int E, int pre_norm,
                                                        float *__restrict__ logits)
 {
-    const int e = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x;
+    const int e0 = blockIdx.x * kRouteExp;
     const int64_t tb = int64_t(blockIdx.y) * kRouteTok;
     const int nt = int(T - tb < kRouteTok ? T - tb : kRouteTok);
+    const int ne = E - e0 < kRouteExp ? E - e0 : kRouteExp;
     const int nch = d >> 3;
-    float wv[2][8], xv[kRouteTok][2][8];
+    constexpr int NPR = kRouteExp * kRouteTok + kRouteTok;   // pairs + sums of squares
+    __shared__ __attribute__((aligned(16))) float part[NPR][256];
+    float xv[kRouteTok][NCH][8];
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const int c = t + 256 * i;
-        if (c < nch) {
-            load_chunk8(wr, e, d, c, w_bf16, wv[i]);
-        } else {
+    for (int u = 0; u < kRouteTok; u++)
 #pragma unroll
-            for (int j = 0; j < 8; j++) wv[i][j] = 0.0f;
-        }
-#pragma unroll
-        for (int u = 0; u < kRouteTok; u++) {
+        for (int i = 0; i < NCH; i++) {
+            const int c = t + 256 * i;
             if (u < nt && c < nch) {
                 load_chunk8(x, tb + u, d, c, x_bf16, xv[u][i]);
             } else {
@@ -118,33 +154,49 @@ __global__ __launch_bounds__(256) void k_route_experts(const void *__restrict__ 
                 for (int q = 0; q < 8; q++) xv[u][i][q] = 0.0f;
             }
         }
-    }
-    __shared__ float red[4][2][kRouteTok];
 #pragma unroll
     for (int u = 0; u < kRouteTok; u++) {
-        float dot = 0.0f, ss = 0.0f;
+        float ss = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
-            if (t + 256 * i < nch) {
+        for (int i = 0; i < NCH; i++)
 #pragma unroll
-                for (int q = 0; q < 8; q++) {
-                    dot = dot + wv[i][q] * xv[u][i][q];
-                    ss = ss + xv[u][i][q] * xv[u][i][q];
-                }
+            for (int q = 0; q < 8; q++) ss = ss + xv[u][i][q] * xv[u][i][q];
+        part[kRouteExp * kRouteTok + u][t] = ss;
+    }
+#pragma unroll
+    for (int m = 0; m < kRouteExp; m++) {
+        float wv[NCH][8];
+#pragma unroll
+        for (int i = 0; i < NCH; i++) {
+            const int c = t + 256 * i;
+            if (m < ne && c < nch) {
+                load_chunk8(wr, e0 + m, d, c, w_bf16, wv[i]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; q++) wv[i][q] = 0.0f;
             }
         }
-        dot = wave_sum(dot);
-        if (pre_norm) ss = wave_sum(ss);
-        if (lane == 0) {
-            red[wave][0][u] = dot;
-            red[wave][1][u] = ss;
+#pragma unroll
+        for (int u = 0; u < kRouteTok; u++) {
+            float dot = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NCH; i++)
+#pragma unroll
+                for (int q = 0; q < 8; q++) dot = dot + wv[i][q] * xv[u][i][q];
+            part[m * kRouteTok + u][t] = dot;
         }
     }
     __syncthreads();
-    if (t < nt) {
-        float v = (red[0][0][t] + red[1][0][t]) + (red[2][0][t] + red[3][0][t]);
-        if (pre_norm) v = v * inv_rms_of((red[0][1][t] + red[1][1][t]) + (red[2][1][t] + red[3][1][t]), d);
-        logits[(tb + t) * E + e] = v;
+    __shared__ float s_inv[kRouteTok];
+    if (t < kRouteTok) s_inv[t] = inv_rms_of(tree256(part[kRouteExp * kRouteTok + t]), d);
+    __syncthreads();
+    if (t < kRouteExp * kRouteTok) {
+        const int m = t / kRouteTok, u = t % kRouteTok;
+        if (m < ne && u < nt) {
+            float v = tree256(part[t]);
+            if (pre_norm) v = v * s_inv[u];
+            logits[(tb + u) * E + e0 + m] = v;
+        }
     }
 }
 
@@ -352,36 +404,70 @@ struct BatchedArgs {
 
 // Digit planes of every token (int8 mode: one plane, scale amax/127; float mode: P planes, shift).
 template <int P, bool INT8>
-__global__ __launch_bounds__(64) void k_bat_quant_x(BatchedArgs a, const void *__restrict__ x,
-                                                    int x_bf16, uint8_t *__restrict__ ws)
+__global__ __launch_bounds__(256) void k_bat_quant_x(BatchedArgs a, const void *__restrict__ x,
+                                                     int x_bf16, uint8_t *__restrict__ ws)
 {
-    const int lane = threadIdx.x;
-    const int64_t t = blockIdx.x;
-    const int d = a.dm.d;
-    const int64_t xo = t * d;
-    float am = 0.0f;
-    for (int i = lane; i < d; i += 64) am = fmaxf(am, fabsf(load_act(x, xo + i, x_bf16)));
+    // one workgroup per token; thread t holds the 8-element chunks t, t + 256 of the token
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t tok = blockIdx.x;
+    const int d = a.dm.d, nch = d >> 3;
+    float v[2][8];
+    float am = 0.0f, ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int c = t + 256 * i;
+        if (c < nch) {
+            load_chunk8(x, tok, d, c, x_bf16, v[i]);
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                am = fmaxf(am, fabsf(v[i][j]));
+                ss = ss + v[i][j] * v[i][j];
+            }
+        }
+    }
+    __shared__ float red[4][2];
     am = wave_max(am);
-    int8_t *xd = reinterpret_cast<int8_t *>(ws + a.L.xdig) + t * int64_t(P) * d;
-    float *ti = reinterpret_cast<float *>(ws + a.L.tinfo) + 2 * t;
+    if (!INT8 && a.dm.pre_norm) ss = wave_sum(ss);
+    if (lane == 0) {
+        red[wave][0] = am;
+        red[wave][1] = ss;
+    }
+    __syncthreads();
+    am = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
+    int8_t *xd = reinterpret_cast<int8_t *>(ws + a.L.xdig) + tok * int64_t(P) * d;
+    float *ti = reinterpret_cast<float *>(ws + a.L.tinfo) + 2 * tok;
     if (INT8) {
         const float inv = am > 0.0f ? 127.0f / am : 0.0f;
-        for (int i = lane; i < d; i += 64)
-            xd[perm16(i)] = am > 0.0f ? int8_quant(load_act(x, xo + i, x_bf16), inv) : int8_t(0);
-        if (lane == 0) ti[0] = am > 0.0f ? am / 127.0f : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int c = t + 256 * i;
+            if (c < nch) {
+#pragma unroll
+                for (int j = 0; j < 8; j++)
+                    xd[perm16(8 * c + j)] = am > 0.0f ? int8_quant(v[i][j], inv) : int8_t(0);
+            }
+        }
+        if (t == 0) ti[0] = am > 0.0f ? am / 127.0f : 0.0f;
     } else {
         const int sh = float_digit_shift(am, P);
-        for (int i = lane; i < d; i += 64) {
-            int8_t dg[P];
-            float_digits<P>(load_act(x, xo + i, x_bf16), sh, dg);
 #pragma unroll
-            for (int p = 0; p < P; p++) xd[p * d + perm16(i)] = dg[p];
+        for (int i = 0; i < 2; i++) {
+            const int c = t + 256 * i;
+            if (c < nch) {
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    int8_t dg[P];
+                    float_digits<P>(v[i][j], sh, dg);
+#pragma unroll
+                    for (int p = 0; p < P; p++) xd[p * d + perm16(8 * c + j)] = dg[p];
+                }
+            }
         }
-        auto xv = [&](int i) { return load_act(x, xo + i, x_bf16); };
-        const float inv = a.dm.pre_norm ? inv_rms_of(canon_dot(d, lane, xv, xv), d) : 1.0f;
-        if (lane == 0) {
+        if (t == 0) {
+            // the pre-RMSNorm sum of squares in the canonical order (partials t, waves in pairs)
+            const float tot = (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]);
             reinterpret_cast<int32_t *>(ti)[0] = sh;
-            ti[1] = inv;
+            ti[1] = a.dm.pre_norm ? inv_rms_of(tot, d) : 1.0f;
         }
     }
 }
@@ -718,32 +804,74 @@ __global__ __launch_bounds__(256) void k_bat_dn(BatchedArgs a, LayerPtrs lp, uin
 }
 
 // out[t] = ((x[t] + g_0 y_0) + g_1 y_1) + ..., j in selection order.  Slots whose expert id is
-// outside [0, E) contribute nothing (k_group does not place them either).
+// outside [0, E) contribute nothing (k_group does not place them either).  One workgroup per token;
+// thread t owns the 8-element chunks t, t + 256; every load of the token is issued at once.
 __global__ __launch_bounds__(256) void k_bat_combine(BatchedArgs a, const void *__restrict__ x,
                                                      int x_bf16, void *__restrict__ out,
                                                      int out_bf16, const int32_t *__restrict__ ids,
                                                      const float *__restrict__ gates,
                                                      uint8_t *__restrict__ ws)
 {
-    const int d = a.dm.d, k = a.dm.k, E = a.dm.E;
-    const int64_t n = a.T * d;
+    const int d = a.dm.d, k = a.dm.k, E = a.dm.E, nch = d >> 3;
+    const int64_t tok = blockIdx.x;
     const float *ybuf = reinterpret_cast<const float *>(ws + a.L.y);
-    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-         i += int64_t(gridDim.x) * blockDim.x) {
-        const int64_t t = i / d;
-        const int r = int(i % d);
-        float o = load_act(x, i, x_bf16);
-        for (int j = 0; j < k; j++) {
-            const int id = ids[t * k + j];
-            if (id < 0 || id >= E) continue;
-            const float c = gates[t * k + j] * ybuf[(t * k + j) * d + r];
-            o = o + c;
+    for (int i = 0; i < 2; i++) {
+        const int c = threadIdx.x + 256 * i;
+        if (c >= nch) break;
+        float o[8];
+        load_chunk8(x, tok, d, c, x_bf16, o);
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            float yv[8][8];
+            float g[8];
+            bool ok[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                const int j = j0 + u;
+                const int id = j < k ? ids[tok * k + j] : -1;
+                ok[u] = id >= 0 && id < E;
+                g[u] = ok[u] ? gates[tok * k + j] : 0.0f;
+                if (ok[u]) {
+                    const int4 *yp = reinterpret_cast<const int4 *>(ybuf + (tok * k + j) * d + 8 * c);
+                    const int4 p0 = yp[0], p1 = yp[1];
+                    yv[u][0] = __int_as_float(p0.x); yv[u][1] = __int_as_float(p0.y);
+                    yv[u][2] = __int_as_float(p0.z); yv[u][3] = __int_as_float(p0.w);
+                    yv[u][4] = __int_as_float(p1.x); yv[u][5] = __int_as_float(p1.y);
+                    yv[u][6] = __int_as_float(p1.z); yv[u][7] = __int_as_float(p1.w);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                if (ok[u]) {
+#pragma unroll
+                    for (int q = 0; q < 8; q++) o[q] = o[q] + g[u] * yv[u][q];
+                }
+            }
         }
-        store_act(out, i, o, out_bf16);
+        if (out_bf16) {
+            uint32_t w[4];
+#pragma unroll
+            for (int q = 0; q < 4; q++) w[q] = pack_bf16x2(o[2 * q], o[2 * q + 1]);
+            reinterpret_cast<int4 *>(static_cast<uint16_t *>(out) + tok * d)[c] =
+                make_int4(int(w[0]), int(w[1]), int(w[2]), int(w[3]));
+        } else {
+            int4 *op = reinterpret_cast<int4 *>(static_cast<float *>(out) + tok * d) + 2 * c;
+            op[0] = make_int4(__float_as_int(o[0]), __float_as_int(o[1]), __float_as_int(o[2]), __float_as_int(o[3]));
+            op[1] = make_int4(__float_as_int(o[4]), __float_as_int(o[5]), __float_as_int(o[6]), __float_as_int(o[7]));
+        }
     }
 }
 
 inline hipStream_t S(void *s) { return static_cast<hipStream_t>(s); }
+
+void launch_router(const void *x, int x_bf16, const void *wr, int w_bf16, int64_t T, const Dims &dm,
+                   float *logits, void *stream)
+{
+    const dim3 grid(unsigned((dm.E + kRouteExp - 1) / kRouteExp), unsigned((T + kRouteTok - 1) / kRouteTok));
+    if (dm.d <= 2048)
+        k_route_experts<1><<<grid, 256, 0, S(stream)>>>(x, x_bf16, wr, w_bf16, T, dm.d, dm.E, dm.pre_norm, logits);
+    else
+        k_route_experts<2><<<grid, 256, 0, S(stream)>>>(x, x_bf16, wr, w_bf16, T, dm.d, dm.E, dm.pre_norm, logits);
+}
 
 int last_error() { return int(hipGetLastError()); }
 
@@ -779,22 +907,18 @@ int batched_p(const Dims &dm, const LayerPtrs &lp, int64_t T, const void *x_in, 
         float *logits = reinterpret_cast<float *>(w + a.L.logits);
         int32_t *wid = reinterpret_cast<int32_t *>(w + a.L.ids);
         float *wg = reinterpret_cast<float *>(w + a.L.gates);
-        k_route_experts<<<dim3(unsigned(dm.E), unsigned((T + kRouteTok - 1) / kRouteTok)), 256, 0,
-                          S(stream)>>>(x_in, in_bf16, lp.w_router, dm.router_bf16, T, dm.d, dm.E,
-                                       dm.pre_norm, logits);
+        launch_router(x_in, in_bf16, lp.w_router, dm.router_bf16, T, dm, logits, stream);
         k_topk<<<unsigned((T + 3) / 4), 256, 0, S(stream)>>>(logits, T, dm.E, dm.k, wid, wg);
         ids = wid;
         gates = wg;
     }
-    k_bat_quant_x<P, INT8><<<unsigned(T), 64, 0, S(stream)>>>(a, x_in, in_bf16, w);
+    k_bat_quant_x<P, INT8><<<unsigned(T), 256, 0, S(stream)>>>(a, x_in, in_bf16, w);
     int tile = kTileTokens;
     if (grouped_mfma_serves(dm, T, P, &tile)) {
         k_group<<<1, 1024, 0, S(stream)>>>(a, ids, w, tile);
         const int r = launch_grouped_mfma(dm, lp, T, P, tile, a.L, w, stream);
         if (r != 0) return r;
-        const int64_t n = T * dm.d;
-        const unsigned nb = unsigned(n / 256 + 1 < 65536 ? n / 256 + 1 : 65536);
-        k_bat_combine<<<nb, 256, 0, S(stream)>>>(a, x_in, in_bf16, x_out, out_bf16, ids, gates, w);
+        k_bat_combine<<<unsigned(T), 256, 0, S(stream)>>>(a, x_in, in_bf16, x_out, out_bf16, ids, gates, w);
         return last_error();
     }
     k_group<<<1, 1024, 0, S(stream)>>>(a, ids, w, kTileTokens);
@@ -807,9 +931,7 @@ int batched_p(const Dims &dm, const LayerPtrs &lp, int64_t T, const void *x_in, 
         k_bat_dn<P, INT8, 2><<<kBatG, 256, size_t(td) * P * dm.F, S(stream)>>>(a, lp, w, td);
     else
         k_bat_dn<P, INT8, 16><<<kBatG, 256, size_t(td) * P * dm.F, S(stream)>>>(a, lp, w, td);
-    const int64_t n = T * dm.d;
-    const unsigned nb = unsigned(n / 256 + 1 < 65536 ? n / 256 + 1 : 65536);
-    k_bat_combine<<<nb, 256, 0, S(stream)>>>(a, x_in, in_bf16, x_out, out_bf16, ids, gates, w);
+    k_bat_combine<<<unsigned(T), 256, 0, S(stream)>>>(a, x_in, in_bf16, x_out, out_bf16, ids, gates, w);
     return last_error();
 }
 
@@ -834,8 +956,7 @@ int launch_pack(const int8_t *w, int64_t rows, int64_t cols, uint8_t *packed, in
 int launch_route(const void *x, int x_bf16, const void *w_router, int w_bf16, int64_t T,
                  const Dims &dm, float *logits, int32_t *ids, float *gates, void *stream)
 {
-    k_route_experts<<<dim3(unsigned(dm.E), unsigned((T + kRouteTok - 1) / kRouteTok)), 256, 0,
-                      S(stream)>>>(x, x_bf16, w_router, w_bf16, T, dm.d, dm.E, dm.pre_norm, logits);
+    launch_router(x, x_bf16, w_router, w_bf16, T, dm, logits, stream);
     k_topk<<<unsigned((T + 3) / 4), 256, 0, S(stream)>>>(logits, T, dm.E, dm.k, ids, gates);
     return last_error();
 }

@@ -38,8 +38,13 @@ namespace {
 
 typedef int32_t v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kPfT = 512;   // threads per workgroup
-constexpr int kPfW = kPfT / 64;
+// Waves per workgroup: 8 for 64-token tiles; 16 for 16-token tiles (at <= 128 VGPRs, four waves
+// per SIMD hide each other's code-row loads).
+template <int MT>
+struct PfShape {
+    static constexpr int W = MT <= 16 ? 16 : 8;
+    static constexpr int T = 64 * W;
+};
 
 // The 16 int8 weights of one 32-bit code word, in the transposed order of the activation digits.
 __device__ __forceinline__ v4i decode16(uint32_t w)
@@ -76,10 +81,11 @@ __device__ __forceinline__ v4i mfma8(const v4i &a, const v4i &b, const v4i &c)
 }
 
 template <int D, int F, int P, int MT>
-__global__ __launch_bounds__(kPfT) void k_pf_ffn(Dims dm, BatchedWs L, LayerPtrs lp, uint8_t *ws, int nb)
+__global__ __launch_bounds__(PfShape<MT>::T) void k_pf_ffn(Dims dm, BatchedWs L, LayerPtrs lp, uint8_t *ws, int nb)
 {
+    constexpr int kPfW = PfShape<MT>::W, kPfT = PfShape<MT>::T;
     static_assert(D % 256 == 0 && F % 256 == 0 && F % (16 * kPfW) == 0 && D % (16 * kPfW) == 0, "shape");
-    static_assert(MT % 16 == 0, "tile");
+    static_assert(MT % 16 == 0 && MT <= kPfT, "tile");
     constexpr bool INT8 = P == 1;
     constexpr int MS = MT / 16;           // token sub-tiles
     constexpr int GPW = F / 16 / kPfW;    // h-row groups of 16 per wave
@@ -128,7 +134,7 @@ __global__ __launch_bounds__(kPfT) void k_pf_ffn(Dims dm, BatchedWs L, LayerPtrs
 
     // 2. gate/up.  With small tiles (PF) the code rows of group gi+1 are requested before group gi
     //    is computed (two register buffers, fully unrolled so every index is static).
-    constexpr bool PF = MT <= 16;
+    constexpr bool PF = false;
     float hreg[GPW][MS][4];
     int4 cg[PF ? 2 : 1][SG], cu[PF ? 2 : 1][SG];
     auto load_gu = [&](int gi, int4 (&g)[SG], int4 (&u)[SG]) {
@@ -308,7 +314,7 @@ int pf_run(const Dims &dm, const LayerPtrs &lp, int64_t T, const BatchedWs &L, u
         attr_set.store(1, std::memory_order_relaxed);
     }
     const int nb = int((max_tiles(dm, T, MT) + 15) / 16 * 16);
-    k_pf_ffn<D, F, P, MT><<<nb, kPfT, lds, static_cast<hipStream_t>(stream)>>>(dm, L, lp, ws, nb);
+    k_pf_ffn<D, F, P, MT><<<nb, PfShape<MT>::T, lds, static_cast<hipStream_t>(stream)>>>(dm, L, lp, ws, nb);
     return int(hipGetLastError());
 }
 
