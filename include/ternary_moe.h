@@ -43,9 +43,9 @@
  *   - A workspace belongs to one in-flight call at a time; two calls in flight on different
  *     streams must use different workspaces.  Its contents need no initialisation.
  *   - Supported shapes: d_model and d_ff powers of two in [64, 4096]; 1 <= top_k <= min(E, 32);
- *     n_experts in [1, 1024].  Packed weights, router weights and the activations of the routing
- *     and batched calls must be 16-byte aligned (torch allocations are).  Others return
- *     TW_E_UNSUPPORTED.
+ *     n_experts in [1, 1024].  Packed weights, scales, router weights and the activations of the
+ *     routing and batched calls must be 16-byte aligned, workspaces 256-byte aligned (torch
+ *     allocations are).  Others return TW_E_UNSUPPORTED.
  */
 #ifndef TERNARY_MOE_H
 #define TERNARY_MOE_H

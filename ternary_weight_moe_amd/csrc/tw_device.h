@@ -32,6 +32,11 @@ namespace {
 constexpr uint32_t kCodeMask = 0x03030303u;
 // Byte c of this word is the int8 weight of code c: 00 -> 0, 01 -> +1, 10 -> -1, 11 -> 0.
 constexpr uint32_t kCodeLut = 0x00FF0100u;
+// The same table for a code left in bits 2-3 of a selector byte (selector 4c): byte permute
+// selector 0 picks low byte 0 (0x00), 4 picks high byte 0 (0x01), 8 replicates the sign bit of low
+// byte 1 (0xFF), 12 gives 0x00.
+constexpr uint32_t kCodeMaskHi = 0x0C0C0C0Cu;
+constexpr uint32_t kCodeLutHiLow = 0x00008000u, kCodeLutHiHigh = 0x00000001u;
 
 // ------------------------------------------------------------------------------------------------
 // scalar helpers
@@ -110,16 +115,17 @@ __device__ __forceinline__ float wave_max(float v)
 // high part whose 12 low significand bits are zero (so n * hi is exact) and a low part, a degree-7
 // Taylor polynomial of e^r in Horner form (coefficients 1/m! rounded to fp32), then a scaling by
 // 2^n.  Arguments above 80 give +inf and below -80 give 0, so no result is subnormal.  Compiled
-// with -ffp-contract=off: every step is one rounded fp32 operation.
+// with -ffp-contract=off: every step is one rounded fp32 operation.  Branch-free: the steps run on
+// the argument clamped to [-80, 80] (equal to it wherever their result is used) and the special
+// cases are selected afterwards.
 __device__ __forceinline__ float tw_exp(float z)
 {
-    if (z > 80.0f) return __builtin_inff();
-    if (z < -80.0f) return 0.0f;
     const float kLog2e = 1.44269504088896340736f;
     const float kLn2Hi = 0.693145751953125f;
     const float kLn2Lo = 1.42860682030941723212e-6f;
-    float n = __builtin_rintf(z * kLog2e);
-    float r = z - n * kLn2Hi;
+    const float zc = __builtin_fminf(__builtin_fmaxf(z, -80.0f), 80.0f);
+    float n = __builtin_rintf(zc * kLog2e);
+    float r = zc - n * kLn2Hi;
     r = r - n * kLn2Lo;
     float p = 1.98412698412698412698e-4f;    // 1/7!
     p = p * r + 1.38888888888888888889e-3f;  // 1/6!
@@ -129,7 +135,11 @@ __device__ __forceinline__ float tw_exp(float z)
     p = p * r + 0.5f;
     p = p * r + 1.0f;
     p = p * r + 1.0f;
-    return __builtin_ldexpf(p, int(n));
+    const uint32_t v = __float_as_uint(__builtin_ldexpf(p, int(n)));
+    // special cases by masks (sign-extended comparisons), not by branches
+    const uint32_t hi = uint32_t(-int32_t(z > 80.0f)), lo = uint32_t(-int32_t(z < -80.0f));
+    const uint32_t nan = uint32_t(-int32_t(z != z));
+    return __uint_as_float((v & ~(hi | lo | nan)) | (hi & 0x7f800000u) | (nan & __float_as_uint(z)));
 }
 
 // SiLU(z) = z / (1 + e^-z), as the division of z by one rounded denominator.
@@ -176,16 +186,25 @@ __device__ __forceinline__ int32_t lut4(uint32_t sel)
     return int32_t(__builtin_amdgcn_perm(0u, kCodeLut, sel));
 }
 
+// The four int8x4 weight words of one 32-bit code word: word m holds codes 4j + m (bits 8j + 2m)
+// of its bytes j.  Nine ALU operations: the codes in bits 2-3 of a byte are looked up in place.
+__device__ __forceinline__ void decode_word(uint32_t w, int32_t &t0, int32_t &t1, int32_t &t2, int32_t &t3)
+{
+    const uint32_t h = w >> 4;
+    t0 = int32_t(__builtin_amdgcn_perm(0u, kCodeLut, w & kCodeMask));
+    t1 = int32_t(__builtin_amdgcn_perm(kCodeLutHiHigh, kCodeLutHiLow, w & kCodeMaskHi));
+    t2 = int32_t(__builtin_amdgcn_perm(0u, kCodeLut, h & kCodeMask));
+    t3 = int32_t(__builtin_amdgcn_perm(kCodeLutHiHigh, kCodeLutHiLow, h & kCodeMaskHi));
+}
+
 template <int P>
 __device__ __forceinline__ void chunk_dot(const int4 code, const int4 (&dg)[P][4], int32_t (&acc)[P])
 {
     const uint32_t w[4] = {uint32_t(code.x), uint32_t(code.y), uint32_t(code.z), uint32_t(code.w)};
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-        const int32_t t0 = lut4(w[q] & kCodeMask);
-        const int32_t t1 = lut4((w[q] >> 2) & kCodeMask);
-        const int32_t t2 = lut4((w[q] >> 4) & kCodeMask);
-        const int32_t t3 = lut4((w[q] >> 6) & kCodeMask);
+        int32_t t0, t1, t2, t3;
+        decode_word(w[q], t0, t1, t2, t3);
 #pragma unroll
         for (int p = 0; p < P; p++) {
             acc[p] = __builtin_amdgcn_sdot4(t0, dg[p][q].x, acc[p], false);
@@ -203,8 +222,7 @@ __device__ __forceinline__ void decode_chunk(const int4 code, int32_t (&wd)[16])
     const uint32_t w[4] = {uint32_t(code.x), uint32_t(code.y), uint32_t(code.z), uint32_t(code.w)};
 #pragma unroll
     for (int q = 0; q < 4; q++)
-#pragma unroll
-        for (int m = 0; m < 4; m++) wd[4 * q + m] = lut4((w[q] >> (2 * m)) & kCodeMask);
+        decode_word(w[q], wd[4 * q], wd[4 * q + 1], wd[4 * q + 2], wd[4 * q + 3]);
 }
 
 template <int P>

@@ -45,8 +45,9 @@ tw_status check_layer(const tw_moe_layer *L)
     if (!L->w_router || !L->w_gate || !L->w_up || !L->w_down || !L->s_gate || !L->s_up ||
         !L->s_down)
         return TW_E_NULL;
-    // packed rows and router rows are read 16 bytes at a time
-    if (((uintptr_t)L->w_gate | (uintptr_t)L->w_up | (uintptr_t)L->w_down | (uintptr_t)L->w_router) & 15)
+    // packed rows, router rows and scales are read 16 bytes at a time
+    if (((uintptr_t)L->w_gate | (uintptr_t)L->w_up | (uintptr_t)L->w_down | (uintptr_t)L->w_router |
+         (uintptr_t)L->s_gate | (uintptr_t)L->s_up | (uintptr_t)L->s_down) & 15)
         return TW_E_UNSUPPORTED;
     return TW_OK;
 }
@@ -161,6 +162,7 @@ tw_status ternary_moe_ffn_decode(const tw_moe_layer *layers, int32_t n_layers, c
     }
     if (!valid_float(io_dtype)) return TW_E_DTYPE;
     if (!x_in || !x_out || !workspace) return TW_E_NULL;
+    if ((uintptr_t)workspace & 255) return TW_E_UNSUPPORTED;   // its regions are 256-byte aligned
     tw::Dims dm = dims_of(&layers[0]);
     // the down kernel keeps the digit planes of all k expert activations in 64 KiB of LDS
     if (size_t(dm.k) * 3 * dm.F > 65536 - 1024) return TW_E_UNSUPPORTED;
@@ -203,6 +205,7 @@ tw_status ternary_moe_ffn_batched(const tw_moe_layer *layer, int64_t n_tokens, c
     if (n_tokens == 0) return TW_OK;
     if (!x_in || !x_out || !workspace) return TW_E_NULL;
     if (((uintptr_t)x_in | (uintptr_t)x_out) & 15) return TW_E_UNSUPPORTED;   // 16-byte accesses
+    if ((uintptr_t)workspace & 255) return TW_E_UNSUPPORTED;   // its regions are 256-byte aligned
     tw::Dims dm = dims_of(layer);
     int planes = act == TW_ACT_INT8 ? 1 : 3;
     size_t need = tw::batched_ws_layout(dm, n_tokens, planes).total;

@@ -57,6 +57,7 @@ inline DecodeWs decode_ws_layout(const Dims &dm) {
 // ---- batched workspace ------------------------------------------------------------------------
 struct BatchedWs {
     size_t ctrl, logits, ids, gates, tinfo, xdig, counts, offsets, pairs, tiles, h, y, total;
+    int64_t spare_row;   // y row behind the last pair: stores of padding tokens land there
 };
 constexpr int kTileTokens = 64;     // tokens per tile: large tiles (many tokens per expert)
 constexpr int kSmallTile = 16;      // tokens per tile: small tiles (few tokens per expert)
@@ -82,7 +83,8 @@ inline BatchedWs batched_ws_layout(const Dims &dm, int64_t T, int planes) {
     w.pairs = o;   o += align256(sizeof(int32_t) * pairs);
     w.tiles = o;   o += align256(sizeof(int32_t) * size_t(max_tiles(dm, T, kSmallTile) + 16));
     w.h = o;       o += align256(sizeof(float) * pairs * dm.F);
-    w.y = o;       o += align256(sizeof(float) * pairs * dm.d);
+    w.y = o;       o += align256(sizeof(float) * (pairs + 1) * dm.d);
+    w.spare_row = int64_t(pairs);
     w.total = o;
     return w;
 }

@@ -2,6 +2,8 @@
 // packing, routing, the per-layer batch-1 decode kernels and the expert-grouped batched path.
 // The ternary dot product and the activation digit planes are described in tw_device.h.
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stdint.h>
 
 #include "tw_device.h"
@@ -476,22 +478,44 @@ __global__ __launch_bounds__(256) void k_bat_quant_x(BatchedArgs a, const void *
 // expert e at offsets[e]..offsets[e+1]; their order inside a group is not fixed, and no result
 // depends on it: every pair is computed on its own), plus the list of (expert, tile of tt tokens)
 // work items: tiles[0] = their number, tiles[1 + i] = e | (tile << 10).
-// One workgroup of 1024 threads; counts and placement use LDS atomics.
+// One workgroup of 1024 threads; counts and placement use LDS atomics.  The ids are read in passes
+// of 32 per thread, all loads of a pass issued before any is used (one memory round trip per pass
+// instead of one per id); with a single pass they stay in registers for the placement.  Up to
+// kGrpStage pairs the placement is staged in LDS and written out with 16-byte stores (scattered
+// 4-byte stores from one workgroup are limited by its address rate).
+constexpr int kGrpPer = 32;                    // ids per thread per pass
+constexpr int kGrpPass = 1024 * kGrpPer;       // pairs per pass
+constexpr int kGrpStage = kGrpPass;            // pairs staged in LDS (128 KiB)
+
 __global__ __launch_bounds__(1024) void k_group(BatchedArgs a, const int32_t *__restrict__ ids,
                                                 uint8_t *__restrict__ ws, int tt)
 {
+    extern __shared__ __attribute__((aligned(16))) int32_t stage[];   // [npairs] when staged
     const int E = a.dm.E, t = threadIdx.x;
     const int64_t npairs = a.T * a.dm.k;
+    const bool staged = npairs <= kGrpStage;
     int32_t *counts = reinterpret_cast<int32_t *>(ws + a.L.counts);
     int32_t *offsets = reinterpret_cast<int32_t *>(ws + a.L.offsets);
     int32_t *pairs = reinterpret_cast<int32_t *>(ws + a.L.pairs);
     int32_t *tiles = reinterpret_cast<int32_t *>(ws + a.L.tiles);
     __shared__ int32_t cnt[kMaxExperts], cur[kMaxExperts], scan[1024], tscan[1024];
+    const int64_t npass = (npairs + kGrpPass - 1) / kGrpPass;
+    int v[kGrpPer];
+    // v[i] = id of pair base + t + 1024 i, or -1 past the end
+    auto load = [&](int64_t base) {
+#pragma unroll
+        for (int i = 0; i < kGrpPer; i++) {
+            const int64_t p = base + t + 1024 * i;
+            v[i] = p < npairs ? ids[p] : -1;
+        }
+    };
     for (int e = t; e < E; e += 1024) cnt[e] = 0;
     __syncthreads();
-    for (int64_t p = t; p < npairs; p += 1024) {
-        const int id = ids[p];
-        if (id >= 0 && id < E) atomicAdd(&cnt[id], 1);
+    for (int64_t ps = 0; ps < npass; ps++) {
+        load(ps * kGrpPass);
+#pragma unroll
+        for (int i = 0; i < kGrpPer; i++)
+            if (v[i] >= 0 && v[i] < E) atomicAdd(&cnt[v[i]], 1);
     }
     __syncthreads();
     const int c = t < E ? cnt[t] : 0;
@@ -507,6 +531,7 @@ __global__ __launch_bounds__(1024) void k_group(BatchedArgs a, const int32_t *__
         __syncthreads();
     }
     const int off_e = scan[t] - c, tile0 = tscan[t] - nt;
+    const int placed = scan[1023];   // pairs with a valid id
     if (t < E) {
         counts[t] = c;
         offsets[t] = off_e;
@@ -514,14 +539,50 @@ __global__ __launch_bounds__(1024) void k_group(BatchedArgs a, const int32_t *__
         for (int i = 0; i < nt; i++) tiles[1 + tile0 + i] = t | (i << 10);
     }
     if (t == 1023) {
-        offsets[E] = scan[1023];
+        offsets[E] = placed;
         tiles[0] = tscan[1023];
     }
     __syncthreads();
-    for (int64_t p = t; p < npairs; p += 1024) {
-        const int id = ids[p];
-        if (id >= 0 && id < E) pairs[atomicAdd(&cur[id], 1)] = int32_t(p);
+    for (int64_t ps = 0; ps < npass; ps++) {
+        const int64_t base = ps * kGrpPass;
+        if (npass > 1) load(base);
+#pragma unroll
+        for (int i = 0; i < kGrpPer; i++)
+            if (v[i] >= 0 && v[i] < E) {
+                const int pos = atomicAdd(&cur[v[i]], 1);
+                const int32_t pr = int32_t(base + t + 1024 * i);
+                if (staged)
+                    stage[pos] = pr;
+                else
+                    pairs[pos] = pr;
+            }
     }
+    if (!staged) return;
+    __syncthreads();
+    // pairs is 256-byte aligned inside the workspace
+    for (int i = t; 4 * i < placed; i += 1024) {
+        if (4 * i + 3 < placed)
+            reinterpret_cast<int4 *>(pairs)[i] = reinterpret_cast<const int4 *>(stage)[i];
+        else
+            for (int j = 4 * i; j < placed; j++) pairs[j] = stage[j];
+    }
+}
+
+// Launches k_group (one workgroup) with the LDS staging area when the pairs fit in it.
+int launch_group(const BatchedArgs &a, const int32_t *ids, uint8_t *ws, int tt, void *stream)
+{
+    const int64_t npairs = a.T * a.dm.k;
+    const size_t lds = npairs <= kGrpStage ? size_t(npairs) * sizeof(int32_t) : 0;
+    static std::atomic<int> attr_set{0};
+    if (lds > 0 && !attr_set.load(std::memory_order_relaxed)) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_group),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                int(kGrpStage * sizeof(int32_t))) != hipSuccess)
+            return int(hipErrorInvalidValue);
+        attr_set.store(1, std::memory_order_relaxed);
+    }
+    k_group<<<1, 1024, lds, static_cast<hipStream_t>(stream)>>>(a, ids, ws, tt);
+    return 0;
 }
 
 // Batched gate/up and down.  Work items are (expert tile, row block) -- a tile is up to 64 of an
@@ -915,13 +976,15 @@ int batched_p(const Dims &dm, const LayerPtrs &lp, int64_t T, const void *x_in, 
     k_bat_quant_x<P, INT8><<<unsigned(T), 256, 0, S(stream)>>>(a, x_in, in_bf16, w);
     int tile = kTileTokens;
     if (grouped_mfma_serves(dm, T, P, &tile)) {
-        k_group<<<1, 1024, 0, S(stream)>>>(a, ids, w, tile);
-        const int r = launch_grouped_mfma(dm, lp, T, P, tile, a.L, w, stream);
+        int r = launch_group(a, ids, w, tile, stream);
+        if (r != 0) return r;
+        r = launch_grouped_mfma(dm, lp, T, P, tile, a.L, w, stream);
         if (r != 0) return r;
         k_bat_combine<<<unsigned(T), 256, 0, S(stream)>>>(a, x_in, in_bf16, x_out, out_bf16, ids, gates, w);
         return last_error();
     }
-    k_group<<<1, 1024, 0, S(stream)>>>(a, ids, w, kTileTokens);
+    const int rg = launch_group(a, ids, w, kTileTokens, stream);
+    if (rg != 0) return rg;
     const int tg = tokens_per_round(P * dm.d), td = tokens_per_round(P * dm.F);
     if (dm.d <= 2048)
         k_bat_gu<P, INT8, 4><<<kBatG, 256, size_t(tg) * P * dm.d, S(stream)>>>(a, lp, w, tg);

@@ -38,23 +38,24 @@ namespace {
 
 typedef int32_t v4i __attribute__((ext_vector_type(4)));
 
-// Waves per workgroup: 8 for 64-token tiles; 16 for 16-token tiles (at <= 128 VGPRs, four waves
-// per SIMD hide each other's code-row loads).
-template <int MT>
+// Waves per workgroup: 16 for 16-token tiles of at most two planes (at <= 128 VGPRs, four waves
+// per SIMD); 8 otherwise (256 VGPRs: the h values of a 64-token tile stay in registers).
+template <int MT, int P>
 struct PfShape {
-    static constexpr int W = MT <= 16 ? 16 : 8;
+    static constexpr int W = (MT <= 16 && P <= 2) ? 16 : 8;
     static constexpr int T = 64 * W;
 };
+
+// Code units (one 16-row block of gate and up codes over 256 inputs, or one 16-row block of down
+// codes) each wave keeps in flight ahead of the one it computes.
+constexpr int kPfAhead = 4;
 
 // The 16 int8 weights of one 32-bit code word, in the transposed order of the activation digits.
 __device__ __forceinline__ v4i decode16(uint32_t w)
 {
-    v4i r;
-    r.x = lut4(w & kCodeMask);
-    r.y = lut4((w >> 2) & kCodeMask);
-    r.z = lut4((w >> 4) & kCodeMask);
-    r.w = lut4((w >> 6) & kCodeMask);
-    return r;
+    int32_t a, b, c, d;
+    decode_word(w, a, b, c, d);
+    return v4i{a, b, c, d};
 }
 
 __device__ __forceinline__ uint32_t word_of(const int4 &v, int s)
@@ -62,41 +63,41 @@ __device__ __forceinline__ uint32_t word_of(const int4 &v, int s)
     return uint32_t(s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w);
 }
 
-// Row maximum over the 16 lanes of each DPP row (every lane of the row receives it).
-__device__ __forceinline__ float row16_max(float v)
+__device__ __forceinline__ float comp(const float4 &v, int r)
 {
-    v = fmaxf(v, dpp_f<kDppXor1>(v));
-    v = fmaxf(v, dpp_f<kDppXor2>(v));
-    v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
-    v = fmaxf(v, dpp_f<kDppMirror>(v));
-    return v;
+    return r == 0 ? v.x : r == 1 ? v.y : r == 2 ? v.z : v.w;
 }
 
 // Address of 16-byte chunk c of row r in a tile of rows of `rowb` bytes, each padded by 16 bytes.
 __device__ __forceinline__ int tofs(int r, int c, int rowb) { return r * (rowb + 16) + 16 * c; }
 
-__device__ __forceinline__ v4i mfma8(const v4i &a, const v4i &b, const v4i &c)
+// Weights as the A operand, activations as B: the result tile is [weight row][token], so lane l
+// holds rows 4 (l / 16) .. +3 of token l % 16.
+__device__ __forceinline__ v4i mfma8(const v4i &w, const v4i &x, const v4i &c)
 {
-    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(w, x, c, 0, 0, 0);
 }
 
 template <int D, int F, int P, int MT>
-__global__ __launch_bounds__(PfShape<MT>::T) void k_pf_ffn(Dims dm, BatchedWs L, LayerPtrs lp, uint8_t *ws, int nb)
+__global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, BatchedWs L, LayerPtrs lp, uint8_t *ws, int nb)
 {
-    constexpr int kPfW = PfShape<MT>::W, kPfT = PfShape<MT>::T;
-    static_assert(D % 256 == 0 && F % 256 == 0 && F % (16 * kPfW) == 0 && D % (16 * kPfW) == 0, "shape");
-    static_assert(MT % 16 == 0 && MT <= kPfT, "tile");
+    constexpr int W = PfShape<MT, P>::W, NT = PfShape<MT, P>::T;
+    static_assert(D % 256 == 0 && F % 256 == 0 && F % (16 * W) == 0 && D % (16 * W) == 0, "shape");
+    static_assert(MT % 16 == 0 && MT <= NT, "tile");
     constexpr bool INT8 = P == 1;
     constexpr int MS = MT / 16;           // token sub-tiles
-    constexpr int GPW = F / 16 / kPfW;    // h-row groups of 16 per wave
-    constexpr int NSD = D / 16 / kPfW;    // down sub-tiles of 16 rows per wave
+    constexpr int GPW = F / 16 / W;       // h-row groups of 16 per wave
+    constexpr int NSD = D / 16 / W;       // down row blocks of 16 per wave
     constexpr int SG = D / 256, SD = F / 256;
+    constexpr int NGU = GPW * SG;         // gate/up code units per wave, then NSD down units
+    constexpr int NU = NGU + NSD, RING = kPfAhead + 1;
+    static_assert(SD <= 2, "a down unit is at most two 16-byte chunks per lane");
     extern __shared__ __attribute__((aligned(16))) int8_t sm[];   // [MT][P] rows of D, later of F
     __shared__ int32_t s_pair[MT];
     __shared__ float s_tk[MT][2];         // per token: s_x (int8) or digit shift bits; 1/rms
     __shared__ float s_hk[MT];            // per token: s_h (int8) or digit shift bits of h
     __shared__ float s_amx[MT];
-    __shared__ float s_pam[kPfW][MT];
+    __shared__ float s_pam[W][MT];
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l16 = lane & 15, g4 = lane >> 4;
     const int32_t *tiles = reinterpret_cast<const int32_t *>(ws + L.tiles);
@@ -104,86 +105,130 @@ __global__ __launch_bounds__(PfShape<MT>::T) void k_pf_ffn(Dims dm, BatchedWs L,
     // and every 16 workgroups cover 16 consecutive tiles, so work spreads evenly over the XCDs
     const int b = blockIdx.x;
     const int ti = (b / 16) * 16 + (b % 8) * 2 + ((b / 8) & 1);
-    if (ti >= tiles[0]) return;
-    const int tile = tiles[1 + ti], e = tile & 1023, mt = tile >> 10;
+    const int ntiles = tiles[0], tile = tiles[1 + ti];   // ti < nb: inside the tile list's storage
+    if (ti >= ntiles) return;
+    const int e = tile & 1023, mt = tile >> 10;
+
+    // Code units of this wave, in the order they are computed.  Unit u < NGU: gate and up chunk
+    // u % SG of h-row group u / SG (plus, with the first chunk, the group's gate and up scales);
+    // unit NGU + n: the down codes and scales of output row block n.  All loops over units are
+    // unrolled, so ring slots and scale registers are static.
+    int4 ring[RING][2];
+    float4 gsc[GPW][2], dsc[NSD];
+    // uniform bases (scalar registers) plus one 32-bit offset per lane
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const uint8_t *gbase = lp.w_gate + (int64_t(e) * F + wv * GPW * 16) * (D / 4);
+    const uint8_t *ubase = lp.w_up + (int64_t(e) * F + wv * GPW * 16) * (D / 4);
+    const uint8_t *dbase = lp.w_down + (int64_t(e) * D + wv * NSD * 16) * (F / 4);
+    const float *gsbase = lp.s_gate + int64_t(e) * F + wv * GPW * 16;
+    const float *usbase = lp.s_up + int64_t(e) * F + wv * GPW * 16;
+    const float *dsbase = lp.s_down + int64_t(e) * D + wv * NSD * 16;
+    const uint32_t gofs = uint32_t(l16 * (D / 4) + 16 * g4), dofs = uint32_t(l16 * (F / 4) + 16 * g4);
+    const uint32_t sofs = uint32_t(4 * g4);
+    auto issue = [&](int u) {
+        if (u >= NU) return;
+        int4 (&slot)[2] = ring[u % RING];
+        if (u < NGU) {
+            const int gi = u / SG, kc = u % SG;
+            slot[0] = *reinterpret_cast<const int4 *>(gbase + gi * 16 * (D / 4) + 64 * kc + gofs);
+            slot[1] = *reinterpret_cast<const int4 *>(ubase + gi * 16 * (D / 4) + 64 * kc + gofs);
+            if (kc == 0) {
+                gsc[gi][0] = *reinterpret_cast<const float4 *>(gsbase + gi * 16 + sofs);
+                gsc[gi][1] = *reinterpret_cast<const float4 *>(usbase + gi * 16 + sofs);
+            }
+        } else {
+            const int n = u - NGU;
+            slot[0] = *reinterpret_cast<const int4 *>(dbase + n * 16 * (F / 4) + dofs);
+            if (SD > 1) slot[1] = *reinterpret_cast<const int4 *>(dbase + n * 16 * (F / 4) + 64 + dofs);
+            dsc[n] = *reinterpret_cast<const float4 *>(dsbase + n * 16 + sofs);
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < kPfAhead; u++) issue(u);
+
     const int32_t *counts = reinterpret_cast<const int32_t *>(ws + L.counts);
     const int32_t *offsets = reinterpret_cast<const int32_t *>(ws + L.offsets);
     const int32_t *pairs = reinterpret_cast<const int32_t *>(ws + L.pairs);
     const float *tinfo = reinterpret_cast<const float *>(ws + L.tinfo);
     const int8_t *xdig = reinterpret_cast<const int8_t *>(ws + L.xdig);
     float *ybuf = reinterpret_cast<float *>(ws + L.y);
-    const int nv = min(MT, counts[e] - mt * MT);
-    const int p0 = offsets[e] + mt * MT;
     const int k = dm.k;
-
+    const int nv = min(MT, counts[e] - mt * MT);   // tokens in this tile (>= 1)
+    const int msv = (nv + 15) >> 4;                 // token sub-tiles holding any of them
     if (t < MT) {
-        const int pr = t < nv ? pairs[p0 + t] : -1;
+        const int pr = t < nv ? pairs[offsets[e] + mt * MT + t] : -1;
         s_pair[t] = pr;
         s_tk[t][0] = pr >= 0 ? tinfo[2 * (pr / k)] : 0.0f;
         s_tk[t][1] = pr >= 0 ? tinfo[2 * (pr / k) + 1] : 0.0f;
     }
     __syncthreads();
-    // 1. activation tile: row (m, plane) = plane of token m
-    for (int idx = t; idx < MT * P * (D / 16); idx += kPfT) {
-        const int r = idx / (D / 16), c = idx % (D / 16), m = r / P, pr = s_pair[m];
-        const int4 v = pr >= 0 ? reinterpret_cast<const int4 *>(xdig + (int64_t(pr / k) * P + r % P) * D)[c]
-                               : make_int4(0, 0, 0, 0);
-        *reinterpret_cast<int4 *>(sm + tofs(r, c, D)) = v;
+    // 1. activation tile: row (m, plane) = plane of token m; every load of a thread is issued
+    //    before its first LDS store
+    {
+        constexpr int NCH = MT * P * (D / 16), PER = (NCH + NT - 1) / NT;
+        int4 v[PER];
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            const int idx = t + i * NT;
+            const int r = idx / (D / 16), c = idx % (D / 16);
+            const int pr = idx < NCH ? s_pair[r / P] : -1;
+            v[i] = pr >= 0 ? reinterpret_cast<const int4 *>(xdig + (int64_t(pr / k) * P + r % P) * D)[c]
+                           : make_int4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            const int idx = t + i * NT;
+            if (idx < NCH) *reinterpret_cast<int4 *>(sm + tofs(idx / (D / 16), idx % (D / 16), D)) = v[i];
+        }
     }
     __syncthreads();
 
-    // 2. gate/up.  With small tiles (PF) the code rows of group gi+1 are requested before group gi
-    //    is computed (two register buffers, fully unrolled so every index is static).
-    constexpr bool PF = false;
+    // 2. gate/up, one unit (4 steps of 64 inputs) at a time, kPfAhead units in flight
     float hreg[GPW][MS][4];
-    int4 cg[PF ? 2 : 1][SG], cu[PF ? 2 : 1][SG];
-    auto load_gu = [&](int gi, int4 (&g)[SG], int4 (&u)[SG]) {
-        const int r0 = (wave * GPW + gi) * 16;
-        const int4 *grow = reinterpret_cast<const int4 *>(lp.w_gate + (int64_t(e) * F + r0 + l16) * (D / 4));
-        const int4 *urow = reinterpret_cast<const int4 *>(lp.w_up + (int64_t(e) * F + r0 + l16) * (D / 4));
-#pragma unroll
-        for (int S = 0; S < SG; S++) {
-            g[S] = grow[4 * S + g4];
-            u[S] = urow[4 * S + g4];
-        }
-    };
-    if (PF) load_gu(0, cg[0], cu[0]);
 #pragma unroll
     for (int gi = 0; gi < GPW; gi++) {
-        const int r0 = (wave * GPW + gi) * 16;
-        const int bi = PF ? (gi & 1) : 0;
-        if (!PF) load_gu(gi, cg[0], cu[0]);
-        if (PF && gi + 1 < GPW) load_gu(gi + 1, cg[bi ^ 1], cu[bi ^ 1]);
         v4i accg[P][MS], accu[P][MS];
 #pragma unroll
         for (int pl = 0; pl < P; pl++)
 #pragma unroll
             for (int ms = 0; ms < MS; ms++) accg[pl][ms] = accu[pl][ms] = v4i{0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < 4 * SG; i++) {
-            const int S = i >> 2, s = i & 3;
-            const int c = 16 * S + 4 * g4 + s;
-            const v4i bg = decode16(word_of(cg[bi][S], s)), bu = decode16(word_of(cu[bi][S], s));
+        for (int kc = 0; kc < SG; kc++) {
+            const int u = gi * SG + kc;
+            issue(u + kPfAhead);
+            const int4 gq = ring[u % RING][0], uq = ring[u % RING][1];
 #pragma unroll
-            for (int ms = 0; ms < MS; ms++)
+            for (int s = 0; s < 4; s++) {
+                const int c = 16 * kc + 4 * g4 + s;
+                const v4i bg = decode16(word_of(gq, s)), bu = decode16(word_of(uq, s));
 #pragma unroll
-                for (int pl = 0; pl < P; pl++) {
-                    const v4i av = *reinterpret_cast<const v4i *>(sm + tofs((ms * 16 + l16) * P + pl, c, D));
-                    accg[pl][ms] = mfma8(av, bg, accg[pl][ms]);
-                    accu[pl][ms] = mfma8(av, bu, accu[pl][ms]);
-                }
-            if (!PF) __builtin_amdgcn_sched_barrier(0);
+                for (int ms = 0; ms < MS; ms++)
+#pragma unroll
+                    for (int pl = 0; pl < P; pl++) {
+                        const v4i av = *reinterpret_cast<const v4i *>(sm + tofs((ms * 16 + l16) * P + pl, c, D));
+                        accg[pl][ms] = mfma8(bg, av, accg[pl][ms]);
+                        accu[pl][ms] = mfma8(bu, av, accu[pl][ms]);
+                    }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        const float sgv = lp.s_gate[int64_t(e) * F + r0 + l16], suv = lp.s_up[int64_t(e) * F + r0 + l16];
+        // epilogue: lane holds h rows 16 gi' + 4 g4 + r of token ms * 16 + l16
 #pragma unroll
-        for (int ms = 0; ms < MS; ms++)
+        for (int ms = 0; ms < MS; ms++) {
+            if (ms > 0 && ms >= msv) {
+#pragma unroll
+                for (int r = 0; r < 4; r++) hreg[gi][ms][r] = 0.0f;
+                continue;
+            }
+            const int m = ms * 16 + l16;
+            const float tk0 = s_tk[m][0], tk1 = s_tk[m][1];
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const int m = ms * 16 + 4 * g4 + r;
+                const float sgv = comp(gsc[gi][0], r), suv = comp(gsc[gi][1], r);
                 float gate, up;
                 if (INT8) {
-                    gate = (float(accg[0][ms][r]) * s_tk[m][0]) * sgv;
-                    up = (float(accu[0][ms][r]) * s_tk[m][0]) * suv;
+                    gate = (float(accg[0][ms][r]) * tk0) * sgv;
+                    up = (float(accu[0][ms][r]) * tk0) * suv;
                 } else {
                     int32_t ag[P], au[P];
 #pragma unroll
@@ -191,31 +236,34 @@ __global__ __launch_bounds__(PfShape<MT>::T) void k_pf_ffn(Dims dm, BatchedWs L,
                         ag[pl] = accg[pl][ms][r];
                         au[pl] = accu[pl][ms][r];
                     }
-                    const int sh = __float_as_int(s_tk[m][0]);
-                    gate = float_value<P>(ag, sh) * sgv * s_tk[m][1];
-                    up = float_value<P>(au, sh) * suv * s_tk[m][1];
+                    const int sh = __float_as_int(tk0);
+                    gate = float_value<P>(ag, sh) * sgv * tk1;
+                    up = float_value<P>(au, sh) * suv * tk1;
                 }
                 hreg[gi][ms][r] = tw_silu(gate) * up;
             }
-        if (!PF) __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_sched_barrier(0);   // four SiLUs at a time: bounded temporaries
+        }
     }
 
-    // 3. per-token max |h|, then int8 re-quantisation or digit planes of h into LDS
+    // 3. per-token max |h| (registers, the four lanes of a token, LDS over waves), then int8
+    //    re-quantisation or digit planes of h into LDS
 #pragma unroll
-    for (int ms = 0; ms < MS; ms++)
+    for (int ms = 0; ms < MS; ms++) {
+        float v = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
-            float v = 0.0f;
+        for (int gi = 0; gi < GPW; gi++)
 #pragma unroll
-            for (int gi = 0; gi < GPW; gi++) v = fmaxf(v, fabsf(hreg[gi][ms][r]));
-            v = row16_max(v);
-            if (l16 == 0) s_pam[wave][ms * 16 + 4 * g4 + r] = v;
-        }
+            for (int r = 0; r < 4; r++) v = fmaxf(v, fabsf(hreg[gi][ms][r]));
+        v = fmaxf(v, __shfl_xor(v, 16));
+        v = fmaxf(v, __shfl_xor(v, 32));
+        if (g4 == 0) s_pam[wave][ms * 16 + l16] = v;
+    }
     __syncthreads();   // every wave is done with the activation tile
     if (t < MT) {
         float am = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kPfW; w++) am = fmaxf(am, s_pam[w][t]);
+        for (int w = 0; w < W; w++) am = fmaxf(am, s_pam[w][t]);
         s_amx[t] = am;
         if (INT8)
             s_hk[t] = am > 0.0f ? am / 127.0f : 0.0f;
@@ -224,21 +272,20 @@ __global__ __launch_bounds__(PfShape<MT>::T) void k_pf_ffn(Dims dm, BatchedWs L,
     }
     __syncthreads();
 #pragma unroll
-    for (int gi = 0; gi < GPW; gi++) {
-        const int row = (wave * GPW + gi) * 16 + l16;
-        const int pos = perm16(row);
+    for (int ms = 0; ms < MS; ms++) {
+        const int m = ms * 16 + l16;
+        const float am = s_amx[m], hk = s_hk[m];
 #pragma unroll
-        for (int ms = 0; ms < MS; ms++)
+        for (int gi = 0; gi < GPW; gi++)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const int m = ms * 16 + 4 * g4 + r;
+                const int pos = perm16((wave * GPW + gi) * 16 + 4 * g4 + r);
                 if (INT8) {
-                    const float am = s_amx[m];
                     const int8_t q = am > 0.0f ? int8_quant(hreg[gi][ms][r], 127.0f / am) : int8_t(0);
                     sm[tofs(m, pos >> 4, F) + (pos & 15)] = q;
                 } else {
                     int8_t dg[P];
-                    float_digits<P>(hreg[gi][ms][r], __float_as_int(s_hk[m]), dg);
+                    float_digits<P>(hreg[gi][ms][r], __float_as_int(hk), dg);
 #pragma unroll
                     for (int pl = 0; pl < P; pl++) sm[tofs(m * P + pl, pos >> 4, F) + (pos & 15)] = dg[pl];
                 }
@@ -246,22 +293,15 @@ __global__ __launch_bounds__(PfShape<MT>::T) void k_pf_ffn(Dims dm, BatchedWs L,
     }
     __syncthreads();
 
-    // 4. down (with small tiles, the next sub-tile's code rows are requested before the current
-    //    one is computed)
-    int4 cdv[PF ? 2 : 1][SD];
-    auto load_dn = [&](int nt, int4 (&cd)[SD]) {
-        const int R0 = (wave * NSD + nt) * 16;
-        const int4 *drow = reinterpret_cast<const int4 *>(lp.w_down + (int64_t(e) * D + R0 + l16) * (F / 4));
+    // 4. down, one 16-row block per unit; lane holds output rows R0 + 4 g4 .. +3 of token
+    //    ms * 16 + l16 and stores them as one 16-byte vector (padding tokens write the spare row
+    //    behind the last pair, so every store is unconditional)
 #pragma unroll
-        for (int S = 0; S < SD; S++) cd[S] = drow[4 * S + g4];
-    };
-    if (PF) load_dn(0, cdv[0]);
-#pragma unroll
-    for (int nt = 0; nt < NSD; nt++) {
-        const int R0 = (wave * NSD + nt) * 16;
-        const int bi = PF ? (nt & 1) : 0;
-        if (!PF) load_dn(nt, cdv[0]);
-        if (PF && nt + 1 < NSD) load_dn(nt + 1, cdv[bi ^ 1]);
+    for (int n = 0; n < NSD; n++) {
+        const int u = NGU + n;
+        issue(u + kPfAhead);
+        const int R0 = (wave * NSD + n) * 16;
+        const int4 q0 = ring[u % RING][0], q1 = ring[u % RING][1];
         v4i acc[P][MS];
 #pragma unroll
         for (int pl = 0; pl < P; pl++)
@@ -270,34 +310,37 @@ __global__ __launch_bounds__(PfShape<MT>::T) void k_pf_ffn(Dims dm, BatchedWs L,
 #pragma unroll
         for (int i = 0; i < 4 * SD; i++) {
             const int S = i >> 2, s = i & 3;
-            const v4i bd = decode16(word_of(cdv[bi][S], s));
+            const v4i bd = decode16(word_of(S == 0 ? q0 : q1, s));
             const int c = 16 * S + 4 * g4 + s;
 #pragma unroll
             for (int ms = 0; ms < MS; ms++)
 #pragma unroll
                 for (int pl = 0; pl < P; pl++) {
                     const v4i av = *reinterpret_cast<const v4i *>(sm + tofs((ms * 16 + l16) * P + pl, c, F));
-                    acc[pl][ms] = mfma8(av, bd, acc[pl][ms]);
+                    acc[pl][ms] = mfma8(bd, av, acc[pl][ms]);
                 }
-            if (!PF) __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        const float sdv = lp.s_down[int64_t(e) * D + R0 + l16];
 #pragma unroll
-        for (int ms = 0; ms < MS; ms++)
+        for (int ms = 0; ms < MS; ms++) {
+            if (ms > 0 && ms >= msv) break;
+            const int m = ms * 16 + l16, pr = s_pair[m];
+            const float hk = s_hk[m];
+            float y[4];
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const int m = ms * 16 + 4 * g4 + r, pr = s_pair[m];
-                float y;
                 if (INT8) {
-                    y = (float(acc[0][ms][r]) * s_hk[m]) * sdv;
+                    y[r] = (float(acc[0][ms][r]) * hk) * comp(dsc[n], r);
                 } else {
                     int32_t ad[P];
 #pragma unroll
                     for (int pl = 0; pl < P; pl++) ad[pl] = acc[pl][ms][r];
-                    y = float_value<P>(ad, __float_as_int(s_hk[m])) * sdv;
+                    y[r] = float_value<P>(ad, __float_as_int(hk)) * comp(dsc[n], r);
                 }
-                if (pr >= 0) ybuf[int64_t(pr) * D + R0 + l16] = y;
             }
+            const int64_t row = pr >= 0 ? int64_t(pr) : L.spare_row;
+            *reinterpret_cast<float4 *>(ybuf + row * D + R0 + 4 * g4) = make_float4(y[0], y[1], y[2], y[3]);
+        }
     }
 }
 
@@ -314,7 +357,7 @@ int pf_run(const Dims &dm, const LayerPtrs &lp, int64_t T, const BatchedWs &L, u
         attr_set.store(1, std::memory_order_relaxed);
     }
     const int nb = int((max_tiles(dm, T, MT) + 15) / 16 * 16);
-    k_pf_ffn<D, F, P, MT><<<nb, PfShape<MT>::T, lds, static_cast<hipStream_t>(stream)>>>(dm, L, lp, ws, nb);
+    k_pf_ffn<D, F, P, MT><<<nb, PfShape<MT, P>::T, lds, static_cast<hipStream_t>(stream)>>>(dm, L, lp, ws, nb);
     return int(hipGetLastError());
 }
 

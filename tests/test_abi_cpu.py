@@ -112,6 +112,10 @@ def test_decode_errors(L):
     l0 = layer()
     l0.w_down = A[3] + 8                                             # packed rows need 16-B alignment
     assert call((tw.TwLayer * 1)(l0)) == E_UNSUP
+    l0 = layer()
+    l0.s_up = A[5] + 4                                               # scales need 16-B alignment
+    assert call((tw.TwLayer * 1)(l0)) == E_UNSUP
+    assert call(one, ws=A[10] + 16) == E_UNSUP                       # workspace needs 256-B alignment
     two = (tw.TwLayer * 2)(layer(), layer(F=256))
     assert call(two, n=2) == E_SHAPE                                  # layers must match
     two = (tw.TwLayer * 2)(layer(), layer(pre=1))
@@ -137,4 +141,6 @@ def test_batched_errors(L):
     assert call(xo=A[8] + 64) == E_ALIAS
     assert call(T=0, xi=None, xo=None, ws=None) == OK
     assert call(act=1, ll=layer(pre=1), wsb=need8) == E_UNSUP         # int8 with pre-norm
+    assert call(ws=A[10] + 128) == E_UNSUP                            # workspace needs 256-B alignment
+    assert call(xi=A[8] + 8) == E_UNSUP                               # activations need 16-B alignment
     assert L.ternary_moe_ffn_batched(None, 4, A[8], 1, A[9], 1, 0, None, None, A[10], need, s) == E_NULL
