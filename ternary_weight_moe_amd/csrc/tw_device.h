@@ -366,10 +366,15 @@ __device__ void topk_softmax_wave_t(const float *logits, int E, int k, int32_t *
     uint32_t idv[KPER];
 #pragma unroll
     for (int s = 0; s < KPER; s++) {
+        // every load issued before the first use (the index is clamped, the key selected after)
         const int e = lane + 64 * s;
-        key[s] = e < E ? float_order_key(logits[e] + 0.0f) : 0u;   // 0: no candidate
+        key[s] = __float_as_uint(logits[e < E ? e : E - 1]);
         idv[s] = uint32_t(e);
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < KPER; s++)   // 0: no candidate
+        key[s] = int(idv[s]) < E ? float_order_key(__uint_as_float(key[s]) + 0.0f) : 0u;
     // sort the lane's candidates: key descending, id ascending (ids already ascending in s)
 #pragma unroll
     for (int i = 1; i < KPER; i++)

@@ -56,9 +56,11 @@ inline DecodeWs decode_ws_layout(const Dims &dm) {
 
 // ---- batched workspace ------------------------------------------------------------------------
 struct BatchedWs {
-    size_t ctrl, logits, ids, gates, tinfo, xdig, counts, offsets, pairs, tiles, h, y, total;
-    int64_t spare_row;   // y row behind the last pair: stores of padding tokens land there
+    size_t ctrl, logits, ids, gates, tinfo, xdig, counts, offsets, pairs, tiles, tilemeta, h, y, total;
+    int64_t spare_row;   // first of kSpareRows y rows behind the last pair: stores of padding
+                         // tokens land there (workgroup b uses row spare_row + b % kSpareRows)
 };
+constexpr int kSpareRows = 256;
 constexpr int kTileTokens = 64;     // tokens per tile: large tiles (many tokens per expert)
 constexpr int kSmallTile = 16;      // tokens per tile: small tiles (few tokens per expert)
 // Upper bound on the (expert, tile) work items of T tokens in tiles of `tt` tokens, rounded up to a
@@ -82,8 +84,9 @@ inline BatchedWs batched_ws_layout(const Dims &dm, int64_t T, int planes) {
     w.offsets = o; o += align256(sizeof(int32_t) * (dm.E + 1));
     w.pairs = o;   o += align256(sizeof(int32_t) * pairs);
     w.tiles = o;   o += align256(sizeof(int32_t) * size_t(max_tiles(dm, T, kSmallTile) + 16));
+    w.tilemeta = o; o += align256(2 * sizeof(int32_t) * size_t(max_tiles(dm, T, kSmallTile) + 16));
     w.h = o;       o += align256(sizeof(float) * pairs * dm.F);
-    w.y = o;       o += align256(sizeof(float) * (pairs + 1) * dm.d);
+    w.y = o;       o += align256(sizeof(float) * (pairs + kSpareRows) * dm.d);
     w.spare_row = int64_t(pairs);
     w.total = o;
     return w;

@@ -91,51 +91,147 @@ __device__ __forceinline__ void load_chunk8(const void *x, int64_t row, int d, i
     }
 }
 
-// The canonical sum of 256 partials (tw_device.h: wave_sum per 64, then (w0+w1)+(w2+w3)) is a
-// balanced binary tree over the partials in natural order; a single lane can form it from LDS.
-__device__ __forceinline__ float tree16(const float *p)
+// The 8 int8 values of chunk c (elements 8c .. 8c+7) of one plane, stored in the 4x4-transposed
+// layout of tw_device.h: the lanes holding chunks 2i and 2i+1 (adjacent lanes; chunk parity =
+// lane parity) fill one 16-byte group together, exchanging half of their bytes, so every lane
+// stores 8 contiguous bytes.  Both lanes of a pair must call it.
+__device__ __forceinline__ void store_chunk_digits(int8_t *plane, int c, const int8_t (&q)[8])
 {
-    float v[16];
+    uint32_t h[4];
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-        const float4 f = reinterpret_cast<const float4 *>(p)[q];
-        v[4 * q] = f.x;
-        v[4 * q + 1] = f.y;
-        v[4 * q + 2] = f.z;
-        v[4 * q + 3] = f.w;
+    for (int s = 0; s < 4; s++) h[s] = uint32_t(uint8_t(q[s])) | (uint32_t(uint8_t(q[4 + s])) << 8);
+    const bool odd = c & 1;
+    const uint32_t send = odd ? (h[0] | (h[1] << 16)) : (h[2] | (h[3] << 16));
+    const uint32_t recv = uint32_t(dpp_i<kDppXor1>(int32_t(send)));
+    uint2 o;
+    if (!odd) {
+        o.x = h[0] | ((recv & 0xffffu) << 16);
+        o.y = h[1] | ((recv >> 16) << 16);
+    } else {
+        o.x = (recv & 0xffffu) | (h[2] << 16);
+        o.y = (recv >> 16) | (h[3] << 16);
     }
-#pragma unroll
-    for (int w = 1; w < 16; w <<= 1)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2 * w) v[i] = v[i] + v[i + w];
-    return v[0];
+    *reinterpret_cast<uint2 *>(plane + 16 * (c >> 1) + 8 * (c & 1)) = o;
 }
 
-__device__ __forceinline__ float tree256(const float *p)
-{
-    float g[16];
-#pragma unroll
-    for (int i = 0; i < 16; i++) g[i] = tree16(p + 16 * i);
-#pragma unroll
-    for (int w = 1; w < 16; w <<= 1)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2 * w) g[i] = g[i] + g[i + w];
-    return g[0];
-}
-
-// Workgroup (experts 4 f .. 4 f + 3, tokens 8 g .. 8 g + 7): thread t forms the canonical partial of
-// its chunks for every (expert, token) pair and for every token's sum of squares; the partials go
-// to LDS and one lane per pair adds them in the canonical tree.  All loads are issued at once.
-// NCH: 8-element chunks per thread (1 for d <= 2048, 2 for d <= 4096).
-constexpr int kRouteExp = 4;
-
-template <int NCH>
-__global__ __launch_bounds__(256) void k_route_experts(const void *__restrict__ x, int x_bf16,
-                                                       const void *__restrict__ wr, int w_bf16,
-                                                       int64_t T, int d, int E, int pre_norm,
-                                                       float *__restrict__ logits)
+// Digit planes (QP = 2, 3) or int8 absmax codes (QP = 1) of a token whose chunks c = t + 256 i
+// this thread holds, given the token's max |x| and canonical sum of squares.
+template <int QP, int NCH>
+__device__ __forceinline__ void quantize_token(const float (&v)[NCH][8], int nch, float am, float ss, int d,
+                                               int pre_norm, int8_t *xd, float *ti)
 {
     const int t = threadIdx.x;
+    if constexpr (QP == 1) {
+        const float inv = am > 0.0f ? 127.0f / am : 0.0f;
+#pragma unroll
+        for (int i = 0; i < NCH; i++) {
+            const int c = t + 256 * i;
+            if (c < nch) {
+                int8_t q[8];
+#pragma unroll
+                for (int j = 0; j < 8; j++) q[j] = am > 0.0f ? int8_quant(v[i][j], inv) : int8_t(0);
+                store_chunk_digits(xd, c, q);
+            }
+        }
+        if (t == 0) ti[0] = am > 0.0f ? am / 127.0f : 0.0f;
+    } else {
+        const int sh = float_digit_shift(am, QP);
+#pragma unroll
+        for (int i = 0; i < NCH; i++) {
+            const int c = t + 256 * i;
+            if (c < nch) {
+                int8_t q[QP][8];
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    int8_t dg[QP];
+                    float_digits<QP>(v[i][j], sh, dg);
+#pragma unroll
+                    for (int p = 0; p < QP; p++) q[p][j] = dg[p];
+                }
+#pragma unroll
+                for (int p = 0; p < QP; p++) store_chunk_digits(xd + p * d, c, q[p]);
+            }
+        }
+        if (t == 0) {
+            reinterpret_cast<int32_t *>(ti)[0] = sh;
+            ti[1] = pre_norm ? inv_rms_of(ss, d) : 1.0f;
+        }
+    }
+}
+
+// Chunk t + 256 i (8 elements) of rows row0 + r, r < R, of d bf16 or fp32 elements: raw_rows8
+// issues the loads (rows past the n valid ones re-read the last valid row: their values are never
+// used; the dtype branch is uniform, so the loads form one straight run), cvt_rows8 turns them into
+// fp32 after every load of the caller has been issued.  Chunks past the row read as zeros.
+template <int R, int NCH>
+__device__ __forceinline__ void raw_rows8(const void *base, int bf16, int64_t row0, int n, int d,
+                                          int4 (&raw)[R][NCH][2])
+{
+    const int t = threadIdx.x, nch = d >> 3;
+    if (bf16) {
+        const uint16_t *b = static_cast<const uint16_t *>(base);
+#pragma unroll
+        for (int r = 0; r < R; r++)
+#pragma unroll
+            for (int i = 0; i < NCH; i++) {
+                const int c = min(t + 256 * i, nch - 1);
+                raw[r][i][0] = reinterpret_cast<const int4 *>(b + (row0 + min(r, n - 1)) * d)[c];
+            }
+    } else {
+        const float *f = static_cast<const float *>(base);
+#pragma unroll
+        for (int r = 0; r < R; r++)
+#pragma unroll
+            for (int i = 0; i < NCH; i++) {
+                const int c = min(t + 256 * i, nch - 1);
+                const int4 *p = reinterpret_cast<const int4 *>(f + (row0 + min(r, n - 1)) * d) + 2 * c;
+                raw[r][i][0] = p[0];
+                raw[r][i][1] = p[1];
+            }
+    }
+}
+
+template <int R, int NCH>
+__device__ __forceinline__ void cvt_rows8(const int4 (&raw)[R][NCH][2], int bf16, int d,
+                                          float (&v)[R][NCH][8])
+{
+    const int t = threadIdx.x, nch = d >> 3;
+#pragma unroll
+    for (int r = 0; r < R; r++)
+#pragma unroll
+        for (int i = 0; i < NCH; i++) {
+            const int4 a = raw[r][i][0], b = raw[r][i][1];
+            const bool in = t + 256 * i < nch;
+            if (bf16) {
+                const uint32_t w[4] = {uint32_t(a.x), uint32_t(a.y), uint32_t(a.z), uint32_t(a.w)};
+#pragma unroll
+                for (int j = 0; j < 8; j++) v[r][i][j] = in ? bf16_to_f32(uint16_t(w[j >> 1] >> (16 * (j & 1)))) : 0.0f;
+            } else {
+                const int q[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int j = 0; j < 8; j++) v[r][i][j] = in ? __int_as_float(q[j]) : 0.0f;
+            }
+        }
+}
+
+// Router logits.  Workgroup (experts 8 f .. 8 f + 7, tokens 8 g .. 8 g + 7), 256 threads: thread t
+// holds the 8-element chunks t + 256 i of the 8 tokens and of the 8 router rows (every load issued
+// at once) and forms the canonical partial of each (expert, token) pair and each token's sum of
+// squares; the partials go to LDS and each wave adds those of two tokens in the canonical tree
+// (4 partials per lane, then wave_sum), so the pre-RMSNorm factor multiplies the logits in the same
+// wave.  With QP > 0 the workgroups of the first expert group also write the tokens' activation
+// codes (quantize_token) and their scale words: the router has every chunk of its tokens in
+// registers already.
+constexpr int kRouteExp = 8;
+
+template <int NCH, int QP>
+__global__ __launch_bounds__(256) void k_route(const void *__restrict__ x, int x_bf16,
+                                               const void *__restrict__ wr, int w_bf16, int64_t T,
+                                               int d, int E, int pre_norm,
+                                               float *__restrict__ logits, int8_t *__restrict__ xdig,
+                                               float *__restrict__ tinfo)
+{
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int e0 = blockIdx.x * kRouteExp;
     const int64_t tb = int64_t(blockIdx.y) * kRouteTok;
     const int nt = int(T - tb < kRouteTok ? T - tb : kRouteTok);
@@ -143,19 +239,15 @@ __global__ __launch_bounds__(256) void k_route_experts(const void *__restrict__ 
     const int nch = d >> 3;
     constexpr int NPR = kRouteExp * kRouteTok + kRouteTok;   // pairs + sums of squares
     __shared__ __attribute__((aligned(16))) float part[NPR][256];
-    float xv[kRouteTok][NCH][8];
-#pragma unroll
-    for (int u = 0; u < kRouteTok; u++)
-#pragma unroll
-        for (int i = 0; i < NCH; i++) {
-            const int c = t + 256 * i;
-            if (u < nt && c < nch) {
-                load_chunk8(x, tb + u, d, c, x_bf16, xv[u][i]);
-            } else {
-#pragma unroll
-                for (int q = 0; q < 8; q++) xv[u][i][q] = 0.0f;
-            }
-        }
+    __shared__ float s_am[4][kRouteTok];
+    float xv[kRouteTok][NCH][8], wv[kRouteExp][NCH][8];
+    {
+        int4 rx[kRouteTok][NCH][2], rw[kRouteExp][NCH][2];
+        raw_rows8<kRouteTok, NCH>(x, x_bf16, tb, nt, d, rx);
+        raw_rows8<kRouteExp, NCH>(wr, w_bf16, e0, ne, d, rw);
+        cvt_rows8<kRouteTok, NCH>(rx, x_bf16, d, xv);
+        cvt_rows8<kRouteExp, NCH>(rw, w_bf16, d, wv);
+    }
 #pragma unroll
     for (int u = 0; u < kRouteTok; u++) {
         float ss = 0.0f;
@@ -164,44 +256,73 @@ __global__ __launch_bounds__(256) void k_route_experts(const void *__restrict__ 
 #pragma unroll
             for (int q = 0; q < 8; q++) ss = ss + xv[u][i][q] * xv[u][i][q];
         part[kRouteExp * kRouteTok + u][t] = ss;
-    }
 #pragma unroll
-    for (int m = 0; m < kRouteExp; m++) {
-        float wv[NCH][8];
-#pragma unroll
-        for (int i = 0; i < NCH; i++) {
-            const int c = t + 256 * i;
-            if (m < ne && c < nch) {
-                load_chunk8(wr, e0 + m, d, c, w_bf16, wv[i]);
-            } else {
-#pragma unroll
-                for (int q = 0; q < 8; q++) wv[i][q] = 0.0f;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kRouteTok; u++) {
+        for (int m = 0; m < kRouteExp; m++) {
             float dot = 0.0f;
 #pragma unroll
             for (int i = 0; i < NCH; i++)
 #pragma unroll
-                for (int q = 0; q < 8; q++) dot = dot + wv[i][q] * xv[u][i][q];
+                for (int q = 0; q < 8; q++) dot = dot + wv[m][i][q] * xv[u][i][q];
             part[m * kRouteTok + u][t] = dot;
         }
     }
+    const bool quant = QP > 0 && blockIdx.x == 0;
+    if (quant) {
+#pragma unroll
+        for (int u = 0; u < kRouteTok; u++) {
+            float am = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NCH; i++)
+#pragma unroll
+                for (int q = 0; q < 8; q++) am = fmaxf(am, fabsf(xv[u][i][q]));
+            am = wave_max(am);
+            if (lane == 0) s_am[wave][u] = am;
+        }
+    }
     __syncthreads();
-    __shared__ float s_inv[kRouteTok];
-    if (t < kRouteTok) s_inv[t] = inv_rms_of(tree256(part[kRouteExp * kRouteTok + t]), d);
-    __syncthreads();
-    if (t < kRouteExp * kRouteTok) {
-        const int m = t / kRouteTok, u = t % kRouteTok;
-        if (m < ne && u < nt) {
-            float v = tree256(part[t]);
-            if (pre_norm) v = v * s_inv[u];
-            logits[(tb + u) * E + e0 + m] = v;
+    // wave w: tokens 2w, 2w + 1 -- the sum of squares, then the 8 logits
+    float ssv[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const int u = 2 * wave + h;
+        auto tree = [&](int r) {
+            const float4 f = reinterpret_cast<const float4 *>(part[r])[lane];
+            return wave_sum((f.x + f.y) + (f.z + f.w));
+        };
+        const float ss = tree(kRouteExp * kRouteTok + u);
+        ssv[h] = ss;
+        const float inv = pre_norm ? inv_rms_of(ss, d) : 1.0f;
+        float out = 0.0f;
+#pragma unroll
+        for (int m = 0; m < kRouteExp; m++) {
+            float v = tree(m * kRouteTok + u);
+            if (pre_norm) v = v * inv;
+            if (lane == m) out = v;
+        }
+        if (u < nt && lane < ne) logits[(tb + u) * E + e0 + lane] = out;
+    }
+    if constexpr (QP > 0) {
+        if (!quant) return;
+        // the token's sum of squares is needed by thread 0 only (its scale word); wave w has those
+        // of tokens 2w, 2w + 1, so it is passed through LDS
+        __shared__ float s_ss[kRouteTok];
+        if (lane == 0) {
+            s_ss[2 * wave] = ssv[0];
+            s_ss[2 * wave + 1] = ssv[1];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kRouteTok; u++) {
+            if (u >= nt) break;
+            const float am = fmaxf(fmaxf(s_am[0][u], s_am[1][u]), fmaxf(s_am[2][u], s_am[3][u]));
+            quantize_token<QP, NCH>(xv[u], nch, am, s_ss[u], d, pre_norm,
+                                    xdig + (tb + u) * int64_t(QP) * d, tinfo + 2 * (tb + u));
         }
     }
 }
 
+// Top-k and gates of T tokens, one wave per token; KPER = candidates per lane (E <= 64 KPER).
+template <int KPER>
 __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, int64_t T, int E,
                                               int k, int32_t *__restrict__ ids,
                                               float *__restrict__ gates)
@@ -209,7 +330,18 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
     const int lane = threadIdx.x & 63;
     const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    topk_softmax_wave(logits + t * E, E, k, ids + t * k, gates + t * k, lane);
+    topk_softmax_wave_t<KPER>(logits + t * E, E, k, ids + t * k, gates + t * k, lane);
+}
+
+void launch_topk(const float *logits, int64_t T, int E, int k, int32_t *ids, float *gates, void *stream)
+{
+    const unsigned g = unsigned((T + 3) / 4);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (E <= 64) k_topk<1><<<g, 256, 0, st>>>(logits, T, E, k, ids, gates);
+    else if (E <= 128) k_topk<2><<<g, 256, 0, st>>>(logits, T, E, k, ids, gates);
+    else if (E <= 256) k_topk<4><<<g, 256, 0, st>>>(logits, T, E, k, ids, gates);
+    else if (E <= 512) k_topk<8><<<g, 256, 0, st>>>(logits, T, E, k, ids, gates);
+    else k_topk<16><<<g, 256, 0, st>>>(logits, T, E, k, ids, gates);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -413,7 +545,7 @@ __global__ __launch_bounds__(256) void k_bat_quant_x(BatchedArgs a, const void *
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int64_t tok = blockIdx.x;
     const int d = a.dm.d, nch = d >> 3;
-    float v[2][8];
+    float v[2][8] = {};
     float am = 0.0f, ss = 0.0f;
 #pragma unroll
     for (int i = 0; i < 2; i++) {
@@ -436,48 +568,18 @@ __global__ __launch_bounds__(256) void k_bat_quant_x(BatchedArgs a, const void *
     }
     __syncthreads();
     am = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
-    int8_t *xd = reinterpret_cast<int8_t *>(ws + a.L.xdig) + tok * int64_t(P) * d;
-    float *ti = reinterpret_cast<float *>(ws + a.L.tinfo) + 2 * tok;
-    if (INT8) {
-        const float inv = am > 0.0f ? 127.0f / am : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const int c = t + 256 * i;
-            if (c < nch) {
-#pragma unroll
-                for (int j = 0; j < 8; j++)
-                    xd[perm16(8 * c + j)] = am > 0.0f ? int8_quant(v[i][j], inv) : int8_t(0);
-            }
-        }
-        if (t == 0) ti[0] = am > 0.0f ? am / 127.0f : 0.0f;
-    } else {
-        const int sh = float_digit_shift(am, P);
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const int c = t + 256 * i;
-            if (c < nch) {
-#pragma unroll
-                for (int j = 0; j < 8; j++) {
-                    int8_t dg[P];
-                    float_digits<P>(v[i][j], sh, dg);
-#pragma unroll
-                    for (int p = 0; p < P; p++) xd[p * d + perm16(8 * c + j)] = dg[p];
-                }
-            }
-        }
-        if (t == 0) {
-            // the pre-RMSNorm sum of squares in the canonical order (partials t, waves in pairs)
-            const float tot = (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]);
-            reinterpret_cast<int32_t *>(ti)[0] = sh;
-            ti[1] = a.dm.pre_norm ? inv_rms_of(tot, d) : 1.0f;
-        }
-    }
+    // the pre-RMSNorm sum of squares in the canonical order (partials t, waves in pairs)
+    const float tot = (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]);
+    quantize_token<INT8 ? 1 : P, 2>(v, nch, am, tot, d, a.dm.pre_norm,
+                                    reinterpret_cast<int8_t *>(ws + a.L.xdig) + tok * int64_t(P) * d,
+                                    reinterpret_cast<float *>(ws + a.L.tinfo) + 2 * tok);
 }
 
 // Groups the T*k (token, slot) pairs by expert: counts[e], offsets[E+1] and pairs[] (the pairs of
 // expert e at offsets[e]..offsets[e+1]; their order inside a group is not fixed, and no result
 // depends on it: every pair is computed on its own), plus the list of (expert, tile of tt tokens)
-// work items: tiles[0] = their number, tiles[1 + i] = e | (tile << 10).
+// work items: tiles[0] = their number, tiles[1 + i] = e | (tile << 10), tilemeta[i] = (position of the
+// tile's first pair in pairs[], its number of pairs).
 // One workgroup of 1024 threads; counts and placement use LDS atomics.  The ids are read in passes
 // of 32 per thread, all loads of a pass issued before any is used (one memory round trip per pass
 // instead of one per id); with a single pass they stay in registers for the placement.  Up to
@@ -498,7 +600,8 @@ __global__ __launch_bounds__(1024) void k_group(BatchedArgs a, const int32_t *__
     int32_t *offsets = reinterpret_cast<int32_t *>(ws + a.L.offsets);
     int32_t *pairs = reinterpret_cast<int32_t *>(ws + a.L.pairs);
     int32_t *tiles = reinterpret_cast<int32_t *>(ws + a.L.tiles);
-    __shared__ int32_t cnt[kMaxExperts], cur[kMaxExperts], scan[1024], tscan[1024];
+    int2 *tmeta = reinterpret_cast<int2 *>(ws + a.L.tilemeta);
+    __shared__ int32_t cnt[kMaxExperts], cur[kMaxExperts], s_wc[16], s_wt[16];
     const int64_t npass = (npairs + kGrpPass - 1) / kGrpPass;
     int v[kGrpPer];
     // v[i] = id of pair base + t + 1024 i, or -1 past the end
@@ -520,27 +623,44 @@ __global__ __launch_bounds__(1024) void k_group(BatchedArgs a, const int32_t *__
     __syncthreads();
     const int c = t < E ? cnt[t] : 0;
     const int nt = (c + tt - 1) / tt;
-    scan[t] = c;
-    tscan[t] = nt;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {   // inclusive scans (Hillis-Steele)
-        const int x = t >= off ? scan[t - off] : 0, y = t >= off ? tscan[t - off] : 0;
-        __syncthreads();
-        scan[t] += x;
-        tscan[t] += y;
-        __syncthreads();
+    // exclusive scans of the counts and tile counts over the experts: inside each wave, then over
+    // the 16 wave totals
+    const int lane = t & 63, wave = t >> 6;
+    int ic = c, it = nt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int uc = __shfl_up(ic, off), ut = __shfl_up(it, off);
+        if (lane >= off) {
+            ic += uc;
+            it += ut;
+        }
     }
-    const int off_e = scan[t] - c, tile0 = tscan[t] - nt;
-    const int placed = scan[1023];   // pairs with a valid id
+    if (lane == 63) {
+        s_wc[wave] = ic;
+        s_wt[wave] = it;
+    }
+    __syncthreads();
+    int bc = 0, bt = 0, placed = 0, ntiles = 0;
+#pragma unroll
+    for (int w = 0; w < 16; w++) {
+        bc += w < wave ? s_wc[w] : 0;
+        bt += w < wave ? s_wt[w] : 0;
+        placed += s_wc[w];   // pairs with a valid id
+        ntiles += s_wt[w];
+    }
+    const int off_e = bc + ic - c, tile0 = bt + it - nt;
     if (t < E) {
         counts[t] = c;
         offsets[t] = off_e;
         cur[t] = off_e;
-        for (int i = 0; i < nt; i++) tiles[1 + tile0 + i] = t | (i << 10);
+        for (int i = 0; i < nt; i++) {
+            tiles[1 + tile0 + i] = t | (i << 10);
+            tmeta[tile0 + i] = make_int2(off_e + i * tt, min(tt, c - i * tt));
+        }
     }
     if (t == 1023) {
         offsets[E] = placed;
-        tiles[0] = tscan[1023];
+        tiles[0] = ntiles;
     }
     __syncthreads();
     for (int64_t ps = 0; ps < npass; ps++) {
@@ -887,11 +1007,13 @@ __global__ __launch_bounds__(256) void k_bat_combine(BatchedArgs a, const void *
             bool ok[8];
 #pragma unroll
             for (int u = 0; u < 8; u++) {
-                const int j = j0 + u;
-                const int id = j < k ? ids[tok * k + j] : -1;
+                // the y row of every slot exists (unwritten for slots without a valid expert, and
+                // then unused), so its load does not wait for the id
+                const int j = j0 + u < k ? j0 + u : k - 1;
+                const int id = j0 + u < k ? ids[tok * k + j] : -1;
                 ok[u] = id >= 0 && id < E;
-                g[u] = ok[u] ? gates[tok * k + j] : 0.0f;
-                if (ok[u]) {
+                g[u] = gates[tok * k + j];
+                {
                     const int4 *yp = reinterpret_cast<const int4 *>(ybuf + (tok * k + j) * d + 8 * c);
                     const int4 p0 = yp[0], p1 = yp[1];
                     yv[u][0] = __int_as_float(p0.x); yv[u][1] = __int_as_float(p0.y);
@@ -924,14 +1046,30 @@ __global__ __launch_bounds__(256) void k_bat_combine(BatchedArgs a, const void *
 
 inline hipStream_t S(void *s) { return static_cast<hipStream_t>(s); }
 
+// Router logits of T tokens; with quant_planes > 0 the first expert group of workgroups also writes
+// the tokens' activation codes (quant_planes = 1: int8 absmax, 2 or 3: digit planes) and scale words.
 void launch_router(const void *x, int x_bf16, const void *wr, int w_bf16, int64_t T, const Dims &dm,
-                   float *logits, void *stream)
+                   float *logits, void *stream, int quant_planes = 0, int8_t *xdig = nullptr,
+                   float *tinfo = nullptr)
 {
     const dim3 grid(unsigned((dm.E + kRouteExp - 1) / kRouteExp), unsigned((T + kRouteTok - 1) / kRouteTok));
-    if (dm.d <= 2048)
-        k_route_experts<1><<<grid, 256, 0, S(stream)>>>(x, x_bf16, wr, w_bf16, T, dm.d, dm.E, dm.pre_norm, logits);
-    else
-        k_route_experts<2><<<grid, 256, 0, S(stream)>>>(x, x_bf16, wr, w_bf16, T, dm.d, dm.E, dm.pre_norm, logits);
+#define TW_ROUTE(NCH, QP) k_route<NCH, QP><<<grid, 256, 0, S(stream)>>>(x, x_bf16, wr, w_bf16, T, dm.d, dm.E, dm.pre_norm, logits, xdig, tinfo)
+    if (dm.d <= 2048) {
+        switch (quant_planes) {
+        case 1: TW_ROUTE(1, 1); break;
+        case 2: TW_ROUTE(1, 2); break;
+        case 3: TW_ROUTE(1, 3); break;
+        default: TW_ROUTE(1, 0); break;
+        }
+    } else {
+        switch (quant_planes) {
+        case 1: TW_ROUTE(2, 1); break;
+        case 2: TW_ROUTE(2, 2); break;
+        case 3: TW_ROUTE(2, 3); break;
+        default: TW_ROUTE(2, 0); break;
+        }
+    }
+#undef TW_ROUTE
 }
 
 int last_error() { return int(hipGetLastError()); }
@@ -965,15 +1103,18 @@ int batched_p(const Dims &dm, const LayerPtrs &lp, int64_t T, const void *x_in, 
     BatchedArgs a{dm, batched_ws_layout(dm, T, INT8 ? 1 : 3), T, INT8};
     uint8_t *w = static_cast<uint8_t *>(ws);
     if (!ids) {
+        // routing inside: the router also writes the activation codes
         float *logits = reinterpret_cast<float *>(w + a.L.logits);
         int32_t *wid = reinterpret_cast<int32_t *>(w + a.L.ids);
         float *wg = reinterpret_cast<float *>(w + a.L.gates);
-        launch_router(x_in, in_bf16, lp.w_router, dm.router_bf16, T, dm, logits, stream);
-        k_topk<<<unsigned((T + 3) / 4), 256, 0, S(stream)>>>(logits, T, dm.E, dm.k, wid, wg);
+        launch_router(x_in, in_bf16, lp.w_router, dm.router_bf16, T, dm, logits, stream, P,
+                      reinterpret_cast<int8_t *>(w + a.L.xdig), reinterpret_cast<float *>(w + a.L.tinfo));
+        launch_topk(logits, T, dm.E, dm.k, wid, wg, stream);
         ids = wid;
         gates = wg;
+    } else {
+        k_bat_quant_x<P, INT8><<<unsigned(T), 256, 0, S(stream)>>>(a, x_in, in_bf16, w);
     }
-    k_bat_quant_x<P, INT8><<<unsigned(T), 256, 0, S(stream)>>>(a, x_in, in_bf16, w);
     int tile = kTileTokens;
     if (grouped_mfma_serves(dm, T, P, &tile)) {
         int r = launch_group(a, ids, w, tile, stream);
@@ -1020,7 +1161,7 @@ int launch_route(const void *x, int x_bf16, const void *w_router, int w_bf16, in
                  const Dims &dm, float *logits, int32_t *ids, float *gates, void *stream)
 {
     launch_router(x, x_bf16, w_router, w_bf16, T, dm, logits, stream);
-    k_topk<<<unsigned((T + 3) / 4), 256, 0, S(stream)>>>(logits, T, dm.E, dm.k, ids, gates);
+    launch_topk(logits, T, dm.E, dm.k, ids, gates, stream);
     return last_error();
 }
 

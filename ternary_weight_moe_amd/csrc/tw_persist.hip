@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
     __shared__ float sums[2 * C::Q];
     __shared__ float ys[K * C::RD];
     __shared__ float red[4][2 + kEM];
-    __shared__ int32_t s_hmax[K];                                // per-expert max |h| (float bits)
+    __shared__ float s_wmax[C::HW / 64];                         // max |h| per 64-word chunk
     __shared__ int32_t s_ids[kMaxTopK];
     __shared__ float s_gates[kMaxTopK];
     __shared__ int s_hsh[K];
@@ -183,7 +183,6 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
                 }
             }
         }
-        if (t < K) s_hmax[t] = 0;
         __syncthreads();
 
         // 2. router threads: their 8-element chunks of x (amax, sum of squares, router partials in
@@ -323,13 +322,16 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
 #pragma unroll
             for (int n = 0; n < N; n++) {
                 const float am = wave_max(fabsf(__uint_as_float(uint32_t(v[n]))));
-                if (lane == 0) atomicMax(&s_hmax[(t + kPT * n) / F], __float_as_int(am));
+                if (lane == 0) s_wmax[n * kNW + wave] = am;   // chunk (t + kPT n) / 64
             }
             __syncthreads();
 #pragma unroll
             for (int n = 0; n < N; n++) {
                 const int w = t + kPT * n, j = w / F, i = w % F;
-                const int sh = float_digit_shift(__int_as_float(s_hmax[j]), 2);
+                float hm = 0.0f;
+#pragma unroll
+                for (int c = 0; c < F / 64; c++) hm = fmaxf(hm, s_wmax[j * (F / 64) + c]);
+                const int sh = float_digit_shift(hm, 2);
                 if (i == 0) s_hsh[j] = sh;
                 int8_t dg[2];
                 float_digits<2>(__uint_as_float(uint32_t(v[n])), sh, dg);

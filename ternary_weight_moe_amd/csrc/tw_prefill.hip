@@ -40,15 +40,14 @@ typedef int32_t v4i __attribute__((ext_vector_type(4)));
 
 // Waves per workgroup: 16 for 16-token tiles of at most two planes (at <= 128 VGPRs, four waves
 // per SIMD); 8 otherwise (256 VGPRs: the h values of a 64-token tile stay in registers).
+// AHEAD: code units (one 16-row block of gate and up codes over 256 inputs, or one 16-row block of
+// down codes) each wave keeps in flight ahead of the one it computes.
 template <int MT, int P>
 struct PfShape {
     static constexpr int W = (MT <= 16 && P <= 2) ? 16 : 8;
     static constexpr int T = 64 * W;
+    static constexpr int AHEAD = 4;
 };
-
-// Code units (one 16-row block of gate and up codes over 256 inputs, or one 16-row block of down
-// codes) each wave keeps in flight ahead of the one it computes.
-constexpr int kPfAhead = 4;
 
 // The 16 int8 weights of one 32-bit code word, in the transposed order of the activation digits.
 __device__ __forceinline__ v4i decode16(uint32_t w)
@@ -90,6 +89,7 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
     constexpr int NSD = D / 16 / W;       // down row blocks of 16 per wave
     constexpr int SG = D / 256, SD = F / 256;
     constexpr int NGU = GPW * SG;         // gate/up code units per wave, then NSD down units
+    constexpr int kPfAhead = PfShape<MT, P>::AHEAD;
     constexpr int NU = NGU + NSD, RING = kPfAhead + 1;
     static_assert(SD <= 2, "a down unit is at most two 16-byte chunks per lane");
     extern __shared__ __attribute__((aligned(16))) int8_t sm[];   // [MT][P] rows of D, later of F
@@ -105,9 +105,12 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
     // and every 16 workgroups cover 16 consecutive tiles, so work spreads evenly over the XCDs
     const int b = blockIdx.x;
     const int ti = (b / 16) * 16 + (b % 8) * 2 + ((b / 8) & 1);
-    const int ntiles = tiles[0], tile = tiles[1 + ti];   // ti < nb: inside the tile list's storage
+    const int2 *tmeta = reinterpret_cast<const int2 *>(ws + L.tilemeta);
+    // ti < nb: inside the tile lists' storage (read before the count is known, then checked)
+    const int ntiles = tiles[0], tile = tiles[1 + ti];
+    const int2 meta = tmeta[ti];
     if (ti >= ntiles) return;
-    const int e = tile & 1023, mt = tile >> 10;
+    const int e = tile & 1023;
 
     // Code units of this wave, in the order they are computed.  Unit u < NGU: gate and up chunk
     // u % SG of h-row group u / SG (plus, with the first chunk, the group's gate and up scales);
@@ -146,39 +149,46 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
 #pragma unroll
     for (int u = 0; u < kPfAhead; u++) issue(u);
 
-    const int32_t *counts = reinterpret_cast<const int32_t *>(ws + L.counts);
-    const int32_t *offsets = reinterpret_cast<const int32_t *>(ws + L.offsets);
     const int32_t *pairs = reinterpret_cast<const int32_t *>(ws + L.pairs);
     const float *tinfo = reinterpret_cast<const float *>(ws + L.tinfo);
     const int8_t *xdig = reinterpret_cast<const int8_t *>(ws + L.xdig);
     float *ybuf = reinterpret_cast<float *>(ws + L.y);
     const int k = dm.k;
-    const int nv = min(MT, counts[e] - mt * MT);   // tokens in this tile (>= 1)
+    const int nv = meta.y;                          // tokens in this tile (1 .. MT)
     const int msv = (nv + 15) >> 4;                 // token sub-tiles holding any of them
-    if (t < MT) {
-        const int pr = t < nv ? pairs[offsets[e] + mt * MT + t] : -1;
-        s_pair[t] = pr;
-        s_tk[t][0] = pr >= 0 ? tinfo[2 * (pr / k)] : 0.0f;
-        s_tk[t][1] = pr >= 0 ? tinfo[2 * (pr / k) + 1] : 0.0f;
-    }
+    if (t < MT) s_pair[t] = t < nv ? pairs[meta.x + t] : -1;
     __syncthreads();
-    // 1. activation tile: row (m, plane) = plane of token m; every load of a thread is issued
-    //    before its first LDS store
+    // 1. activation tile: row (m, plane) = plane of token m, and each token's scale words; every
+    //    load is issued before the first LDS store (padding tokens re-read token 0's row, which
+    //    every tile has, and store zeros)
     {
         constexpr int NCH = MT * P * (D / 16), PER = (NCH + NT - 1) / NT;
+        const int pr0 = s_pair[0];
         int4 v[PER];
+        float tk0 = 0.0f, tk1 = 0.0f;
+        if (t < MT) {
+            const int pr = s_pair[t] >= 0 ? s_pair[t] : pr0;
+            tk0 = tinfo[2 * (pr / k)];
+            tk1 = tinfo[2 * (pr / k) + 1];
+        }
 #pragma unroll
         for (int i = 0; i < PER; i++) {
-            const int idx = t + i * NT;
+            const int idx = min(t + i * NT, NCH - 1);
             const int r = idx / (D / 16), c = idx % (D / 16);
-            const int pr = idx < NCH ? s_pair[r / P] : -1;
-            v[i] = pr >= 0 ? reinterpret_cast<const int4 *>(xdig + (int64_t(pr / k) * P + r % P) * D)[c]
-                           : make_int4(0, 0, 0, 0);
+            const int pr = s_pair[r / P] >= 0 ? s_pair[r / P] : pr0;
+            v[i] = reinterpret_cast<const int4 *>(xdig + (int64_t(pr / k) * P + r % P) * D)[c];
+        }
+        if (t < MT) {
+            s_tk[t][0] = s_pair[t] >= 0 ? tk0 : 0.0f;
+            s_tk[t][1] = s_pair[t] >= 0 ? tk1 : 0.0f;
         }
 #pragma unroll
         for (int i = 0; i < PER; i++) {
             const int idx = t + i * NT;
-            if (idx < NCH) *reinterpret_cast<int4 *>(sm + tofs(idx / (D / 16), idx % (D / 16), D)) = v[i];
+            const int r = idx / (D / 16);
+            if (idx < NCH)
+                *reinterpret_cast<int4 *>(sm + tofs(r, idx % (D / 16), D)) =
+                    s_pair[r / P] >= 0 ? v[i] : make_int4(0, 0, 0, 0);
         }
     }
     __syncthreads();
@@ -192,6 +202,17 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
         for (int pl = 0; pl < P; pl++)
 #pragma unroll
             for (int ms = 0; ms < MS; ms++) accg[pl][ms] = accu[pl][ms] = v4i{0, 0, 0, 0};
+        // the activation fragments of step q + 1 are read from LDS while step q is computed
+        v4i avc[MS][P], avn[MS][P];
+        auto read_av = [&](int q, v4i (&av)[MS][P]) {
+            const int c = 16 * (q >> 2) + 4 * g4 + (q & 3);
+#pragma unroll
+            for (int ms = 0; ms < MS; ms++)
+#pragma unroll
+                for (int pl = 0; pl < P; pl++)
+                    av[ms][pl] = *reinterpret_cast<const v4i *>(sm + tofs((ms * 16 + l16) * P + pl, c, D));
+        };
+        read_av(0, avc);
 #pragma unroll
         for (int kc = 0; kc < SG; kc++) {
             const int u = gi * SG + kc;
@@ -199,18 +220,22 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
             const int4 gq = ring[u % RING][0], uq = ring[u % RING][1];
 #pragma unroll
             for (int s = 0; s < 4; s++) {
-                const int c = 16 * kc + 4 * g4 + s;
+                const int q = 4 * kc + s;
+                if (q + 1 < 4 * SG) read_av(q + 1, avn);
                 const v4i bg = decode16(word_of(gq, s)), bu = decode16(word_of(uq, s));
 #pragma unroll
                 for (int ms = 0; ms < MS; ms++)
 #pragma unroll
                     for (int pl = 0; pl < P; pl++) {
-                        const v4i av = *reinterpret_cast<const v4i *>(sm + tofs((ms * 16 + l16) * P + pl, c, D));
-                        accg[pl][ms] = mfma8(bg, av, accg[pl][ms]);
-                        accu[pl][ms] = mfma8(bu, av, accu[pl][ms]);
+                        accg[pl][ms] = mfma8(bg, avc[ms][pl], accg[pl][ms]);
+                        accu[pl][ms] = mfma8(bu, avc[ms][pl], accu[pl][ms]);
                     }
-                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ms = 0; ms < MS; ms++)
+#pragma unroll
+                    for (int pl = 0; pl < P; pl++) avc[ms][pl] = avn[ms][pl];
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         // epilogue: lane holds h rows 16 gi' + 4 g4 + r of token ms * 16 + l16
 #pragma unroll
@@ -244,6 +269,9 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
             }
             __builtin_amdgcn_sched_barrier(0);   // four SiLUs at a time: bounded temporaries
         }
+        // keep the waves of the workgroup in step: the two waves of a SIMD then stay busy together
+        // instead of one finishing early and waiting at the end of the phase
+        if (gi + 1 < GPW) __syncthreads();
     }
 
     // 3. per-token max |h| (registers, the four lanes of a token, LDS over waves), then int8
@@ -294,8 +322,9 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
     __syncthreads();
 
     // 4. down, one 16-row block per unit; lane holds output rows R0 + 4 g4 .. +3 of token
-    //    ms * 16 + l16 and stores them as one 16-byte vector (padding tokens write the spare row
-    //    behind the last pair, so every store is unconditional)
+    //    ms * 16 + l16 and stores them as one 16-byte vector (padding tokens write a spare row
+    //    behind the last pair, one per workgroup slot so that few workgroups share one; every store
+    //    is unconditional, so the wait for a code unit never has to wait for a store)
 #pragma unroll
     for (int n = 0; n < NSD; n++) {
         const int u = NGU + n;
@@ -307,20 +336,32 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
         for (int pl = 0; pl < P; pl++)
 #pragma unroll
             for (int ms = 0; ms < MS; ms++) acc[pl][ms] = v4i{0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < 4 * SD; i++) {
-            const int S = i >> 2, s = i & 3;
-            const v4i bd = decode16(word_of(S == 0 ? q0 : q1, s));
-            const int c = 16 * S + 4 * g4 + s;
+        // h fragments of step i + 1 are read from LDS while step i is computed
+        v4i hc[MS][P], hn[MS][P];
+        auto read_h = [&](int i, v4i (&hv)[MS][P]) {
+            const int c = 16 * (i >> 2) + 4 * g4 + (i & 3);
 #pragma unroll
             for (int ms = 0; ms < MS; ms++)
 #pragma unroll
-                for (int pl = 0; pl < P; pl++) {
-                    const v4i av = *reinterpret_cast<const v4i *>(sm + tofs((ms * 16 + l16) * P + pl, c, F));
-                    acc[pl][ms] = mfma8(bd, av, acc[pl][ms]);
-                }
-            __builtin_amdgcn_sched_barrier(0);
+                for (int pl = 0; pl < P; pl++)
+                    hv[ms][pl] = *reinterpret_cast<const v4i *>(sm + tofs((ms * 16 + l16) * P + pl, c, F));
+        };
+        read_h(0, hc);
+#pragma unroll
+        for (int i = 0; i < 4 * SD; i++) {
+            const int S = i >> 2, s = i & 3;
+            if (i + 1 < 4 * SD) read_h(i + 1, hn);
+            const v4i bd = decode16(word_of(S == 0 ? q0 : q1, s));
+#pragma unroll
+            for (int ms = 0; ms < MS; ms++)
+#pragma unroll
+                for (int pl = 0; pl < P; pl++) acc[pl][ms] = mfma8(bd, hc[ms][pl], acc[pl][ms]);
+#pragma unroll
+            for (int ms = 0; ms < MS; ms++)
+#pragma unroll
+                for (int pl = 0; pl < P; pl++) hc[ms][pl] = hn[ms][pl];
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ms = 0; ms < MS; ms++) {
             if (ms > 0 && ms >= msv) break;
@@ -338,9 +379,10 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
                     y[r] = float_value<P>(ad, __float_as_int(hk)) * comp(dsc[n], r);
                 }
             }
-            const int64_t row = pr >= 0 ? int64_t(pr) : L.spare_row;
+            const int64_t row = pr >= 0 ? int64_t(pr) : L.spare_row + (blockIdx.x % kSpareRows);
             *reinterpret_cast<float4 *>(ybuf + row * D + R0 + 4 * g4) = make_float4(y[0], y[1], y[2], y[3]);
         }
+        if ((n & 3) == 3 && n + 1 < NSD) __syncthreads();   // waves in step, as in gate/up
     }
 }
 
