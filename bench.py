@@ -260,7 +260,7 @@ def main():
     ap.add_argument("--workload", default="stack24_b1",
                     choices=["stack24_b1", "layer_b1", "batched_b64", "batched_b64_int8",
                              "prefill_4096", "copy_calib"])
-    ap.add_argument("--cpu-tokens", type=int, default=12)
+    ap.add_argument("--cpu-tokens", type=int, default=36)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

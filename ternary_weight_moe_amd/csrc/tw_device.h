@@ -359,7 +359,7 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
 }
 
 template <int KPER>
-__device__ void topk_softmax_wave_t(const float *logits, int E, int k, int32_t *ids_out,
+__device__ __forceinline__ void topk_softmax_wave_t(const float *logits, int E, int k, int32_t *ids_out,
                                     float *gates_out, int lane)
 {
     uint32_t key[KPER];
