@@ -62,7 +62,7 @@ struct BatchedWs {
 };
 constexpr int kSpareRows = 256;
 constexpr int kTileTokens = 64;     // tokens per tile: large tiles (many tokens per expert)
-constexpr int kSmallTile = 16;      // tokens per tile: small tiles (few tokens per expert)
+constexpr int kMinTile = 8;         // fewest tokens per tile of any grouping (sizes the tile lists)
 // Upper bound on the (expert, tile) work items of T tokens in tiles of `tt` tokens, rounded up to a
 // multiple of 8.
 inline int64_t max_tiles(const Dims &dm, int64_t T, int tt)
@@ -83,8 +83,8 @@ inline BatchedWs batched_ws_layout(const Dims &dm, int64_t T, int planes) {
     w.counts = o;  o += align256(sizeof(int32_t) * (dm.E + 1));
     w.offsets = o; o += align256(sizeof(int32_t) * (dm.E + 1));
     w.pairs = o;   o += align256(sizeof(int32_t) * pairs);
-    w.tiles = o;   o += align256(sizeof(int32_t) * size_t(max_tiles(dm, T, kSmallTile) + 16));
-    w.tilemeta = o; o += align256(2 * sizeof(int32_t) * size_t(max_tiles(dm, T, kSmallTile) + 16));
+    w.tiles = o;   o += align256(sizeof(int32_t) * size_t(max_tiles(dm, T, kMinTile) + 16));
+    w.tilemeta = o; o += align256(2 * sizeof(int32_t) * size_t(max_tiles(dm, T, kMinTile) + 16));
     w.h = o;       o += align256(sizeof(float) * pairs * dm.F);
     w.y = o;       o += align256(sizeof(float) * (pairs + kSpareRows) * dm.d);
     w.spare_row = int64_t(pairs);

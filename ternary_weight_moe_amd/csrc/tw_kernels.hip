@@ -219,9 +219,9 @@ __device__ __forceinline__ void cvt_rows8(const int4 (&raw)[R][NCH][2], int bf16
 // at once) and forms the canonical partial of each (expert, token) pair and each token's sum of
 // squares; the partials go to LDS and each wave adds those of two tokens in the canonical tree
 // (4 partials per lane, then wave_sum), so the pre-RMSNorm factor multiplies the logits in the same
-// wave.  With QP > 0 the workgroups of the first expert group also write the tokens' activation
-// codes (quantize_token) and their scale words: the router has every chunk of its tokens in
-// registers already.
+// wave.  With QP > 0 the workgroups also write the tokens' activation codes (quantize_token) and
+// their scale words, token u of a group by expert group u: the router has every chunk of its
+// tokens in registers already.
 constexpr int kRouteExp = 8;
 
 template <int NCH, int QP>
@@ -266,10 +266,14 @@ __global__ __launch_bounds__(256) void k_route(const void *__restrict__ x, int x
             part[m * kRouteTok + u][t] = dot;
         }
     }
-    const bool quant = QP > 0 && blockIdx.x == 0;
+    // token u's codes are written by expert group u % gridDim.x, so the work spreads over the
+    // expert groups (one token each when there are at least 8)
+    const bool quant = QP > 0 && int(blockIdx.x) < kRouteTok;
+    auto mine = [&](int u) { return u % int(gridDim.x) == int(blockIdx.x); };
     if (quant) {
 #pragma unroll
         for (int u = 0; u < kRouteTok; u++) {
+            if (!mine(u)) continue;
             float am = 0.0f;
 #pragma unroll
             for (int i = 0; i < NCH; i++)
@@ -314,6 +318,7 @@ __global__ __launch_bounds__(256) void k_route(const void *__restrict__ x, int x
 #pragma unroll
         for (int u = 0; u < kRouteTok; u++) {
             if (u >= nt) break;
+            if (!mine(u)) continue;
             const float am = fmaxf(fmaxf(s_am[0][u], s_am[1][u]), fmaxf(s_am[2][u], s_am[3][u]));
             quantize_token<QP, NCH>(xv[u], nch, am, s_ss[u], d, pre_norm,
                                     xdig + (tb + u) * int64_t(QP) * d, tinfo + 2 * (tb + u));

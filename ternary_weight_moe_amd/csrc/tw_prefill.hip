@@ -44,7 +44,7 @@ typedef int32_t v4i __attribute__((ext_vector_type(4)));
 // down codes) each wave keeps in flight ahead of the one it computes.
 template <int MT, int P>
 struct PfShape {
-    static constexpr int W = (MT <= 16 && P <= 2) ? 16 : 8;
+    static constexpr int W = MT * P <= 16 ? 16 : 8;
     static constexpr int T = 64 * W;
     static constexpr int AHEAD = 4;
 };
@@ -82,9 +82,14 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
 {
     constexpr int W = PfShape<MT, P>::W, NT = PfShape<MT, P>::T;
     static_assert(D % 256 == 0 && F % 256 == 0 && F % (16 * W) == 0 && D % (16 * W) == 0, "shape");
-    static_assert(MT % 16 == 0 && MT <= NT, "tile");
+    static_assert((P == 1 || P == 2) && (MT * P) % 16 == 0 && MT <= NT, "tile");
     constexpr bool INT8 = P == 1;
-    constexpr int MS = MT / 16;           // token sub-tiles
+    // The activation tile has MT * P rows (token m, plane pl at row m P + pl); an MFMA takes 16 of
+    // them, so the 16 result columns of sub-tile rs are 16 / P tokens x P planes: column l16 is
+    // token rs * TPS + l16 / P, plane l16 % P.  With two planes the two lanes of a token combine
+    // their sums with one DPP exchange.
+    constexpr int RS = MT * P / 16;       // row sub-tiles
+    constexpr int TPS = 16 / P;           // tokens per row sub-tile
     constexpr int GPW = F / 16 / W;       // h-row groups of 16 per wave
     constexpr int NSD = D / 16 / W;       // down row blocks of 16 per wave
     constexpr int SG = D / 256, SD = F / 256;
@@ -155,7 +160,8 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
     float *ybuf = reinterpret_cast<float *>(ws + L.y);
     const int k = dm.k;
     const int nv = meta.y;                          // tokens in this tile (1 .. MT)
-    const int msv = (nv + 15) >> 4;                 // token sub-tiles holding any of them
+    const int rsv = (nv + TPS - 1) / TPS;           // row sub-tiles holding any of them
+    const int pl = l16 % P;                         // this lane's plane in every sub-tile
     if (t < MT) s_pair[t] = t < nv ? pairs[meta.x + t] : -1;
     __syncthreads();
     // 1. activation tile: row (m, plane) = plane of token m, and each token's scale words; every
@@ -194,23 +200,19 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
     __syncthreads();
 
     // 2. gate/up, one unit (4 steps of 64 inputs) at a time, kPfAhead units in flight
-    float hreg[GPW][MS][4];
+    float hreg[GPW][RS][4];
 #pragma unroll
     for (int gi = 0; gi < GPW; gi++) {
-        v4i accg[P][MS], accu[P][MS];
+        v4i accg[RS], accu[RS];
 #pragma unroll
-        for (int pl = 0; pl < P; pl++)
-#pragma unroll
-            for (int ms = 0; ms < MS; ms++) accg[pl][ms] = accu[pl][ms] = v4i{0, 0, 0, 0};
+        for (int rs = 0; rs < RS; rs++) accg[rs] = accu[rs] = v4i{0, 0, 0, 0};
         // the activation fragments of step q + 1 are read from LDS while step q is computed
-        v4i avc[MS][P], avn[MS][P];
-        auto read_av = [&](int q, v4i (&av)[MS][P]) {
+        v4i avc[RS], avn[RS];
+        auto read_av = [&](int q, v4i (&av)[RS]) {
             const int c = 16 * (q >> 2) + 4 * g4 + (q & 3);
 #pragma unroll
-            for (int ms = 0; ms < MS; ms++)
-#pragma unroll
-                for (int pl = 0; pl < P; pl++)
-                    av[ms][pl] = *reinterpret_cast<const v4i *>(sm + tofs((ms * 16 + l16) * P + pl, c, D));
+            for (int rs = 0; rs < RS; rs++)
+                av[rs] = *reinterpret_cast<const v4i *>(sm + tofs(rs * 16 + l16, c, D));
         };
         read_av(0, avc);
 #pragma unroll
@@ -224,48 +226,41 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
                 if (q + 1 < 4 * SG) read_av(q + 1, avn);
                 const v4i bg = decode16(word_of(gq, s)), bu = decode16(word_of(uq, s));
 #pragma unroll
-                for (int ms = 0; ms < MS; ms++)
+                for (int rs = 0; rs < RS; rs++) {
+                    accg[rs] = mfma8(bg, avc[rs], accg[rs]);
+                    accu[rs] = mfma8(bu, avc[rs], accu[rs]);
+                }
 #pragma unroll
-                    for (int pl = 0; pl < P; pl++) {
-                        accg[pl][ms] = mfma8(bg, avc[ms][pl], accg[pl][ms]);
-                        accu[pl][ms] = mfma8(bu, avc[ms][pl], accu[pl][ms]);
-                    }
-#pragma unroll
-                for (int ms = 0; ms < MS; ms++)
-#pragma unroll
-                    for (int pl = 0; pl < P; pl++) avc[ms][pl] = avn[ms][pl];
+                for (int rs = 0; rs < RS; rs++) avc[rs] = avn[rs];
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        // epilogue: lane holds h rows 16 gi' + 4 g4 + r of token ms * 16 + l16
+        // epilogue: lane holds h rows 16 gi' + 4 g4 + r of token rs * TPS + l16 / P
 #pragma unroll
-        for (int ms = 0; ms < MS; ms++) {
-            if (ms > 0 && ms >= msv) {
+        for (int rs = 0; rs < RS; rs++) {
+            if (rs > 0 && rs >= rsv) {
 #pragma unroll
-                for (int r = 0; r < 4; r++) hreg[gi][ms][r] = 0.0f;
+                for (int r = 0; r < 4; r++) hreg[gi][rs][r] = 0.0f;
                 continue;
             }
-            const int m = ms * 16 + l16;
+            const int m = rs * TPS + l16 / P;
             const float tk0 = s_tk[m][0], tk1 = s_tk[m][1];
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const float sgv = comp(gsc[gi][0], r), suv = comp(gsc[gi][1], r);
                 float gate, up;
-                if (INT8) {
-                    gate = (float(accg[0][ms][r]) * tk0) * sgv;
-                    up = (float(accu[0][ms][r]) * tk0) * suv;
+                if constexpr (INT8) {
+                    gate = (float(accg[rs][r]) * tk0) * sgv;
+                    up = (float(accu[rs][r]) * tk0) * suv;
                 } else {
-                    int32_t ag[P], au[P];
-#pragma unroll
-                    for (int pl = 0; pl < P; pl++) {
-                        ag[pl] = accg[pl][ms][r];
-                        au[pl] = accu[pl][ms][r];
-                    }
+                    const int32_t og = dpp_i<kDppXor1>(accg[rs][r]), ou = dpp_i<kDppXor1>(accu[rs][r]);
+                    const int32_t ag[2] = {pl == 0 ? accg[rs][r] : og, pl == 0 ? og : accg[rs][r]};
+                    const int32_t au[2] = {pl == 0 ? accu[rs][r] : ou, pl == 0 ? ou : accu[rs][r]};
                     const int sh = __float_as_int(tk0);
-                    gate = float_value<P>(ag, sh) * sgv * tk1;
-                    up = float_value<P>(au, sh) * suv * tk1;
+                    gate = float_value<2>(ag, sh) * sgv * tk1;
+                    up = float_value<2>(au, sh) * suv * tk1;
                 }
-                hreg[gi][ms][r] = tw_silu(gate) * up;
+                hreg[gi][rs][r] = tw_silu(gate) * up;
             }
             __builtin_amdgcn_sched_barrier(0);   // four SiLUs at a time: bounded temporaries
         }
@@ -275,17 +270,18 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
     }
 
     // 3. per-token max |h| (registers, the four lanes of a token, LDS over waves), then int8
-    //    re-quantisation or digit planes of h into LDS
+    //    re-quantisation or digit planes of h into LDS (with two planes, each lane of a token
+    //    writes its own plane)
 #pragma unroll
-    for (int ms = 0; ms < MS; ms++) {
+    for (int rs = 0; rs < RS; rs++) {
         float v = 0.0f;
 #pragma unroll
         for (int gi = 0; gi < GPW; gi++)
 #pragma unroll
-            for (int r = 0; r < 4; r++) v = fmaxf(v, fabsf(hreg[gi][ms][r]));
+            for (int r = 0; r < 4; r++) v = fmaxf(v, fabsf(hreg[gi][rs][r]));
         v = fmaxf(v, __shfl_xor(v, 16));
         v = fmaxf(v, __shfl_xor(v, 32));
-        if (g4 == 0) s_pam[wave][ms * 16 + l16] = v;
+        if (g4 == 0 && pl == 0) s_pam[wave][rs * TPS + l16 / P] = v;
     }
     __syncthreads();   // every wave is done with the activation tile
     if (t < MT) {
@@ -300,23 +296,23 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
     }
     __syncthreads();
 #pragma unroll
-    for (int ms = 0; ms < MS; ms++) {
-        const int m = ms * 16 + l16;
+    for (int rs = 0; rs < RS; rs++) {
+        const int m = rs * TPS + l16 / P;
         const float am = s_amx[m], hk = s_hk[m];
 #pragma unroll
         for (int gi = 0; gi < GPW; gi++)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int pos = perm16((wave * GPW + gi) * 16 + 4 * g4 + r);
-                if (INT8) {
-                    const int8_t q = am > 0.0f ? int8_quant(hreg[gi][ms][r], 127.0f / am) : int8_t(0);
-                    sm[tofs(m, pos >> 4, F) + (pos & 15)] = q;
+                int8_t q;
+                if constexpr (INT8) {
+                    q = am > 0.0f ? int8_quant(hreg[gi][rs][r], 127.0f / am) : int8_t(0);
                 } else {
-                    int8_t dg[P];
-                    float_digits<P>(hreg[gi][ms][r], __float_as_int(hk), dg);
-#pragma unroll
-                    for (int pl = 0; pl < P; pl++) sm[tofs(m * P + pl, pos >> 4, F) + (pos & 15)] = dg[pl];
+                    int8_t dg[2];
+                    float_digits<2>(hreg[gi][rs][r], __float_as_int(hk), dg);
+                    q = pl == 0 ? dg[0] : dg[1];
                 }
+                sm[tofs(m * P + pl, pos >> 4, F) + (pos & 15)] = q;
             }
     }
     __syncthreads();
@@ -331,20 +327,16 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
         issue(u + kPfAhead);
         const int R0 = (wave * NSD + n) * 16;
         const int4 q0 = ring[u % RING][0], q1 = ring[u % RING][1];
-        v4i acc[P][MS];
+        v4i acc[RS];
 #pragma unroll
-        for (int pl = 0; pl < P; pl++)
-#pragma unroll
-            for (int ms = 0; ms < MS; ms++) acc[pl][ms] = v4i{0, 0, 0, 0};
+        for (int rs = 0; rs < RS; rs++) acc[rs] = v4i{0, 0, 0, 0};
         // h fragments of step i + 1 are read from LDS while step i is computed
-        v4i hc[MS][P], hn[MS][P];
-        auto read_h = [&](int i, v4i (&hv)[MS][P]) {
+        v4i hc[RS], hn[RS];
+        auto read_h = [&](int i, v4i (&hv)[RS]) {
             const int c = 16 * (i >> 2) + 4 * g4 + (i & 3);
 #pragma unroll
-            for (int ms = 0; ms < MS; ms++)
-#pragma unroll
-                for (int pl = 0; pl < P; pl++)
-                    hv[ms][pl] = *reinterpret_cast<const v4i *>(sm + tofs((ms * 16 + l16) * P + pl, c, F));
+            for (int rs = 0; rs < RS; rs++)
+                hv[rs] = *reinterpret_cast<const v4i *>(sm + tofs(rs * 16 + l16, c, F));
         };
         read_h(0, hc);
 #pragma unroll
@@ -353,33 +345,29 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
             if (i + 1 < 4 * SD) read_h(i + 1, hn);
             const v4i bd = decode16(word_of(S == 0 ? q0 : q1, s));
 #pragma unroll
-            for (int ms = 0; ms < MS; ms++)
+            for (int rs = 0; rs < RS; rs++) acc[rs] = mfma8(bd, hc[rs], acc[rs]);
 #pragma unroll
-                for (int pl = 0; pl < P; pl++) acc[pl][ms] = mfma8(bd, hc[ms][pl], acc[pl][ms]);
-#pragma unroll
-            for (int ms = 0; ms < MS; ms++)
-#pragma unroll
-                for (int pl = 0; pl < P; pl++) hc[ms][pl] = hn[ms][pl];
+            for (int rs = 0; rs < RS; rs++) hc[rs] = hn[rs];
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ms = 0; ms < MS; ms++) {
-            if (ms > 0 && ms >= msv) break;
-            const int m = ms * 16 + l16, pr = s_pair[m];
+        for (int rs = 0; rs < RS; rs++) {
+            if (rs > 0 && rs >= rsv) break;
+            const int m = rs * TPS + l16 / P, pr = s_pair[m];
             const float hk = s_hk[m];
             float y[4];
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                if (INT8) {
-                    y[r] = (float(acc[0][ms][r]) * hk) * comp(dsc[n], r);
+                if constexpr (INT8) {
+                    y[r] = (float(acc[rs][r]) * hk) * comp(dsc[n], r);
                 } else {
-                    int32_t ad[P];
-#pragma unroll
-                    for (int pl = 0; pl < P; pl++) ad[pl] = acc[pl][ms][r];
-                    y[r] = float_value<P>(ad, __float_as_int(hk)) * comp(dsc[n], r);
+                    const int32_t o = dpp_i<kDppXor1>(acc[rs][r]);
+                    const int32_t ad[2] = {pl == 0 ? acc[rs][r] : o, pl == 0 ? o : acc[rs][r]};
+                    y[r] = float_value<2>(ad, __float_as_int(hk)) * comp(dsc[n], r);
                 }
             }
-            const int64_t row = pr >= 0 ? int64_t(pr) : L.spare_row + (blockIdx.x % kSpareRows);
+            // the second lane of a two-plane token holds the same values: it writes a spare row
+            const int64_t row = pr >= 0 && pl == 0 ? int64_t(pr) : L.spare_row + (blockIdx.x % kSpareRows);
             *reinterpret_cast<float4 *>(ybuf + row * D + R0 + 4 * g4) = make_float4(y[0], y[1], y[2], y[3]);
         }
         if ((n & 3) == 3 && n + 1 < NSD) __syncthreads();   // waves in step, as in gate/up
@@ -408,11 +396,11 @@ int pf_dispatch(const Dims &dm, const LayerPtrs &lp, int64_t T, int planes, int 
                 const BatchedWs &L, uint8_t *ws, void *stream)
 {
     if (planes == 1) {
-        if (tile == kTileTokens) return pf_run<D, F, 1, kTileTokens>(dm, lp, T, L, ws, stream);
-        return pf_run<D, F, 1, kSmallTile>(dm, lp, T, L, ws, stream);
+        if (tile == 64) return pf_run<D, F, 1, 64>(dm, lp, T, L, ws, stream);
+        return pf_run<D, F, 1, 16>(dm, lp, T, L, ws, stream);
     }
-    if (planes == 2) return pf_run<D, F, 2, kSmallTile>(dm, lp, T, L, ws, stream);
-    return pf_run<D, F, 3, kSmallTile>(dm, lp, T, L, ws, stream);
+    if (tile == 32) return pf_run<D, F, 2, 32>(dm, lp, T, L, ws, stream);
+    return pf_run<D, F, 2, 8>(dm, lp, T, L, ws, stream);
 }
 
 }  // namespace
@@ -420,9 +408,11 @@ int pf_dispatch(const Dims &dm, const LayerPtrs &lp, int64_t T, int planes, int 
 bool grouped_mfma_serves(const Dims &dm, int64_t T, int planes, int *tile)
 {
     const bool shape = (dm.d == 2048 && dm.F == 512) || (dm.d == 1024 && dm.F == 256);
-    if (!shape || dm.E > 1024 || planes < 1 || planes > 3) return false;
-    // int8 with at least 32 tokens per expert on average: 64-token tiles; otherwise 16-token tiles
-    *tile = (planes == 1 && T * dm.k >= int64_t(32) * dm.E) ? kTileTokens : kSmallTile;
+    if (!shape || dm.E > 1024 || planes < 1 || planes > 2) return false;
+    // tiles of 64 activation rows when there are at least 32 of them per expert on average (int8:
+    // 64 tokens, two planes: 32 tokens), else of 16 rows (16 or 8 tokens)
+    const bool big = T * dm.k * planes >= int64_t(32) * dm.E;
+    *tile = planes == 1 ? (big ? 64 : 16) : (big ? 32 : 8);
     return true;
 }
 

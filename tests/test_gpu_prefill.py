@@ -1,7 +1,8 @@
-"""Parity of the grouped int8 MFMA path (many tokens per expert, prefill-shaped) with the CPU
-oracle's int8 specification and with the per-pair v_dot4 path, bit for bit.  The int8 path is
-exact, so the three must agree in every bit of the fp32 output.  Routing is an input (computed by
-moe_route_topk on the GPU and handed to both sides)."""
+"""Parity of the grouped MFMA path (many tokens per expert, prefill-shaped) with the CPU oracle's
+int8 specification and with the per-pair v_dot4 path, bit for bit.  The int8 path is exact, so the
+three must agree in every bit of the fp32 output.  Routing is an input (computed by moe_route_topk
+on the GPU and handed to both sides).  The two-plane (bf16) tiles are checked against the small-tile
+path bit for bit and against the oracle's truth mode; fp32 inputs are checked on the v_dot4 path."""
 import os
 
 import numpy as np
@@ -112,3 +113,47 @@ def test_prefill_int8_second_shape():
     assert np.array_equal(bits(out), ref.view(np.uint32))
     ref_dot = dot_path_in_chunks(pair.gpu, x, ids, gates)
     assert np.array_equal(bits(out), bits(ref_dot))
+
+
+def run_float(layer, x, ids, gates):
+    out = tw.ternary_moe_ffn_batched(layer, x, act="float", expert_ids=ids, gate_w=gates)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_batched_bf16_large_tiles_match_small_tiles(full):
+    # 1024 bf16 tokens (32 pairs per expert on average): 32-token tiles of two digit planes; the same
+    # tokens in 64-token calls take 8-token tiles.  The ternary sums are exact integer sums of the same
+    # digits, so both give the same bits; a sample is also checked against the oracle.
+    T = 1024
+    x = synth.activations(synth.BATCHED_B64, T, seed=91).cuda()
+    _, ids, gates = tw.moe_route_topk(x, full.gpu.w_router, 8)
+    step("batched bf16 T=%d (32-token tiles)" % T)
+    out = run_float(full.gpu, x, ids, gates)
+    step("same tokens in 64-token calls (8-token tiles)")
+    ref = torch.cat([run_float(full.gpu, x[i:i + 64].contiguous(), ids[i:i + 64].contiguous(),
+                               gates[i:i + 64].contiguous()) for i in range(0, T, 64)])
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    step("oracle truth mode on sampled tokens")
+    xs = x.cpu()
+    ids_np, g_np = ids.cpu().numpy(), gates.cpu().numpy()
+    for t in (0, 1, 511, T - 1):
+        o = oracle.ffn_token(full.ora, xs[t].double().numpy(), ids_np[t], g_np[t].astype(np.float64))
+        got = out[t].float().cpu().numpy()
+        assert np.max(np.abs(got - o)) <= 2e-2 * np.max(np.abs(o)), t
+
+
+def test_batched_fp32_input_served_by_dot4_kernels(full):
+    # fp32 activations need three digit planes, which the grouped MFMA kernel does not take: the
+    # per-pair v_dot4 kernels serve the call
+    T = 16
+    x = synth.activations(synth.BATCHED_B64, T, seed=93).float()
+    oids, og, _ = oracle.route(full.ora, x, n_threads=8)
+    ids = torch.from_numpy(oids).cuda()
+    gates = torch.from_numpy(og.astype(np.float32)).cuda()
+    step("batched fp32 input T=%d" % T)
+    out = run_float(full.gpu, x.cuda(), ids, gates)
+    for t in range(T):
+        o = oracle.ffn_token(full.ora, x[t].double().numpy(), oids[t], og[t])
+        got = out[t].cpu().numpy()
+        assert np.max(np.abs(got - o)) <= 1e-4 * np.max(np.abs(o)), t
