@@ -358,7 +358,8 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
     return min(min(a, b), min(c, d));
 }
 
-template <int KPER>
+// GATES = false leaves the selected logits in gates_out (softmax_gates_wave finishes the gates).
+template <int KPER, bool GATES = true>
 __device__ __forceinline__ void topk_softmax_wave_t(const float *logits, int E, int k, int32_t *ids_out,
                                     float *gates_out, int lane)
 {
@@ -409,6 +410,14 @@ __device__ __forceinline__ void topk_softmax_wave_t(const float *logits, int E, 
             my_id = int32_t(id);
         }
     }
+    if (!GATES) {
+        // the selected logits (canonical, in selection order) for softmax_gates_wave
+        if (lane < k) {
+            ids_out[lane] = my_id;
+            gates_out[lane] = my_v;
+        }
+        return;
+    }
     // gates: softmax over the selected logits; e^(l_j - l_0) in parallel, the sum in order
     const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
     const float ex = tw_exp(my_v - v0);
@@ -418,6 +427,18 @@ __device__ __forceinline__ void topk_softmax_wave_t(const float *logits, int E, 
         ids_out[lane] = my_id;
         gates_out[lane] = ex / den;
     }
+}
+
+// The gates of topk_softmax_wave_t<KPER, false>: g[j] holds the j-th selected logit on entry and
+// its gate on return, the same operations in the same order as the fused form.  One wave.
+__device__ __forceinline__ void softmax_gates_wave(float *g, int k, int lane)
+{
+    const float my_v = lane < k ? g[lane] : 0.0f;
+    const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
+    const float ex = tw_exp(my_v - v0);
+    float den = 0.0f;
+    for (int j = 0; j < k; j++) den = den + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+    if (lane < k) g[lane] = ex / den;
 }
 
 __device__ __forceinline__ void topk_softmax_wave(const float *logits, int E, int k, int32_t *ids_out,

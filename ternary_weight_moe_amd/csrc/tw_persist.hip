@@ -16,11 +16,12 @@
 //              pre-RMSNorm is a scalar on the logits and on the gate/up sums.
 //   3. top-k   every workgroup gathers all E logits and selects the same top-k (same values, same
 //              deterministic selection), so nothing else has to be broadcast.
-//   4. loads   all of this workgroup's expert bytes for the layer are requested at once: its share
-//              of gate/up rows (2 x k*F/256 rows of d/4 bytes) and of down rows (k experts x
-//              d/256 output rows of F/4 bytes), with their scales; then the next layer's router
-//              row.  Little's law wants megabytes in flight across the chip; issuing everything
-//              before the first use gives ~6 MB for the 2048/512/top-8 layer.
+//   4. loads   the workgroup's share of gate/up rows (2 x k*F/256 rows of d/4 bytes, ~4 MB
+//              across the chip for the 2048/512/top-8 layer) is requested at once, with its scales;
+//              the gates are formed while it is in flight.  Once it has arrived, the share of down
+//              rows (k experts x d/256 output rows of F/4 bytes) and the next layer's router row
+//              are requested: they are needed only after the h hand-off, and keeping them out of
+//              the first burst lets the gate/up bytes, which are on the critical path, arrive sooner.
 //   5. gate/up the ternary dots (tw_device.h) against the digit planes of x, h = SiLU(gate)*up
 //              in fp32, published one value per word.
 //   6. down    gather all k*F values of h, digit planes per expert, the down dots for the
@@ -258,10 +259,12 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
                 if (t + kPT * n < E) lg[t + kPT * n] = __uint_as_float(uint32_t(v[n]));
         }
         __syncthreads();
-        if (wave == 0) topk_softmax_wave_t<kPB / 64>(lg, E, K, s_ids, s_gates, lane);
+        if (wave == 0) topk_softmax_wave_t<kPB / 64, false>(lg, E, K, s_ids, s_gates, lane);
         __syncthreads();
 
-        // 4. request every expert byte of this workgroup's share at once
+        // 4. request the gate/up rows of this workgroup's share at once (the down rows and the next
+        //    router rows follow once these have arrived, so that these, on the critical path, do
+        //    not share the memory system with them); the gates are formed meanwhile
         int4 cg[C::PGU];
         float sg[C::PGU];
 #pragma unroll
@@ -275,22 +278,11 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
             cg[p] = valid ? reinterpret_cast<const int4 *>(row)[c_gu] : make_int4(0, 0, 0, 0);
             sg[p] = (valid && c_gu == 0) ? (kind ? P.s_up : P.s_gate)[size_t(e) * F + r] : 0.0f;
         }
-        int4 cd[C::PD];
-        float sd[C::PD];
-#pragma unroll
-        for (int p = 0; p < C::PD; p++) {
-            const int jd = p * C::RPPD + t / C::LPRD;
-            const bool valid = jd < K * C::RD;
-            const int j = valid ? jd / C::RD : 0, rl = jd % C::RD;
-            const int R = b * C::RD + rl;
-            const int e = min(max(s_ids[j], 0), E - 1);
-            const uint8_t *row = P.w_down + (size_t(e) * D + R) * (F / 4);
-            cd[p] = valid ? reinterpret_cast<const int4 *>(row)[c_d] : make_int4(0, 0, 0, 0);
-            sd[p] = (valid && c_d == 0) ? P.s_down[size_t(e) * D + R] : 0.0f;
-        }
-        if (l + 1 < a.n_layers) load_router<C::NRC>(rw, a.L[l + 1].w_router, b, E, D);
+        if (wave == 0) softmax_gates_wave(s_gates, K, lane);
 
         // 5. gate/up dots, h = SiLU(gate) * up in fp32, published one value per word
+        int4 cd[C::PD];
+        float sd[C::PD];
         {
             int4 dg[2][4];
 #pragma unroll
@@ -306,6 +298,19 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
                 group_reduce<2>(acc, C::LPR);
                 if (c_gu == 0 && jb < 2 * C::Q) sums[jb] = float_value<2>(acc, s_xsh) * sg[p] * s_inv;
             }
+            // the down rows of this workgroup's outputs and the next layer's router rows
+#pragma unroll
+            for (int p = 0; p < C::PD; p++) {
+                const int jd = p * C::RPPD + t / C::LPRD;
+                const bool valid = jd < K * C::RD;
+                const int j = valid ? jd / C::RD : 0, rl = jd % C::RD;
+                const int R = b * C::RD + rl;
+                const int e = min(max(s_ids[j], 0), E - 1);
+                const uint8_t *row = P.w_down + (size_t(e) * D + R) * (F / 4);
+                cd[p] = valid ? reinterpret_cast<const int4 *>(row)[c_d] : make_int4(0, 0, 0, 0);
+                sd[p] = (valid && c_d == 0) ? P.s_down[size_t(e) * D + R] : 0.0f;
+            }
+            if (l + 1 < a.n_layers) load_router<C::NRC>(rw, a.L[l + 1].w_router, b, E, D);
         }
         __syncthreads();
         if (t < C::Q) {
