@@ -171,6 +171,19 @@ __device__ __forceinline__ void float_digits(float v, int sh, int8_t (&dg)[P])
     }
 }
 
+// Stores one int8 value per lane into the digit-plane layout: element i of a plane goes to byte
+// perm16(i).  The 16 lanes of each DPP row must hold elements 16g .. 16g + 15 of the plane, lane
+// i % 16; byte 4k + r of the group is element 4r + k, so lane k (< 4) collects the bytes of lanes
+// k + 4, k + 8, k + 12 (DPP row shifts) and writes the group's dword k.  Every lane must call it.
+__device__ __forceinline__ void store_digits16(int8_t *plane, int i, int8_t q)
+{
+    constexpr int kRowShl4 = 0x104, kRowShl8 = 0x108, kRowShl12 = 0x10C;
+    const int32_t b0 = int32_t(uint8_t(q));
+    const int32_t b1 = dpp_i<kRowShl4>(b0), b2 = dpp_i<kRowShl8>(b0), b3 = dpp_i<kRowShl12>(b0);
+    const uint32_t dw = uint32_t(b0) | (uint32_t(b1) << 8) | (uint32_t(b2) << 16) | (uint32_t(b3) << 24);
+    if ((i & 15) < 4) *reinterpret_cast<uint32_t *>(plane + (i & ~15) + 4 * (i & 15)) = dw;
+}
+
 // int8 activation mode: q = clamp(rint(v * inv), -127, 127) with inv = 127 / amax.
 __device__ __forceinline__ int8_t int8_quant(float v, float inv)
 {

@@ -86,7 +86,7 @@ struct PC {
     static_assert(LPR >= 1 && LPR <= 64 && LPRD >= 1 && LPRD <= 64, "row widths 64..4096");
     static_assert(K <= kMaxTopK && K <= 16, "top-k");
     static_assert(HW % kPT == 0 && F % 64 == 0, "k*F a multiple of 1024");
-    static_assert(XW % 64 == 0, "d a multiple of 128");
+    static_assert(XW % 64 == 0 && D % kPT == 0, "d a multiple of 1024");
 };
 
 // Waits until the words base[t + kPT*n] (n < N, index < W) carry `tag`; v receives them.
@@ -241,11 +241,13 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
                 s_xsh = sh;
                 s_inv = inv;
             }
-            for (int i = t; i < D; i += kPT) {
+#pragma unroll
+            for (int n = 0; n < D / kPT; n++) {
+                const int i = t + kPT * n;
                 int8_t dg[2];
                 float_digits<2>(xs[i], sh, dg);
-                xd[perm16(i)] = dg[0];
-                xd[D + perm16(i)] = dg[1];
+                store_digits16(xd, i, dg[0]);
+                store_digits16(xd + D, i, dg[1]);
             }
         }
 
@@ -330,18 +332,20 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
                 if (lane == 0) s_wmax[n * kNW + wave] = am;   // chunk (t + kPT n) / 64
             }
             __syncthreads();
+            if (t < K) {   // the expert's shift, once
+                float hm = 0.0f;
+#pragma unroll
+                for (int c = 0; c < F / 64; c++) hm = fmaxf(hm, s_wmax[t * (F / 64) + c]);
+                s_hsh[t] = float_digit_shift(hm, 2);
+            }
+            __syncthreads();
 #pragma unroll
             for (int n = 0; n < N; n++) {
                 const int w = t + kPT * n, j = w / F, i = w % F;
-                float hm = 0.0f;
-#pragma unroll
-                for (int c = 0; c < F / 64; c++) hm = fmaxf(hm, s_wmax[j * (F / 64) + c]);
-                const int sh = float_digit_shift(hm, 2);
-                if (i == 0) s_hsh[j] = sh;
                 int8_t dg[2];
-                float_digits<2>(__uint_as_float(uint32_t(v[n])), sh, dg);
-                hd[(j * 2) * F + perm16(i)] = dg[0];
-                hd[(j * 2 + 1) * F + perm16(i)] = dg[1];
+                float_digits<2>(__uint_as_float(uint32_t(v[n])), s_hsh[j], dg);
+                store_digits16(hd + (j * 2) * F, i, dg[0]);
+                store_digits16(hd + (j * 2 + 1) * F, i, dg[1]);
             }
         }
         __syncthreads();
