@@ -68,11 +68,11 @@ __global__ void k_pack_any(const int8_t *__restrict__ w, int64_t rows, int64_t c
 }
 
 // ------------------------------------------------------------------------------------------------
-// Router logits for T tokens: one workgroup of 256 threads per expert.  Thread t holds the expert's
-// router chunks t, t+256 (8 elements each) in registers and, for each token, adds its chunks'
-// products in order; the 256 partials are summed by wave_sum per wave and then (w0+w1)+(w2+w3): the
-// canonical order of canon_dot.  The pre-RMSNorm factor comes from the token's sum of squares in
-// the same order, folded in as a scalar: W_r (x / rms) = (W_r x) / rms.
+// Router logits for T tokens (k_route below).  Every logit is summed in the canonical order of
+// canon_dot: 256 partials, partial t adding the products of chunks t, t + 256 (8 elements each) in
+// order, then a balanced tree over the partials (wave_sum per 64, (w0+w1)+(w2+w3)).  The
+// pre-RMSNorm factor comes from the token's sum of squares in the same order, folded in as a
+// scalar: W_r (x / rms) = (W_r x) / rms.
 constexpr int kRouteTok = 8;   // tokens per workgroup of the router
 
 // The 8 activations of chunk c of row `row` (bf16 or fp32), as fp32.

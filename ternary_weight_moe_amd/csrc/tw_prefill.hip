@@ -2,24 +2,29 @@
 // instantiated for, from a few tokens per expert (batched decode) to many (prefill-shaped).
 //
 // The ternary products are int8 contractions and run on the matrix cores:
-// v_mfma_i32_16x16x64_i8 multiplies a 16x64 int8 tile of activations by a 64x16 int8 tile of
-// weights into exact 16x16 int32 sums.  Activations enter as P int8 planes (P = 1: int8 absmax
-// mode; P = 2, 3: the float digit planes of tw_device.h), each contracted on its own, so every
-// result is bit-identical to the per-pair v_dot4 path and to the batch-1 decode.
+// v_mfma_i32_16x16x64_i8 multiplies a 16x64 int8 tile of weights (A operand, decoded in registers
+// from the 2-bit codes) by a 64x16 int8 tile of activations (B operand, from LDS) into exact 16x16
+// int32 sums.  Activations enter as P int8 planes (P = 1: int8 absmax mode; P = 2: the digit planes
+// of bf16 inputs, tw_device.h); the activation tile holds MT x P rows (token m, plane pl at row
+// m P + pl) and each MFMA takes 16 of them, so with two planes its 16 columns are 8 tokens x 2
+// planes and the two lanes of a token combine their sums with one DPP exchange.  Every result is
+// bit-identical to the per-pair v_dot4 path and to the batch-1 decode.
 //
-// One workgroup (512 threads, 8 waves) takes one (expert e, tile of MT tokens) work item:
-//   1. the tile's MT x P planes of activation digits (d bytes each, 4x4-transposed inside groups
-//      of 16 as in tw_device.h) are copied into LDS, rows padded by 16 bytes so that the 16 rows
-//      read by one MFMA operand fetch spread over the banks;
-//   2. gate/up: wave w owns h rows [F/8 w, F/8 (w+1)) in groups of 16; for each group it loads the
-//      16 gate and 16 up code rows (each lane: one row, 16 bytes per 256 inputs), decodes 16 codes
-//      into the 16 int8 weights of its MFMA B operand with four v_perm_b32 (no LDS round trip), and
-//      runs MT/16 token sub-tiles x P planes x (gate, up) MFMAs per 64 inputs; the epilogue forms
-//      gate, up and h = SiLU(gate) * up in fp32 in the order of the specification, in registers;
-//   3. per token: max |h| over all F rows (registers, DPP inside 16-lane rows, LDS over waves), h
-//      re-quantised (int8 absmax) or split into digit planes (float) into LDS;
-//   4. down: wave w owns d/8 output rows; same MFMA scheme with the down codes; y in fp32, stored
-//      per (token, slot) pair for the ordered combine.
+// One workgroup (8 or 16 waves) takes one (expert e, tile of MT tokens) work item:
+//   1. the tile's MT x P rows of activation digits (d bytes each, 4x4-transposed inside groups of
+//      16 as in tw_device.h) are copied into LDS, rows padded by 16 bytes so that the 16 rows read
+//      by one MFMA operand fetch spread over the banks;
+//   2. gate/up: wave w owns h rows [F/W w, F/W (w+1)) in groups of 16; the group's gate and up code
+//      rows stream through a ring of register slots (each lane: one row, 16 bytes per 256 inputs,
+//      several units in flight), each code word is decoded into the 16 int8 weights of an MFMA A
+//      operand with nine ALU operations (no LDS round trip), and the activation fragments of the
+//      next step are read from LDS while the current one is computed; the epilogue forms gate, up
+//      and h = SiLU(gate) * up in fp32 in the order of the specification, in registers;
+//   3. per token: max |h| over all F rows (registers, lane shuffles, LDS over waves), h re-quantised
+//      (int8 absmax) or split into digit planes into LDS;
+//   4. down: wave w owns d/W output rows; same scheme with the down codes; y in fp32, four
+//      consecutive outputs of a token per lane stored as one 16-byte vector per (token, slot) pair
+//      for the ordered combine.
 // K order: lane group g of an MFMA at step (S, s) covers inputs 256 S + 64 g + 16 s .. +16 -- a
 // permutation of the inputs shared by both operands, so every int32 sum is the exact dot product.
 // Work items are mapped to workgroups so that pairs of consecutive tiles (usually one expert) run on
