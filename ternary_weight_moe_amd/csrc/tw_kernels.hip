@@ -992,12 +992,14 @@ __global__ __launch_bounds__(256) void k_bat_dn(BatchedArgs a, LayerPtrs lp, uin
 // out[t] = ((x[t] + g_0 y_0) + g_1 y_1) + ..., j in selection order.  Slots whose expert id is
 // outside [0, E) contribute nothing (k_group does not place them either).  One workgroup per token;
 // thread t owns the 8-element chunks t, t + 256; every load of the token is issued at once.
+template <bool XB, bool OB>
 __global__ __launch_bounds__(256) void k_bat_combine(BatchedArgs a, const void *__restrict__ x,
-                                                     int x_bf16, void *__restrict__ out,
-                                                     int out_bf16, const int32_t *__restrict__ ids,
+                                                     void *__restrict__ out,
+                                                     const int32_t *__restrict__ ids,
                                                      const float *__restrict__ gates,
                                                      uint8_t *__restrict__ ws)
 {
+    typedef float f4 __attribute__((ext_vector_type(4)));
     const int d = a.dm.d, k = a.dm.k, E = a.dm.E, nch = d >> 3;
     const int64_t tok = blockIdx.x;
     const float *ybuf = reinterpret_cast<const float *>(ws + a.L.y);
@@ -1005,48 +1007,73 @@ __global__ __launch_bounds__(256) void k_bat_combine(BatchedArgs a, const void *
         const int c = threadIdx.x + 256 * i;
         if (c >= nch) break;
         float o[8];
-        load_chunk8(x, tok, d, c, x_bf16, o);
+        if constexpr (XB) {
+            const int4 q = reinterpret_cast<const int4 *>(static_cast<const uint16_t *>(x) + tok * d)[c];
+            const uint32_t w[4] = {uint32_t(q.x), uint32_t(q.y), uint32_t(q.z), uint32_t(q.w)};
+#pragma unroll
+            for (int jj = 0; jj < 8; jj++) o[jj] = bf16_to_f32(uint16_t(w[jj >> 1] >> (16 * (jj & 1))));
+        } else {
+            const f4 *p = reinterpret_cast<const f4 *>(static_cast<const float *>(x) + tok * d) + 2 * c;
+            const f4 p0 = p[0], p1 = p[1];
+            o[0] = p0.x; o[1] = p0.y; o[2] = p0.z; o[3] = p0.w;
+            o[4] = p1.x; o[5] = p1.y; o[6] = p1.z; o[7] = p1.w;
+        }
         for (int j0 = 0; j0 < k; j0 += 8) {
-            float yv[8][8];
+            // every load of the chunk is issued before the first is used: the residual chunk, the y
+            // rows of the slots (still in the last-level cache after the expert kernel, for the
+            // most part), the ids and the gates.  The y row of every slot exists (unwritten for
+            // slots without a valid expert, and then unused).
+            f4 yv[8][2];
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                const int j = j0 + u < k ? j0 + u : k - 1;
+                const f4 *yp = reinterpret_cast<const f4 *>(ybuf + (tok * k + j) * d + 8 * c);
+                yv[u][0] = yp[0];
+                yv[u][1] = yp[1];
+            }
             float g[8];
             bool ok[8];
 #pragma unroll
             for (int u = 0; u < 8; u++) {
-                // the y row of every slot exists (unwritten for slots without a valid expert, and
-                // then unused), so its load does not wait for the id
                 const int j = j0 + u < k ? j0 + u : k - 1;
-                const int id = j0 + u < k ? ids[tok * k + j] : -1;
-                ok[u] = id >= 0 && id < E;
+                const int id = ids[tok * k + j];
+                ok[u] = j0 + u < k && id >= 0 && id < E;
                 g[u] = gates[tok * k + j];
-                {
-                    const int4 *yp = reinterpret_cast<const int4 *>(ybuf + (tok * k + j) * d + 8 * c);
-                    const int4 p0 = yp[0], p1 = yp[1];
-                    yv[u][0] = __int_as_float(p0.x); yv[u][1] = __int_as_float(p0.y);
-                    yv[u][2] = __int_as_float(p0.z); yv[u][3] = __int_as_float(p0.w);
-                    yv[u][4] = __int_as_float(p1.x); yv[u][5] = __int_as_float(p1.y);
-                    yv[u][6] = __int_as_float(p1.z); yv[u][7] = __int_as_float(p1.w);
-                }
             }
 #pragma unroll
             for (int u = 0; u < 8; u++) {
                 if (ok[u]) {
+                    const float yy[8] = {yv[u][0].x, yv[u][0].y, yv[u][0].z, yv[u][0].w,
+                                         yv[u][1].x, yv[u][1].y, yv[u][1].z, yv[u][1].w};
 #pragma unroll
-                    for (int q = 0; q < 8; q++) o[q] = o[q] + g[u] * yv[u][q];
+                    for (int q = 0; q < 8; q++) o[q] = o[q] + g[u] * yy[q];
                 }
             }
-        }
-        if (out_bf16) {
-            uint32_t w[4];
+            if (j0 + 8 < k) continue;
+            if constexpr (OB) {
+                uint32_t w[4];
 #pragma unroll
-            for (int q = 0; q < 4; q++) w[q] = pack_bf16x2(o[2 * q], o[2 * q + 1]);
-            reinterpret_cast<int4 *>(static_cast<uint16_t *>(out) + tok * d)[c] =
-                make_int4(int(w[0]), int(w[1]), int(w[2]), int(w[3]));
-        } else {
-            int4 *op = reinterpret_cast<int4 *>(static_cast<float *>(out) + tok * d) + 2 * c;
-            op[0] = make_int4(__float_as_int(o[0]), __float_as_int(o[1]), __float_as_int(o[2]), __float_as_int(o[3]));
-            op[1] = make_int4(__float_as_int(o[4]), __float_as_int(o[5]), __float_as_int(o[6]), __float_as_int(o[7]));
+                for (int q = 0; q < 4; q++) w[q] = pack_bf16x2(o[2 * q], o[2 * q + 1]);
+                reinterpret_cast<int4 *>(static_cast<uint16_t *>(out) + tok * d)[c] =
+                    make_int4(int(w[0]), int(w[1]), int(w[2]), int(w[3]));
+            } else {
+                f4 *op = reinterpret_cast<f4 *>(static_cast<float *>(out) + tok * d) + 2 * c;
+                op[0] = f4{o[0], o[1], o[2], o[3]};
+                op[1] = f4{o[4], o[5], o[6], o[7]};
+            }
         }
     }
+}
+
+void launch_combine(const BatchedArgs &a, const void *x, int in_bf16, void *out, int out_bf16,
+                    const int32_t *ids, const float *gates, uint8_t *ws, void *stream)
+{
+    const unsigned g = unsigned(a.T);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (in_bf16 && out_bf16) k_bat_combine<true, true><<<g, 256, 0, st>>>(a, x, out, ids, gates, ws);
+    else if (in_bf16) k_bat_combine<true, false><<<g, 256, 0, st>>>(a, x, out, ids, gates, ws);
+    else if (out_bf16) k_bat_combine<false, true><<<g, 256, 0, st>>>(a, x, out, ids, gates, ws);
+    else k_bat_combine<false, false><<<g, 256, 0, st>>>(a, x, out, ids, gates, ws);
 }
 
 inline hipStream_t S(void *s) { return static_cast<hipStream_t>(s); }
@@ -1126,7 +1153,7 @@ int batched_p(const Dims &dm, const LayerPtrs &lp, int64_t T, const void *x_in, 
         if (r != 0) return r;
         r = launch_grouped_mfma(dm, lp, T, P, tile, a.L, w, stream);
         if (r != 0) return r;
-        k_bat_combine<<<unsigned(T), 256, 0, S(stream)>>>(a, x_in, in_bf16, x_out, out_bf16, ids, gates, w);
+        launch_combine(a, x_in, in_bf16, x_out, out_bf16, ids, gates, w, stream);
         return last_error();
     }
     const int rg = launch_group(a, ids, w, kTileTokens, stream);
@@ -1140,7 +1167,7 @@ int batched_p(const Dims &dm, const LayerPtrs &lp, int64_t T, const void *x_in, 
         k_bat_dn<P, INT8, 2><<<kBatG, 256, size_t(td) * P * dm.F, S(stream)>>>(a, lp, w, td);
     else
         k_bat_dn<P, INT8, 16><<<kBatG, 256, size_t(td) * P * dm.F, S(stream)>>>(a, lp, w, td);
-    k_bat_combine<<<unsigned(T), 256, 0, S(stream)>>>(a, x_in, in_bf16, x_out, out_bf16, ids, gates, w);
+    launch_combine(a, x_in, in_bf16, x_out, out_bf16, ids, gates, w, stream);
     return last_error();
 }
 

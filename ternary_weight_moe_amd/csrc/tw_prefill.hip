@@ -42,6 +42,7 @@ namespace tw {
 namespace {
 
 typedef int32_t v4i __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
 
 // Waves per workgroup: 16 for 16-token tiles of at most two planes (at <= 128 VGPRs, four waves
 // per SIMD); 8 otherwise (256 VGPRs: the h values of a 64-token tile stay in registers).
@@ -373,7 +374,7 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
             }
             // the second lane of a two-plane token holds the same values: it writes a spare row
             const int64_t row = pr >= 0 && pl == 0 ? int64_t(pr) : L.spare_row + (blockIdx.x % kSpareRows);
-            *reinterpret_cast<float4 *>(ybuf + row * D + R0 + 4 * g4) = make_float4(y[0], y[1], y[2], y[3]);
+            *reinterpret_cast<f4 *>(ybuf + row * D + R0 + 4 * g4) = f4{y[0], y[1], y[2], y[3]};
         }
         if ((n & 3) == 3 && n + 1 < NSD) __syncthreads();   // waves in step, as in gate/up
     }
