@@ -222,6 +222,40 @@ def test_decode_stack_teacher_forced_and_chained(stack3):
         assert drift <= 2e-2
 
 
+def test_decode_full_stack24(stack3):
+    # the measured configuration: 24 layers of d=2048, 256 experts, F=512, top-8, pre-RMSNorm, one
+    # launch.  The fused call equals 24 chained single-layer calls bit for bit; layers 0, 1, 2 (the
+    # stack3 fixture), 11 and 23 are checked against the oracle on the GPU's own input to them.
+    wl = synth.STACK24_B1
+    layers = [p.gpu for p in stack3]
+    for l in range(3, wl.n_layers):
+        step("build stack layer %d (GPU only)" % l)
+        w = synth.layer_weights(wl, l, device="cuda")
+        layers.append(tw.MoELayer.from_ternary(w["w_router"], w["t_gate"], w["t_up"], w["t_down"],
+                                               w["s_gate"], w["s_up"], w["s_down"],
+                                               top_k=wl.top_k, pre_rmsnorm=wl.pre_rmsnorm))
+        del w
+    x0 = synth.activations(wl, 1, seed=25)[0].cuda()
+    step("decode 24 layers, one call")
+    fused = tw.ternary_moe_ffn_decode(layers, x0)
+    step("decode 24 layers, chained single-layer calls")
+    inputs, cur = [], x0
+    for layer in layers:
+        inputs.append(cur)
+        cur = tw.ternary_moe_ffn_decode([layer], cur)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), cur.view(torch.int16))
+    assert torch.isfinite(fused.float()).all()
+    for l in (0, 1, 2, 11, 23):
+        step("stack24 layer %d against the oracle" % l)
+        ora = stack3[l].ora if l < 3 else make_pair(wl, layer=l).ora
+        xin = to_np(inputs[l])
+        got = to_np(tw.ternary_moe_ffn_decode([layers[l]], inputs[l]))
+        cands = oracle_decode_expect(ora, xin)
+        errs = [normwise(got, c) for c in cands]
+        assert_bf16_close(got, cands[int(np.argmin(errs))], "layer %d" % l)
+
+
 @pytest.fixture(scope="module")
 def mid3():
     layers = []
