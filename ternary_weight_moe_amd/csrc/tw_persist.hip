@@ -89,7 +89,10 @@ struct PC {
     static_assert(XW % 64 == 0 && D % kPT == 0, "d a multiple of 1024");
 };
 
-// Waits until the words base[t + kPT*n] (n < N, index < W) carry `tag`; v receives them.
+// Waits until the words base[t + kPT*n] (n < N, index < W) carry `tag`; v receives them.  Words
+// that never arrive end the wait after kSpinLimit polls and mark the workgroup aborted; after that
+// the workgroup's later waits return at once (the flag is read once per wait, not per poll: a
+// per-poll read of it would also wait for every memory read in flight).
 template <int N>
 __device__ __forceinline__ void wait_words(const uint64_t *base, int W, uint32_t tag, uint64_t (&v)[N],
                                            volatile int *s_abort, uint32_t *err)
@@ -99,6 +102,7 @@ __device__ __forceinline__ void wait_words(const uint64_t *base, int W, uint32_t
 #pragma unroll
     for (int n = 0; n < N; n++)
         if (t + kPT * n < W) pend |= 1u << n;
+    if (*s_abort) return;
     for (uint32_t it = 0; pend; ++it) {
 #pragma unroll
         for (int n = 0; n < N; n++)
@@ -106,7 +110,7 @@ __device__ __forceinline__ void wait_words(const uint64_t *base, int W, uint32_t
 #pragma unroll
         for (int n = 0; n < N; n++)
             if (((pend >> n) & 1u) && uint32_t(v[n] >> 32) == tag) pend &= ~(1u << n);
-        if (pend && (it > kSpinLimit || *s_abort)) {
+        if (pend && it > kSpinLimit) {
             *s_abort = 1;
             atomicOr(err, 1u);
             break;
