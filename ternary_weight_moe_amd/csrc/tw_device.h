@@ -171,17 +171,30 @@ __device__ __forceinline__ void float_digits(float v, int sh, int8_t (&dg)[P])
     }
 }
 
-// Stores one int8 value per lane into the digit-plane layout: element i of a plane goes to byte
-// perm16(i).  The 16 lanes of each DPP row must hold elements 16g .. 16g + 15 of the plane, lane
-// i % 16; byte 4k + r of the group is element 4r + k, so lane k (< 4) collects the bytes of lanes
-// k + 4, k + 8, k + 12 (DPP row shifts) and writes the group's dword k.  Every lane must call it.
-__device__ __forceinline__ void store_digits16(int8_t *plane, int i, int8_t q)
+// The two digits of s = clamp(rint(v 2^sh), -(2^14 - 1), 2^14 - 1) as a floor split, packed in one
+// word: byte 0 holds lo = s mod 128 (0..127), byte 2 holds hi = floor(s / 128) (-128..127), so
+// s = 128 hi + lo.  float_digits<2> splits |s| instead and puts the sign on both digits; the planes
+// differ but every integer dot against them recombines (128 * sum_hi + sum_lo) to the same exact
+// sum, so the results are identical bit for bit.  NaN maps to +(2^14 - 1) in both.
+__device__ __forceinline__ uint32_t float_digit_pair(float v, int sh)
 {
-    constexpr int kRowShl4 = 0x104, kRowShl8 = 0x108, kRowShl12 = 0x10C;
-    const int32_t b0 = int32_t(uint8_t(q));
-    const int32_t b1 = dpp_i<kRowShl4>(b0), b2 = dpp_i<kRowShl8>(b0), b3 = dpp_i<kRowShl12>(b0);
-    const uint32_t dw = uint32_t(b0) | (uint32_t(b1) << 8) | (uint32_t(b2) << 16) | (uint32_t(b3) << 24);
-    if ((i & 15) < 4) *reinterpret_cast<uint32_t *>(plane + (i & ~15) + 4 * (i & 15)) = dw;
+    const float X = __builtin_rintf(__builtin_ldexpf(v, sh));
+    const int a = int(fminf(fabsf(X), 16383.0f));
+    const uint32_t s = uint32_t(X < 0.0f ? -a : a);
+    return (s & 127u) | ((s << 9) & 0x00ff0000u);
+}
+
+// Digit-plane layout: element i of a plane is byte perm16(i), i.e. byte 4k + r of a 16-element group
+// is element 4r + k.  Given the digit pairs of the elements 4r + k (r = 0..3) of one group, returns
+// the group's dword k of the low-digit plane and of the high-digit plane (the high plane is plane 0
+// of float_value<2>, the low plane plane 1).
+__device__ __forceinline__ void digit_pair_dwords(const uint32_t (&p)[4], uint32_t &lo, uint32_t &hi)
+{
+    // v_perm byte selectors: 0..3 pick bytes of the second operand, 4..7 bytes of the first
+    const uint32_t m01 = __builtin_amdgcn_perm(p[1], p[0], 0x06020400u);   // lo0 lo1 hi0 hi1
+    const uint32_t m23 = __builtin_amdgcn_perm(p[3], p[2], 0x06020400u);   // lo2 lo3 hi2 hi3
+    lo = __builtin_amdgcn_perm(m23, m01, 0x05040100u);
+    hi = __builtin_amdgcn_perm(m23, m01, 0x07060302u);
 }
 
 // int8 activation mode: q = clamp(rint(v * inv), -127, 127) with inv = 127 / amax.

@@ -24,7 +24,8 @@
 //              the first burst lets the gate/up bytes, which are on the critical path, arrive sooner.
 //   5. gate/up the ternary dots (tw_device.h) against the digit planes of x, h = SiLU(gate)*up
 //              in fp32, published one value per word.
-//   6. down    gather all k*F values of h, digit planes per expert, the down dots for the
+//   6. down    gather all k*F values of h, digit planes per expert (h passes through LDS so that each
+//              thread packs whole digit dwords; one barrier gives the per-expert max), the down dots for the
 //              workgroup's output rows, out = x + sum_j g_j y_j in selection order, rounded to
 //              bf16 and published (or stored to x_out after the last layer).
 // Tags are the layer index + 1 and the words alternate between two parities by layer, so a word
@@ -85,28 +86,27 @@ struct PC {
     static_assert(RD >= 2 && RD % 2 == 0, "d must be a multiple of 512");
     static_assert(LPR >= 1 && LPR <= 64 && LPRD >= 1 && LPRD <= 64, "row widths 64..4096");
     static_assert(K <= kMaxTopK && K <= 16, "top-k");
-    static_assert(HW % kPT == 0 && F % 64 == 0, "k*F a multiple of 1024");
+    static_assert(HW % kPT == 0 && HW <= 4 * kPT && F % 64 == 0, "k*F in {1024, 2048, 3072, 4096}");
     static_assert(XW % 64 == 0 && D % kPT == 0, "d a multiple of 1024");
 };
 
-// Waits until the words base[t + kPT*n] (n < N, index < W) carry `tag`; v receives them.  Words
+// Waits until the words base[first + stride*n] (n < N, index < W) carry `tag`; v receives them.  Words
 // that never arrive end the wait after kSpinLimit polls and mark the workgroup aborted; after that
 // the workgroup's later waits return at once (the flag is read once per wait, not per poll: a
 // per-poll read of it would also wait for every memory read in flight).
 template <int N>
-__device__ __forceinline__ void wait_words(const uint64_t *base, int W, uint32_t tag, uint64_t (&v)[N],
-                                           volatile int *s_abort, uint32_t *err)
+__device__ __forceinline__ void wait_words(const uint64_t *base, int first, int stride, int W, uint32_t tag,
+                                           uint64_t (&v)[N], volatile int *s_abort, uint32_t *err)
 {
-    const int t = threadIdx.x;
     uint32_t pend = 0;
 #pragma unroll
     for (int n = 0; n < N; n++)
-        if (t + kPT * n < W) pend |= 1u << n;
+        if (first + stride * n < W) pend |= 1u << n;
     if (*s_abort) return;
     for (uint32_t it = 0; pend; ++it) {
 #pragma unroll
         for (int n = 0; n < N; n++)
-            if ((pend >> n) & 1u) v[n] = ld_tagged(base + t + kPT * n);
+            if ((pend >> n) & 1u) v[n] = ld_tagged(base + first + stride * n);
 #pragma unroll
         for (int n = 0; n < N; n++)
             if (((pend >> n) & 1u) && uint32_t(v[n] >> 32) == tag) pend &= ~(1u << n);
@@ -151,6 +151,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
     __shared__ float sums[2 * C::Q];
     __shared__ float ys[K * C::RD];
     __shared__ float red[4][2 + kEM];
+    __shared__ __attribute__((aligned(16))) float hs[C::HW];     // h, in digit-plane byte order
     __shared__ float s_wmax[C::HW / 64];                         // max |h| per 64-word chunk
     __shared__ int32_t s_ids[kMaxTopK];
     __shared__ float s_gates[kMaxTopK];
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
             const uint64_t *xprev = a.ll + size_t((l - 1) & 1) * lls + E + C::HW;
             constexpr int N = (C::XW + kPT - 1) / kPT;
             uint64_t v[N];
-            wait_words<N>(xprev, C::XW, tag - 1, v, &s_abort, a.err);
+            wait_words<N>(xprev, t, kPT, C::XW, tag - 1, v, &s_abort, a.err);
 #pragma unroll
             for (int n = 0; n < N; n++) {
                 const int i = t + kPT * n;
@@ -245,13 +246,14 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
                 s_xsh = sh;
                 s_inv = inv;
             }
+            if (t < D / 4) {   // dword t % 4 of 16-element group t / 4 of both planes
+                const int o = 16 * (t >> 2) + (t & 3);
+                uint32_t pr[4], lo, hi;
 #pragma unroll
-            for (int n = 0; n < D / kPT; n++) {
-                const int i = t + kPT * n;
-                int8_t dg[2];
-                float_digits<2>(xs[i], sh, dg);
-                store_digits16(xd, i, dg[0]);
-                store_digits16(xd + D, i, dg[1]);
+                for (int r = 0; r < 4; r++) pr[r] = float_digit_pair(xs[o + 4 * r], sh);
+                digit_pair_dwords(pr, lo, hi);
+                *reinterpret_cast<uint32_t *>(xd + 4 * t) = hi;        // plane 0: high digits
+                *reinterpret_cast<uint32_t *>(xd + D + 4 * t) = lo;
             }
         }
 
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
         {
             constexpr int N = (kPB + kPT - 1) / kPT;
             uint64_t v[N];
-            wait_words<N>(lgw, E, tag, v, &s_abort, a.err);
+            wait_words<N>(lgw, t, kPT, E, tag, v, &s_abort, a.err);
 #pragma unroll
             for (int n = 0; n < N; n++)
                 if (t + kPT * n < E) lg[t + kPT * n] = __uint_as_float(uint32_t(v[n]));
@@ -324,32 +326,36 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
             st_tagged(hw + b * C::Q + t, tag, __float_as_uint(h));
         }
 
-        // 6. gather h (word w = t + kPT n: expert w / F, element w % F; a wave's 64 words share
-        //    one expert), per-expert max |h|, digit planes, down dots, combine
+        // 6. gather h (word w = t + kPT n: expert w / F, element w % F; a wave's 64 words share one
+        //    expert), per-chunk max |h| and h itself into LDS in the digit-plane byte order; after
+        //    one barrier thread t (< k*F/4) turns elements 4r + c of 16-element group t / 4 (c = t % 4,
+        //    r < 4) into dword c of the group in both digit planes; then the down dots and the combine
         {
-            constexpr int N = C::HW / kPT;
+            constexpr int N = C::HW / kPT, NT = C::HW / 4, CPE = F / 64;
             uint64_t v[N];
-            wait_words<N>(hw, C::HW, tag, v, &s_abort, a.err);
+            wait_words<N>(hw, t, kPT, C::HW, tag, v, &s_abort, a.err);
 #pragma unroll
             for (int n = 0; n < N; n++) {
-                const float am = wave_max(fabsf(__uint_as_float(uint32_t(v[n]))));
+                const float h = __uint_as_float(uint32_t(v[n]));
+                hs[perm16(t + kPT * n)] = h;
+                const float am = wave_max(fabsf(h));
                 if (lane == 0) s_wmax[n * kNW + wave] = am;   // chunk (t + kPT n) / 64
             }
             __syncthreads();
-            if (t < K) {   // the expert's shift, once
-                float hm = 0.0f;
+            if (t < NT) {
+                const int j = (t >> 2) / (F / 16), g = (t >> 2) % (F / 16);
+                float hm = s_wmax[j * CPE];
 #pragma unroll
-                for (int c = 0; c < F / 64; c++) hm = fmaxf(hm, s_wmax[t * (F / 64) + c]);
-                s_hsh[t] = float_digit_shift(hm, 2);
-            }
-            __syncthreads();
-#pragma unroll
-            for (int n = 0; n < N; n++) {
-                const int w = t + kPT * n, j = w / F, i = w % F;
-                int8_t dg[2];
-                float_digits<2>(__uint_as_float(uint32_t(v[n])), s_hsh[j], dg);
-                store_digits16(hd + (j * 2) * F, i, dg[0]);
-                store_digits16(hd + (j * 2 + 1) * F, i, dg[1]);
+                for (int c = 1; c < CPE; c++) hm = fmaxf(hm, s_wmax[j * CPE + c]);
+                const int sh = float_digit_shift(hm, 2);
+                if (t % (F / 4) == 0) s_hsh[j] = sh;   // the expert's first thread
+                const float4 hv = *reinterpret_cast<const float4 *>(hs + 4 * t);
+                const uint32_t pr[4] = {float_digit_pair(hv.x, sh), float_digit_pair(hv.y, sh),
+                                        float_digit_pair(hv.z, sh), float_digit_pair(hv.w, sh)};
+                uint32_t lo, hi;
+                digit_pair_dwords(pr, lo, hi);
+                *reinterpret_cast<uint32_t *>(hd + (j * 2) * F + 16 * g + 4 * (t & 3)) = hi;
+                *reinterpret_cast<uint32_t *>(hd + (j * 2 + 1) * F + 16 * g + 4 * (t & 3)) = lo;
             }
         }
         __syncthreads();
