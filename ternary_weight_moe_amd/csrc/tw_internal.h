@@ -103,12 +103,16 @@ int launch_decode_persist(const Dims &dm, const LayerPtrs *layers, int n_layers,
                           void *x_out, int io_bf16, void *ws, void *stream);
 int launch_decode(const Dims &dm, const LayerPtrs *layers, int n_layers, const void *x_in,
                   void *x_out, int io_bf16, void *ws, void *stream);
-// Grouped MFMA path of the batched FFN (after quantisation/digit planes and grouping into tiles of
-// `tile` tokens): planes = 1 (int8 activations) or 2, 3 (float digit planes).
+// Grouped MFMA path of the batched FFN (after quantisation/digit planes): planes = 1 (int8
+// activations) or 2 (digit planes of bf16 inputs).  sel_ids == nullptr: tiles of `tile` tokens from
+// k_group's lists; else the T k expert ids themselves (one workgroup per expert finds its pairs,
+// only where grouped_mfma_self holds).
 int launch_grouped_mfma(const Dims &dm, const LayerPtrs &layer, int64_t T, int planes, int tile,
-                        const BatchedWs &L, uint8_t *ws, void *stream);
+                        const BatchedWs &L, uint8_t *ws, const int32_t *sel_ids, void *stream);
 // Whether that path serves this shape; *tile receives the tile size to group with.
 bool grouped_mfma_serves(const Dims &dm, int64_t T, int planes, int *tile);
+// Whether it can take the ids directly (no k_group) at this batch size and tile.
+bool grouped_mfma_self(const Dims &dm, int64_t T, int tile);
 int launch_batched(const Dims &dm, const LayerPtrs &layer, int64_t T, const void *x_in,
                    int in_bf16, void *x_out, int out_bf16, int int8_act, const int32_t *ids,
                    const float *gates, void *ws, void *stream);

@@ -1149,9 +1149,11 @@ int batched_p(const Dims &dm, const LayerPtrs &lp, int64_t T, const void *x_in, 
     }
     int tile = kTileTokens;
     if (grouped_mfma_serves(dm, T, P, &tile)) {
-        int r = launch_group(a, ids, w, tile, stream);
+        // small batches: each expert's workgroup finds its own tokens, no grouping kernel
+        const bool self = grouped_mfma_self(dm, T, tile);
+        int r = self ? 0 : launch_group(a, ids, w, tile, stream);
         if (r != 0) return r;
-        r = launch_grouped_mfma(dm, lp, T, P, tile, a.L, w, stream);
+        r = launch_grouped_mfma(dm, lp, T, P, tile, a.L, w, self ? ids : nullptr, stream);
         if (r != 0) return r;
         launch_combine(a, x_in, in_bf16, x_out, out_bf16, ids, gates, w, stream);
         return last_error();

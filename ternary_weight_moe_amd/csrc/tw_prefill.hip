@@ -83,8 +83,14 @@ __device__ __forceinline__ v4i mfma8(const v4i &w, const v4i &x, const v4i &c)
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(w, x, c, 0, 0, 0);
 }
 
-template <int D, int F, int P, int MT>
-__global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, BatchedWs L, LayerPtrs lp, uint8_t *ws, int nb)
+// SELF: every workgroup builds the tile list itself from the T k expert ids (at most one id per
+// thread): per-expert counts, the tiles of MT tokens per expert in expert order, this workgroup's
+// tile, and the tile's pairs (the expert's pairs in ascending order).  The list is the one k_group
+// writes (the same tiles in the same order; inside a tile k_group's order may differ, which changes
+// nothing), so no grouping kernel runs.  Otherwise the work item comes from k_group's lists.
+template <int D, int F, int P, int MT, bool SELF>
+__global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, BatchedWs L, LayerPtrs lp, uint8_t *ws, int nb,
+                                                               const int32_t *__restrict__ sel_ids, int npairs)
 {
     constexpr int W = PfShape<MT, P>::W, NT = PfShape<MT, P>::T;
     static_assert(D % 256 == 0 && F % 256 == 0 && F % (16 * W) == 0 && D % (16 * W) == 0, "shape");
@@ -109,19 +115,71 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
     __shared__ float s_hk[MT];            // per token: s_h (int8) or digit shift bits of h
     __shared__ float s_amx[MT];
     __shared__ float s_pam[W][MT];
+    __shared__ int32_t s_cnt[SELF ? NT : 1];    // SELF: pairs per expert, then the expert's pairs
+    __shared__ int32_t s_wcnt[W], s_wtil[W];
+    __shared__ int32_t s_sel[2];
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l16 = lane & 15, g4 = lane >> 4;
-    const int32_t *tiles = reinterpret_cast<const int32_t *>(ws + L.tiles);
     // workgroups b and b + 8 run on the same XCD: they take consecutive tiles (usually one expert),
     // and every 16 workgroups cover 16 consecutive tiles, so work spreads evenly over the XCDs
     const int b = blockIdx.x;
     const int ti = (b / 16) * 16 + (b % 8) * 2 + ((b / 8) & 1);
-    const int2 *tmeta = reinterpret_cast<const int2 *>(ws + L.tilemeta);
-    // ti < nb: inside the tile lists' storage (read before the count is known, then checked)
-    const int ntiles = tiles[0], tile = tiles[1 + ti];
-    const int2 meta = tmeta[ti];
-    if (ti >= ntiles) return;
-    const int e = tile & 1023;
+    int e;
+    int2 meta;   // first pair position (k_group lists) or tile (SELF), tokens of the tile
+    if constexpr (SELF) {
+        const int E = dm.E;
+        const int id = t < npairs ? sel_ids[t] : -1;
+        const bool valid = id >= 0 && id < E;
+        if (t < E) s_cnt[t] = 0;
+        __syncthreads();
+        if (valid) atomicAdd(&s_cnt[id], 1);
+        __syncthreads();
+        // exclusive scan of the tiles per expert (expert t per thread), inside each wave and then
+        // over the wave totals
+        const int c = t < E ? s_cnt[t] : 0, nt = (c + MT - 1) / MT;
+        int it = nt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int u = __shfl_up(it, off);
+            if (lane >= off) it += u;
+        }
+        if (lane == 63) s_wtil[wave] = it;
+        if (t < 2) s_sel[t] = -1;
+        __syncthreads();
+        int bt = 0;
+#pragma unroll
+        for (int w = 0; w < W; w++) bt += w < wave ? s_wtil[w] : 0;
+        const int tile0 = bt + it - nt;
+        if (ti >= tile0 && ti < tile0 + nt) {   // this workgroup's tile belongs to expert t
+            s_sel[0] = t;
+            s_sel[1] = ti - tile0;
+        }
+        __syncthreads();
+        e = s_sel[0];
+        if (e < 0) return;   // past the last tile (uniform over the workgroup)
+        const int tl = s_sel[1];
+        // the expert's pairs in ascending order: a ballot per wave, then the waves' counts
+        const uint64_t hit = __ballot(id == e);
+        const int rank = __popcll(hit & ((uint64_t(1) << lane) - 1));
+        if (lane == 0) s_wcnt[wave] = __popcll(hit);
+        __syncthreads();   // every read of s_cnt is done
+        int before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < W; w++) {
+            before += w < wave ? s_wcnt[w] : 0;
+            total += s_wcnt[w];
+        }
+        if (id == e) s_cnt[before + rank] = t;
+        meta = make_int2(tl * MT, min(MT, total - tl * MT));
+    } else {
+        const int32_t *tiles = reinterpret_cast<const int32_t *>(ws + L.tiles);
+        const int2 *tmeta = reinterpret_cast<const int2 *>(ws + L.tilemeta);
+        // ti < nb: inside the tile lists' storage (read before the count is known, then checked)
+        const int ntiles = tiles[0], tile = tiles[1 + ti];
+        meta = tmeta[ti];
+        if (ti >= ntiles) return;
+        e = tile & 1023;
+    }
 
     // Code units of this wave, in the order they are computed.  Unit u < NGU: gate and up chunk
     // u % SG of h-row group u / SG (plus, with the first chunk, the group's gate and up scales);
@@ -165,10 +223,11 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
     const int8_t *xdig = reinterpret_cast<const int8_t *>(ws + L.xdig);
     float *ybuf = reinterpret_cast<float *>(ws + L.y);
     const int k = dm.k;
+    const int pl = l16 % P;                         // this lane's plane in every sub-tile
     const int nv = meta.y;                          // tokens in this tile (1 .. MT)
     const int rsv = (nv + TPS - 1) / TPS;           // row sub-tiles holding any of them
-    const int pl = l16 % P;                         // this lane's plane in every sub-tile
-    if (t < MT) s_pair[t] = t < nv ? pairs[meta.x + t] : -1;
+    if constexpr (SELF) __syncthreads();            // the expert's pair list is complete
+    if (t < MT) s_pair[t] = t < nv ? (SELF ? s_cnt[meta.x + t] : pairs[meta.x + t]) : -1;
     __syncthreads();
     // 1. activation tile: row (m, plane) = plane of token m, and each token's scale words; every
     //    load is issued before the first LDS store (padding tokens re-read token 0's row, which
@@ -380,33 +439,40 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
     }
 }
 
-template <int D, int F, int P, int MT>
+// One workgroup per tile slot; sel_ids != nullptr: the workgroups build the tile list themselves
+// (needs T k and E <= the workgroup size), else they read k_group's.
+template <int D, int F, int P, int MT, bool SELF>
 int pf_run(const Dims &dm, const LayerPtrs &lp, int64_t T, const BatchedWs &L, uint8_t *ws,
-           void *stream)
+           const int32_t *sel_ids, void *stream)
 {
     constexpr size_t lds = size_t(MT) * P * ((D > F ? D : F) + 16);
     static std::atomic<int> attr_set{0};
     if (!attr_set.load(std::memory_order_relaxed)) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_pf_ffn<D, F, P, MT>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_pf_ffn<D, F, P, MT, SELF>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
             return int(hipErrorInvalidValue);
         attr_set.store(1, std::memory_order_relaxed);
     }
+    const int64_t npairs = T * dm.k;
+    if (SELF && (npairs > PfShape<MT, P>::T || dm.E > PfShape<MT, P>::T)) return -1;
     const int nb = int((max_tiles(dm, T, MT) + 15) / 16 * 16);
-    k_pf_ffn<D, F, P, MT><<<nb, PfShape<MT, P>::T, lds, static_cast<hipStream_t>(stream)>>>(dm, L, lp, ws, nb);
+    k_pf_ffn<D, F, P, MT, SELF><<<nb, PfShape<MT, P>::T, lds, static_cast<hipStream_t>(stream)>>>(
+        dm, L, lp, ws, nb, sel_ids, int(npairs));
     return int(hipGetLastError());
 }
 
 template <int D, int F>
 int pf_dispatch(const Dims &dm, const LayerPtrs &lp, int64_t T, int planes, int tile,
-                const BatchedWs &L, uint8_t *ws, void *stream)
+                const BatchedWs &L, uint8_t *ws, const int32_t *sel_ids, void *stream)
 {
     if (planes == 1) {
-        if (tile == 64) return pf_run<D, F, 1, 64>(dm, lp, T, L, ws, stream);
-        return pf_run<D, F, 1, 16>(dm, lp, T, L, ws, stream);
+        if (tile == 64) return pf_run<D, F, 1, 64, false>(dm, lp, T, L, ws, nullptr, stream);
+        if (sel_ids) return pf_run<D, F, 1, 16, true>(dm, lp, T, L, ws, sel_ids, stream);
+        return pf_run<D, F, 1, 16, false>(dm, lp, T, L, ws, nullptr, stream);
     }
-    if (tile == 32) return pf_run<D, F, 2, 32>(dm, lp, T, L, ws, stream);
-    return pf_run<D, F, 2, 8>(dm, lp, T, L, ws, stream);
+    if (tile == 32) return pf_run<D, F, 2, 32, false>(dm, lp, T, L, ws, nullptr, stream);
+    if (sel_ids) return pf_run<D, F, 2, 8, true>(dm, lp, T, L, ws, sel_ids, stream);
+    return pf_run<D, F, 2, 8, false>(dm, lp, T, L, ws, nullptr, stream);
 }
 
 }  // namespace
@@ -422,11 +488,20 @@ bool grouped_mfma_serves(const Dims &dm, int64_t T, int planes, int *tile)
     return true;
 }
 
-int launch_grouped_mfma(const Dims &dm, const LayerPtrs &layer, int64_t T, int planes, int tile,
-                        const BatchedWs &L, uint8_t *ws, void *stream)
+bool grouped_mfma_self(const Dims &dm, int64_t T, int tile)
 {
-    if (dm.d == 2048 && dm.F == 512) return pf_dispatch<2048, 512>(dm, layer, T, planes, tile, L, ws, stream);
-    if (dm.d == 1024 && dm.F == 256) return pf_dispatch<1024, 256>(dm, layer, T, planes, tile, L, ws, stream);
+    // small tiles (16 activation rows: one 1024-thread workgroup per expert), at most one id per
+    // thread
+    return (tile == 16 || tile == 8) && T * dm.k <= 1024;
+}
+
+int launch_grouped_mfma(const Dims &dm, const LayerPtrs &layer, int64_t T, int planes, int tile,
+                        const BatchedWs &L, uint8_t *ws, const int32_t *sel_ids, void *stream)
+{
+    if (dm.d == 2048 && dm.F == 512)
+        return pf_dispatch<2048, 512>(dm, layer, T, planes, tile, L, ws, sel_ids, stream);
+    if (dm.d == 1024 && dm.F == 256)
+        return pf_dispatch<1024, 256>(dm, layer, T, planes, tile, L, ws, sel_ids, stream);
     return -1;
 }
 
