@@ -990,8 +990,10 @@ __global__ __launch_bounds__(256) void k_bat_dn(BatchedArgs a, LayerPtrs lp, uin
 }
 
 // out[t] = ((x[t] + g_0 y_0) + g_1 y_1) + ..., j in selection order.  Slots whose expert id is
-// outside [0, E) contribute nothing (k_group does not place them either).  One workgroup per token;
-// thread t owns the 8-element chunks t, t + 256; every load of the token is issued at once.
+// outside [0, E) contribute nothing (the expert kernels do not compute them either).  Workgroup
+// (token, s) covers the 8-element chunks s * blockDim + i of the token, one per thread (a small
+// batch takes one-wave workgroups so that its few tokens still spread over the compute units);
+// every load of a chunk is issued at once.
 template <bool XB, bool OB>
 __global__ __launch_bounds__(256) void k_bat_combine(BatchedArgs a, const void *__restrict__ x,
                                                      void *__restrict__ out,
@@ -1003,9 +1005,9 @@ __global__ __launch_bounds__(256) void k_bat_combine(BatchedArgs a, const void *
     const int d = a.dm.d, k = a.dm.k, E = a.dm.E, nch = d >> 3;
     const int64_t tok = blockIdx.x;
     const float *ybuf = reinterpret_cast<const float *>(ws + a.L.y);
-    for (int i = 0; i < 2; i++) {
-        const int c = threadIdx.x + 256 * i;
-        if (c >= nch) break;
+    {
+        const int c = int(blockIdx.y * blockDim.x + threadIdx.x);
+        if (c >= nch) return;
         float o[8];
         if constexpr (XB) {
             const int4 q = reinterpret_cast<const int4 *>(static_cast<const uint16_t *>(x) + tok * d)[c];
@@ -1068,12 +1070,13 @@ __global__ __launch_bounds__(256) void k_bat_combine(BatchedArgs a, const void *
 void launch_combine(const BatchedArgs &a, const void *x, int in_bf16, void *out, int out_bf16,
                     const int32_t *ids, const float *gates, uint8_t *ws, void *stream)
 {
-    const unsigned g = unsigned(a.T);
+    const int nt = a.T >= 1024 ? 256 : 64, nch = a.dm.d >> 3;
+    const dim3 g(unsigned(a.T), unsigned((nch + nt - 1) / nt));
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (in_bf16 && out_bf16) k_bat_combine<true, true><<<g, 256, 0, st>>>(a, x, out, ids, gates, ws);
-    else if (in_bf16) k_bat_combine<true, false><<<g, 256, 0, st>>>(a, x, out, ids, gates, ws);
-    else if (out_bf16) k_bat_combine<false, true><<<g, 256, 0, st>>>(a, x, out, ids, gates, ws);
-    else k_bat_combine<false, false><<<g, 256, 0, st>>>(a, x, out, ids, gates, ws);
+    if (in_bf16 && out_bf16) k_bat_combine<true, true><<<g, nt, 0, st>>>(a, x, out, ids, gates, ws);
+    else if (in_bf16) k_bat_combine<true, false><<<g, nt, 0, st>>>(a, x, out, ids, gates, ws);
+    else if (out_bf16) k_bat_combine<false, true><<<g, nt, 0, st>>>(a, x, out, ids, gates, ws);
+    else k_bat_combine<false, false><<<g, nt, 0, st>>>(a, x, out, ids, gates, ws);
 }
 
 inline hipStream_t S(void *s) { return static_cast<hipStream_t>(s); }
