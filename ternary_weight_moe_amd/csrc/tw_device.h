@@ -384,24 +384,20 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
     return min(min(a, b), min(c, d));
 }
 
+// Top-k of one wave over logits in registers: lv[s] is the logit of expert lane + 64 s (any value
+// where that is >= E).  ids_out / gates_out receive the k ids and gates in selection order;
 // GATES = false leaves the selected logits in gates_out (softmax_gates_wave finishes the gates).
 template <int KPER, bool GATES = true>
-__device__ __forceinline__ void topk_softmax_wave_t(const float *logits, int E, int k, int32_t *ids_out,
-                                    float *gates_out, int lane)
+__device__ __forceinline__ void topk_softmax_wave_regs(const float (&lv)[KPER], int E, int k,
+                                                       int32_t *ids_out, float *gates_out, int lane)
 {
     uint32_t key[KPER];
     uint32_t idv[KPER];
 #pragma unroll
     for (int s = 0; s < KPER; s++) {
-        // every load issued before the first use (the index is clamped, the key selected after)
-        const int e = lane + 64 * s;
-        key[s] = __float_as_uint(logits[e < E ? e : E - 1]);
-        idv[s] = uint32_t(e);
+        idv[s] = uint32_t(lane + 64 * s);
+        key[s] = int(idv[s]) < E ? float_order_key(lv[s] + 0.0f) : 0u;   // 0: no candidate
     }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < KPER; s++)   // 0: no candidate
-        key[s] = int(idv[s]) < E ? float_order_key(__uint_as_float(key[s]) + 0.0f) : 0u;
     // sort the lane's candidates: key descending, id ascending (ids already ascending in s)
 #pragma unroll
     for (int i = 1; i < KPER; i++)
@@ -453,6 +449,21 @@ __device__ __forceinline__ void topk_softmax_wave_t(const float *logits, int E, 
         ids_out[lane] = my_id;
         gates_out[lane] = ex / den;
     }
+}
+
+// The same, the logits read from logits[0 .. E).
+template <int KPER, bool GATES = true>
+__device__ __forceinline__ void topk_softmax_wave_t(const float *logits, int E, int k, int32_t *ids_out,
+                                    float *gates_out, int lane)
+{
+    float lv[KPER];
+#pragma unroll
+    for (int s = 0; s < KPER; s++) {   // every load issued before the first use (index clamped)
+        const int e = lane + 64 * s;
+        lv[s] = logits[e < E ? e : E - 1];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    topk_softmax_wave_regs<KPER, GATES>(lv, E, k, ids_out, gates_out, lane);
 }
 
 // The gates of topk_softmax_wave_t<KPER, false>: g[j] holds the j-th selected logit on entry and

@@ -10,12 +10,14 @@
 //
 // Per layer, workgroup b (of 256) does:
 //   1. input   x: layer 0 reads x_in; later layers gather the d/2 words of packed bf16 pairs that
-//              the previous layer published (every workgroup needs all of x).
+//              the previous layer published (every workgroup needs all of x): each router thread
+//              polls the four words of its own 8-element chunk and works on them at once.
 //   2. router  the workgroup computes the logits of experts b + 256 m (router rows prefetched
 //              during the previous layer, one 16-byte chunk per thread) and publishes them; the
 //              pre-RMSNorm is a scalar on the logits and on the gate/up sums.
-//   3. top-k   every workgroup gathers all E logits and selects the same top-k (same values, same
-//              deterministic selection), so nothing else has to be broadcast.
+//   3. top-k   in every workgroup one wave gathers all E logits into registers and selects the
+//              same top-k (same values, same deterministic selection), so nothing else has to be
+//              broadcast.
 //   4. loads   the workgroup's share of gate/up rows (2 x k*F/256 rows of d/4 bytes, ~4 MB
 //              across the chip for the 2048/512/top-8 layer) is requested at once, with its scales;
 //              the gates are formed while it is in flight.  Once it has arrived, the share of down
@@ -144,10 +146,9 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
     using C = PC<D, F, K>;
     const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int E = a.E;
-    __shared__ float xs[D];                                      // layer input x
+    __shared__ __attribute__((aligned(16))) float xs[D];         // layer input x
     __shared__ __attribute__((aligned(16))) int8_t xd[2 * D];    // its digit planes
     __shared__ __attribute__((aligned(16))) int8_t hd[K * 2 * F];// digit planes of h, per expert
-    __shared__ float lg[kPB];
     __shared__ float sums[2 * C::Q];
     __shared__ float ys[K * C::RD];
     __shared__ float red[4][2 + kEM];
@@ -172,27 +173,18 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
         const uint32_t tag = uint32_t(l + 1);
         uint64_t *lgw = a.ll + size_t(l & 1) * lls, *hw = lgw + E, *xw = hw + C::HW;
 
-        // 1. layer input
+        // 1. layer input: layer 0 reads x_in into LDS; later layers are read by the router threads
+        //    below, each polling the four words (bf16 pairs) of its own 8-element chunks
+        const uint64_t *xprev = a.ll + size_t((l + 1) & 1) * lls + E + C::HW;   // layer l - 1's
         if (l == 0) {
             for (int i = t; i < D; i += kPT) xs[i] = bf16_to_f32(a.x_in[i]);
-        } else {
-            const uint64_t *xprev = a.ll + size_t((l - 1) & 1) * lls + E + C::HW;
-            constexpr int N = (C::XW + kPT - 1) / kPT;
-            uint64_t v[N];
-            wait_words<N>(xprev, t, kPT, C::XW, tag - 1, v, &s_abort, a.err);
-#pragma unroll
-            for (int n = 0; n < N; n++) {
-                const int i = t + kPT * n;
-                if (i < C::XW) {
-                    xs[2 * i] = bf16_lo(uint32_t(v[n]));
-                    xs[2 * i + 1] = bf16_hi(uint32_t(v[n]));
-                }
-            }
+            __syncthreads();
         }
-        __syncthreads();
 
         // 2. router threads: their 8-element chunks of x (amax, sum of squares, router partials in
-        //    the canonical order), wave reductions, then block totals, logits and digit planes
+        //    the canonical order; from layer 1 on straight from the polled words, which are also
+        //    stored to LDS for the digit planes and the combine), wave reductions, then block
+        //    totals, logits and digit planes
         if (t < kCT) {
             float am = 0.0f, ss = 0.0f, rp[kEM];
 #pragma unroll
@@ -202,9 +194,22 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
                 const int c = t + kCT * n;
                 if (c < (D >> 3)) {
                     float xv[8];
+                    if (l == 0) {
+#pragma unroll
+                        for (int j = 0; j < 8; j++) xv[j] = xs[8 * c + j];
+                    } else {
+                        uint64_t v[4] = {0, 0, 0, 0};
+                        wait_words<4>(xprev, 4 * c, 1, C::XW, tag - 1, v, &s_abort, a.err);
+#pragma unroll
+                        for (int q = 0; q < 4; q++) {
+                            xv[2 * q] = bf16_lo(uint32_t(v[q]));
+                            xv[2 * q + 1] = bf16_hi(uint32_t(v[q]));
+                        }
+                        *reinterpret_cast<float4 *>(xs + 8 * c) = make_float4(xv[0], xv[1], xv[2], xv[3]);
+                        *reinterpret_cast<float4 *>(xs + 8 * c + 4) = make_float4(xv[4], xv[5], xv[6], xv[7]);
+                    }
 #pragma unroll
                     for (int j = 0; j < 8; j++) {
-                        xv[j] = xs[8 * c + j];
                         am = fmaxf(am, fabsf(xv[j]));
                         ss = ss + xv[j] * xv[j];
                     }
@@ -257,17 +262,19 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
             }
         }
 
-        // 3. routing: every workgroup gathers all logits and selects the same experts
-        {
-            constexpr int N = (kPB + kPT - 1) / kPT;
-            uint64_t v[N];
-            wait_words<N>(lgw, t, kPT, E, tag, v, &s_abort, a.err);
+        // 3. routing: in every workgroup wave 0 gathers all E logits (lane l: experts l + 64 s) into
+        //    registers and selects the same experts
+        if (wave == 0) {
+            constexpr int S = kPB / 64;
+            uint64_t v[S];
+            float lv[S];
 #pragma unroll
-            for (int n = 0; n < N; n++)
-                if (t + kPT * n < E) lg[t + kPT * n] = __uint_as_float(uint32_t(v[n]));
+            for (int q = 0; q < S; q++) v[q] = 0;
+            wait_words<S>(lgw, lane, 64, E, tag, v, &s_abort, a.err);
+#pragma unroll
+            for (int q = 0; q < S; q++) lv[q] = __uint_as_float(uint32_t(v[q]));
+            topk_softmax_wave_regs<S, false>(lv, E, K, s_ids, s_gates, lane);
         }
-        __syncthreads();
-        if (wave == 0) topk_softmax_wave_t<kPB / 64, false>(lg, E, K, s_ids, s_gates, lane);
         __syncthreads();
 
         // 4. request the gate/up rows of this workgroup's share at once (the down rows and the next
