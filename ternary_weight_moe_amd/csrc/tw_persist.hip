@@ -54,6 +54,14 @@ constexpr int kPT = 1024;              // threads per workgroup (16 waves)
 constexpr int kNW = kPT / 64;          // waves per workgroup
 constexpr int kCT = 256;               // threads of the canonical router order (4 waves)
 constexpr uint32_t kSpinLimit = 1u << 21;
+// Waits before the first poll of a hand-off, in s_sleep units (64 clocks, ~27 ns): the words cannot
+// arrive sooner than about a memory round trip after the slowest producer, and early polls from
+// every workgroup only add traffic to the memory system that the producers' stores and the expert
+// rows go through.  Measured on MI355X (24-layer stack, tokens/s): no waits 252.6 us per token;
+// 20 before the h words 232.6 (15: 234.8, 25: 234.0, 40: 243.9); and 10 before the residual words
+// 220.3 (5: 223.0, 15: 222.5, 20: 224.7); a wait before the logits or between polls adds nothing.
+constexpr int kSleepX = 10;            // before polling the residual words
+constexpr int kSleepH = 20;            // before polling the h words
 constexpr int kEM = 1;                 // router rows per workgroup: expert b (E <= 256)
 
 struct PLayer {
@@ -199,6 +207,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
                         for (int j = 0; j < 8; j++) xv[j] = xs[8 * c + j];
                     } else {
                         uint64_t v[4] = {0, 0, 0, 0};
+                        if (n == 0) __builtin_amdgcn_s_sleep(kSleepX);
                         wait_words<4>(xprev, 4 * c, 1, C::XW, tag - 1, v, &s_abort, a.err);
 #pragma unroll
                         for (int q = 0; q < 4; q++) {
@@ -340,6 +349,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
         {
             constexpr int N = C::HW / kPT, NT = C::HW / 4, CPE = F / 64;
             uint64_t v[N];
+            __builtin_amdgcn_s_sleep(kSleepH);
             wait_words<N>(hw, t, kPT, C::HW, tag, v, &s_abort, a.err);
 #pragma unroll
             for (int n = 0; n < N; n++) {
