@@ -26,10 +26,11 @@
 //              the first burst lets the gate/up bytes, which are on the critical path, arrive sooner.
 //   5. gate/up the ternary dots (tw_device.h) against the digit planes of x, h = SiLU(gate)*up
 //              in fp32, published one value per word.
-//   6. down    gather all k*F values of h, digit planes per expert (h passes through LDS so that each
-//              thread packs whole digit dwords; one barrier gives the per-expert max), the down dots for the
-//              workgroup's output rows, out = x + sum_j g_j y_j in selection order, rounded to
-//              bf16 and published (or stored to x_out after the last layer).
+//   6. down    wave j gathers the F values of expert j's h, takes their max, writes the digit
+//              planes to its own LDS region and computes expert j's down rows of the workgroup's
+//              outputs (no workgroup barrier until the combine); then out = x + sum_j g_j y_j in
+//              selection order, rounded to bf16 and published (or stored to x_out after the last
+//              layer).
 // Tags are the layer index + 1 and the words alternate between two parities by layer, so a word
 // is never overwritten while a reader may still need its previous value (a workgroup can be at
 // most one hand-off ahead of any other).  A small kernel zeroes the words before each launch.
@@ -87,8 +88,7 @@ struct PC {
     static constexpr int PGU = (2 * Q + RPP - 1) / RPP;      // gate/up passes
     static constexpr int RD = D / kPB;                       // output rows per workgroup
     static constexpr int LPRD = F / 64;                      // lanes per down row
-    static constexpr int RPPD = kPT / LPRD;                  // down rows per pass
-    static constexpr int PD = (K * RD + RPPD - 1) / RPPD;    // down passes
+    static constexpr int DL = RD * LPRD;                     // lanes of an expert's down rows
     static constexpr int XW = D / 2;                         // residual words (bf16 pairs)
     static constexpr int HW = K * F;                         // h words (fp32)
     static constexpr int NRC = (D / 8 + kCT - 1) / kCT;      // 8-element chunks per router thread
@@ -96,7 +96,8 @@ struct PC {
     static_assert(RD >= 2 && RD % 2 == 0, "d must be a multiple of 512");
     static_assert(LPR >= 1 && LPR <= 64 && LPRD >= 1 && LPRD <= 64, "row widths 64..4096");
     static_assert(K <= kMaxTopK && K <= 16, "top-k");
-    static_assert(HW % kPT == 0 && HW <= 4 * kPT && F % 64 == 0, "k*F in {1024, 2048, 3072, 4096}");
+    static_assert(HW % kPT == 0 && HW <= 4 * kPT && F % 256 == 0, "k*F in {1024, 2048, 3072, 4096}");
+    static_assert(DL <= 64 && K <= kPT / 64, "wave j takes expert j's down rows");
     static_assert(XW % 64 == 0 && D % kPT == 0, "d a multiple of 1024");
 };
 
@@ -161,10 +162,8 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
     __shared__ float ys[K * C::RD];
     __shared__ float red[4][2 + kEM];
     __shared__ __attribute__((aligned(16))) float hs[C::HW];     // h, in digit-plane byte order
-    __shared__ float s_wmax[C::HW / 64];                         // max |h| per 64-word chunk
     __shared__ int32_t s_ids[kMaxTopK];
     __shared__ float s_gates[kMaxTopK];
-    __shared__ int s_hsh[K];
     __shared__ int s_xsh;
     __shared__ float s_inv;
     __shared__ int s_abort;
@@ -305,8 +304,8 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
         if (wave == 0) softmax_gates_wave(s_gates, K, lane);
 
         // 5. gate/up dots, h = SiLU(gate) * up in fp32, published one value per word
-        int4 cd[C::PD];
-        float sd[C::PD];
+        int4 cd;   // wave j < k: row lane / (F/64) of expert j's down rows, 64 columns
+        float sd;
         {
             int4 dg[2][4];
 #pragma unroll
@@ -322,17 +321,16 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
                 group_reduce<2>(acc, C::LPR);
                 if (c_gu == 0 && jb < 2 * C::Q) sums[jb] = float_value<2>(acc, s_xsh) * sg[p] * s_inv;
             }
-            // the down rows of this workgroup's outputs and the next layer's router rows
-#pragma unroll
-            for (int p = 0; p < C::PD; p++) {
-                const int jd = p * C::RPPD + t / C::LPRD;
-                const bool valid = jd < K * C::RD;
-                const int j = valid ? jd / C::RD : 0, rl = jd % C::RD;
-                const int R = b * C::RD + rl;
+            // the down rows of this workgroup's outputs (wave j: expert j) and the next layer's
+            // router rows
+            {
+                const bool valid = wave < K && lane < C::DL;
+                const int j = valid ? wave : 0, rl = lane / C::LPRD;
+                const int R = b * C::RD + (valid ? rl : 0);
                 const int e = min(max(s_ids[j], 0), E - 1);
                 const uint8_t *row = P.w_down + (size_t(e) * D + R) * (F / 4);
-                cd[p] = valid ? reinterpret_cast<const int4 *>(row)[c_d] : make_int4(0, 0, 0, 0);
-                sd[p] = (valid && c_d == 0) ? P.s_down[size_t(e) * D + R] : 0.0f;
+                cd = valid ? reinterpret_cast<const int4 *>(row)[c_d] : make_int4(0, 0, 0, 0);
+                sd = (valid && c_d == 0) ? P.s_down[size_t(e) * D + R] : 0.0f;
             }
             if (l + 1 < a.n_layers) load_router<C::NRC>(rw, a.L[l + 1].w_router, b, E, D);
         }
@@ -342,45 +340,40 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
             st_tagged(hw + b * C::Q + t, tag, __float_as_uint(h));
         }
 
-        // 6. gather h (word w = t + kPT n: expert w / F, element w % F; a wave's 64 words share one
-        //    expert), per-chunk max |h| and h itself into LDS in the digit-plane byte order; after
-        //    one barrier thread t (< k*F/4) turns elements 4r + c of 16-element group t / 4 (c = t % 4,
-        //    r < 4) into dword c of the group in both digit planes; then the down dots and the combine
-        {
-            constexpr int N = C::HW / kPT, NT = C::HW / 4, CPE = F / 64;
-            uint64_t v[N];
+        // 6. wave j (< k) gathers the F words of expert j's h itself (lane l: elements l + 64 m),
+        //    takes the expert's max |h| with one wave reduction, stores h in the digit-plane byte
+        //    order to its own LDS region and turns it into both digit planes (four elements of a
+        //    dword at a time), then computes expert j's down rows of this workgroup's outputs: no
+        //    workgroup barrier until the combine, and an expert goes ahead as soon as its h is
+        //    complete (the LDS accesses of one wave take effect in order)
+        if (wave < K) {
+            constexpr int M = F / 64;
+            const int j = wave;
+            float *hsj = hs + j * F;
+            uint64_t v[M];
+#pragma unroll
+            for (int m = 0; m < M; m++) v[m] = 0;
             __builtin_amdgcn_s_sleep(kSleepH);
-            wait_words<N>(hw, t, kPT, C::HW, tag, v, &s_abort, a.err);
+            wait_words<M>(hw + j * F, lane, 64, F, tag, v, &s_abort, a.err);
+            float am = 0.0f;
 #pragma unroll
-            for (int n = 0; n < N; n++) {
-                const float h = __uint_as_float(uint32_t(v[n]));
-                hs[perm16(t + kPT * n)] = h;
-                const float am = wave_max(fabsf(h));
-                if (lane == 0) s_wmax[n * kNW + wave] = am;   // chunk (t + kPT n) / 64
+            for (int m = 0; m < M; m++) {
+                const float h = __uint_as_float(uint32_t(v[m]));
+                hsj[perm16(lane + 64 * m)] = h;
+                am = fmaxf(am, fabsf(h));
             }
-            __syncthreads();
-            if (t < NT) {
-                const int j = (t >> 2) / (F / 16), g = (t >> 2) % (F / 16);
-                float hm = s_wmax[j * CPE];
+            const int sh = float_digit_shift(wave_max(am), 2);
 #pragma unroll
-                for (int c = 1; c < CPE; c++) hm = fmaxf(hm, s_wmax[j * CPE + c]);
-                const int sh = float_digit_shift(hm, 2);
-                if (t % (F / 4) == 0) s_hsh[j] = sh;   // the expert's first thread
-                const float4 hv = *reinterpret_cast<const float4 *>(hs + 4 * t);
+            for (int u = 0; u < F / 256; u++) {   // dword q of both planes: elements 4q .. 4q + 3
+                const int q = lane + 64 * u;
+                const float4 hv = *reinterpret_cast<const float4 *>(hsj + 4 * q);
                 const uint32_t pr[4] = {float_digit_pair(hv.x, sh), float_digit_pair(hv.y, sh),
                                         float_digit_pair(hv.z, sh), float_digit_pair(hv.w, sh)};
                 uint32_t lo, hi;
                 digit_pair_dwords(pr, lo, hi);
-                *reinterpret_cast<uint32_t *>(hd + (j * 2) * F + 16 * g + 4 * (t & 3)) = hi;
-                *reinterpret_cast<uint32_t *>(hd + (j * 2 + 1) * F + 16 * g + 4 * (t & 3)) = lo;
+                *reinterpret_cast<uint32_t *>(hd + (j * 2) * F + 4 * q) = hi;   // plane 0: high
+                *reinterpret_cast<uint32_t *>(hd + (j * 2 + 1) * F + 4 * q) = lo;
             }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int p = 0; p < C::PD; p++) {
-            const int jd = p * C::RPPD + t / C::LPRD;
-            const bool valid = jd < K * C::RD;
-            const int j = valid ? jd / C::RD : 0, rl = jd % C::RD;
             int4 dh[2][4];
 #pragma unroll
             for (int pl = 0; pl < 2; pl++)
@@ -388,9 +381,9 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
                 for (int qq = 0; qq < 4; qq++)
                     dh[pl][qq] = reinterpret_cast<const int4 *>(hd + (j * 2 + pl) * F + c_d * 64)[qq];
             int32_t acc[2] = {0, 0};
-            chunk_dot<2>(cd[p], dh, acc);
+            chunk_dot<2>(cd, dh, acc);
             group_reduce<2>(acc, C::LPRD);
-            if (c_d == 0 && valid) ys[j * C::RD + rl] = float_value<2>(acc, s_hsh[j]) * sd[p];
+            if (c_d == 0 && lane < C::DL) ys[j * C::RD + lane / C::LPRD] = float_value<2>(acc, sh) * sd;
         }
         __syncthreads();
         if (t < C::RD / 2) {
