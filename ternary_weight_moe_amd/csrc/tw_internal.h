@@ -36,7 +36,11 @@ struct DecodeWs {
 };
 // Tagged words of the one-launch stacked decode: two parities of (E logits, k*F fp32 h values,
 // d/2 packed bf16 residual pairs).
-inline size_t persist_words(const Dims &dm) { return 2 * (size_t(dm.E) + size_t(dm.k) * dm.F + dm.d / 2); }
+// Logit words of the one-launch decode lie kLgStride words apart (each workgroup publishes one; four
+// writers per 128-byte line measured faster than sixteen, and than one with sixteen times the
+// lines to poll).
+constexpr int kLgStride = 4;
+inline size_t persist_words(const Dims &dm) { return 2 * (size_t(dm.E) * kLgStride + size_t(dm.k) * dm.F + dm.d / 2); }
 inline DecodeWs decode_ws_layout(const Dims &dm) {
     DecodeWs w{};
     size_t o = 0;

@@ -171,18 +171,18 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
 
     int4 rw[kEM][C::NRC];
     load_router<C::NRC>(rw, a.L[0].w_router, b, E, D);
-    const size_t lls = size_t(E) + C::HW + C::XW;
+    const size_t lls = size_t(E) * kLgStride + C::HW + C::XW;
     const int c_gu = t % C::LPR, c_d = t % C::LPRD;
     __syncthreads();
 
     for (int l = 0; l < a.n_layers; l++) {
         const PLayer &P = a.L[l];
         const uint32_t tag = uint32_t(l + 1);
-        uint64_t *lgw = a.ll + size_t(l & 1) * lls, *hw = lgw + E, *xw = hw + C::HW;
+        uint64_t *lgw = a.ll + size_t(l & 1) * lls, *hw = lgw + E * kLgStride, *xw = hw + C::HW;
 
         // 1. layer input: layer 0 reads x_in into LDS; later layers are read by the router threads
         //    below, each polling the four words (bf16 pairs) of its own 8-element chunks
-        const uint64_t *xprev = a.ll + size_t((l + 1) & 1) * lls + E + C::HW;   // layer l - 1's
+        const uint64_t *xprev = a.ll + size_t((l + 1) & 1) * lls + E * kLgStride + C::HW;   // layer l - 1's
         if (l == 0) {
             for (int i = t; i < D; i += kPT) xs[i] = bf16_to_f32(a.x_in[i]);
             __syncthreads();
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
             if (t < kEM && b + kPB * t < E) {
                 float lgt = (red[0][2 + t] + red[1][2 + t]) + (red[2][2 + t] + red[3][2 + t]);
                 if (a.pre_norm) lgt = lgt * inv;
-                st_tagged(lgw + b + kPB * t, tag, __float_as_uint(lgt));
+                st_tagged(lgw + (b + kPB * t) * kLgStride, tag, __float_as_uint(lgt));
             }
             if (t == 0) {
                 s_xsh = sh;
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
             float lv[S];
 #pragma unroll
             for (int q = 0; q < S; q++) v[q] = 0;
-            wait_words<S>(lgw, lane, 64, E, tag, v, &s_abort, a.err);
+            wait_words<S>(lgw, lane * kLgStride, 64 * kLgStride, E * kLgStride, tag, v, &s_abort, a.err);
 #pragma unroll
             for (int q = 0; q < S; q++) lv[q] = __uint_as_float(uint32_t(v[q]));
             topk_softmax_wave_regs<S, false>(lv, E, K, s_ids, s_gates, lane);
