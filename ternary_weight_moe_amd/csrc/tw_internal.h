@@ -34,13 +34,18 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 struct DecodeWs {
     size_t ctrl, logits, ids, gates, xinfo, xdig, h, xbuf, ll, err, total;
 };
-// Tagged words of the one-launch stacked decode: two parities of (E logits, k*F fp32 h values,
-// d/2 packed bf16 residual pairs).
+// Tagged words of the one-launch stacked decode: two parities of kLlCopies copies of one set of
+// (E logits, k*F fp32 h values, d/2 packed bf16 residual pairs).  Every word is stored into each
+// copy and each workgroup polls the copy of its own XCD, so that the polls of all 256 workgroups do
+// not converge on the same few lines (an all-to-all round of tagged words over 256 workgroups
+// measured 2.42 us with one copy, 2.07 with two, 1.90 with four, 1.86 with eight).
 // Logit words of the one-launch decode lie kLgStride words apart (each workgroup publishes one; four
 // writers per 128-byte line measured faster than sixteen, and than one with sixteen times the
 // lines to poll).
 constexpr int kLgStride = 4;
-inline size_t persist_words(const Dims &dm) { return 2 * (size_t(dm.E) * kLgStride + size_t(dm.k) * dm.F + dm.d / 2); }
+constexpr int kLlCopies = 8;
+inline size_t persist_set_words(const Dims &dm) { return size_t(dm.E) * kLgStride + size_t(dm.k) * dm.F + dm.d / 2; }
+inline size_t persist_words(const Dims &dm) { return 2 * size_t(kLlCopies) * persist_set_words(dm); }
 inline DecodeWs decode_ws_layout(const Dims &dm) {
     DecodeWs w{};
     size_t o = 0;

@@ -6,7 +6,10 @@
 // 256 workgroups of 1024 threads (one per compute unit) stay resident for the whole stack and hand each other the
 // three small vectors of every layer through tagged 64-bit words (tw_device.h): each word is one
 // device-scope atomic store of (tag, data) and is read by polling, so a hand-off costs one memory
-// round trip and needs no grid barrier, no fence and no atomic read-modify-write.
+// round trip and needs no grid barrier, no fence and no atomic read-modify-write.  Every word is
+// stored into eight copies and each workgroup polls the copy of its own XCD (hardware register
+// XCC_ID), which spreads the polls of the 256 workgroups over eight sets of lines; any copy holds
+// the same values, so which one a workgroup reads never changes a result.
 //
 // Per layer, workgroup b (of 256) does:
 //   1. input   x: layer 0 reads x_in; later layers gather the d/2 words of packed bf16 pairs that
@@ -171,18 +174,23 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
 
     int4 rw[kEM][C::NRC];
     load_router<C::NRC>(rw, a.L[0].w_router, b, E, D);
-    const size_t lls = size_t(E) * kLgStride + C::HW + C::XW;
+    const size_t lls = size_t(E) * kLgStride + C::HW + C::XW;   // words of one copy
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    const size_t own = size_t(xcc & uint32_t(kLlCopies - 1)) * lls;   // the copy this workgroup polls
     const int c_gu = t % C::LPR, c_d = t % C::LPRD;
     __syncthreads();
 
     for (int l = 0; l < a.n_layers; l++) {
         const PLayer &P = a.L[l];
         const uint32_t tag = uint32_t(l + 1);
-        uint64_t *lgw = a.ll + size_t(l & 1) * lls, *hw = lgw + E * kLgStride, *xw = hw + C::HW;
+        // copy 0 of this layer's parity (stores go to every copy) and the copy read here
+        uint64_t *set0 = a.ll + size_t(l & 1) * kLlCopies * lls;
+        const uint64_t *lgw = set0 + own, *hw = lgw + E * kLgStride;
 
         // 1. layer input: layer 0 reads x_in into LDS; later layers are read by the router threads
         //    below, each polling the four words (bf16 pairs) of its own 8-element chunks
-        const uint64_t *xprev = a.ll + size_t((l + 1) & 1) * lls + E * kLgStride + C::HW;   // layer l - 1's
+        const uint64_t *xprev = a.ll + size_t((l + 1) & 1) * kLlCopies * lls + own + E * kLgStride + C::HW;   // layer l - 1's
         if (l == 0) {
             for (int i = t; i < D; i += kPT) xs[i] = bf16_to_f32(a.x_in[i]);
             __syncthreads();
@@ -250,10 +258,11 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
             const float ss = (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]);
             const float inv = a.pre_norm ? inv_rms_of(ss, D) : 1.0f;
             const int sh = float_digit_shift(am, 2);
-            if (t < kEM && b + kPB * t < E) {
-                float lgt = (red[0][2 + t] + red[1][2 + t]) + (red[2][2 + t] + red[3][2 + t]);
+            if (t < kEM * kLlCopies && b + kPB * (t / kLlCopies) < E) {   // thread t: copy t % kLlCopies
+                const int m = t / kLlCopies;
+                float lgt = (red[0][2 + m] + red[1][2 + m]) + (red[2][2 + m] + red[3][2 + m]);
                 if (a.pre_norm) lgt = lgt * inv;
-                st_tagged(lgw + (b + kPB * t) * kLgStride, tag, __float_as_uint(lgt));
+                st_tagged(set0 + (t % kLlCopies) * lls + (b + kPB * m) * kLgStride, tag, __float_as_uint(lgt));
             }
             if (t == 0) {
                 s_xsh = sh;
@@ -335,9 +344,10 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
             if (l + 1 < a.n_layers) load_router<C::NRC>(rw, a.L[l + 1].w_router, b, E, D);
         }
         __syncthreads();
-        if (t < C::Q) {
-            const float h = tw_silu(sums[2 * t]) * sums[2 * t + 1];
-            st_tagged(hw + b * C::Q + t, tag, __float_as_uint(h));
+        if (t < C::Q * kLlCopies) {   // thread t: value t % Q into copy t / Q
+            const int i = t % C::Q;
+            const float h = tw_silu(sums[2 * i]) * sums[2 * i + 1];
+            st_tagged(set0 + (t / C::Q) * lls + E * kLgStride + b * C::Q + i, tag, __float_as_uint(h));
         }
 
         // 6. wave j (< k) gathers the F words of expert j's h itself (lane l: elements l + 64 m),
@@ -386,18 +396,21 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
             if (c_d == 0 && lane < C::DL) ys[j * C::RD + lane / C::LPRD] = float_value<2>(acc, sh) * sd;
         }
         __syncthreads();
-        if (t < C::RD / 2) {
-            const int R0 = b * C::RD + 2 * t;
+        if (t < (C::RD / 2) * kLlCopies) {   // thread t: row pair t % (RD/2) into copy t / (RD/2)
+            const int i = t % (C::RD / 2), c = t / (C::RD / 2);
+            const int R0 = b * C::RD + 2 * i;
             float o0 = xs[R0], o1 = xs[R0 + 1];
             for (int j = 0; j < K; j++) {
-                o0 = o0 + s_gates[j] * ys[j * C::RD + 2 * t];
-                o1 = o1 + s_gates[j] * ys[j * C::RD + 2 * t + 1];
+                o0 = o0 + s_gates[j] * ys[j * C::RD + 2 * i];
+                o1 = o1 + s_gates[j] * ys[j * C::RD + 2 * i + 1];
             }
             if (l == a.n_layers - 1) {
-                a.x_out[R0] = f32_to_bf16(o0);
-                a.x_out[R0 + 1] = f32_to_bf16(o1);
+                if (c == 0) {
+                    a.x_out[R0] = f32_to_bf16(o0);
+                    a.x_out[R0 + 1] = f32_to_bf16(o1);
+                }
             } else {
-                st_tagged(xw + (b * C::RD) / 2 + t, tag, pack_bf16x2(o0, o1));
+                st_tagged(set0 + c * lls + E * kLgStride + C::HW + (b * C::RD) / 2 + i, tag, pack_bf16x2(o0, o1));
             }
         }
         __syncthreads();
@@ -463,7 +476,7 @@ int persist_run(const Dims &dm, const LayerPtrs *layers, int n, const void *x_in
             a.L[i] = PLayer{static_cast<const uint16_t *>(p.w_router), p.w_gate, p.w_up, p.w_down,
                             p.s_gate, p.s_up, p.s_down};
         }
-        k_persist_zero<<<16, 256, 0, s>>>(ll, nw, err);
+        k_persist_zero<<<int((nw + 2047) / 2048), 256, 0, s>>>(ll, nw, err);
         k_persist<D, F, K><<<kPB, kPT, 0, s>>>(a);
         done += m;
         chunk++;
