@@ -82,6 +82,7 @@ def lib():
                 "or_ffn_token_i8": (None, [_P(_LayerI8), fp, ip, fp, fp, i8p, fp, ip, ip, i8p, fp,
                                            ip, fp]),
                 "or_ffn_batch_i8": (None, [_P(_LayerI8), fp, i64, ip, fp, fp, i32]),
+                "or_quantize_absmean": (C.c_int, [fp, i64, i64, i8p, fp]),
             }
             for name, (res, args) in sig.items():
                 f = getattr(L, name)
@@ -128,6 +129,20 @@ def pack(w) -> tuple[np.ndarray, int]:
     out = np.empty(w.shape[:-1] + ((cols + 3) // 4,), dtype=np.uint8)
     bad = lib().or_pack(_ptr(w, C.c_int8), rows, cols, _ptr(out, C.c_uint8))
     return out, int(bad)
+
+
+def quantize_absmean(w) -> tuple[np.ndarray, np.ndarray]:
+    """float [..., cols] (fp32 or bf16 values) -> (int8 codes in {-1,0,1} [..., cols], fp32 scales
+    [...]): per-row absmean quantisation, tw_oracle.c."""
+    w = _np(w, np.float32)
+    cols = w.shape[-1]
+    rows = int(np.prod(w.shape[:-1])) if w.ndim > 1 else 1
+    t = np.empty(w.shape, dtype=np.int8)
+    s = np.empty(w.shape[:-1] if w.ndim > 1 else (1,), dtype=np.float32)
+    if lib().or_quantize_absmean(_ptr(w, C.c_float), rows, cols, _ptr(t, C.c_int8),
+                                 _ptr(s, C.c_float)) != 0:
+        raise ValueError("cols must be a multiple of 8")
+    return t, s
 
 
 def unpack(packed, cols: int) -> tuple[np.ndarray, int]:

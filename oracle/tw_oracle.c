@@ -435,3 +435,61 @@ void or_ffn_batch_i8(const or_layer_i8 *L, const float *x, int64_t n_tokens, con
         or_ffn_token_i8(L, x + t * d, ids + t * k, gates + t * k, out + t * d, NULL, NULL, NULL,
                         NULL, NULL, NULL, NULL, NULL);
 }
+
+/* ---- float -> ternary quantisation (per-row absmean) ---------------------------------------
+ * The pages describe ternary weights as float weights mapped onto three states with scale factors
+ * kept beside them ([Hub] "Ternary Quantization Is More Than Simply Compressing Weights into Three
+ * Values"), and contrast models quantised to ternary after training with ones trained ternary
+ * ([MacMini] "Why Everyone Else Quantizes After Training").  They give no formula; the reading here
+ * is the per-row absmean rule: g = mean_i |w_i| over the row, t_i = clamp(rint(w_i / g), -1, 1)
+ * (rint: to nearest, ties to even), and g is the row's scale, so that g * t approximates w.  A row
+ * of zeros gives t = 0 and g = 0.
+ * Because g decides integer codes, the sum of |w_i| is taken in one fixed fp32 order: the row is
+ * cut into 8-element chunks; partial p (p < 256) adds, in increasing order, the elements of chunks
+ * p, p + 256, p + 512, ... (elements of a chunk in order), starting from 0; partials 64m .. 64m+63
+ * are added by a balanced pairwise tree (neighbours first) into s_m; the sum is (s_0 + s_1) +
+ * (s_2 + s_3).  g = sum / cols and q_i = w_i / g are single fp32 divisions.  cols must be a
+ * multiple of 8.  Returns 0, or -1 when cols is not a multiple of 8. */
+
+static float pairwise_tree64(const float *v)
+{
+    float t[64];
+    for (int i = 0; i < 64; i++) t[i] = v[i];
+    for (int n = 64; n > 1; n /= 2)
+        for (int i = 0; i < n / 2; i++) t[i] = t[2 * i] + t[2 * i + 1];
+    return t[0];
+}
+
+int or_quantize_absmean(const float *w, int64_t rows, int64_t cols, int8_t *t, float *scale)
+{
+    if (cols % 8 != 0) return -1;
+    int64_t nch = cols / 8;
+    for (int64_t r = 0; r < rows; r++) {
+        const float *row = w + r * cols;
+        float part[256];
+        for (int p = 0; p < 256; p++) {
+            float acc = 0.0f;
+            for (int64_t c = p; c < nch; c += 256)
+                for (int j = 0; j < 8; j++) acc = acc + fabsf(row[8 * c + j]);
+            part[p] = acc;
+        }
+        float s0 = pairwise_tree64(part), s1 = pairwise_tree64(part + 64);
+        float s2 = pairwise_tree64(part + 128), s3 = pairwise_tree64(part + 192);
+        float sum = (s0 + s1) + (s2 + s3);
+        float g = sum / (float)cols;
+        int8_t *tr = t + r * cols;
+        if (g == 0.0f) {
+            for (int64_t i = 0; i < cols; i++) tr[i] = 0;
+            scale[r] = 0.0f;
+            continue;
+        }
+        for (int64_t i = 0; i < cols; i++) {
+            float q = rintf(row[i] / g);
+            if (q > 1.0f) q = 1.0f;
+            if (q < -1.0f) q = -1.0f;
+            tr[i] = (int8_t)q;
+        }
+        scale[r] = g;
+    }
+    return 0;
+}

@@ -103,6 +103,11 @@ void or_decode_stack(const or_layer *layers, int32_t n_layers, const double *x0,
 void or_dense_ffn_token(const or_layer *L, const double *x, const int32_t *ids,
                         const double *gates, double *out);
 
+/* ---- float -> ternary quantisation ----------------------------------------------------------
+ * Per row: g = mean |w| (fp32, in the fixed order given in tw_oracle.c), t = clamp(rint(w / g),
+ * -1, 1), scale = g; zero rows give t = 0, g = 0.  cols must be a multiple of 8 (else -1). */
+int or_quantize_absmean(const float *w, int64_t rows, int64_t cols, int8_t *t, float *scale);
+
 /* ---- int8 spec mode ----------------------------------------------------------------------- */
 float or_spec_expf(float z);
 /* absmax quantisation of n fp32 values: q in [-127,127], scale s (0 when all inputs are 0). */

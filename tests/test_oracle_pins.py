@@ -413,3 +413,63 @@ def test_workload_byte_accounting():
     assert accounting.stack_bytes_per_token(synth.STACK24_B1) == 178_716_672
     assert 24 * 8 * 786_432 == 150_994_944      # expert codes per token in the stack
     assert accounting.layer_bytes(synth.SMALL_LAYER_B1) == 2 * 26_624 + 16_384 + 2 * 1024
+
+
+# ---- float -> ternary quantisation (per-row absmean) --------------------------------------------
+
+def test_quantize_equal_magnitudes_give_signs_and_that_magnitude():
+    # every |w| = 2^-3: the mean is exactly 2^-3, w / g = +-1
+    signs = np.where(rng.random((5, 2048)) < 0.5, -1.0, 1.0).astype(np.float32)
+    t, s = oracle.quantize_absmean(signs * 0.125)
+    assert np.array_equal(t, signs.astype(np.int8))
+    assert np.all(s == np.float32(0.125))
+
+
+@pytest.mark.parametrize("cols", [8, 512, 2048, 2056])
+def test_quantize_scaled_trits_round_trip(cols):
+    # w = a * T with a = 2^-5: the absolute sum a * nnz is exact in any order, g = a nnz / cols
+    # (a power-of-two cols divides exactly; 2056 = 8 * 257 checked against the exact quotient),
+    # and |w| / g = cols / nnz >= 1 for every nonzero, so the codes reproduce T
+    T = rand_trits(6, cols)
+    T[0] = 0
+    T[0, 3] = -1          # a single nonzero: |w| / g = cols
+    T[1] = 1              # all +1: g = a
+    t, s = oracle.quantize_absmean(T.astype(np.float32) * np.float32(2.0 ** -5))
+    nnz = np.count_nonzero(T, axis=1)
+    assert np.array_equal(t, T)
+    assert np.array_equal(s, (np.float32(2.0 ** -5) * nnz.astype(np.float32)) / np.float32(cols))
+    assert s[1] == np.float32(2.0 ** -5)
+
+
+def test_quantize_zero_row():
+    w = np.zeros((2, 64), np.float32)
+    w[1, 5] = 3.0
+    t, s = oracle.quantize_absmean(w)
+    assert np.all(t[0] == 0) and s[0] == 0.0
+    assert t[1, 5] == 1 and np.count_nonzero(t[1]) == 1 and s[1] == np.float32(3.0 / 64)
+
+
+def test_quantize_threshold_and_ties_to_even():
+    # cols 8: seven entries 15 and one v give g = (105 + |v|) / 8.  v = +-7: g = 14 and v / g =
+    # +-0.5 exactly, which rounds to 0 (ties to even); 15 / 14 rounds to 1.  v = 1.875: g =
+    # 3.734375, v / g = 0.502 -> 1 (against seven 4s); v = 1.75 -> 0.4706 -> 0.  v = 21 against
+    # seven 1s: g = 3.5, 21 / 3.5 = 6 -> clamped to 1.
+    w = np.array([[15] * 7 + [7], [15] * 7 + [-7], [4] * 7 + [1.875], [4] * 7 + [1.75],
+                  [1] * 7 + [21], [-1] * 7 + [-21]], np.float32)
+    t, s = oracle.quantize_absmean(w)
+    assert t[:, 7].tolist() == [0, 0, 1, 0, 1, -1]
+    assert t[0, :7].tolist() == [1] * 7 and t[5, :7].tolist() == [0] * 7
+    assert s.tolist() == [14.0, 14.0, 3.734375, 3.71875, 3.5, 3.5]
+
+
+def test_quantize_scale_is_the_mean_magnitude():
+    # against the fp64 mean: the fp32 sum of n terms is within n * 2^-24 relative of it
+    w = (rng.normal(0, 0.02, (16, 2048))).astype(np.float32)
+    _, s = oracle.quantize_absmean(w)
+    ref = np.mean(np.abs(w.astype(np.float64)), axis=1)
+    assert np.all(np.abs(s - ref) <= ref * 2048 * 2.0 ** -24)
+
+
+def test_quantize_rejects_ragged_rows():
+    with pytest.raises(ValueError):
+        oracle.quantize_absmean(np.ones((1, 12), np.float32))
