@@ -12,7 +12,8 @@ bounded sample of the same workload.
 
 Other workloads (--workload): layer_b1 (one layer, batch 1), batched_b64 / batched_b64_int8 (one
 layer, 64 tokens grouped by expert), prefill_4096 (one layer, 4096 tokens, int8 activations, routing
-passed in; reported as int8 MFMA throughput); single-layer workloads rotate 8 independently seeded
+passed in; reported as int8 MFMA throughput), quantize_layer (float expert weights of one layer to
+packed ternary codes and per-row scales); single-layer workloads rotate 8 independently seeded
 layer copies so that the 256 MB last-level cache never holds the layer being timed.
 """
 from __future__ import annotations
@@ -231,6 +232,49 @@ def run_single_layer(args, name):
     )
 
 
+def run_quantize(args):
+    """ternary_quantize of one full layer's float expert weights (gate, up, down: 805 M bf16
+    weights, 1.6 GB, larger than the last-level cache) per step."""
+    wl = synth.QUANTIZE_LAYER
+    w = synth.float_expert_weights(wl, 0, device="cuda")
+    mats = [w["w_gate"], w["w_up"], w["w_down"]]
+    outs = [(torch.empty(m.shape[:-1] + (m.shape[-1] // 4,), dtype=torch.uint8, device="cuda"),
+             torch.empty(m.shape[:-1], dtype=torch.float32, device="cuda")) for m in mats]
+    torch.cuda.synchronize()
+
+    def step(t):
+        for m, (p, sc) in zip(mats, outs):
+            tw.ternary_quantize(m, packed=p, scales=sc)
+
+    G = min(args.graph_steps, 16)
+    steps = max(G, (args.steps // 10) // G * G)
+    total, _ = time_graph(step, G, min(args.warmup, 4 * G), steps)
+    sec = total / steps
+    n_w = sum(m.numel() for m in mats)
+    bytes_per_step = accounting.quantize_bytes(wl)
+    achieved = bytes_per_step / sec / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle  # the CPU baseline leg: the oracle as it stands, one thread
+        sample = mats[0].reshape(-1, wl.d_model)[:131072].cpu()
+        t0 = time.perf_counter()
+        oracle.quantize_absmean(sample)
+        dt = time.perf_counter() - t0
+        cpu = dict(value=sample.numel() / dt, unit="weights/s", cores=1, kind="oracle",
+                   sample="131072 rows of 2048 bf16 weights (the gate matrix, %.1f s), one thread" % dt)
+    return dict(
+        metric="quantize_layer weights/s (float -> packed ternary, one layer's experts)",
+        value=n_w / sec, unit="weights/s", n_gpus=1, steps=steps, warmup=args.warmup,
+        ms_per_step=sec * 1e3, higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="bf16 -> 2-bit codes + fp32 scales", data="synthetic",
+        config=dict(workload="quantize_layer", weights=n_w, bytes_per_step=bytes_per_step),
+        roofline=dict(bound="hbm", achieved=achieved, peak=accounting.HBM_PEAK_BPS / 1e9,
+                      unit="GB/s", frac=achieved * 1e9 / accounting.HBM_PEAK_BPS, traffic=None,
+                      kernel="k_quant_absmean<bf16> x 3 (gate, up, down)"),
+        cpu_baseline=cpu,
+    )
+
+
 def run_copy_calib(args):
     """A plain device-to-device copy of a known size (4 x 1 GiB), for scaling the FETCH_SIZE and
     WRITE_SIZE hardware counters of the measured kernels."""
@@ -259,7 +303,7 @@ def main():
     ap.add_argument("--graph-steps", type=int, default=256)
     ap.add_argument("--workload", default="stack24_b1",
                     choices=["stack24_b1", "layer_b1", "batched_b64", "batched_b64_int8",
-                             "prefill_4096", "copy_calib"])
+                             "prefill_4096", "quantize_layer", "copy_calib"])
     ap.add_argument("--cpu-tokens", type=int, default=36)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -277,6 +321,8 @@ def main():
         res = run_stack(args)
     elif args.workload == "copy_calib":
         res = run_copy_calib(args)
+    elif args.workload == "quantize_layer":
+        res = run_quantize(args)
     else:
         res = run_single_layer(args, args.workload)
     res["device"] = torch.cuda.get_device_properties(0).gcnArchName

@@ -105,6 +105,30 @@ tw_status ternary_pack(const int8_t *w, int64_t rows, int64_t cols, uint8_t *pac
                        int32_t *bad_count, void *stream);
 
 /*
+ * ternary_quantize -- float weights to the packed ternary layout above with one scale per row, by
+ * the per-row absmean rule: g = mean_i |w_i|, t_i = clamp(rint(w_i / g), -1, 1) (rint: nearest,
+ * ties to even), scale = g, so that scale * T approximates the row; a row of zeros gives codes 0
+ * and scale 0.  The codes and scales are the w_gate/w_up/w_down and s_gate/s_up/s_down operands of
+ * tw_moe_layer (row = output channel).
+ *   w        [rows][cols] in w_dtype (TW_F32 or TW_BF16), device, row-major.
+ *   packed   [rows][cols/4] uint8 output, device; scales [rows] fp32 output, device.
+ *   Precision: because g decides integer codes, the sum of |w_i| is taken in one fixed fp32 order
+ *   (the row in 8-element chunks; partial p < 256 adds chunks p, p + 256, ... in order; partials
+ *   64m..64m+63 by a balanced pairwise tree into s_m; sum = (s_0 + s_1) + (s_2 + s_3)); g = sum /
+ *   cols and w_i / g are correctly rounded fp32 divisions.  Equal inputs give equal codes on any
+ *   device and in any call.
+ *   Errors: TW_E_SHAPE (rows or cols < 0), TW_E_DTYPE, TW_E_NULL, TW_E_UNSUPPORTED (cols not a
+ *   multiple of 8 or above 65536; w or packed not 16-byte aligned; scales not 4-byte aligned),
+ *   TW_E_ALIAS (any two of w, packed, scales overlap).  rows == 0 or cols == 0 is a no-op.
+ *   Source: ternary weights as float weights mapped onto three states with scale factors kept
+ *   beside them, [Hub] "Ternary Quantization Is More Than Simply Compressing Weights into Three
+ *   Values"; models quantised to ternary after training, [MacMini] "Why Everyone Else Quantizes
+ *   After Training".  The pages give no formula; the absmean rule is the reading taken here.
+ */
+tw_status ternary_quantize(const void *w, int32_t w_dtype, int64_t rows, int64_t cols,
+                           uint8_t *packed, float *scales, void *stream);
+
+/*
  * moe_route_topk -- router logits, top-k selection and softmax gates for n_tokens tokens.
  *   x          [T][d] in x_dtype (TW_F32 or TW_BF16).
  *   w_router   [E][d] in w_dtype.

@@ -63,11 +63,16 @@ MID_STACK_B1 = Workload("mid_stack_b1", 1024, 64, 256, 4, "bf16", "bf16", "bf16"
                         pre_rmsnorm=True, seed=1005)
 NARROW_LAYER_B1 = Workload("narrow_layer_b1", 512, 16, 128, 2, "bf16", "bf16", "bf16", seed=1006)
 
+# float expert weights of one full-size layer, quantised to ternary (gate/up [E][F][d], down
+# [E][d][F], bf16 ~ N(0, 0.02))
+QUANTIZE_LAYER = Workload("quantize_layer", 2048, 256, 512, 8, "bf16", "bf16", "bf16", seed=1007)
+
 WORKLOADS = {w.name: w for w in (SMALL_LAYER_B1, LAYER_B1, STACK24_B1, BATCHED_B64,
-                                 BATCHED_B64_INT8, PREFILL_4096, MID_STACK_B1, NARROW_LAYER_B1)}
+                                 BATCHED_B64_INT8, PREFILL_4096, MID_STACK_B1, NARROW_LAYER_B1,
+                                 QUANTIZE_LAYER)}
 
 _KINDS = {"router": 1, "gate": 2, "up": 3, "down": 4, "s_gate": 5, "s_up": 6, "s_down": 7,
-          "x": 8}
+          "x": 8, "fgate": 9, "fup": 10, "fdown": 11}
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -113,6 +118,22 @@ def layer_weights(w: Workload, layer: int = 0, device="cpu", seed: int | None = 
         s_gate=uniform((E, F), 0.01, 0.1, device, s, layer, "s_gate"),
         s_up=uniform((E, F), 0.01, 0.1, device, s, layer, "s_up"),
         s_down=uniform((E, d), 0.01, 0.1, device, s, layer, "s_down"),
+    )
+
+
+def float_expert_weights(w: Workload, layer: int = 0, device="cpu", seed: int | None = None,
+                         n_experts: int | None = None, dtype: str | None = None,
+                         std: float = 0.02) -> dict:
+    """Float (not yet ternary) expert weights of one layer: w_gate, w_up [E][F][d] and w_down
+    [E][d][F] ~ N(0, std) in the workload's router dtype (or `dtype`)."""
+    s = w.seed if seed is None else seed
+    E = w.n_experts if n_experts is None else n_experts
+    d, F = w.d_model, w.d_ff
+    dt = _DT[dtype or w.router_dtype]
+    return dict(
+        w_gate=normal((E, F, d), std, dt, device, s, layer, "fgate"),
+        w_up=normal((E, F, d), std, dt, device, s, layer, "fup"),
+        w_down=normal((E, d, F), std, dt, device, s, layer, "fdown"),
     )
 
 

@@ -40,7 +40,7 @@ class TwLayer(C.Structure):
                 ("s_down", C.c_void_p)]
 
 
-EXPORTS = ("tw_status_str", "ternary_pack", "moe_route_topk", "ternary_moe_ffn_decode",
+EXPORTS = ("tw_status_str", "ternary_pack", "ternary_quantize", "moe_route_topk", "ternary_moe_ffn_decode",
            "ternary_moe_decode_workspace_bytes", "ternary_moe_ffn_batched",
            "ternary_moe_batched_workspace_bytes")
 
@@ -59,6 +59,7 @@ def lib():
             sig = {
                 "tw_status_str": (C.c_char_p, [i32]),
                 "ternary_pack": (i32, [vp, i64, i64, vp, vp, vp]),
+                "ternary_quantize": (i32, [vp, i32, i64, i64, vp, vp, vp]),
                 "moe_route_topk": (i32, [vp, i32, vp, i32, i64, i32, i32, i32, i32, vp, vp, vp,
                                          vp]),
                 "ternary_moe_ffn_decode": (i32, [LP, i32, vp, vp, i32, vp, sz, vp]),
@@ -112,6 +113,24 @@ def ternary_pack(w: torch.Tensor, bad_count: torch.Tensor | None = None, out=Non
     return out
 
 
+def ternary_quantize(w: torch.Tensor, packed: torch.Tensor | None = None,
+                     scales: torch.Tensor | None = None, stream=None):
+    """float [..., cols] (fp32 or bf16, cols a multiple of 8) -> (packed uint8 [..., cols/4],
+    fp32 scales [...]) by the per-row absmean rule."""
+    _need_cuda(w, packed, scales)
+    if w.dtype not in _DT:
+        raise ValueError("ternary_quantize expects fp32 or bf16")
+    cols = w.shape[-1]
+    rows = w.numel() // cols if cols else 0
+    if packed is None:
+        packed = torch.empty(w.shape[:-1] + (cols // 4,), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(w.shape[:-1], dtype=torch.float32, device=w.device)
+    _check(lib().ternary_quantize(_ptr(w), _DT[w.dtype], rows, cols, _ptr(packed), _ptr(scales),
+                                  _stream(stream)), "ternary_quantize")
+    return packed, scales
+
+
 # ---- routing -------------------------------------------------------------------------------------
 
 def moe_route_topk(x: torch.Tensor, w_router: torch.Tensor, top_k: int, pre_rmsnorm: bool = False,
@@ -160,6 +179,17 @@ class MoELayer:
                     s_up.to(dev).contiguous(), s_down.to(dev).contiguous(), top_k, pre_rmsnorm)
         layer.bad_count = bad
         return layer
+
+
+    @classmethod
+    def from_float(cls, w_router, w_gate, w_up, w_down, top_k: int, pre_rmsnorm: bool = False,
+                   stream=None):
+        """Quantises float expert weights (gate/up [E][F][d], down [E][d][F]) with
+        ternary_quantize (on the device) and keeps the packed codes and per-row scales."""
+        dev = w_router.device
+        q = [ternary_quantize(t.to(dev).contiguous(), stream=stream) for t in (w_gate, w_up, w_down)]
+        return cls(w_router.to(dev).contiguous(), q[0][0], q[1][0], q[2][0], q[0][1], q[1][1],
+                   q[2][1], top_k, pre_rmsnorm)
 
 
 def decode_workspace_bytes(layers) -> int:

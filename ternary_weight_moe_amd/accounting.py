@@ -51,6 +51,15 @@ def int8_ops(w, n_pairs: int) -> int:
     return n_pairs * 3 * w.d_model * w.d_ff * 2
 
 
+def quantize_bytes(w) -> int:
+    """Algorithmic HBM bytes of quantising one layer's float expert weights (gate, up, down) to
+    packed ternary codes: every float read once, every code byte and per-row scale written once."""
+    E, d, F = w.n_experts, w.d_model, w.d_ff
+    n_w = 3 * E * F * d
+    rows = 2 * E * F + E * d
+    return n_w * _dt_bytes(w.router_dtype) + n_w // 4 + 4 * rows
+
+
 def ceiling_rate(bytes_per_unit: float, bandwidth_bps: float) -> float:
     """Units per second at which the bytes alone saturate the bandwidth."""
     return bandwidth_bps / bytes_per_unit

@@ -111,6 +111,24 @@ tw_status ternary_pack(const int8_t *w, int64_t rows, int64_t cols, uint8_t *pac
     return tw::launch_pack(w, rows, cols, packed, bad_count, stream) ? TW_E_HIP : TW_OK;
 }
 
+tw_status ternary_quantize(const void *w, int32_t w_dtype, int64_t rows, int64_t cols,
+                           uint8_t *packed, float *scales, void *stream)
+{
+    if (rows < 0 || cols < 0) return TW_E_SHAPE;
+    if (!valid_float(w_dtype)) return TW_E_DTYPE;
+    if (rows == 0 || cols == 0) return TW_OK;
+    if (!w || !packed || !scales) return TW_E_NULL;
+    if (cols % 8 != 0 || cols > 65536) return TW_E_UNSUPPORTED;
+    if (rows > (int64_t(1) << 40) / cols) return TW_E_SHAPE;
+    if ((((uintptr_t)w | (uintptr_t)packed) & 15) || ((uintptr_t)scales & 3)) return TW_E_UNSUPPORTED;
+    const size_t nw = size_t(rows * cols) * fsize(w_dtype), np = size_t(rows * cols / 4),
+                 ns = size_t(rows) * 4;
+    if (overlap(w, nw, packed, np) || overlap(w, nw, scales, ns) || overlap(packed, np, scales, ns))
+        return TW_E_ALIAS;
+    return tw::launch_quantize(w, w_dtype == TW_BF16, rows, cols, packed, scales, stream) ? TW_E_HIP
+                                                                                          : TW_OK;
+}
+
 tw_status moe_route_topk(const void *x, int32_t x_dtype, const void *w_router, int32_t w_dtype,
                          int64_t n_tokens, int32_t d_model, int32_t n_experts, int32_t top_k,
                          int32_t pre_rmsnorm, float *logits, int32_t *expert_ids, float *gate_w,

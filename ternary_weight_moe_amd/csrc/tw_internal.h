@@ -104,6 +104,8 @@ inline BatchedWs batched_ws_layout(const Dims &dm, int64_t T, int planes) {
 // ---- launchers (tw_kernels.hip); each returns 0 or a hipError_t value --------------------------
 int launch_pack(const int8_t *w, int64_t rows, int64_t cols, uint8_t *packed, int32_t *bad,
                 void *stream);
+int launch_quantize(const void *w, int w_bf16, int64_t rows, int64_t cols, uint8_t *packed,
+                    float *scales, void *stream);
 int launch_route(const void *x, int x_bf16, const void *w_router, int w_bf16, int64_t T,
                  const Dims &dm, float *logits, int32_t *ids, float *gates, void *stream);
 // One launch per (up to kMaxPersistLayers) layers; returns -1 when the shape or device is not

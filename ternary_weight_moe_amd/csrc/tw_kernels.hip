@@ -68,6 +68,111 @@ __global__ void k_pack_any(const int8_t *__restrict__ w, int64_t rows, int64_t c
 }
 
 // ------------------------------------------------------------------------------------------------
+// ternary_quantize: one wave per row.  Lane l holds the partial sums l + 64 m (m < 4) of |w| in the
+// canonical order of canon_dot (chunks l + 64 m, + 256, ... in order, then wave_sum per m and
+// (s_0 + s_1) + (s_2 + s_3)), so the row's absmean, and with it every code, is the same in every
+// call.  Rows of at most 256 chunks keep their chunks in registers between the sum and the codes;
+// longer rows read them again.  Each chunk of 8 weights becomes two bytes of codes.
+template <bool BF16>
+__device__ __forceinline__ void quant_chunk(const void *row, int c, float (&v)[8])
+{
+    if (BF16) {
+        const int4 q = reinterpret_cast<const int4 *>(row)[c];
+        const uint32_t w[4] = {uint32_t(q.x), uint32_t(q.y), uint32_t(q.z), uint32_t(q.w)};
+#pragma unroll
+        for (int j = 0; j < 8; j++) v[j] = bf16_to_f32(uint16_t(w[j >> 1] >> (16 * (j & 1))));
+    } else {
+        const float4 *p = reinterpret_cast<const float4 *>(row) + 2 * c;
+        const float4 a = p[0], b = p[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+}
+
+// Codes of 8 weights: clamp(rint(w / g), -1, 1) with w / g one rounded fp32 division.  For g of at
+// least 2^-125 (so that g / 2 is exact) that is a comparison with g / 2: if g / 2 = M 2^e (M a
+// 24-bit integer), the next fp32 value above it, (M + 1) 2^e, gives w / g = 1/2 + 1/(2M) > 1/2 +
+// 2^-25, the midpoint between 1/2 and the next fp32 value, so the quotient rounds above 1/2 and
+// rint gives 1; w = g / 2 gives exactly 1/2, which rint takes to 0 (ties to even); every w below
+// gives a quotient of at most 1/2.  So the code is +1 iff w > g / 2 and -1 iff w < -g / 2, with no
+// division.  Smaller g (and g = 0) take the division itself.
+__device__ __forceinline__ uint32_t quant_codes8(const float (&v)[8], float g)
+{
+    uint32_t bits = 0;
+    if (g >= 0x1p-125f) {
+        const float hg = 0.5f * g;
+#pragma unroll
+        for (int j = 0; j < 8; j++) bits |= (v[j] > hg ? 1u : (v[j] < -hg ? 2u : 0u)) << (2 * j);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            float q = g == 0.0f ? 0.0f : __builtin_rintf(v[j] / g);
+            q = fminf(fmaxf(q, -1.0f), 1.0f);
+            bits |= (q > 0.0f ? 1u : (q < 0.0f ? 2u : 0u)) << (2 * j);
+        }
+    }
+    return bits;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_quant_absmean(const void *__restrict__ w, int64_t rows, int cols,
+                                                      uint8_t *__restrict__ packed,
+                                                      float *__restrict__ scales)
+{
+    const int lane = threadIdx.x & 63;
+    const int nch = cols >> 3;
+    const size_t eb = BF16 ? 2 : 4;
+    for (int64_t r = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6); r < rows;
+         r += int64_t(gridDim.x) * 4) {
+        const void *row = static_cast<const uint8_t *>(w) + size_t(r) * cols * eb;
+        uint16_t *prow = reinterpret_cast<uint16_t *>(packed + size_t(r) * (cols >> 2));
+        float s[4];
+        if (nch <= 256) {
+            float v[4][8];
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                const int c = 64 * m + lane;
+                if (c < nch) quant_chunk<BF16>(row, c, v[m]);
+            }
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                float acc = 0.0f;
+                if (64 * m + lane < nch) {
+#pragma unroll
+                    for (int j = 0; j < 8; j++) acc = acc + fabsf(v[m][j]);
+                }
+                s[m] = wave_sum(acc);
+            }
+            const float g = ((s[0] + s[1]) + (s[2] + s[3])) / float(cols);
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                const int c = 64 * m + lane;
+                if (c < nch) prow[c] = uint16_t(quant_codes8(v[m], g));
+            }
+            if (lane == 0) scales[r] = g;
+        } else {
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                float acc = 0.0f;
+                for (int c = 64 * m + lane; c < nch; c += 256) {
+                    float v[8];
+                    quant_chunk<BF16>(row, c, v);
+#pragma unroll
+                    for (int j = 0; j < 8; j++) acc = acc + fabsf(v[j]);
+                }
+                s[m] = wave_sum(acc);
+            }
+            const float g = ((s[0] + s[1]) + (s[2] + s[3])) / float(cols);
+            for (int c = lane; c < nch; c += 64) {
+                float v[8];
+                quant_chunk<BF16>(row, c, v);
+                prow[c] = uint16_t(quant_codes8(v, g));
+            }
+            if (lane == 0) scales[r] = g;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
 // Router logits for T tokens (k_route below).  Every logit is summed in the canonical order of
 // canon_dot: 256 partials, partial t adding the products of chunks t, t + 256 (8 elements each) in
 // order, then a balanced tree over the partials (wave_sum per 64, (w0+w1)+(w2+w3)).  The
@@ -1191,6 +1296,18 @@ int launch_pack(const int8_t *w, int64_t rows, int64_t cols, uint8_t *packed, in
         const unsigned nb = unsigned(n / 256 + 1 < 16384 ? n / 256 + 1 : 16384);
         k_pack_any<<<nb, 256, 0, S(stream)>>>(w, rows, cols, packed, bad);
     }
+    return last_error();
+}
+
+int launch_quantize(const void *w, int w_bf16, int64_t rows, int64_t cols, uint8_t *packed,
+                    float *scales, void *stream)
+{
+    const int64_t nb64 = (rows + 3) / 4;
+    const unsigned nb = unsigned(nb64 < 65536 ? nb64 : 65536);
+    if (w_bf16)
+        k_quant_absmean<true><<<nb, 256, 0, S(stream)>>>(w, rows, int(cols), packed, scales);
+    else
+        k_quant_absmean<false><<<nb, 256, 0, S(stream)>>>(w, rows, int(cols), packed, scales);
     return last_error();
 }
 

@@ -144,3 +144,23 @@ def test_batched_errors(L):
     assert call(ws=A[10] + 128) == E_UNSUP                            # workspace needs 256-B alignment
     assert call(xi=A[8] + 8) == E_UNSUP                               # activations need 16-B alignment
     assert L.ternary_moe_ffn_batched(None, 4, A[8], 1, A[9], 1, 0, None, None, A[10], need, s) == E_NULL
+
+
+def test_quantize_errors(L):
+    s = None
+    F32, BF16 = 0, 1
+    assert L.ternary_quantize(A[0], BF16, -1, 64, A[1], A[2], s) == E_SHAPE
+    assert L.ternary_quantize(A[0], BF16, 4, -8, A[1], A[2], s) == E_SHAPE
+    assert L.ternary_quantize(A[0], 7, 4, 64, A[1], A[2], s) == E_DTYPE
+    assert L.ternary_quantize(None, BF16, 0, 64, None, None, s) == OK       # empty: no-op
+    assert L.ternary_quantize(None, BF16, 4, 64, A[1], A[2], s) == E_NULL
+    assert L.ternary_quantize(A[0], BF16, 4, 64, None, A[2], s) == E_NULL
+    assert L.ternary_quantize(A[0], BF16, 4, 64, A[1], None, s) == E_NULL
+    assert L.ternary_quantize(A[0], F32, 4, 12, A[1], A[2], s) == E_UNSUP    # cols % 8
+    assert L.ternary_quantize(A[0], F32, 4, 65544, A[1], A[2], s) == E_UNSUP
+    assert L.ternary_quantize(A[0] + 8, F32, 4, 64, A[1], A[2], s) == E_UNSUP
+    assert L.ternary_quantize(A[0], F32, 4, 64, A[1] + 8, A[2], s) == E_UNSUP
+    assert L.ternary_quantize(A[0], F32, 4, 64, A[1], A[2] + 2, s) == E_UNSUP
+    assert L.ternary_quantize(A[0], F32, 4, 64, A[0] + 512, A[2], s) == E_ALIAS   # inside w
+    assert L.ternary_quantize(A[0], F32, 4, 64, A[1], A[0] + 16, s) == E_ALIAS
+    assert L.ternary_quantize(A[0], F32, 4, 64, A[1], A[1] + 32, s) == E_ALIAS    # inside packed

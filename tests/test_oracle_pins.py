@@ -473,3 +473,14 @@ def test_quantize_scale_is_the_mean_magnitude():
 def test_quantize_rejects_ragged_rows():
     with pytest.raises(ValueError):
         oracle.quantize_absmean(np.ones((1, 12), np.float32))
+
+
+def test_quantize_neighbours_of_the_half_scale():
+    # seven 15s and v = 7 (1 ulp up/down): the fp32 sum 105 + v rounds to 112 either way, g = 14,
+    # and v / g rounds above 1/2 (code 1) for the next float above 7, to 1/2 exactly (code 0, ties
+    # to even) for 7, below 1/2 (code 0) for the float below 7
+    up, dn = np.nextafter(np.float32(7), np.float32(8)), np.nextafter(np.float32(7), np.float32(6))
+    w = np.array([[15] * 7 + [up], [15] * 7 + [7], [15] * 7 + [dn], [15] * 7 + [-up]], np.float32)
+    t, s = oracle.quantize_absmean(w)
+    assert s.tolist() == [14.0] * 4
+    assert t[:, 7].tolist() == [1, 0, 0, -1]
