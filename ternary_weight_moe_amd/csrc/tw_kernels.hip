@@ -172,6 +172,61 @@ __global__ __launch_bounds__(256) void k_quant_absmean(const void *__restrict__ 
     }
 }
 
+// Rows of at most 64 chunks: 16 lanes per row, four rows per wave.  Lane i of a row's 16 holds the
+// partials 4i .. 4i + 3 (chunk p is partial p; partials beyond the row are 0) and adds them as
+// (p0 + p1) + (p2 + p3); the DPP butterfly inside the 16 lanes finishes the same balanced tree
+// over partials 0 .. 63 that wave_sum forms, and the other three groups of 64 partials are 0.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_quant_absmean16(const void *__restrict__ w, int64_t rows,
+                                                        int cols, uint8_t *__restrict__ packed,
+                                                        float *__restrict__ scales)
+{
+    const int lane = threadIdx.x & 63, li = lane & 15;
+    const int nch = cols >> 3;
+    const size_t eb = BF16 ? 2 : 4;
+    for (int64_t r0 = (int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6)) * 4; r0 < rows;
+         r0 += int64_t(gridDim.x) * 16) {
+        const int64_t r = r0 + (lane >> 4);
+        const bool live = r < rows;
+        const void *row = static_cast<const uint8_t *>(w) + size_t(live ? r : 0) * cols * eb;
+        float v[4][8], p[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int c = 4 * li + q;
+            p[q] = 0.0f;
+            if (live && c < nch) {
+                quant_chunk<BF16>(row, c, v[q]);
+#pragma unroll
+                for (int j = 0; j < 8; j++) p[q] = p[q] + fabsf(v[q][j]);
+            }
+        }
+        float acc = (p[0] + p[1]) + (p[2] + p[3]);
+        acc = acc + dpp_f<kDppXor1>(acc);
+        acc = acc + dpp_f<kDppXor2>(acc);
+        acc = acc + dpp_f<kDppHalfMirror>(acc);
+        acc = acc + dpp_f<kDppMirror>(acc);
+        const float g = acc / float(cols);
+        if (live) {
+            uint16_t *prow = reinterpret_cast<uint16_t *>(packed + size_t(r) * (cols >> 2));
+            if ((nch & 3) == 0) {   // the lane's four chunks are 8 contiguous, aligned code bytes
+                if (4 * li < nch) {
+                    uint64_t c8 = 0;
+#pragma unroll
+                    for (int q = 0; q < 4; q++) c8 |= uint64_t(quant_codes8(v[q], g)) << (16 * q);
+                    reinterpret_cast<uint64_t *>(prow)[li] = c8;
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const int c = 4 * li + q;
+                    if (c < nch) prow[c] = uint16_t(quant_codes8(v[q], g));
+                }
+            }
+            if (li == 0) scales[r] = g;
+        }
+    }
+}
+
 // ------------------------------------------------------------------------------------------------
 // Router logits for T tokens (k_route below).  Every logit is summed in the canonical order of
 // canon_dot: 256 partials, partial t adding the products of chunks t, t + 256 (8 elements each) in
@@ -1302,6 +1357,15 @@ int launch_pack(const int8_t *w, int64_t rows, int64_t cols, uint8_t *packed, in
 int launch_quantize(const void *w, int w_bf16, int64_t rows, int64_t cols, uint8_t *packed,
                     float *scales, void *stream)
 {
+    if (cols <= 512) {   // at most 64 chunks: four rows per wave
+        const int64_t nb64 = (rows + 15) / 16;
+        const unsigned nb = unsigned(nb64 < 65536 ? nb64 : 65536);
+        if (w_bf16)
+            k_quant_absmean16<true><<<nb, 256, 0, S(stream)>>>(w, rows, int(cols), packed, scales);
+        else
+            k_quant_absmean16<false><<<nb, 256, 0, S(stream)>>>(w, rows, int(cols), packed, scales);
+        return last_error();
+    }
     const int64_t nb64 = (rows + 3) / 4;
     const unsigned nb = unsigned(nb64 < 65536 ? nb64 : 65536);
     if (w_bf16)

@@ -63,9 +63,11 @@ def test_quantize_whole_matrices(E):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("cols", [8, 520, 2048, 4096, 6152])
+@pytest.mark.parametrize("cols", [8, 40, 264, 512, 520, 2048, 4096, 6152])
 def test_quantize_ragged_long_and_special_rows(dtype, cols):
-    # 520 = 65 chunks (a ragged last lane group), 4096 and 6152 (> 256 chunks: the two-pass form)
+    # up to 512 (64 chunks): four rows per wave, 40 and 264 with partly filled lanes; 520 = 65
+    # chunks (a ragged last lane group), 4096 and 6152 (> 256 chunks: the two-pass form); 37 rows
+    # leave the last wave's row groups partly empty
     step("quantize: %s cols %d" % (dtype, cols))
     g = torch.Generator().manual_seed(cols)
     w = (torch.randn((37, cols), generator=g) * 0.05)
