@@ -167,6 +167,19 @@ tw_status ternary_moe_ffn_decode(const tw_moe_layer *layers, int32_t n_layers, c
 size_t ternary_moe_decode_workspace_bytes(const tw_moe_layer *layers, int32_t n_layers);
 
 /*
+ * ternary_moe_decode_error_offset -- byte offset, inside a decode workspace for these layers, of a
+ * uint32 health word.  Every ternary_moe_ffn_decode call clears it first (in stream order).  The
+ * one-launch stacked decode keeps all its workgroups resident and hands vectors between them
+ * through polled words; each wait is bounded (about 2^21 polls), and a wait that runs out, which
+ * happens only when the GPU cannot hold every workgroup of the launch at once (for instance while
+ * other work occupies its compute units), ends the launch early, sets the word nonzero and leaves
+ * x_out undefined.  The caller may read it after the call has completed.  Returns 0 for layers that
+ * ternary_moe_decode_workspace_bytes rejects (the word never sits at offset 0).
+ * Source: not a step of the method; a property of the persistent kernel that serves it.
+ */
+size_t ternary_moe_decode_error_offset(const tw_moe_layer *layers, int32_t n_layers);
+
+/*
  * ternary_moe_ffn_batched -- one layer for n_tokens independent tokens, each expert's weights read
  * once per call: (token, slot) pairs are grouped by expert and each expert's rows are applied to
  * all of its tokens.

@@ -41,7 +41,8 @@ class TwLayer(C.Structure):
 
 
 EXPORTS = ("tw_status_str", "ternary_pack", "ternary_quantize", "moe_route_topk", "ternary_moe_ffn_decode",
-           "ternary_moe_decode_workspace_bytes", "ternary_moe_ffn_batched",
+           "ternary_moe_decode_workspace_bytes", "ternary_moe_decode_error_offset",
+           "ternary_moe_ffn_batched",
            "ternary_moe_batched_workspace_bytes")
 
 
@@ -64,6 +65,7 @@ def lib():
                                          vp]),
                 "ternary_moe_ffn_decode": (i32, [LP, i32, vp, vp, i32, vp, sz, vp]),
                 "ternary_moe_decode_workspace_bytes": (sz, [LP, i32]),
+                "ternary_moe_decode_error_offset": (sz, [LP, i32]),
                 "ternary_moe_ffn_batched": (i32, [LP, i64, vp, i32, vp, i32, i32, vp, vp, vp, sz,
                                                   vp]),
                 "ternary_moe_batched_workspace_bytes": (sz, [LP, i64, i32]),
@@ -195,6 +197,18 @@ class MoELayer:
 def decode_workspace_bytes(layers) -> int:
     arr = (TwLayer * len(layers))(*[l.c for l in layers])
     return int(lib().ternary_moe_decode_workspace_bytes(arr, len(layers)))
+
+
+def decode_error_flag(layers, workspace: torch.Tensor) -> int:
+    """The decode health word of `workspace` after a completed ternary_moe_ffn_decode call on it
+    (synchronises the device): nonzero if a hand-off wait of the stacked decode ran out."""
+    layers = list(layers)
+    arr = (TwLayer * len(layers))(*[l.c for l in layers])
+    off = int(lib().ternary_moe_decode_error_offset(arr, len(layers)))
+    if off == 0:
+        raise ValueError("layers rejected by the library")
+    torch.cuda.synchronize(workspace.device)
+    return int(workspace[off:off + 4].view(torch.int32).item())
 
 
 def batched_workspace_bytes(layer: MoELayer, n_tokens: int, act: str = "float") -> int:

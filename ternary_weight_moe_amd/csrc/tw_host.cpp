@@ -162,6 +162,12 @@ size_t ternary_moe_decode_workspace_bytes(const tw_moe_layer *layers, int32_t n_
     return tw::decode_ws_layout(dims_of(&layers[0])).total;
 }
 
+size_t ternary_moe_decode_error_offset(const tw_moe_layer *layers, int32_t n_layers)
+{
+    if (!layers || n_layers < 1 || check_layer(&layers[0]) != TW_OK) return 0;
+    return tw::decode_ws_layout(dims_of(&layers[0])).err;
+}
+
 tw_status ternary_moe_ffn_decode(const tw_moe_layer *layers, int32_t n_layers, const void *x_in,
                                  void *x_out, int32_t io_dtype, void *workspace, size_t ws_bytes,
                                  void *stream)

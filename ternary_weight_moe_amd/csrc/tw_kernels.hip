@@ -1278,6 +1278,7 @@ int decode_p(const Dims &dm, const LayerPtrs *layers, int n, const void *x_in, v
     const size_t eb = io_bf16 ? 2 : 4;
     void *buf[2] = {w + a.L.xbuf, w + a.L.xbuf + size_t(dm.d) * eb};
     k_zero_u32<<<1, 64, 0, S(stream)>>>(reinterpret_cast<uint32_t *>(w + a.L.ctrl), 64);
+    k_zero_u32<<<1, 64, 0, S(stream)>>>(reinterpret_cast<uint32_t *>(w + a.L.err), 4);   // health word
     const size_t smem_down = size_t(dm.k) * P * dm.F + sizeof(int) * kMaxTopK +
                              sizeof(float) * dm.k * kDecRowsDown;
     for (int l = 0; l < n; l++) {

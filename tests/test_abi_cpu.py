@@ -164,3 +164,12 @@ def test_quantize_errors(L):
     assert L.ternary_quantize(A[0], F32, 4, 64, A[0] + 512, A[2], s) == E_ALIAS   # inside w
     assert L.ternary_quantize(A[0], F32, 4, 64, A[1], A[0] + 16, s) == E_ALIAS
     assert L.ternary_quantize(A[0], F32, 4, 64, A[1], A[1] + 32, s) == E_ALIAS    # inside packed
+
+
+def test_decode_error_offset_inside_the_workspace(L):
+    lay = layer()
+    n = L.ternary_moe_decode_workspace_bytes(C.byref(lay), 1)
+    off = L.ternary_moe_decode_error_offset(C.byref(lay), 1)
+    assert 0 < off and off + 4 <= n and off % 4 == 0
+    assert L.ternary_moe_decode_error_offset(None, 1) == 0
+    assert L.ternary_moe_decode_error_offset(C.byref(layer(k=0)), 1) == 0

@@ -125,11 +125,13 @@ def oracle_decode_expect(L, x_row, tau=TAU):
 
 def test_decode_small_layer_fp32(small):
     x = synth.activations(synth.SMALL_LAYER_B1, 16, seed=5)
-    ws = torch.empty(tw.decode_workspace_bytes([small.gpu]), dtype=torch.uint8, device="cuda")
+    ws = torch.full((tw.decode_workspace_bytes([small.gpu]),), 0xA5, dtype=torch.uint8, device="cuda")
     for t in range(16):
         step("decode small_layer_b1 token %d" % t)
         out = tw.ternary_moe_ffn_decode([small.gpu], x[t].cuda(), workspace=ws)
         torch.cuda.synchronize()
+        if t == 0:   # the per-layer kernels clear the health word too
+            assert tw.decode_error_flag([small.gpu], ws) == 0
         got = to_np(out)
         xr = x[t].double().numpy()
         cands = oracle_decode_expect(small.ora, xr)
@@ -237,7 +239,9 @@ def test_decode_full_stack24(stack3):
         del w
     x0 = synth.activations(wl, 1, seed=25)[0].cuda()
     step("decode 24 layers, one call")
-    fused = tw.ternary_moe_ffn_decode(layers, x0)
+    ws = torch.full((tw.decode_workspace_bytes(layers),), 0xA5, dtype=torch.uint8, device="cuda")
+    fused = tw.ternary_moe_ffn_decode(layers, x0, workspace=ws)
+    assert tw.decode_error_flag(layers, ws) == 0   # the call cleared the word; no wait ran out
     step("decode 24 layers, chained single-layer calls")
     inputs, cur = [], x0
     for layer in layers:
