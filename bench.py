@@ -158,7 +158,8 @@ def run_stack(args):
                     n_experts=wl.n_experts, d_ff=wl.d_ff, top_k=wl.top_k, batch=1,
                     graph_steps=G, bytes_per_token=bytes_per_step,
                     us_per_token_median=per_tok_us[len(per_tok_us) // 2],
-                    us_per_token_min=per_tok_us[0]),
+                    us_per_token_min=per_tok_us[0],
+                    us_per_token_p90=per_tok_us[int(0.9 * (len(per_tok_us) - 1))]),
         roofline=dict(bound="hbm", achieved=achieved, peak=accounting.HBM_PEAK_BPS / 1e9,
                       unit="GB/s", frac=achieved * 1e9 / accounting.HBM_PEAK_BPS,
                       traffic=traffic,
@@ -326,6 +327,7 @@ def main():
     else:
         res = run_single_layer(args, args.workload)
     res["device"] = torch.cuda.get_device_properties(0).gcnArchName
+    res["rocm"] = torch.version.hip
     print(json.dumps(res))
 
 

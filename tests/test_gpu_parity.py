@@ -350,6 +350,24 @@ def test_batched_float_matches_oracle_and_decode(full):
         assert torch.equal(d1.view(torch.int16), out[t].view(torch.int16)), t
 
 
+def test_small_layer_10k_tokens(small):
+    # the oracle-sized configuration (d 256, 16 experts, F 128, top-2, fp32 in and out) over 10,000
+    # seeded tokens in one batched call, every output element against the oracle (1e-4 normwise per
+    # token; near-tie routings compared with the oracle's output for the GPU's choice)
+    T = 10000
+    x = synth.activations(synth.SMALL_LAYER_B1, T, seed=77)
+    step("small layer, %d tokens in one batched call" % T)
+    out = tw.ternary_moe_ffn_batched(small.gpu, x.cuda())
+    torch.cuda.synchronize()
+    got = to_np(out)
+    oout, oids, og, olg = oracle.moe_layer(small.ora, x, n_threads=8)
+    err = np.max(np.abs(got - oout), axis=1) / np.max(np.abs(oout), axis=1)
+    for t in np.nonzero(err > 1e-4)[0]:
+        cands = [oracle.ffn_token(small.ora, x[t].double().numpy(), sel, g)
+                 for sel, g in routing_alternatives(olg[t], oids[t], small.ora.k)[1:]]
+        assert cands and min(normwise(got[t], c) for c in cands) <= 1e-4, (int(t), float(err[t]))
+
+
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_batched_int8_bit_exact(full, out_dtype):
     T = 64
