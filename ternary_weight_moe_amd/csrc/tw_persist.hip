@@ -101,6 +101,7 @@ struct PC {
     static_assert(K <= kMaxTopK && K <= 16, "top-k");
     static_assert(HW % kPT == 0 && HW <= 4 * kPT && F % 256 == 0, "k*F in {1024, 2048, 3072, 4096}");
     static_assert(DL <= 64 && K <= kPT / 64, "wave j takes expert j's down rows");
+    static_assert(2 * Q <= 64, "one wave loads the scales of the workgroup's gate/up rows");
     static_assert(XW % 64 == 0 && D % kPT == 0, "d a multiple of 1024");
 };
 
@@ -162,6 +163,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
     __shared__ __attribute__((aligned(16))) int8_t xd[2 * D];    // its digit planes
     __shared__ __attribute__((aligned(16))) int8_t hd[K * 2 * F];// digit planes of h, per expert
     __shared__ float sums[2 * C::Q];
+    __shared__ float s_scl[2 * C::Q];   // scales of the workgroup's gate/up rows
     __shared__ float ys[K * C::RD];
     __shared__ float red[4][2 + kEM];
     __shared__ __attribute__((aligned(16))) float hs[C::HW];     // h, in digit-plane byte order
@@ -296,9 +298,11 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
 
         // 4. request the gate/up rows of this workgroup's share at once (the down rows and the next
         //    router rows follow once these have arrived, so that these, on the critical path, do
-        //    not share the memory system with them); the gates are formed meanwhile
+        //    not share the memory system with them); the gates are formed meanwhile.  The rows'
+        //    scales (two 64-byte runs) come in one instruction of wave 0, not one per wave and row:
+        //    a compute unit keeps only so many lines in flight, and the code rows need them (with
+        //    a load per wave and row the token took 199.5 us, with one 193.9 us)
         int4 cg[C::PGU];
-        float sg[C::PGU];
 #pragma unroll
         for (int p = 0; p < C::PGU; p++) {
             const int jb = p * C::RPP + t / C::LPR;
@@ -308,7 +312,13 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
             const int e = min(max(s_ids[j], 0), E - 1);
             const uint8_t *row = (kind ? P.w_up : P.w_gate) + (size_t(e) * F + r) * (D / 4);
             cg[p] = valid ? reinterpret_cast<const int4 *>(row)[c_gu] : make_int4(0, 0, 0, 0);
-            sg[p] = (valid && c_gu == 0) ? (kind ? P.s_up : P.s_gate)[size_t(e) * F + r] : 0.0f;
+        }
+        float scl = 0.0f;   // wave 0, lane jb < 2Q: the scale of gate/up row jb (jb odd: up)
+        if (wave == 0 && lane < 2 * C::Q) {
+            const int i = lane >> 1, kind = lane & 1;
+            const int q = b * C::Q + i, j = q / F, r = q % F;
+            const int e = min(max(s_ids[j], 0), E - 1);
+            scl = (kind ? P.s_up : P.s_gate)[size_t(e) * F + r];
         }
         if (wave == 0) softmax_gates_wave(s_gates, K, lane);
 
@@ -328,8 +338,9 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
                 int32_t acc[2] = {0, 0};
                 chunk_dot<2>(cg[p], dg, acc);
                 group_reduce<2>(acc, C::LPR);
-                if (c_gu == 0 && jb < 2 * C::Q) sums[jb] = float_value<2>(acc, s_xsh) * sg[p] * s_inv;
+                if (c_gu == 0 && jb < 2 * C::Q) sums[jb] = float_value<2>(acc, s_xsh);
             }
+            if (wave == 0 && lane < 2 * C::Q) s_scl[lane] = scl;
             // the down rows of this workgroup's outputs (wave j: expert j) and the next layer's
             // router rows
             {
@@ -346,7 +357,10 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
         __syncthreads();
         if (t < C::Q * kLlCopies) {   // thread t: value t % Q into copy t / Q
             const int i = t % C::Q;
-            const float h = tw_silu(sums[2 * i]) * sums[2 * i + 1];
+            // (sum * scale) * inverse RMS, as the other kernels form a gate or up value
+            const float gv = sums[2 * i] * s_scl[2 * i] * s_inv;
+            const float uv = sums[2 * i + 1] * s_scl[2 * i + 1] * s_inv;
+            const float h = tw_silu(gv) * uv;
             st_tagged(set0 + (t / C::Q) * lls + E * kLgStride + b * C::Q + i, tag, __float_as_uint(h));
         }
 
