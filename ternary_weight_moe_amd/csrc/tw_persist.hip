@@ -24,9 +24,10 @@
 //   4. loads   the workgroup's share of gate/up rows (2 x k*F/256 rows of d/4 bytes, ~4 MB
 //              across the chip for the 2048/512/top-8 layer) is requested at once, with its scales;
 //              the gates are formed while it is in flight.  Once it has arrived, the share of down
-//              rows (k experts x d/256 output rows of F/4 bytes) and the next layer's router row
-//              are requested: they are needed only after the h hand-off, and keeping them out of
-//              the first burst lets the gate/up bytes, which are on the critical path, arrive sooner.
+//              rows (k experts x d/256 output rows of F/4 bytes) is requested: it is needed only
+//              after the h hand-off, and keeping it out of the first burst lets the gate/up bytes,
+//              which are on the critical path, arrive sooner.  The next layer's router row is
+//              requested after the combine, once the down rows are in.
 //   5. gate/up the ternary dots (tw_device.h) against the digit planes of x, h = SiLU(gate)*up
 //              in fp32, published one value per word.
 //   6. down    wave j gathers the F values of expert j's h, takes their max, writes the digit
@@ -341,8 +342,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
                 if (c_gu == 0 && jb < 2 * C::Q) sums[jb] = float_value<2>(acc, s_xsh);
             }
             if (wave == 0 && lane < 2 * C::Q) s_scl[lane] = scl;
-            // the down rows of this workgroup's outputs (wave j: expert j) and the next layer's
-            // router rows
+            // the down rows of this workgroup's outputs (wave j: expert j)
             {
                 const bool valid = wave < K && lane < C::DL;
                 const int j = valid ? wave : 0, rl = lane / C::LPRD;
@@ -352,7 +352,6 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
                 cd = valid ? reinterpret_cast<const int4 *>(row)[c_d] : make_int4(0, 0, 0, 0);
                 sd = (valid && c_d == 0) ? P.s_down[size_t(e) * D + R] : 0.0f;
             }
-            if (l + 1 < a.n_layers) load_router<C::NRC>(rw, a.L[l + 1].w_router, b, E, D);
         }
         __syncthreads();
         if (t < C::Q * kLlCopies) {   // thread t: value t % Q into copy t / Q
@@ -427,6 +426,9 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
                 st_tagged(set0 + c * lls + E * kLgStride + C::HW + (b * C::RD) / 2 + i, tag, pack_bf16x2(o0, o1));
             }
         }
+        // the next layer's router rows, requested once this layer's rows are in: in flight while
+        // the residual is gathered (requested with the down rows, a token took 193.6 us; here 192.1)
+        if (l + 1 < a.n_layers) load_router<C::NRC>(rw, a.L[l + 1].w_router, b, E, D);
         __syncthreads();
     }
 }
