@@ -376,6 +376,10 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
             uint64_t v[M];
 #pragma unroll
             for (int m = 0; m < M; m++) v[m] = 0;
+            // the wave's down rows are in before it starts to poll: its polls (32 lines a round)
+            // would otherwise share the compute unit's lines in flight with them (a token took
+            // 192.0 us polling at once after the wait below, 189.2 us waiting for the rows first)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_sleep(kSleepH);
             wait_words<M>(hw + j * F, lane, 64, F, tag, v, &s_abort, a.err);
             float am = 0.0f;
