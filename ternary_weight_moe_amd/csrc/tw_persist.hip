@@ -13,8 +13,8 @@
 //
 // Per layer, workgroup b (of 256) does:
 //   1. input   x: layer 0 reads x_in; later layers gather the d/2 words of packed bf16 pairs that
-//              the previous layer published (every workgroup needs all of x): each router thread
-//              polls the four words of its own 8-element chunk and works on them at once.
+//              the previous layer published (every workgroup needs all of x): each router wave
+//              polls the 256 words of its lanes' 8-element chunks and passes them on through LDS.
 //   2. router  the workgroup computes the logits of experts b + 256 m (router rows prefetched
 //              during the previous layer, one 16-byte chunk per thread) and publishes them; the
 //              pre-RMSNorm is a scalar on the logits and on the gate/up sums.
@@ -103,6 +103,7 @@ struct PC {
     static_assert(HW % kPT == 0 && HW <= 4 * kPT && F % 256 == 0, "k*F in {1024, 2048, 3072, 4096}");
     static_assert(DL <= 64 && K <= kPT / 64, "wave j takes expert j's down rows");
     static_assert(2 * Q <= 64, "one wave loads the scales of the workgroup's gate/up rows");
+    static_assert(NRC == 1 && D / 8 % 64 == 0, "router wave w holds chunks 64w .. 64w + 63, words 256w ..");
     static_assert(XW % 64 == 0 && D % kPT == 0, "d a multiple of 1024");
 };
 
@@ -200,9 +201,9 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
         }
 
         // 2. router threads: their 8-element chunks of x (amax, sum of squares, router partials in
-        //    the canonical order; from layer 1 on straight from the polled words, which are also
-        //    stored to LDS for the digit planes and the combine), wave reductions, then block
-        //    totals, logits and digit planes
+        //    the canonical order; from layer 1 on from the polled words, which their wave stores
+        //    to LDS, where the digit planes and the combine also read them), wave reductions, then
+        //    block totals, logits and digit planes
         if (t < kCT) {
             float am = 0.0f, ss = 0.0f, rp[kEM];
 #pragma unroll
@@ -216,16 +217,26 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
 #pragma unroll
                         for (int j = 0; j < 8; j++) xv[j] = xs[8 * c + j];
                     } else {
+                        // router wave w polls the words 256 w + lane + 64 q (q < 4), 4 lines an
+                        // instruction, the words its lanes' chunks are made of; they reach the
+                        // lanes through LDS, inside the wave (its LDS accesses take effect in
+                        // order).  Polling each lane's own 4 words (16 lines an instruction)
+                        // took 190.0 us per token, this 187.6
                         uint64_t v[4] = {0, 0, 0, 0};
                         if (n == 0) __builtin_amdgcn_s_sleep(kSleepX);
-                        wait_words<4>(xprev, 4 * c, 1, C::XW, tag - 1, v, &s_abort, a.err);
+                        const int w0 = 256 * (t >> 6) + (t & 63);
+                        wait_words<4>(xprev, w0, 64, C::XW, tag - 1, v, &s_abort, a.err);
 #pragma unroll
                         for (int q = 0; q < 4; q++) {
-                            xv[2 * q] = bf16_lo(uint32_t(v[q]));
-                            xv[2 * q + 1] = bf16_hi(uint32_t(v[q]));
+                            const int k = w0 + 64 * q;
+                            if (k < C::XW)
+                                *reinterpret_cast<float2 *>(xs + 2 * k) =
+                                    make_float2(bf16_lo(uint32_t(v[q])), bf16_hi(uint32_t(v[q])));
                         }
-                        *reinterpret_cast<float4 *>(xs + 8 * c) = make_float4(xv[0], xv[1], xv[2], xv[3]);
-                        *reinterpret_cast<float4 *>(xs + 8 * c + 4) = make_float4(xv[4], xv[5], xv[6], xv[7]);
+                        const float4 a0 = *reinterpret_cast<const float4 *>(xs + 8 * c);
+                        const float4 a1 = *reinterpret_cast<const float4 *>(xs + 8 * c + 4);
+                        xv[0] = a0.x; xv[1] = a0.y; xv[2] = a0.z; xv[3] = a0.w;
+                        xv[4] = a1.x; xv[5] = a1.y; xv[6] = a1.z; xv[7] = a1.w;
                     }
 #pragma unroll
                     for (int j = 0; j < 8; j++) {
