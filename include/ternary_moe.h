@@ -172,8 +172,9 @@ size_t ternary_moe_decode_workspace_bytes(const tw_moe_layer *layers, int32_t n_
  * one-launch stacked decode keeps all its workgroups resident and hands vectors between them
  * through polled words; each wait is bounded (about 2^21 polls), and a wait that runs out, which
  * happens only when the GPU cannot hold every workgroup of the launch at once (for instance while
- * other work occupies its compute units), ends the launch early, sets the word nonzero and leaves
- * x_out undefined.  The caller may read it after the call has completed.  Returns 0 for layers that
+ * other work occupies its compute units, or while another such decode runs on a second stream:
+ * keep these calls on one stream per device), ends the launch early, sets the word nonzero and
+ * leaves x_out undefined.  The caller may read it after the call has completed.  Returns 0 for layers that
  * ternary_moe_decode_workspace_bytes rejects (the word never sits at offset 0).
  * Source: not a step of the method; a property of the persistent kernel that serves it.
  */

@@ -308,9 +308,10 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
         }
         __syncthreads();
 
-        // 4. request the gate/up rows of this workgroup's share at once (the down rows and the next
-        //    router rows follow once these have arrived, so that these, on the critical path, do
-        //    not share the memory system with them); the gates are formed meanwhile.  The rows'
+        // 4. request the gate/up rows of this workgroup's share at once (the down rows follow once
+        //    these have arrived and the next router rows after the combine, so that these, on the
+        //    critical path, do not share the memory system with them); the gates are formed
+        //    meanwhile.  The rows'
         //    scales (two 64-byte runs) come in one instruction of wave 0, not one per wave and row:
         //    a compute unit keeps only so many lines in flight, and the code rows need them (with
         //    a load per wave and row the token took 199.5 us, with one 193.9 us)
