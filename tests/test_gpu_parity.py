@@ -454,3 +454,42 @@ def test_batched_shape_served_by_dot4_kernels():
     torch.cuda.synchronize()
     ref = oracle.ffn_batch_i8(pair.ora, x, oids, og.astype(np.float32), n_threads=8)
     assert np.array_equal(out8.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("d,F,E,k,dt", [(4096, 4096, 8, 2, "bf16"), (4096, 4096, 8, 2, "f32"),
+                                        (64, 64, 4, 4, "bf16"), (64, 64, 4, 4, "f32")])
+def test_extreme_shapes(d, F, E, k, dt):
+    # the largest (d = F = 4096) and smallest (d = F = 64, k = E) shapes the library accepts, in
+    # bf16 and fp32: batch-1 decode and batched float against the oracle, batched int8 bit-exact
+    wl = synth.Workload("extreme_%d_%d_%s" % (d, F, dt), d, E, F, k, dt, dt, dt, seed=1100 + d)
+    step("extreme shape d=%d F=%d E=%d k=%d %s: build" % (d, F, E, k, dt))
+    pair = make_pair(wl)
+    x = synth.activations(wl, 5, seed=91)
+    fp32 = dt == "f32"
+
+    def check(got, ref, what):
+        if fp32:
+            assert normwise(got, ref) <= 1e-4, what
+        else:
+            assert_bf16_close(got, ref, what)
+
+    for t in range(2):
+        step("extreme shape decode token %d" % t)
+        got = to_np(tw.ternary_moe_ffn_decode([pair.gpu], x[t].cuda()))
+        cands = oracle_decode_expect(pair.ora, x[t].double().numpy())
+        check(got, cands[int(np.argmin([normwise(got, c) for c in cands]))], "decode %d" % t)
+    step("extreme shape batched float")
+    out = to_np(tw.ternary_moe_ffn_batched(pair.gpu, x.cuda()))
+    oout, oids, og, olg = oracle.moe_layer(pair.ora, x)
+    for t in range(x.shape[0]):
+        cands = [oout[t]] + [oracle.ffn_token(pair.ora, x[t].double().numpy(), sl, g)
+                             for sl, g in routing_alternatives(olg[t], oids[t], k)[1:]]
+        check(out[t], cands[int(np.argmin([normwise(out[t], c) for c in cands]))], "batched %d" % t)
+    step("extreme shape batched int8")
+    ids = torch.from_numpy(oids).cuda()
+    gates = torch.from_numpy(og.astype(np.float32)).cuda()
+    out8 = tw.ternary_moe_ffn_batched(pair.gpu, x.cuda(), act="int8", out_dtype=torch.float32,
+                                      expert_ids=ids, gate_w=gates)
+    torch.cuda.synchronize()
+    ref = oracle.ffn_batch_i8(pair.ora, x, oids, og.astype(np.float32), n_threads=8)
+    assert np.array_equal(out8.cpu().numpy().view(np.uint32), ref.view(np.uint32))
