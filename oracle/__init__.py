@@ -83,6 +83,9 @@ def lib():
                                            ip, fp]),
                 "or_ffn_batch_i8": (None, [_P(_LayerI8), fp, i64, ip, fp, fp, i32]),
                 "or_quantize_absmean": (C.c_int, [fp, i64, i64, i8p, fp]),
+                "or_pack3": (i64, [i8p, i64, i64, i64, u8p]),
+                "or_unpack3": (i64, [u8p, i64, i64, i64, i8p]),
+                "or_gemv_i8": (None, [i8p, fp, i64, i64, i8p, C.c_float, fp]),
             }
             for name, (res, args) in sig.items():
                 f = getattr(L, name)
@@ -164,6 +167,43 @@ def ternary_gemv(packed, cols: int, scale, x) -> np.ndarray:
     lib().or_ternary_gemv(_ptr(p, C.c_uint8), rows, cols, _ptr(sc, C.c_double),
                           _ptr(xv, C.c_double), _ptr(y, C.c_double))
     _check_codes()
+    return y
+
+
+def pack3(w, row_bytes: int | None = None) -> tuple[np.ndarray, int]:
+    """int8 [..., cols] -> base-3 packed uint8 [..., row_bytes] (five weights per byte, tw_oracle.h;
+    row_bytes defaults to ceil(cols/5)), number of values outside {-1,0,1}."""
+    w = _np(w, np.int8)
+    cols = w.shape[-1]
+    rb = (cols + 4) // 5 if row_bytes is None else int(row_bytes)
+    assert rb >= (cols + 4) // 5
+    rows = int(np.prod(w.shape[:-1])) if w.ndim > 1 else 1
+    out = np.empty(w.shape[:-1] + (rb,), dtype=np.uint8)
+    bad = lib().or_pack3(_ptr(w, C.c_int8), rows, cols, rb, _ptr(out, C.c_uint8))
+    return out, int(bad)
+
+
+def unpack3(packed, cols: int) -> tuple[np.ndarray, int]:
+    """base-3 packed uint8 [..., row_bytes] -> int8 [..., cols], number of bytes above 242 met."""
+    p = _np(packed, np.uint8)
+    rb = p.shape[-1]
+    assert rb >= (cols + 4) // 5
+    rows = int(np.prod(p.shape[:-1])) if p.ndim > 1 else 1
+    out = np.empty(p.shape[:-1] + (cols,), dtype=np.int8)
+    bad = lib().or_unpack3(_ptr(p, C.c_uint8), rows, cols, rb, _ptr(out, C.c_int8))
+    return out, int(bad)
+
+
+def gemv_i8(w, scale, q, sx) -> np.ndarray:
+    """int8 spec of y = s * (W q) on unpacked weights W [rows][cols] in {-1,0,1}: exact integer sum,
+    then (float(sum) * sx) * s_r in fp32 (tw_oracle.h)."""
+    wv = _np(w, np.int8)
+    rows, cols = wv.shape
+    sc = _np(scale, np.float32).reshape(rows)
+    qv = _np(q, np.int8).reshape(cols)
+    y = np.empty(rows, np.float32)
+    lib().or_gemv_i8(_ptr(wv, C.c_int8), _ptr(sc, C.c_float), rows, cols, _ptr(qv, C.c_int8),
+                     float(np.float32(sx)), _ptr(y, C.c_float))
     return y
 
 

@@ -97,6 +97,67 @@ void or_ternary_gemv(const uint8_t *packed, int64_t rows, int64_t cols, const do
     }
 }
 
+/* ---- base-3 packing: five weights per byte ---------------------------------------------------
+ * [Hub] "Ternary Quantization Is More Than Simply Compressing Weights into Three Values": three
+ * states need at least log2 3 bits, and a packing may use another aligned form than 2 bits.
+ * Reading (tw_oracle.h): byte j = sum_i (w_{5j+i} + 1) 3^i, padding positions count as weight 0,
+ * bytes past ceil(cols/5) of a row are 0. */
+
+static int digit_of_value(int8_t w, int64_t *bad)
+{
+    if (w == -1 || w == 0 || w == 1) return w + 1;
+    (*bad)++;
+    return 1;
+}
+
+int64_t or_pack3(const int8_t *w, int64_t rows, int64_t cols, int64_t row_bytes, uint8_t *packed)
+{
+    int64_t nb = (cols + 4) / 5, bad = 0;
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t b = 0; b < row_bytes; b++) {
+            unsigned v = 0, p3 = 1;
+            if (b < nb) {
+                for (int i = 0; i < 5; i++) {
+                    int64_t c = 5 * b + i;
+                    int dg = c < cols ? digit_of_value(w[r * cols + c], &bad) : 1;
+                    v += (unsigned)dg * p3;
+                    p3 *= 3;
+                }
+            }
+            packed[r * row_bytes + b] = (uint8_t)v;
+        }
+    }
+    return bad;
+}
+
+int64_t or_unpack3(const uint8_t *packed, int64_t rows, int64_t cols, int64_t row_bytes, int8_t *w)
+{
+    int64_t bad = 0;
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t c = 0; c < cols; c++) {
+            unsigned v = packed[r * row_bytes + c / 5];
+            if (v > 242) {
+                if (c % 5 == 0) bad++;
+                w[r * cols + c] = 0;
+                continue;
+            }
+            for (int64_t i = 0; i < c % 5; i++) v /= 3;
+            w[r * cols + c] = (int8_t)((int)(v % 3) - 1);
+        }
+    }
+    return bad;
+}
+
+void or_gemv_i8(const int8_t *w, const float *scale, int64_t rows, int64_t cols, const int8_t *q,
+                float sx, float *y)
+{
+    for (int64_t r = 0; r < rows; r++) {
+        int64_t acc = 0;
+        for (int64_t i = 0; i < cols; i++) acc += (int64_t)w[r * cols + i] * q[i];
+        y[r] = ((float)acc * sx) * scale[r];
+    }
+}
+
 /* ---- rounding ---------------------------------------------------------------------------- */
 
 uint16_t or_f64_to_bf16(double v)

@@ -58,6 +58,25 @@ int64_t or_unpack(const uint8_t *packed, int64_t rows, int64_t cols, int8_t *w);
 void or_ternary_gemv(const uint8_t *packed, int64_t rows, int64_t cols, const double *scale,
                      const double *x, double *y);
 
+/* ---- base-3 packing: five weights per byte ---------------------------------------------------
+ * A ternary weight carries log2 3 = 1.585 bits; packings that hardware reads natively spend 2 bits
+ * or another aligned form ([Hub] "Ternary Quantization Is More Than Simply Compressing Weights into
+ * Three Values"; [MacMini] "What Ternary Actually Means": 1.58 bits per weight).  Five trits fit in
+ * a byte because 3^5 = 243 <= 256 (1.6 bits per weight).
+ * Reading: byte j of a row holds weights 5j .. 5j+4 as sum_i (w_{5j+i} + 1) 3^i (weight 5j is the
+ * least significant trit); positions at or past cols count as weight 0; a row occupies row_bytes
+ * bytes (row_bytes >= ceil(cols/5)) and its bytes past ceil(cols/5) are 0.
+ * or_pack3 returns the number of inputs outside {-1,0,+1} (each packed as 0); or_unpack3 returns
+ * the number of content bytes above 242 (each unpacked as five zeros). */
+int64_t or_pack3(const int8_t *w, int64_t rows, int64_t cols, int64_t row_bytes, uint8_t *packed);
+int64_t or_unpack3(const uint8_t *packed, int64_t rows, int64_t cols, int64_t row_bytes, int8_t *w);
+
+/* int8 spec of one ternary matrix-vector product on unpacked weights w [rows][cols] in {-1,0,+1}:
+ * y_r = ((float) sum_i w[r][i] q_i * sx) * scale_r, the sum exact in integers, then two fp32
+ * roundings in that order (the order of the int8 FFN below). */
+void or_gemv_i8(const int8_t *w, const float *scale, int64_t rows, int64_t cols, const int8_t *q,
+                float sx, float *y);
+
 /* ---- rounding ----------------------------------------------------------------------------- */
 /* Round-to-nearest-even of a double straight to bfloat16 (one rounding), returned as raw bits. */
 uint16_t or_f64_to_bf16(double v);

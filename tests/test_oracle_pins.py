@@ -484,3 +484,99 @@ def test_quantize_neighbours_of_the_half_scale():
     t, s = oracle.quantize_absmean(w)
     assert s.tolist() == [14.0] * 4
     assert t[:, 7].tolist() == [1, 0, 0, -1]
+
+
+# ---- base-3 packing (five weights per byte) and the int8 GEMV spec ------------------------------
+
+def test_pack3_worked_bytes():
+    # byte = sum_i (w_i + 1) 3^i, weight 5j the least significant trit; padding counts as weight 0
+    p, bad = oracle.pack3(np.array([[1, 0, -1, 1, 1, 0, -1]], np.int8), 16)
+    assert bad == 0
+    assert p[0, 0] == 2 * 1 + 1 * 3 + 0 * 9 + 2 * 27 + 2 * 81        # 221
+    assert p[0, 1] == 1 * 1 + 0 * 3 + 1 * 9 + 1 * 27 + 1 * 81        # 118: w5 = 0, w6 = -1, 3 pads
+    assert not p[0, 2:].any()                                          # bytes past ceil(7/5)
+    assert oracle.pack3(np.ones((1, 5), np.int8))[0][0, 0] == 242
+    assert oracle.pack3(-np.ones((1, 5), np.int8))[0][0, 0] == 0
+    assert oracle.pack3(np.zeros((1, 5), np.int8))[0][0, 0] == 121
+
+
+def test_pack3_is_a_bijection_on_all_243_groups():
+    import itertools
+    groups = np.array(list(itertools.product([-1, 0, 1], repeat=5)), np.int8)   # 243 x 5
+    p, bad = oracle.pack3(groups)
+    assert bad == 0 and p.shape == (243, 1)
+    assert sorted(p[:, 0].tolist()) == list(range(243))
+    # digit-by-digit division by 3 (textbook base conversion) recovers each weight
+    for g, b in zip(groups, p[:, 0]):
+        v = int(b)
+        for i in range(5):
+            assert v % 3 - 1 == g[i]
+            v //= 3
+    w, bad = oracle.unpack3(p, 5)
+    assert bad == 0 and np.array_equal(w, groups)
+
+
+@pytest.mark.parametrize("cols", [1, 4, 5, 6, 2048, 2051])
+def test_pack3_round_trip_and_size(cols):
+    w = rand_trits(3, cols)
+    rb = ((cols + 4) // 5 + 15) // 16 * 16
+    p, bad = oracle.pack3(w, rb)
+    assert bad == 0 and p.shape == (3, rb)
+    assert not p[:, (cols + 4) // 5:].any()
+    back, bad = oracle.unpack3(p, cols)
+    assert bad == 0 and np.array_equal(back, w)
+
+
+def test_pack3_counts_and_zeroes_invalid_values_and_bytes():
+    w = np.array([[2, 1, -5, 0, 1]], np.int8)
+    p, bad = oracle.pack3(w)
+    assert bad == 2
+    assert np.array_equal(oracle.unpack3(p, 5)[0], np.array([[0, 1, 0, 0, 1]], np.int8))
+    back, bad = oracle.unpack3(np.array([[243, 242, 255]], np.uint8), 15)
+    assert bad == 2 and not back[0, :5].any() and (back[0, 5:10] == 1).all() and not back[0, 10:].any()
+
+
+def test_pack3_size_against_the_information_bound():
+    # five trits per byte: 1.6 bits per weight against log2 3 = 1.585 (within 1%); a 2048-weight
+    # row takes 410 bytes (416 at a 16-byte row stride) against 512 at four weights per byte
+    ex = json.load(open(os.path.join(GOLDEN, "ternary_size_example.json")))
+    assert 3 ** 5 <= 256 < 3 ** 6
+    assert 8 / 5 / ex["bits_per_state_ideal"] < 1.01
+    assert oracle.pack3(rand_trits(1, 2048))[0].shape[1] == 410
+    assert oracle.pack(rand_trits(1, 2048))[0].shape[1] == 512
+
+
+def test_gemv_i8_integer_sums_are_brute_force_dots():
+    # sx = scale = 1: y is the exact integer dot (|sum| < 2^24), checked against Python integers
+    w = rand_trits(7, 53)
+    q = rng.integers(-127, 128, 53).astype(np.int8)
+    y = oracle.gemv_i8(w, np.ones(7, np.float32), q, 1.0)
+    for r in range(7):
+        assert y[r] == sum(int(a) * int(b) for a, b in zip(w[r], q))
+
+
+def test_gemv_i8_one_hot_rows_sign_symmetry_and_power_of_two_scales():
+    cols = 40
+    q = rng.integers(-127, 128, cols).astype(np.int8)
+    w = np.zeros((cols, cols), np.int8)
+    w[np.arange(cols), np.arange(cols)] = 1                           # row r picks input r
+    s = np.full(cols, 0.25, np.float32)
+    y = oracle.gemv_i8(w, s, q, 2.0)
+    assert np.array_equal(y, q.astype(np.float32) * 0.5)             # exact: powers of two
+    w2 = rand_trits(9, cols)
+    s2 = rng.uniform(0.01, 1.0, 9).astype(np.float32)
+    assert np.array_equal(oracle.gemv_i8(-w2, s2, q, 0.37), -oracle.gemv_i8(w2, s2, q, 0.37))
+
+
+def test_gemv_i8_matches_the_int8_ffn_gate_accumulators():
+    # the gate rows of the int8 FFN spec: its tapped integer sums times sx times the row scales,
+    # in that order, are what gemv_i8 gives on the same rows
+    w, L = tiny_layer(d=64, F=32, E=4, k=2)
+    x = rng.normal(0, 1, 64).astype(np.float32)
+    ids = np.array([2, 0], np.int32)
+    out, taps = oracle.ffn_token_i8(L, x, ids, np.array([0.5, 0.5], np.float32))
+    for j, e in enumerate(ids):
+        y = oracle.gemv_i8(w["t_gate"][e], w["s_gate"][e], taps["qx"], taps["sx"][0])
+        ref = (taps["acc_gate"][j].astype(np.float32) * np.float32(taps["sx"][0])) * \
+            w["s_gate"][e].astype(np.float32)
+        assert np.array_equal(y, ref)
