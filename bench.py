@@ -276,6 +276,50 @@ def run_quantize(args):
     )
 
 
+def run_gemv(args, layout):
+    """ternary_gemv_i8 over the gate and up rows of one layer's 256 experts (262144 rows of 2048
+    weights), packed two bits per weight (layout 2) or five weights per byte (layout 3).  Four
+    weight copies are rotated, so that the codes come from HBM rather than the last-level cache."""
+    rows, cols = synth.GEMV_ROWS, synth.GEMV_COLS
+    n_copies = 4
+    mats = []
+    for c in range(n_copies):
+        w = synth.trits((rows, cols), "cuda", 1100 + c, 0, "gate")
+        codes = tw.ternary_pack3(w) if layout == 3 else tw.ternary_pack(w)
+        del w
+        sc = synth.uniform((rows,), 0.01, 0.1, "cuda", 1100 + c, 0, "s_gate").contiguous()
+        mats.append((codes, sc))
+    xq = synth.int8_codes(cols, "cuda", 1100)
+    xs = torch.tensor([0.01], dtype=torch.float32, device="cuda")
+    ys = [torch.empty(rows, dtype=torch.float32, device="cuda") for _ in range(n_copies)]
+    torch.cuda.synchronize()
+
+    def step(t):
+        c = t % n_copies
+        tw.ternary_gemv_i8(mats[c][0], layout, mats[c][1], cols, xq, xs, out=ys[c])
+
+    G = min(args.graph_steps, 64)
+    steps = max(G, (args.steps // 4) // G * G)
+    total, _ = time_graph(step, G, min(args.warmup, 4 * G), steps)
+    sec = total / steps
+    bytes_per_step = accounting.gemv_bytes(rows, cols, layout)
+    achieved = bytes_per_step / sec / 1e9
+    name = "gemv_base3" if layout == 3 else "gemv_2bit"
+    return dict(
+        metric="%s weights/s (int8 ternary GEMV, %d rows x %d weights)" % (name, rows, cols),
+        value=rows * cols / sec, unit="weights/s", n_gpus=1, steps=steps, warmup=args.warmup,
+        ms_per_step=sec * 1e3, higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="int8 x ternary -> int32, fp32 out", data="synthetic",
+        config=dict(workload=name, rows=rows, cols=cols, layout=layout,
+                    row_bytes=tw.ternary_pack3_row_bytes(cols) if layout == 3 else cols // 4,
+                    weight_copies=n_copies, bytes_per_step=bytes_per_step),
+        roofline=dict(bound="hbm", achieved=achieved, peak=accounting.HBM_PEAK_BPS / 1e9,
+                      unit="GB/s", frac=achieved * 1e9 / accounting.HBM_PEAK_BPS, traffic=None,
+                      kernel="k_gemv_i8<%d>" % layout),
+        cpu_baseline=None,
+    )
+
+
 def run_copy_calib(args):
     """A plain device-to-device copy of a known size (4 x 1 GiB), for scaling the FETCH_SIZE and
     WRITE_SIZE hardware counters of the measured kernels."""
@@ -304,7 +348,8 @@ def main():
     ap.add_argument("--graph-steps", type=int, default=256)
     ap.add_argument("--workload", default="stack24_b1",
                     choices=["stack24_b1", "layer_b1", "batched_b64", "batched_b64_int8",
-                             "prefill_4096", "quantize_layer", "copy_calib"])
+                             "prefill_4096", "quantize_layer", "gemv_2bit", "gemv_base3",
+                             "copy_calib"])
     ap.add_argument("--cpu-tokens", type=int, default=36)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -324,6 +369,8 @@ def main():
         res = run_copy_calib(args)
     elif args.workload == "quantize_layer":
         res = run_quantize(args)
+    elif args.workload in ("gemv_2bit", "gemv_base3"):
+        res = run_gemv(args, 3 if args.workload == "gemv_base3" else 2)
     else:
         res = run_single_layer(args, args.workload)
     res["device"] = torch.cuda.get_device_properties(0).gcnArchName

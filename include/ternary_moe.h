@@ -129,6 +129,48 @@ tw_status ternary_quantize(const void *w, int32_t w_dtype, int64_t rows, int64_t
                            uint8_t *packed, float *scales, void *stream);
 
 /*
+ * ternary_pack3_row_bytes -- bytes per row of the base-3 layout: ceil(cols/5) rounded up to a
+ *   multiple of 16 (416 for 2048 weights, against 512 in the 2-bit layout); -1 if cols < 0.
+ * ternary_pack3 -- pack int8 weights with values in {-1, 0, +1} five per byte (3^5 = 243 <= 256,
+ *   1.6 bits per weight): byte j of a row holds weights 5j .. 5j+4 as sum_i (w_{5j+i} + 1) 3^i,
+ *   weight 5j the least significant trit; positions at or past cols count as weight 0; the bytes of
+ *   a row past ceil(cols/5) are 0.
+ *   w         [rows][cols] int8, device, row-major.
+ *   packed    [rows][ternary_pack3_row_bytes(cols)] uint8, device, written in full.
+ *   bad_count nullable device int32: incremented (atomically) by the number of inputs outside
+ *             {-1,0,1}; each such input is packed as 0.  Not cleared by the call.
+ *   Errors: TW_E_NULL, TW_E_SHAPE (rows or cols < 0, rows * cols above 2^40), TW_E_ALIAS (packed
+ *   or bad_count overlapping an input or each other).  rows == 0 or cols == 0 is a no-op.
+ *   Source: a ternary weight needs at least log2 3 = 1.585 bits, and the packing may use another
+ *   aligned representation than 2 bits, [Hub] "Ternary Quantization Is More Than Simply
+ *   Compressing Weights into Three Values"; 1.58 bits per weight, [MacMini] "What Ternary Actually
+ *   Means".  The byte layout is the reading taken here.
+ */
+int64_t ternary_pack3_row_bytes(int64_t cols);
+tw_status ternary_pack3(const int8_t *w, int64_t rows, int64_t cols, uint8_t *packed,
+                        int32_t *bad_count, void *stream);
+
+/*
+ * ternary_gemv_i8 -- one ternary matrix-vector product with int8 activations, from either packed
+ * layout: y_r = (float(sum_i W[r][i] q_i) * x_scale) * scales_r, the sum exact in int32, then two
+ * fp32 roundings in that order (the order of the int8 batched FFN's gate, up and down values).
+ *   codes    layout 2: [rows][cols/4] as written by ternary_pack (cols a multiple of 64, at most
+ *            4096); layout 3: [rows][ternary_pack3_row_bytes(cols)] as written by ternary_pack3
+ *            (cols at most 5120).  Device, 16-byte aligned.
+ *   scales   [rows] fp32, device.   xq [cols] int8 codes, device.   x_scale one fp32, device.
+ *   y        [rows] fp32 output, device.
+ *   Bytes 243..255 in base-3 codes (never written by ternary_pack3) contribute nothing.
+ *   Errors: TW_E_NULL, TW_E_SHAPE (rows or cols < 0), TW_E_DTYPE (layout not 2 or 3),
+ *   TW_E_UNSUPPORTED (cols outside the limits above, codes not 16-byte aligned, scales, y or
+ *   x_scale not 4-byte aligned), TW_E_ALIAS (y overlapping an input).  rows == 0 is a no-op.
+ *   Source: the ternary matrix-vector product of one decode step, in which each weight passes
+ *   its input through, negates it or skips it, [MacMini] "What Ternary Actually Means".
+ */
+tw_status ternary_gemv_i8(const uint8_t *codes, int32_t layout, const float *scales, int64_t rows,
+                          int64_t cols, const int8_t *xq, const float *x_scale, float *y,
+                          void *stream);
+
+/*
  * moe_route_topk -- router logits, top-k selection and softmax gates for n_tokens tokens.
  *   x          [T][d] in x_dtype (TW_F32 or TW_BF16).
  *   w_router   [E][d] in w_dtype.

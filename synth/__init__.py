@@ -72,7 +72,7 @@ WORKLOADS = {w.name: w for w in (SMALL_LAYER_B1, LAYER_B1, STACK24_B1, BATCHED_B
                                  QUANTIZE_LAYER)}
 
 _KINDS = {"router": 1, "gate": 2, "up": 3, "down": 4, "s_gate": 5, "s_up": 6, "s_down": 7,
-          "x": 8, "fgate": 9, "fup": 10, "fdown": 11}
+          "x": 8, "fgate": 9, "fup": 10, "fdown": 11, "xq": 12}
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -143,6 +143,17 @@ def activations(w: Workload, n_tokens: int | None = None, device="cpu", seed: in
     s = w.seed if seed is None else seed
     T = w.batch if n_tokens is None else n_tokens
     return normal((T, w.d_model), 1.0, _DT[w.io_dtype], device, s, 0, "x", stream)
+
+
+def int8_codes(n: int, device="cpu", seed: int = 11, stream: int = 0) -> torch.Tensor:
+    """n int8 activation codes iid uniform over [-127, 127] (the range of absmax quantisation)."""
+    g = _gen(device, seed, 0, "xq", stream)
+    return torch.randint(-127, 128, (n,), dtype=torch.int8, device=device, generator=g)
+
+
+# ternary GEMV over the gate and up rows of one full-size layer's 256 experts (2 x 256 x 512 rows
+# of 2048 weights): 128 MiB of 2-bit codes, 104 MiB in base 3
+GEMV_ROWS, GEMV_COLS = 2 * 256 * 512, 2048
 
 
 def routing(n_tokens: int, n_experts: int, top_k: int, device="cpu", seed: int = 7) -> tuple:

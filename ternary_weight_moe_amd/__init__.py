@@ -40,7 +40,8 @@ class TwLayer(C.Structure):
                 ("s_down", C.c_void_p)]
 
 
-EXPORTS = ("tw_status_str", "ternary_pack", "ternary_quantize", "moe_route_topk", "ternary_moe_ffn_decode",
+EXPORTS = ("tw_status_str", "ternary_pack", "ternary_quantize", "ternary_pack3_row_bytes",
+           "ternary_pack3", "ternary_gemv_i8", "moe_route_topk", "ternary_moe_ffn_decode",
            "ternary_moe_decode_workspace_bytes", "ternary_moe_decode_error_offset",
            "ternary_moe_ffn_batched",
            "ternary_moe_batched_workspace_bytes")
@@ -61,6 +62,9 @@ def lib():
                 "tw_status_str": (C.c_char_p, [i32]),
                 "ternary_pack": (i32, [vp, i64, i64, vp, vp, vp]),
                 "ternary_quantize": (i32, [vp, i32, i64, i64, vp, vp, vp]),
+                "ternary_pack3_row_bytes": (i64, [i64]),
+                "ternary_pack3": (i32, [vp, i64, i64, vp, vp, vp]),
+                "ternary_gemv_i8": (i32, [vp, i32, vp, i64, i64, vp, vp, vp, vp]),
                 "moe_route_topk": (i32, [vp, i32, vp, i32, i64, i32, i32, i32, i32, vp, vp, vp,
                                          vp]),
                 "ternary_moe_ffn_decode": (i32, [LP, i32, vp, vp, i32, vp, sz, vp]),
@@ -112,6 +116,42 @@ def ternary_pack(w: torch.Tensor, bad_count: torch.Tensor | None = None, out=Non
         out = torch.empty(w.shape[:-1] + ((cols + 3) // 4,), dtype=torch.uint8, device=w.device)
     _check(lib().ternary_pack(_ptr(w), rows, cols, _ptr(out), _ptr(bad_count), _stream(stream)),
            "ternary_pack")
+    return out
+
+
+def ternary_pack3_row_bytes(cols: int) -> int:
+    """Bytes per row of the base-3 layout (five weights per byte, rows 16-byte aligned)."""
+    return int(lib().ternary_pack3_row_bytes(int(cols)))
+
+
+def ternary_pack3(w: torch.Tensor, bad_count: torch.Tensor | None = None, out=None,
+                  stream=None) -> torch.Tensor:
+    """int8 [..., cols] with values in {-1,0,1} -> base-3 packed uint8
+    [..., ternary_pack3_row_bytes(cols)]."""
+    _need_cuda(w, bad_count, out)
+    if w.dtype != torch.int8:
+        raise ValueError("ternary_pack3 expects int8")
+    cols = w.shape[-1]
+    rows = w.numel() // cols if cols else 0
+    if out is None:
+        out = torch.empty(w.shape[:-1] + (ternary_pack3_row_bytes(cols),), dtype=torch.uint8,
+                          device=w.device)
+    _check(lib().ternary_pack3(_ptr(w), rows, cols, _ptr(out), _ptr(bad_count), _stream(stream)),
+           "ternary_pack3")
+    return out
+
+
+def ternary_gemv_i8(codes: torch.Tensor, layout: int, scales: torch.Tensor, cols: int,
+                    xq: torch.Tensor, x_scale: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """y = (float(W q) * x_scale) * scales for ternary rows packed by ternary_pack (layout 2) or
+    ternary_pack3 (layout 3); codes [rows][row bytes], scales [rows] fp32, xq [cols] int8,
+    x_scale one fp32 (device), y [rows] fp32."""
+    _need_cuda(codes, scales, xq, x_scale, out)
+    rows = codes.shape[0]
+    if out is None:
+        out = torch.empty(rows, dtype=torch.float32, device=codes.device)
+    _check(lib().ternary_gemv_i8(_ptr(codes), int(layout), _ptr(scales), rows, int(cols), _ptr(xq),
+                                 _ptr(x_scale), _ptr(out), _stream(stream)), "ternary_gemv_i8")
     return out
 
 

@@ -60,6 +60,13 @@ def quantize_bytes(w) -> int:
     return n_w * _dt_bytes(w.router_dtype) + n_w // 4 + 4 * rows
 
 
+def gemv_bytes(rows: int, cols: int, layout: int) -> int:
+    """Algorithmic HBM bytes of one int8 ternary GEMV: every code byte and row scale read once,
+    the int8 input and its scale read once, one fp32 output per row written."""
+    row_bytes = cols // 4 if layout == 2 else ((cols + 4) // 5 + 15) // 16 * 16
+    return rows * row_bytes + 4 * rows + cols + 4 + 4 * rows
+
+
 def ceiling_rate(bytes_per_unit: float, bandwidth_bps: float) -> float:
     """Units per second at which the bytes alone saturate the bandwidth."""
     return bandwidth_bps / bytes_per_unit

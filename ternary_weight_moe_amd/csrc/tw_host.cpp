@@ -129,6 +129,51 @@ tw_status ternary_quantize(const void *w, int32_t w_dtype, int64_t rows, int64_t
                                                                                           : TW_OK;
 }
 
+int64_t ternary_pack3_row_bytes(int64_t cols)
+{
+    if (cols < 0 || cols > (int64_t(1) << 40)) return -1;
+    return tw::pack3_row_bytes(cols);
+}
+
+tw_status ternary_pack3(const int8_t *w, int64_t rows, int64_t cols, uint8_t *packed,
+                        int32_t *bad_count, void *stream)
+{
+    if (rows < 0 || cols < 0) return TW_E_SHAPE;
+    if (rows == 0 || cols == 0) return TW_OK;
+    if (!w || !packed) return TW_E_NULL;
+    if (cols > (int64_t(1) << 40) / rows) return TW_E_SHAPE;
+    const int64_t rb = tw::pack3_row_bytes(cols);
+    if (overlap(w, size_t(rows * cols), packed, size_t(rows * rb))) return TW_E_ALIAS;
+    if (bad_count && (overlap(bad_count, 4, packed, size_t(rows * rb)) ||
+                      overlap(bad_count, 4, w, size_t(rows * cols))))
+        return TW_E_ALIAS;
+    return tw::launch_pack3(w, rows, cols, packed, bad_count, stream) ? TW_E_HIP : TW_OK;
+}
+
+tw_status ternary_gemv_i8(const uint8_t *codes, int32_t layout, const float *scales, int64_t rows,
+                          int64_t cols, const int8_t *xq, const float *x_scale, float *y,
+                          void *stream)
+{
+    if (rows < 0 || cols < 0) return TW_E_SHAPE;
+    if (layout != 2 && layout != 3) return TW_E_DTYPE;
+    if (rows == 0) return TW_OK;
+    if (!codes || !scales || !xq || !x_scale || !y) return TW_E_NULL;
+    if (cols == 0 || (layout == 2 && (cols % 64 != 0 || cols > 4096)) ||
+        (layout == 3 && cols > 5120))
+        return TW_E_UNSUPPORTED;
+    if (rows > (int64_t(1) << 40) / cols) return TW_E_SHAPE;
+    if (((uintptr_t)codes & 15) || (((uintptr_t)scales | (uintptr_t)y | (uintptr_t)x_scale) & 3))
+        return TW_E_UNSUPPORTED;
+    const int64_t rb = layout == 3 ? tw::pack3_row_bytes(cols) : cols / 4;
+    const size_t ny = size_t(rows) * 4;
+    if (overlap(y, ny, codes, size_t(rows * rb)) || overlap(y, ny, scales, size_t(rows) * 4) ||
+        overlap(y, ny, xq, size_t(cols)) || overlap(y, ny, x_scale, 4))
+        return TW_E_ALIAS;
+    return tw::launch_gemv_i8(codes, layout, scales, rows, int(cols), xq, x_scale, y, stream)
+               ? TW_E_HIP
+               : TW_OK;
+}
+
 tw_status moe_route_topk(const void *x, int32_t x_dtype, const void *w_router, int32_t w_dtype,
                          int64_t n_tokens, int32_t d_model, int32_t n_experts, int32_t top_k,
                          int32_t pre_rmsnorm, float *logits, int32_t *expert_ids, float *gate_w,

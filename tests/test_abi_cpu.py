@@ -173,3 +173,43 @@ def test_decode_error_offset_inside_the_workspace(L):
     assert 0 < off and off + 4 <= n and off % 4 == 0
     assert L.ternary_moe_decode_error_offset(None, 1) == 0
     assert L.ternary_moe_decode_error_offset(C.byref(layer(k=0)), 1) == 0
+
+
+def test_pack3_row_bytes_and_errors(L):
+    assert [L.ternary_pack3_row_bytes(c) for c in (0, 1, 5, 80, 81, 2048, 512, 5120)] == \
+        [0, 16, 16, 16, 32, 416, 112, 1024]
+    assert L.ternary_pack3_row_bytes(-1) == -1
+    s = C.c_void_p(0)
+    assert L.ternary_pack3(A[0], -1, 5, A[1], None, s) == E_SHAPE
+    assert L.ternary_pack3(A[0], 4, -1, A[1], None, s) == E_SHAPE
+    assert L.ternary_pack3(None, 4, 5, A[1], None, s) == E_NULL
+    assert L.ternary_pack3(A[0], 4, 5, None, None, s) == E_NULL
+    assert L.ternary_pack3(None, 0, 5, None, None, s) == OK        # empty: no-op
+    assert L.ternary_pack3(A[0], 4, 64, A[0] + 16, None, s) == E_ALIAS
+    assert L.ternary_pack3(A[0], 4, 64, A[1], A[1] + 60, s) == E_ALIAS   # inside 4 x 16 bytes
+    assert L.ternary_pack3(A[0], 4, 64, A[1], A[0] + 4, s) == E_ALIAS
+
+
+def test_gemv_i8_errors(L):
+    s = None
+    g = L.ternary_gemv_i8
+    assert g(A[0], 3, A[1], -1, 2048, A[2], A[3], A[4], s) == E_SHAPE
+    assert g(A[0], 3, A[1], 4, -1, A[2], A[3], A[4], s) == E_SHAPE
+    assert g(A[0], 4, A[1], 4, 2048, A[2], A[3], A[4], s) == E_DTYPE
+    assert g(None, 3, None, 0, 2048, None, None, None, s) == OK     # empty: no-op
+    for i in range(5):
+        args = [A[0], A[1], A[2], A[3], A[4]]
+        args[i] = None
+        assert g(args[0], 3, args[1], 4, 2048, args[2], args[3], args[4], s) == E_NULL
+    assert g(A[0], 2, A[1], 4, 2000, A[2], A[3], A[4], s) == E_UNSUP     # 2-bit: cols % 64
+    assert g(A[0], 2, A[1], 4, 4160, A[2], A[3], A[4], s) == E_UNSUP     # 2-bit: above 4096
+    assert g(A[0], 3, A[1], 4, 5125, A[2], A[3], A[4], s) == E_UNSUP     # base 3: above 5120
+    assert g(A[0], 3, A[1], 4, 0, A[2], A[3], A[4], s) == E_UNSUP
+    assert g(A[0] + 8, 3, A[1], 4, 2048, A[2], A[3], A[4], s) == E_UNSUP
+    assert g(A[0], 3, A[1] + 2, 4, 2048, A[2], A[3], A[4], s) == E_UNSUP
+    assert g(A[0], 3, A[1], 4, 2048, A[2], A[3] + 1, A[4], s) == E_UNSUP
+    assert g(A[0], 3, A[1], 4, 2048, A[2], A[3], A[4] + 2, s) == E_UNSUP
+    assert g(A[0], 3, A[1], 4, 2048, A[2], A[3], A[0] + 1600, s) == E_ALIAS   # inside codes
+    assert g(A[0], 3, A[1], 4, 2048, A[2], A[3], A[1] + 8, s) == E_ALIAS
+    assert g(A[0], 3, A[1], 4, 2048, A[2], A[3], A[2] + 2044, s) == E_ALIAS
+    assert g(A[0], 3, A[1], 4, 2048, A[2], A[3], A[3] - 12, s) == E_ALIAS
