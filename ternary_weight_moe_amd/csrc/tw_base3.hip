@@ -61,7 +61,7 @@ __global__ void k_pack3(const int8_t *__restrict__ w, int64_t rows, int64_t cols
 }
 
 constexpr int kGvWaves = 4;     // waves per workgroup
-constexpr int kGvUnroll = 4;    // rows per lane group in flight
+constexpr int kGvUnroll = 8;    // rows per lane group in flight
 constexpr int kGvMaxChunks = 64;
 
 __device__ __forceinline__ uint32_t bytes4(int a, int b, int c, int d)
@@ -193,7 +193,7 @@ int launch_gemv_i8(const uint8_t *codes, int layout, const float *scales, int64_
     while ((1 << lg) < nc) lg++;
     const int64_t per_wave = int64_t(64 >> lg) * kGvUnroll;
     const int64_t nb64 = ((rows + per_wave - 1) / per_wave + kGvWaves - 1) / kGvWaves;
-    const unsigned nb = unsigned(nb64 < 2048 ? nb64 : 2048);
+    const unsigned nb = unsigned(nb64 < 1024 ? nb64 : 1024);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (layout == 3)
         k_gemv_i8<3><<<nb, 64 * kGvWaves, 0, st>>>(codes, scales, rows, cols, rb, lg, xq, x_scale, y);
