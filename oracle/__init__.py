@@ -86,6 +86,7 @@ def lib():
                 "or_pack3": (i64, [i8p, i64, i64, i64, u8p]),
                 "or_unpack3": (i64, [u8p, i64, i64, i64, i8p]),
                 "or_gemv_i8": (None, [i8p, fp, i64, i64, i8p, C.c_float, fp]),
+                "or_attention_decode": (None, [dp, dp, dp, i64, i32, i32, i32, dp]),
             }
             for name, (res, args) in sig.items():
                 f = getattr(L, name)
@@ -205,6 +206,20 @@ def gemv_i8(w, scale, q, sx) -> np.ndarray:
     lib().or_gemv_i8(_ptr(wv, C.c_int8), _ptr(sc, C.c_float), rows, cols, _ptr(qv, C.c_int8),
                      float(np.float32(sx)), _ptr(y, C.c_float))
     return y
+
+
+def attention_decode(q, k, v) -> np.ndarray:
+    """q [H][dh], k and v [n][Hkv][dh] (exact values widened to double) -> out [H][dh] (double):
+    softmax(q_h . k_t / sqrt(dh)) weighted sum of v_t over the n cached positions, query head h
+    reading KV head h / (H / Hkv) (tw_oracle.h)."""
+    qv, kv, vv = _np(q, np.float64), _np(k, np.float64), _np(v, np.float64)
+    H, dh = qv.shape
+    n, Hkv, dh2 = kv.shape
+    assert dh2 == dh and vv.shape == kv.shape and H % Hkv == 0
+    out = np.empty((H, dh), np.float64)
+    lib().or_attention_decode(_ptr(qv, C.c_double), _ptr(kv, C.c_double), _ptr(vv, C.c_double), n,
+                              H, Hkv, dh, _ptr(out, C.c_double))
+    return out
 
 
 def round_bf16_bits(v) -> np.ndarray:

@@ -158,6 +158,38 @@ void or_gemv_i8(const int8_t *w, const float *scale, int64_t rows, int64_t cols,
     }
 }
 
+/* ---- decode attention over a KV cache --------------------------------------------------------
+ * [MacMini] "The Architecture: Designed for the Hardware": global and 512-token sliding-window
+ * attention layers.  The plain definition: scores, softmax over the cached positions, weighted sum
+ * of the values (tw_oracle.h). */
+void or_attention_decode(const double *q, const double *k, const double *v, int64_t n, int32_t H,
+                         int32_t Hkv, int32_t dh, double *out)
+{
+    double *s = (double *)malloc(sizeof(double) * (n > 0 ? n : 1));
+    int32_t group = H / Hkv;
+    double scale = 1.0 / sqrt((double)dh);
+    for (int32_t h = 0; h < H; h++) {
+        int32_t g = h / group;
+        double m = -INFINITY, l = 0.0;
+        for (int64_t t = 0; t < n; t++) {
+            double d = 0.0;
+            for (int32_t i = 0; i < dh; i++) d += q[(int64_t)h * dh + i] * k[(t * Hkv + g) * dh + i];
+            s[t] = d * scale;
+            if (s[t] > m) m = s[t];
+        }
+        for (int64_t t = 0; t < n; t++) {
+            s[t] = exp(s[t] - m);
+            l += s[t];
+        }
+        for (int32_t i = 0; i < dh; i++) {
+            double o = 0.0;
+            for (int64_t t = 0; t < n; t++) o += s[t] * v[(t * Hkv + g) * dh + i];
+            out[(int64_t)h * dh + i] = o / l;
+        }
+    }
+    free(s);
+}
+
 /* ---- rounding ---------------------------------------------------------------------------- */
 
 uint16_t or_f64_to_bf16(double v)

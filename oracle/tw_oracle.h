@@ -77,6 +77,18 @@ int64_t or_unpack3(const uint8_t *packed, int64_t rows, int64_t cols, int64_t ro
 void or_gemv_i8(const int8_t *w, const float *scale, int64_t rows, int64_t cols, const int8_t *q,
                 float sx, float *y);
 
+/* ---- decode attention over a KV cache --------------------------------------------------------
+ * The pages' model interleaves sliding-window attention (window 512) with global attention at 3:1
+ * (6 global, 18 windowed layers), which bounds the cache of the windowed layers ([MacMini] "The
+ * Architecture: Designed for the Hardware"; [iPhone20B] opening section).  Reading: one query token
+ * attends, per query head h, over n cached positions of KV head h / (H / Hkv) (grouped-query):
+ * out_h = sum_t softmax_t(q_h . k_t / sqrt(dh)) v_t.  A windowed layer keeps its last `window`
+ * positions in a ring of `window` slots, so it attends over its min(ctx, window) filled slots; the
+ * sum does not depend on the slot order.  q [H][dh], k and v [n][Hkv][dh], out [H][dh]; everything
+ * in double, exp from the C library, max-subtracted. */
+void or_attention_decode(const double *q, const double *k, const double *v, int64_t n, int32_t H,
+                         int32_t Hkv, int32_t dh, double *out);
+
 /* ---- rounding ----------------------------------------------------------------------------- */
 /* Round-to-nearest-even of a double straight to bfloat16 (one rounding), returned as raw bits. */
 uint16_t or_f64_to_bf16(double v);

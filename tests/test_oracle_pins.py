@@ -580,3 +580,60 @@ def test_gemv_i8_matches_the_int8_ffn_gate_accumulators():
         ref = (taps["acc_gate"][j].astype(np.float32) * np.float32(taps["sx"][0])) * \
             w["s_gate"][e].astype(np.float32)
         assert np.array_equal(y, ref)
+
+
+# ---- decode attention over a KV cache (grouped-query, global or ring-buffered window) ------------
+
+def test_attention_single_position_returns_its_value():
+    q = rng.normal(size=(8, 16))
+    k = rng.normal(size=(1, 2, 16))
+    v = rng.normal(size=(1, 2, 16))
+    o = oracle.attention_decode(q, k, v)
+    for h in range(8):
+        assert np.array_equal(o[h], v[0, h // 4])      # 4 query heads per KV head
+
+
+def test_attention_equal_scores_average_the_values():
+    # zero query (or identical keys): uniform weights, the output is the mean of the values
+    v = rng.normal(size=(10, 2, 8))
+    o = oracle.attention_decode(np.zeros((4, 8)), rng.normal(size=(10, 2, 8)), v)
+    assert np.allclose(o[0], v[:, 0].mean(axis=0), rtol=0, atol=1e-14)
+    assert np.allclose(o[3], v[:, 1].mean(axis=0), rtol=0, atol=1e-14)
+    k = np.repeat(rng.normal(size=(1, 2, 8)), 10, axis=0)
+    o2 = oracle.attention_decode(rng.normal(size=(4, 8)), k, v)
+    assert np.allclose(o2[1], v[:, 0].mean(axis=0), rtol=0, atol=1e-14)
+
+
+def test_attention_dominant_key_selects_its_value():
+    dh = 8
+    k = np.zeros((6, 1, dh))
+    k[4, 0, 0] = 100.0
+    q = np.zeros((1, dh))
+    q[0, 0] = 100.0                      # score 10000 / sqrt(8) against 0 for the others
+    v = rng.normal(size=(6, 1, dh))
+    assert np.allclose(oracle.attention_decode(q, k, v)[0], v[4, 0], rtol=0, atol=1e-300)
+
+
+def test_attention_matches_library_softmax_and_sdpa():
+    H, Hkv, dh, n = 16, 4, 128, 37
+    q = rng.normal(size=(H, dh))
+    k = rng.normal(size=(n, Hkv, dh))
+    v = rng.normal(size=(n, Hkv, dh))
+    o = oracle.attention_decode(q, k, v)
+    qt = torch.from_numpy(q)[:, None, :]                                     # [H][1][dh]
+    kt = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(H // Hkv, 0)  # [H][n][dh]
+    vt = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(H // Hkv, 0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[:, 0, :].numpy()
+    assert np.allclose(o, ref, rtol=0, atol=1e-12)
+    w = torch.softmax(torch.einsum("hd,hnd->hn", qt[:, 0], kt) / math.sqrt(dh), dim=1)
+    assert np.allclose(o, torch.einsum("hn,hnd->hd", w, vt).numpy(), rtol=0, atol=1e-12)
+
+
+def test_attention_ring_order_does_not_matter():
+    # a windowed layer's ring holds its last positions in rotated slot order
+    q = rng.normal(size=(4, 32))
+    k = rng.normal(size=(20, 2, 32))
+    v = rng.normal(size=(20, 2, 32))
+    rot = np.roll(np.arange(20), 7)
+    assert np.allclose(oracle.attention_decode(q, k, v), oracle.attention_decode(q, k[rot], v[rot]),
+                       rtol=0, atol=1e-13)
