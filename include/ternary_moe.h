@@ -171,6 +171,36 @@ tw_status ternary_gemv_i8(const uint8_t *codes, int32_t layout, const float *sca
                           void *stream);
 
 /*
+ * attention_decode_workspace_bytes -- workspace bytes of attention_decode for n_heads query heads
+ *   of head_dim 128 over n_slots cached positions (0 when the arguments are invalid).
+ * attention_decode -- one query token attending over a KV cache:
+ *   out_h = sum_t softmax_t(q_h . k_t / sqrt(head_dim)) v_t over the n_slots cached positions t,
+ *   query head h reading KV head h / (n_heads / n_kv_heads) (grouped-query attention).
+ *   q        [n_heads][head_dim] bf16, device (after any rotary embedding).
+ *   k_cache, v_cache  [n_slots][n_kv_heads][head_dim] bf16, device: the filled slots of a layer's
+ *            cache.  A global layer holds one slot per position; a sliding-window layer keeps its
+ *            last `window` positions in a ring of `window` slots and passes min(positions, window)
+ *            slots.  The result does not depend on the slot order.
+ *   out      [n_heads][head_dim] fp32 output, device.
+ *   workspace  device, 256-byte aligned, at least attention_decode_workspace_bytes bytes.
+ *   Sums in fp32; the softmax is max-subtracted per split of 16 slots and the splits are merged
+ *   with exp(m_s - M) rescaling.
+ *   Limits: head_dim 128; n_heads / n_kv_heads in {1, 2, 4, 8}; n_heads <= 128; 1 <= n_slots <=
+ *   2^21.  Errors: TW_E_NULL, TW_E_SHAPE (n_slots < 1 or above 2^21, heads < 1, n_heads not a
+ *   multiple of n_kv_heads), TW_E_UNSUPPORTED (limits above, q/k/v not 16-byte aligned, out not
+ *   4-byte aligned, workspace not 256-byte aligned), TW_E_WORKSPACE, TW_E_ALIAS (out or workspace
+ *   overlapping an input or each other).
+ *   Source: interleaved sliding-window (512 tokens) and global attention at 3:1, 6 global and 18
+ *   windowed layers, [MacMini] "The Architecture: Designed for the Hardware"; [iPhone20B] opening
+ *   section.  Head counts and head size are not given by the pages; 16 query heads over 4 KV heads
+ *   of 128 (16 x 128 = d_model 2048) is the shape tested and measured here.
+ */
+size_t attention_decode_workspace_bytes(int32_t n_heads, int32_t head_dim, int64_t n_slots);
+tw_status attention_decode(const void *q, const void *k_cache, const void *v_cache, int64_t n_slots,
+                           int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, float *out,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * moe_route_topk -- router logits, top-k selection and softmax gates for n_tokens tokens.
  *   x          [T][d] in x_dtype (TW_F32 or TW_BF16).
  *   w_router   [E][d] in w_dtype.

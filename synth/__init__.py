@@ -72,7 +72,7 @@ WORKLOADS = {w.name: w for w in (SMALL_LAYER_B1, LAYER_B1, STACK24_B1, BATCHED_B
                                  QUANTIZE_LAYER)}
 
 _KINDS = {"router": 1, "gate": 2, "up": 3, "down": 4, "s_gate": 5, "s_up": 6, "s_down": 7,
-          "x": 8, "fgate": 9, "fup": 10, "fdown": 11, "xq": 12}
+          "x": 8, "fgate": 9, "fup": 10, "fdown": 11, "xq": 12, "q": 13, "k": 14, "v": 15}
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -154,6 +154,22 @@ def int8_codes(n: int, device="cpu", seed: int = 11, stream: int = 0) -> torch.T
 # ternary GEMV over the gate and up rows of one full-size layer's 256 experts (2 x 256 x 512 rows
 # of 2048 weights): 128 MiB of 2-bit codes, 104 MiB in base 3
 GEMV_ROWS, GEMV_COLS = 2 * 256 * 512, 2048
+
+
+# decode attention: 16 query heads over 4 KV heads of 128 (16 x 128 = d_model 2048); the pages'
+# 640-token benchmark context for the 6 global layers, a 512-slot ring for the 18 windowed ones
+ATTN_HEADS, ATTN_KV_HEADS, ATTN_HEAD_DIM = 16, 4, 128
+ATTN_CONTEXT, ATTN_WINDOW, ATTN_GLOBAL_LAYERS, ATTN_WINDOW_LAYERS = 640, 512, 6, 18
+
+
+def attention_inputs(n_slots: int, device="cpu", seed: int = 21, layer: int = 0,
+                     heads: int = ATTN_HEADS, kv_heads: int = ATTN_KV_HEADS,
+                     head_dim: int = ATTN_HEAD_DIM) -> tuple:
+    """q [heads][head_dim], k and v [n_slots][kv_heads][head_dim], all N(0, 1) in bf16."""
+    q = normal((heads, head_dim), 1.0, torch.bfloat16, device, seed, layer, "q")
+    k = normal((n_slots, kv_heads, head_dim), 1.0, torch.bfloat16, device, seed, layer, "k")
+    v = normal((n_slots, kv_heads, head_dim), 1.0, torch.bfloat16, device, seed, layer, "v")
+    return q, k, v
 
 
 def routing(n_tokens: int, n_experts: int, top_k: int, device="cpu", seed: int = 7) -> tuple:

@@ -41,7 +41,8 @@ class TwLayer(C.Structure):
 
 
 EXPORTS = ("tw_status_str", "ternary_pack", "ternary_quantize", "ternary_pack3_row_bytes",
-           "ternary_pack3", "ternary_gemv_i8", "moe_route_topk", "ternary_moe_ffn_decode",
+           "ternary_pack3", "ternary_gemv_i8", "attention_decode_workspace_bytes",
+           "attention_decode", "moe_route_topk", "ternary_moe_ffn_decode",
            "ternary_moe_decode_workspace_bytes", "ternary_moe_decode_error_offset",
            "ternary_moe_ffn_batched",
            "ternary_moe_batched_workspace_bytes")
@@ -65,6 +66,8 @@ def lib():
                 "ternary_pack3_row_bytes": (i64, [i64]),
                 "ternary_pack3": (i32, [vp, i64, i64, vp, vp, vp]),
                 "ternary_gemv_i8": (i32, [vp, i32, vp, i64, i64, vp, vp, vp, vp]),
+                "attention_decode_workspace_bytes": (sz, [i32, i32, i64]),
+                "attention_decode": (i32, [vp, vp, vp, i64, i32, i32, i32, vp, vp, sz, vp]),
                 "moe_route_topk": (i32, [vp, i32, vp, i32, i64, i32, i32, i32, i32, vp, vp, vp,
                                          vp]),
                 "ternary_moe_ffn_decode": (i32, [LP, i32, vp, vp, i32, vp, sz, vp]),
@@ -153,6 +156,33 @@ def ternary_gemv_i8(codes: torch.Tensor, layout: int, scales: torch.Tensor, cols
     _check(lib().ternary_gemv_i8(_ptr(codes), int(layout), _ptr(scales), rows, int(cols), _ptr(xq),
                                  _ptr(x_scale), _ptr(out), _stream(stream)), "ternary_gemv_i8")
     return out
+
+
+def attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, out=None,
+                     workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """One query token over a KV cache: q [H][128] bf16, k_cache and v_cache [n][Hkv][128] bf16
+    (the filled slots) -> out [H][128] fp32; softmax(q_h . k_t / sqrt(128)) weighted sum of v_t,
+    query head h reading KV head h / (H / Hkv)."""
+    _need_cuda(q, k_cache, v_cache, out, workspace)
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise ValueError("attention_decode expects bf16 q, k_cache and v_cache")
+    H, dh = q.shape
+    n, Hkv, dh2 = k_cache.shape
+    if dh2 != dh or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((H, dh), dtype=torch.float32, device=q.device)
+    nbytes = attention_decode_workspace_bytes(H, dh, n)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().attention_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), n, H, Hkv, dh, _ptr(out),
+                                  _ptr(workspace), workspace.numel(), _stream(stream)),
+           "attention_decode")
+    return out
+
+
+def attention_decode_workspace_bytes(n_heads: int, head_dim: int, n_slots: int) -> int:
+    return int(lib().attention_decode_workspace_bytes(int(n_heads), int(head_dim), int(n_slots)))
 
 
 def ternary_quantize(w: torch.Tensor, packed: torch.Tensor | None = None,

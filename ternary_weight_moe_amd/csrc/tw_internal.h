@@ -114,6 +114,14 @@ int launch_pack3(const int8_t *w, int64_t rows, int64_t cols, uint8_t *packed, i
 // bytes per row.
 int launch_gemv_i8(const uint8_t *codes, int layout, const float *scales, int64_t rows, int cols,
                    const int8_t *xq, const float *x_scale, float *y, void *stream);
+// Decode attention (tw_attn.hip): head dimension 128, splits of 16 cached positions; the
+// workspace holds (max, sum, 128 outputs) per (split, query head).
+constexpr int kAttnHeadDim = 128;
+constexpr int kAttnChunk = 16;
+inline int64_t attn_splits(int64_t n) { return (n + kAttnChunk - 1) / kAttnChunk; }
+inline size_t attn_ws_bytes(int64_t n, int H) { return align256(sizeof(float) * size_t(attn_splits(n)) * H * (kAttnHeadDim + 2)); }
+int launch_attn_decode(const void *q, const void *k, const void *v, int64_t n, int H, int Hkv,
+                       float *out, void *ws, void *stream);
 int launch_route(const void *x, int x_bf16, const void *w_router, int w_bf16, int64_t T,
                  const Dims &dm, float *logits, int32_t *ids, float *gates, void *stream);
 // One launch per (up to kMaxPersistLayers) layers; returns -1 when the shape or device is not

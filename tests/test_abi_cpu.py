@@ -213,3 +213,34 @@ def test_gemv_i8_errors(L):
     assert g(A[0], 3, A[1], 4, 2048, A[2], A[3], A[1] + 8, s) == E_ALIAS
     assert g(A[0], 3, A[1], 4, 2048, A[2], A[3], A[2] + 2044, s) == E_ALIAS
     assert g(A[0], 3, A[1], 4, 2048, A[2], A[3], A[3] - 12, s) == E_ALIAS
+
+
+def test_attention_decode_workspace_and_errors(L):
+    ws = L.attention_decode_workspace_bytes
+    assert ws(16, 128, 640) == ((640 + 15) // 16 * 16 * 130 * 4 + 255) // 256 * 256
+    assert ws(16, 64, 640) == 0 and ws(0, 128, 640) == 0 and ws(16, 128, 0) == 0
+    assert ws(16, 128, (1 << 21) + 1) == 0
+    s = None
+    a = L.attention_decode
+    big = 1 << 30
+    assert a(A[0], A[1], A[2], 0, 16, 4, 128, A[3], A[4], big, s) == E_SHAPE
+    assert a(A[0], A[1], A[2], (1 << 21) + 1, 16, 4, 128, A[3], A[4], big, s) == E_SHAPE
+    assert a(A[0], A[1], A[2], 640, 16, 3, 128, A[3], A[4], big, s) == E_SHAPE     # 16 % 3
+    assert a(A[0], A[1], A[2], 640, 0, 1, 128, A[3], A[4], big, s) == E_SHAPE
+    assert a(A[0], A[1], A[2], 640, 16, 4, 64, A[3], A[4], big, s) == E_UNSUP      # head_dim
+    assert a(A[0], A[1], A[2], 640, 48, 3, 128, A[3], A[4], big, s) == E_UNSUP     # group 16
+    assert a(A[0], A[1], A[2], 640, 12, 4, 128, A[3], A[4], big, s) == E_UNSUP     # group 3
+    assert a(A[0], A[1], A[2], 640, 256, 32, 128, A[3], A[4], big, s) == E_UNSUP   # > 128 heads
+    for i in range(5):
+        args = [A[0], A[1], A[2], A[3], A[4]]
+        args[i] = None
+        assert a(args[0], args[1], args[2], 640, 16, 4, 128, args[3], args[4], big, s) == E_NULL
+    assert a(A[0] + 8, A[1], A[2], 640, 16, 4, 128, A[3], A[4], big, s) == E_UNSUP
+    assert a(A[0], A[1], A[2] + 8, 640, 16, 4, 128, A[3], A[4], big, s) == E_UNSUP
+    assert a(A[0], A[1], A[2], 640, 16, 4, 128, A[3] + 2, A[4], big, s) == E_UNSUP
+    assert a(A[0], A[1], A[2], 640, 16, 4, 128, A[3], A[4] + 16, big, s) == E_UNSUP
+    assert a(A[0], A[1], A[2], 640, 16, 4, 128, A[3], A[4], ws(16, 128, 640) - 1, s) == E_WS
+    assert a(A[0], A[1], A[2], 640, 16, 4, 128, A[1] + 4096, A[4], big, s) == E_ALIAS   # in k
+    assert a(A[0], A[1], A[2], 640, 16, 4, 128, A[0], A[4], big, s) == E_ALIAS
+    assert a(A[0], A[1], A[2], 640, 16, 4, 128, A[3], A[2] + 1024, big, s) == E_ALIAS   # ws in v
+    assert a(A[0], A[1], A[2], 640, 16, 4, 128, A[4] + 512, A[4], big, s) == E_ALIAS    # out in ws
