@@ -27,6 +27,7 @@
 #include <stdint.h>
 
 #include "tw_device.h"
+#include "tw_aux.h"
 #include "tw_internal.h"
 
 namespace tw {

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include "../../include/ternary_moe.h"
+#include "tw_aux.h"
 #include "tw_internal.h"
 
 namespace {

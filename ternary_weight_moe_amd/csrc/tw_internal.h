@@ -106,22 +106,6 @@ int launch_pack(const int8_t *w, int64_t rows, int64_t cols, uint8_t *packed, in
                 void *stream);
 int launch_quantize(const void *w, int w_bf16, int64_t rows, int64_t cols, uint8_t *packed,
                     float *scales, void *stream);
-// Base-3 layout (tw_base3.hip): bytes per row, ceil(cols/5) rounded up to a multiple of 16.
-inline int64_t pack3_row_bytes(int64_t cols) { return ((cols + 4) / 5 + 15) / 16 * 16; }
-int launch_pack3(const int8_t *w, int64_t rows, int64_t cols, uint8_t *packed, int32_t *bad,
-                 void *stream);
-// layout 2: ternary_pack's rows (cols / 4 bytes); layout 3: base-3 rows.  At most 64 chunks of 16
-// bytes per row.
-int launch_gemv_i8(const uint8_t *codes, int layout, const float *scales, int64_t rows, int cols,
-                   const int8_t *xq, const float *x_scale, float *y, void *stream);
-// Decode attention (tw_attn.hip): head dimension 128, splits of 16 cached positions; the
-// workspace holds (max, sum, 128 outputs) per (split, query head).
-constexpr int kAttnHeadDim = 128;
-constexpr int kAttnChunk = 16;
-inline int64_t attn_splits(int64_t n) { return (n + kAttnChunk - 1) / kAttnChunk; }
-inline size_t attn_ws_bytes(int64_t n, int H) { return align256(sizeof(float) * size_t(attn_splits(n)) * H * (kAttnHeadDim + 2)); }
-int launch_attn_decode(const void *q, const void *k, const void *v, int64_t n, int H, int Hkv,
-                       float *out, void *ws, void *stream);
 int launch_route(const void *x, int x_bf16, const void *w_router, int w_bf16, int64_t T,
                  const Dims &dm, float *logits, int32_t *ids, float *gates, void *stream);
 // One launch per (up to kMaxPersistLayers) layers; returns -1 when the shape or device is not
