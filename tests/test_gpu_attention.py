@@ -1,6 +1,7 @@
 """Decode attention over a KV cache on the GPU through the C ABI, against the CPU oracle (fp64):
 grouped-query heads, the pages' 640-token global context and 512-slot window, ragged slot counts
-around the 16-slot splits, long contexts, sharp softmaxes and rotated ring slots.
+around the 16-slot splits, long contexts, sharp softmaxes and rotated ring slots, and a reused
+workspace.
 
 Tolerance: the kernel sums in fp32 (128-term score dots, 64-slot value sums per split, a merge over
 splits), so each score carries a relative error of about 128 x 2^-24 of sum |q_i k_i| (about 6e-5
@@ -33,7 +34,7 @@ def check(q, k, v, out):
     return err
 
 
-@pytest.mark.parametrize("n", [1, 5, 15, 16, 17, 63, 64, 65, 512, 640, 4097, 8191])
+@pytest.mark.parametrize("n", [1, 5, 15, 16, 17, 63, 64, 65, 127, 128, 129, 512, 640, 4097, 8191])
 def test_attention_matches_oracle(n):
     step("attention n=%d" % n)
     q, k, v = synth.attention_inputs(n, "cuda", seed=30 + n % 11)
@@ -97,7 +98,8 @@ def test_attention_reuses_workspace_and_is_deterministic():
     ws = torch.empty(tw.attention_decode_workspace_bytes(16, 128, 4097), dtype=torch.uint8, device="cuda")
     a = tw.attention_decode(q, k, v, workspace=ws).clone()
     q2, k2, v2 = synth.attention_inputs(4097, "cuda", seed=46)
-    tw.attention_decode(q2, k2, v2, workspace=ws)
+    c = tw.attention_decode(q2, k2, v2, workspace=ws).clone()
     b = tw.attention_decode(q, k, v, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+    check(q2, k2, v2, c)
