@@ -329,9 +329,6 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
             }
             __builtin_amdgcn_sched_barrier(0);   // four SiLUs at a time: bounded temporaries
         }
-        // keep the waves of the workgroup in step: the two waves of a SIMD then stay busy together
-        // instead of one finishing early and waiting at the end of the phase
-        if (gi + 1 < GPW) __syncthreads();
     }
 
     // 3. per-token max |h| (registers, the four lanes of a token, LDS over waves), then int8
@@ -435,7 +432,6 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
             const int64_t row = pr >= 0 && pl == 0 ? int64_t(pr) : L.spare_row + (blockIdx.x % kSpareRows);
             *reinterpret_cast<f4 *>(ybuf + row * D + R0 + 4 * g4) = f4{y[0], y[1], y[2], y[3]};
         }
-        if ((n & 3) == 3 && n + 1 < NSD) __syncthreads();   // waves in step, as in gate/up
     }
 }
 
