@@ -87,6 +87,7 @@ def lib():
                 "or_unpack3": (i64, [u8p, i64, i64, i64, i8p]),
                 "or_gemv_i8": (None, [i8p, fp, i64, i64, i8p, C.c_float, fp]),
                 "or_attention_decode": (None, [dp, dp, dp, i64, i32, i32, i32, dp]),
+                "or_flash_head": (None, [fp, i32, u8p, fp, i32, dp, ip, i32, i32, ip, ip, dp, fp]),
             }
             for name, (res, args) in sig.items():
                 f = getattr(L, name)
@@ -220,6 +221,31 @@ def attention_decode(q, k, v) -> np.ndarray:
     lib().or_attention_decode(_ptr(qv, C.c_double), _ptr(kv, C.c_double), _ptr(vv, C.c_double), n,
                               H, Hkv, dh, _ptr(out, C.c_double))
     return out
+
+
+def flash_head(h, centroids, c_scale, wc, member_ids, top: int):
+    """Approximate output head (tw_oracle.h): h [d] (fp32 values), centroids [ncl][d/2] u8 (offset
+    nibbles), c_scale [ncl] fp32, wc [ncl][cs][d] (exact values, widened to double), member_ids
+    [ncl][cs] int32 -> (sel [top] int32, ids [top][cs] int32, logits [top][cs] double, scores
+    [ncl] fp32)."""
+    hv = _np(h, np.float32).reshape(-1)
+    d = hv.size
+    cv = _np(centroids, np.uint8)
+    ncl = cv.shape[0]
+    assert cv.shape == (ncl, d // 2)
+    sv = _np(c_scale, np.float32).reshape(ncl)
+    wv = _np(wc, np.float64)
+    cs = wv.shape[1]
+    assert wv.shape == (ncl, cs, d)
+    mv = _np(member_ids, np.int32).reshape(ncl, cs)
+    sel = np.empty(top, np.int32)
+    ids = np.empty((top, cs), np.int32)
+    lg = np.empty((top, cs), np.float64)
+    scores = np.empty(ncl, np.float32)
+    lib().or_flash_head(_ptr(hv, C.c_float), d, _ptr(cv, C.c_uint8), _ptr(sv, C.c_float), ncl,
+                        _ptr(wv, C.c_double), _ptr(mv, C.c_int32), cs, top, _ptr(sel, C.c_int32),
+                        _ptr(ids, C.c_int32), _ptr(lg, C.c_double), _ptr(scores, C.c_float))
+    return sel, ids, lg, scores
 
 
 def round_bf16_bits(v) -> np.ndarray:

@@ -190,6 +190,67 @@ void or_attention_decode(const double *q, const double *k, const double *v, int6
     free(s);
 }
 
+/* ---- approximate output head (clustered vocabulary) ------------------------------------------
+ * [MacMini] "The Architecture: Designed for the Hardware": 4-bit centroid scores pick the top
+ * clusters; only their tokens get full-precision logits.  Readings in tw_oracle.h. */
+
+static int centroid_value(const uint8_t *row, int32_t i)
+{
+    int nib = (i & 1) ? (row[i / 2] >> 4) : (row[i / 2] & 15);
+    return nib - 8;
+}
+
+/* cluster a ranks before cluster b: higher score, or equal score and lower id */
+static int cluster_before(const float *score, int32_t a, int32_t b)
+{
+    if (score[a] != score[b]) return score[a] > score[b];
+    return a < b;
+}
+
+void or_flash_head(const float *h, int32_t d, const uint8_t *centroids, const float *c_scale,
+                   int32_t ncl, const double *wc, const int32_t *member_ids, int32_t cs,
+                   int32_t top, int32_t *sel, int32_t *ids, double *logits, float *scores)
+{
+    int8_t *q = (int8_t *)malloc(d);
+    float *sc = (float *)malloc(sizeof(float) * ncl);
+    int32_t *order = (int32_t *)malloc(sizeof(int32_t) * ncl);
+    float sh;
+    /* 1. 4-bit centroid scores against the int8 image of h */
+    or_quant_absmax(h, d, q, &sh);
+    for (int32_t c = 0; c < ncl; c++) {
+        const uint8_t *row = centroids + (int64_t)c * (d / 2);
+        int64_t acc = 0;
+        for (int32_t i = 0; i < d; i++) acc += (int64_t)centroid_value(row, i) * q[i];
+        sc[c] = ((float)acc * sh) * c_scale[c];
+        if (scores) scores[c] = sc[c];
+    }
+    /* 2. the top clusters: a selection by repeated scans for the best remaining cluster */
+    for (int32_t c = 0; c < ncl; c++) order[c] = c;
+    for (int32_t j = 0; j < top; j++) {
+        int32_t best = j;
+        for (int32_t c = j + 1; c < ncl; c++)
+            if (cluster_before(sc, order[c], order[best])) best = c;
+        int32_t t = order[j];
+        order[j] = order[best];
+        order[best] = t;
+        sel[j] = order[j];
+    }
+    /* 3. full-precision logits of the selected clusters' tokens */
+    for (int32_t j = 0; j < top; j++) {
+        int64_t c = sel[j];
+        for (int32_t m = 0; m < cs; m++) {
+            const double *wr = wc + (c * cs + m) * d;
+            double acc = 0.0;
+            for (int32_t i = 0; i < d; i++) acc += wr[i] * (double)h[i];
+            logits[(int64_t)j * cs + m] = acc;
+            ids[(int64_t)j * cs + m] = member_ids[c * cs + m];
+        }
+    }
+    free(q);
+    free(sc);
+    free(order);
+}
+
 /* ---- rounding ---------------------------------------------------------------------------- */
 
 uint16_t or_f64_to_bf16(double v)

@@ -89,6 +89,22 @@ void or_gemv_i8(const int8_t *w, const float *scale, int64_t rows, int64_t cols,
 void or_attention_decode(const double *q, const double *k, const double *v, int64_t n, int32_t H,
                          int32_t Hkv, int32_t dh, double *out);
 
+/* ---- approximate output head (clustered vocabulary) ------------------------------------------
+ * [MacMini] "The Architecture: Designed for the Hardware": the output head is the costliest step of
+ * decode; the vocabulary (about 151,000 tokens) is split into 4,748 clusters, 4-bit centroid
+ * scores pick the 512 most relevant clusters, and only their tokens get full-precision logits.
+ * Readings: clusters of cs tokens whose head rows are stored cluster-major, wc [ncl][cs][d], with
+ * member_ids [ncl][cs] giving each row's token id; centroids [ncl][d/2] bytes, element 2k in the low
+ * nibble of byte k and 2k+1 in the high nibble, each nibble the value + 8 (values -8..7), one fp32
+ * scale per centroid.  Scoring: h quantised by absmax to int8 (or_quant_absmax), acc_c = exact
+ * sum_i value_c,i q_i, score_c = ((float) acc_c * s_h) * scale_c (two fp32 roundings).  Selection:
+ * the `top` clusters by (score descending, cluster id ascending).  Logits: sum_i w[v][i] h_i in
+ * double for every token of the selected clusters, in selection order then member order.
+ * Outputs: sel [top], ids and logits [top][cs]; scores [ncl] (nullable tap). */
+void or_flash_head(const float *h, int32_t d, const uint8_t *centroids, const float *c_scale,
+                   int32_t ncl, const double *wc, const int32_t *member_ids, int32_t cs,
+                   int32_t top, int32_t *sel, int32_t *ids, double *logits, float *scores);
+
 /* ---- rounding ----------------------------------------------------------------------------- */
 /* Round-to-nearest-even of a double straight to bfloat16 (one rounding), returned as raw bits. */
 uint16_t or_f64_to_bf16(double v);

@@ -637,3 +637,66 @@ def test_attention_ring_order_does_not_matter():
     rot = np.roll(np.arange(20), 7)
     assert np.allclose(oracle.attention_decode(q, k, v), oracle.attention_decode(q, k[rot], v[rot]),
                        rtol=0, atol=1e-13)
+
+
+# ---- approximate output head: 4-bit centroid scores, top clusters, exact logits -----------------
+
+def pack_nibbles(vals):
+    """values -8..7 [..., d] -> offset nibbles, element 2k low and 2k+1 high in byte k"""
+    u = (np.asarray(vals, np.int64) + 8).astype(np.uint8)
+    return (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
+
+
+def flash_inputs(d=64, ncl=20, cs=4, seed=3):
+    r = np.random.default_rng(seed)
+    vals = r.integers(-8, 8, (ncl, d))
+    return dict(h=r.normal(0, 1, d).astype(np.float32), vals=vals, cent=pack_nibbles(vals),
+                cscale=r.uniform(0.01, 0.1, ncl).astype(np.float32),
+                wc=r.normal(0, 0.02, (ncl, cs, d)).astype(np.float32),
+                members=r.permutation(ncl * cs).astype(np.int32).reshape(ncl, cs))
+
+
+def test_flash_head_scores_are_exact_integer_dots_of_the_centroids():
+    f = flash_inputs()
+    sel, ids, lg, scores = oracle.flash_head(f["h"], f["cent"], f["cscale"], f["wc"], f["members"], 5)
+    q, sh = oracle.quant_absmax(f["h"])
+    acc = f["vals"].astype(np.int64) @ q.astype(np.int64)           # brute-force integer dots
+    assert np.array_equal(scores, (acc.astype(np.float32) * np.float32(sh)) * f["cscale"])
+    # a one-hot centroid row scores its single value times that input's code
+    v = np.zeros((1, 64), np.int64)
+    v[0, 9] = -7
+    s1 = oracle.flash_head(f["h"], pack_nibbles(v), np.ones(1, np.float32), f["wc"][:1],
+                           f["members"][:1], 1)[3]
+    assert s1[0] == np.float32(np.float32(-7 * int(q[9])) * np.float32(sh))
+
+
+def test_flash_head_selection_matches_library_sort_with_ties_to_lower_ids():
+    f = flash_inputs(ncl=30)
+    q, _ = oracle.quant_absmax(f["h"])
+    best = np.where(q > 0, 7, -8)[None, :]        # the largest possible score for this input
+    f["cent"][3] = f["cent"][7] = pack_nibbles(best)[0]
+    f["cscale"][3] = f["cscale"][7] = 0.5
+    sel, ids, lg, scores = oracle.flash_head(f["h"], f["cent"], f["cscale"], f["wc"], f["members"], 12)
+    ref = np.lexsort((np.arange(30), -scores.astype(np.float64)))[:12]
+    assert np.array_equal(sel, ref)
+    assert scores[3] == scores[7] and sel[0] == 3 and sel[1] == 7
+
+
+def test_flash_head_logits_match_library_matmul_and_member_ids():
+    f = flash_inputs()
+    sel, ids, lg, scores = oracle.flash_head(f["h"], f["cent"], f["cscale"], f["wc"], f["members"], 6)
+    ref = np.einsum("jmd,d->jm", f["wc"][sel].astype(np.float64), f["h"].astype(np.float64))
+    assert np.allclose(lg, ref, rtol=0, atol=1e-13)
+    assert np.array_equal(ids, f["members"][sel])
+
+
+def test_flash_head_with_every_cluster_is_the_exact_head():
+    # selecting all clusters covers the whole vocabulary: the best logit is the exact head's argmax
+    f = flash_inputs(ncl=16, cs=8)
+    sel, ids, lg, scores = oracle.flash_head(f["h"], f["cent"], f["cscale"], f["wc"], f["members"], 16)
+    assert sorted(ids.reshape(-1).tolist()) == list(range(128))
+    W = np.empty((128, 64))
+    W[f["members"].reshape(-1)] = f["wc"].reshape(128, 64)
+    full = W @ f["h"].astype(np.float64)
+    assert ids.reshape(-1)[np.argmax(lg.reshape(-1))] == np.argmax(full)
+    assert np.isclose(lg.max(), full.max(), rtol=0, atol=1e-13)
