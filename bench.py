@@ -366,6 +366,42 @@ def run_attention(args):
     )
 
 
+def run_flash_head(args):
+    """Approximate output head: 151,936 tokens in 4,748 clusters of 32, hidden size 2048, the top
+    512 clusters (67 MB of head rows per call).  Eight hidden states rotate, so that consecutive
+    calls select different clusters and their rows (together most of the 622 MB head) come from
+    HBM rather than the 256 MB last-level cache."""
+    ncl, cs, d, top = synth.HEAD_CLUSTERS, synth.HEAD_CLUSTER_SIZE, synth.HEAD_D, synth.HEAD_TOP
+    f = synth.head_inputs(ncl, cs, d, "cuda", seed=3000)
+    hs = [synth.head_hidden(d, "cuda", seed=3000, stream=i) for i in range(8)]
+    ws = torch.empty(tw.lib().flash_head_workspace_bytes(ncl), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(t):
+        tw.flash_head(hs[t % 8], f["centroids"], f["centroid_scales"], f["w_clustered"],
+                      f["member_ids"], top, workspace=ws)
+
+    G = min(args.graph_steps, 64)
+    steps = max(G, (args.steps // 4) // G * G)
+    total, _ = time_graph(step, G, min(args.warmup, 4 * G), steps)
+    sec = total / steps
+    bytes_per_step = (ncl * d // 2 + 4 * ncl + 2 * d + top * cs * d * 2 + top * cs * 4
+                      + top * cs * 8 + 4 * top)
+    achieved = bytes_per_step / sec / 1e9
+    return dict(
+        metric="flash_head calls/s (4,748 clusters of 32 tokens, top 512, hidden 2048)",
+        value=1.0 / sec, unit="calls/s", n_gpus=1, steps=steps, warmup=args.warmup,
+        ms_per_step=sec * 1e3, higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="int4 x int8 -> int32 scores, bf16 x bf16 -> fp32 logits", data="synthetic",
+        config=dict(workload="flash_head", clusters=ncl, cluster_size=cs, hidden=d, top=top,
+                    hidden_states=8, bytes_per_step=bytes_per_step),
+        roofline=dict(bound="hbm", achieved=achieved, peak=accounting.HBM_PEAK_BPS / 1e9,
+                      unit="GB/s", frac=achieved * 1e9 / accounting.HBM_PEAK_BPS, traffic=None,
+                      kernel="k_head_score + k_head_select + k_head_logits<4>"),
+        cpu_baseline=None,
+    )
+
+
 def run_copy_calib(args):
     """A plain device-to-device copy of a known size (4 x 1 GiB), for scaling the FETCH_SIZE and
     WRITE_SIZE hardware counters of the measured kernels."""
@@ -395,7 +431,7 @@ def main():
     ap.add_argument("--workload", default="stack24_b1",
                     choices=["stack24_b1", "layer_b1", "batched_b64", "batched_b64_int8",
                              "prefill_4096", "quantize_layer", "gemv_2bit", "gemv_base3",
-                             "attention_24l", "copy_calib"])
+                             "attention_24l", "flash_head", "copy_calib"])
     ap.add_argument("--cpu-tokens", type=int, default=36)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -417,6 +453,8 @@ def main():
         res = run_quantize(args)
     elif args.workload == "attention_24l":
         res = run_attention(args)
+    elif args.workload == "flash_head":
+        res = run_flash_head(args)
     elif args.workload in ("gemv_2bit", "gemv_base3"):
         res = run_gemv(args, 3 if args.workload == "gemv_base3" else 2)
     else:

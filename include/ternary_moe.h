@@ -201,6 +201,39 @@ tw_status attention_decode(const void *q, const void *k_cache, const void *v_cac
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * flash_head_workspace_bytes -- workspace bytes of flash_head for n_clusters clusters (0 if invalid).
+ * flash_head -- approximate output head over a clustered vocabulary: 4-bit centroid scores pick
+ * the `top` most relevant clusters, and only their tokens get full-precision logits.
+ *   h            [d] bf16 hidden state, device.  d in {512, 1024, 2048, 4096}.
+ *   centroids    [n_clusters][d/2] uint8, device, 16-byte aligned: element 2k of a centroid in the
+ *                low nibble of byte k, 2k+1 in the high nibble, each nibble the value + 8 (values
+ *                -8..7).   centroid_scales [n_clusters] fp32, device.
+ *   w_clustered  [n_clusters][cluster_size][d] bf16, device, 16-byte aligned: the head's rows in
+ *                cluster-major order.   member_ids [n_clusters][cluster_size] int32: the token id
+ *                of each of those rows.
+ *   sel_clusters [top] int32 output: the selected clusters, by score descending, ties to the lower
+ *                cluster id.   token_ids, logits [top][cluster_size] int32 / fp32 outputs: the
+ *                selected clusters' tokens in that order and, per cluster, in row order.
+ *   Scores: h is quantised by absmax to int8 (q = clamp(rint(h * (127 / amax)), -127, 127),
+ *   s_h = amax / 127), acc = exact sum_i value_i q_i, score = (float(acc) * s_h) * scale, in that
+ *   order (so equal inputs select equal clusters on any device).  Logits: fp32 sums of bf16 x bf16
+ *   products.
+ *   Limits: 1 <= n_clusters <= 8192, 1 <= cluster_size <= 1024, 1 <= top <= n_clusters.
+ *   Errors: TW_E_NULL, TW_E_SHAPE (sizes out of those ranges), TW_E_UNSUPPORTED (d, alignment:
+ *   centroids and w_clustered 16 bytes, h 2, scales/ids/outputs 4, workspace 256), TW_E_WORKSPACE,
+ *   TW_E_ALIAS (an output or the workspace overlapping an input or another output).
+ *   Source: the approximate output head, [MacMini] "The Architecture: Designed for the Hardware"
+ *   (about 151,000 tokens in 4,748 clusters, top 512 clusters by 4-bit centroid scores, full
+ *   precision only inside them).  The layouts and the int8 image of h are the readings taken here.
+ */
+size_t flash_head_workspace_bytes(int32_t n_clusters);
+tw_status flash_head(const void *h, int32_t d, const uint8_t *centroids,
+                     const float *centroid_scales, int32_t n_clusters, const void *w_clustered,
+                     const int32_t *member_ids, int32_t cluster_size, int32_t top,
+                     int32_t *sel_clusters, int32_t *token_ids, float *logits, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/*
  * moe_route_topk -- router logits, top-k selection and softmax gates for n_tokens tokens.
  *   x          [T][d] in x_dtype (TW_F32 or TW_BF16).
  *   w_router   [E][d] in w_dtype.

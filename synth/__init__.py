@@ -72,7 +72,8 @@ WORKLOADS = {w.name: w for w in (SMALL_LAYER_B1, LAYER_B1, STACK24_B1, BATCHED_B
                                  QUANTIZE_LAYER)}
 
 _KINDS = {"router": 1, "gate": 2, "up": 3, "down": 4, "s_gate": 5, "s_up": 6, "s_down": 7,
-          "x": 8, "fgate": 9, "fup": 10, "fdown": 11, "xq": 12, "q": 13, "k": 14, "v": 15}
+          "x": 8, "fgate": 9, "fup": 10, "fdown": 11, "xq": 12, "q": 13, "k": 14, "v": 15,
+          "head": 16, "perm": 17, "h": 18}
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -170,6 +171,32 @@ def attention_inputs(n_slots: int, device="cpu", seed: int = 21, layer: int = 0,
     k = normal((n_slots, kv_heads, head_dim), 1.0, torch.bfloat16, device, seed, layer, "k")
     v = normal((n_slots, kv_heads, head_dim), 1.0, torch.bfloat16, device, seed, layer, "v")
     return q, k, v
+
+
+# approximate output head: 151,936 tokens in 4,748 clusters of 32 (the pages: about 151,000 tokens
+# in 4,748 clusters), hidden size 2048, the top 512 clusters
+HEAD_CLUSTERS, HEAD_CLUSTER_SIZE, HEAD_TOP, HEAD_D = 4748, 32, 512, 2048
+
+
+def head_inputs(n_clusters: int = HEAD_CLUSTERS, cluster_size: int = HEAD_CLUSTER_SIZE,
+                d: int = HEAD_D, device="cpu", seed: int = 23) -> dict:
+    """Head rows w_clustered [ncl][cs][d] ~ N(0, 0.02) bf16 in cluster-major order, member_ids
+    [ncl][cs] a random permutation of the token ids, centroids [ncl][d/2] uint8 with every nibble
+    iid uniform over 0..15 (values -8..7 in offset binary), centroid scales U[0.01, 0.1] fp32."""
+    w = normal((n_clusters, cluster_size, d), 0.02, torch.bfloat16, device, seed, 0, "head")
+    g = _gen(device, seed, 0, "perm")
+    members = torch.randperm(n_clusters * cluster_size, generator=g, device=device)
+    members = members.to(torch.int32).reshape(n_clusters, cluster_size).contiguous()
+    gc = _gen(device, seed, 1, "perm")
+    cent = torch.randint(0, 256, (n_clusters, d // 2), generator=gc, device=device).to(torch.uint8)
+    scales = uniform((n_clusters,), 0.01, 0.1, device, seed, 1, "head").contiguous()
+    return dict(w_clustered=w.contiguous(), member_ids=members, centroids=cent.contiguous(),
+                centroid_scales=scales)
+
+
+def head_hidden(d: int = HEAD_D, device="cpu", seed: int = 23, stream: int = 0) -> torch.Tensor:
+    """A hidden state h [d] ~ N(0, 1) bf16."""
+    return normal((d,), 1.0, torch.bfloat16, device, seed, 0, "h", stream)
 
 
 def routing(n_tokens: int, n_experts: int, top_k: int, device="cpu", seed: int = 7) -> tuple:

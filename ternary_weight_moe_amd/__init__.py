@@ -42,7 +42,8 @@ class TwLayer(C.Structure):
 
 EXPORTS = ("tw_status_str", "ternary_pack", "ternary_quantize", "ternary_pack3_row_bytes",
            "ternary_pack3", "ternary_gemv_i8", "attention_decode_workspace_bytes",
-           "attention_decode", "moe_route_topk", "ternary_moe_ffn_decode",
+           "attention_decode", "flash_head_workspace_bytes", "flash_head", "moe_route_topk",
+           "ternary_moe_ffn_decode",
            "ternary_moe_decode_workspace_bytes", "ternary_moe_decode_error_offset",
            "ternary_moe_ffn_batched",
            "ternary_moe_batched_workspace_bytes")
@@ -68,6 +69,9 @@ def lib():
                 "ternary_gemv_i8": (i32, [vp, i32, vp, i64, i64, vp, vp, vp, vp]),
                 "attention_decode_workspace_bytes": (sz, [i32, i32, i64]),
                 "attention_decode": (i32, [vp, vp, vp, i64, i32, i32, i32, vp, vp, sz, vp]),
+                "flash_head_workspace_bytes": (sz, [i32]),
+                "flash_head": (i32, [vp, i32, vp, vp, i32, vp, vp, i32, i32, vp, vp, vp, vp, sz,
+                                     vp]),
                 "moe_route_topk": (i32, [vp, i32, vp, i32, i64, i32, i32, i32, i32, vp, vp, vp,
                                          vp]),
                 "ternary_moe_ffn_decode": (i32, [LP, i32, vp, vp, i32, vp, sz, vp]),
@@ -179,6 +183,33 @@ def attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
                                   _ptr(workspace), workspace.numel(), _stream(stream)),
            "attention_decode")
     return out
+
+
+def flash_head(h: torch.Tensor, centroids: torch.Tensor, centroid_scales: torch.Tensor,
+               w_clustered: torch.Tensor, member_ids: torch.Tensor, top: int, workspace=None,
+               stream=None):
+    """Approximate output head: h [d] bf16, centroids [ncl][d/2] uint8 (offset nibbles),
+    centroid_scales [ncl] fp32, w_clustered [ncl][cs][d] bf16, member_ids [ncl][cs] int32 ->
+    (sel_clusters [top] int32, token_ids [top][cs] int32, logits [top][cs] fp32)."""
+    _need_cuda(h, centroids, centroid_scales, w_clustered, member_ids, workspace)
+    if h.dtype != torch.bfloat16 or w_clustered.dtype != torch.bfloat16:
+        raise ValueError("flash_head expects bf16 h and w_clustered")
+    d = h.numel()
+    ncl, cs, d2 = w_clustered.shape
+    if d2 != d or centroids.shape != (ncl, d // 2) or member_ids.shape != (ncl, cs):
+        raise ValueError("shape mismatch")
+    dev = h.device
+    sel = torch.empty(top, dtype=torch.int32, device=dev)
+    ids = torch.empty((top, cs), dtype=torch.int32, device=dev)
+    logits = torch.empty((top, cs), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(int(lib().flash_head_workspace_bytes(ncl)), 1),
+                                dtype=torch.uint8, device=dev)
+    _check(lib().flash_head(_ptr(h), d, _ptr(centroids), _ptr(centroid_scales), ncl,
+                            _ptr(w_clustered), _ptr(member_ids), cs, int(top), _ptr(sel), _ptr(ids),
+                            _ptr(logits), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "flash_head")
+    return sel, ids, logits
 
 
 def attention_decode_workspace_bytes(n_heads: int, head_dim: int, n_slots: int) -> int:

@@ -26,5 +26,13 @@ inline int64_t attn_splits(int64_t n) { return (n + kAttnChunk - 1) / kAttnChunk
 inline size_t attn_ws_bytes(int64_t n, int H) { return align256(sizeof(float) * size_t(attn_splits(n)) * H * (kAttnHeadDim + 2)); }
 int launch_attn_decode(const void *q, const void *k, const void *v, int64_t n, int H, int Hkv,
                        float *out, void *ws, void *stream);
+// Approximate output head (tw_head.hip): d in {512, 1024, 2048, 4096}, at most 8192 clusters; the
+// workspace holds the clusters' fp32 scores.
+constexpr int kHeadMaxD = 4096;
+constexpr int kHeadMaxClusters = 8192;
+inline size_t head_ws_bytes(int ncl) { return align256(sizeof(float) * size_t(ncl)); }
+int launch_flash_head(const void *h, int d, const uint8_t *cent, const float *cscale, int ncl,
+                      const void *wc, const int32_t *members, int cs, int top, int32_t *sel,
+                      int32_t *ids, float *logits, void *ws, void *stream);
 
 }  // namespace tw

@@ -1,0 +1,220 @@
+// tw_head.hip -- approximate output head over a clustered vocabulary ("A 20B AI Model Trained in
+// Ternary Just Hit 218 Tokens/Second on a $599 Mac Mini", section "The Architecture: Designed for
+// the Hardware": the vocabulary is split into 4,748 clusters, 4-bit centroid scores pick the 512
+// most relevant ones, and only their tokens get full-precision logits).
+//
+// Three launches on the caller's stream:
+//   k_head_score   one wave per centroid row: h is quantised to int8 by absmax in every workgroup
+//                  (the same fp32 steps as the int8 FFN path, so the codes are identical), each
+//                  lane holds the codes of its 32-input chunks as even/odd int8x4 words, and the
+//                  offset-binary nibbles (value + 8) of the centroid are masked into int8x4 words
+//                  for v_dot4; the exact sum is corrected by -8 sum(q) and scaled,
+//                  score = (float(acc) * s_h) * scale (two fp32 roundings);
+//   k_head_select  one 1024-thread workgroup: a bitonic sort in LDS of (orderable score key,
+//                  cluster id) pairs, descending by score and ascending by id, then the first
+//                  `top` ids;
+//   k_head_logits  one workgroup per selected cluster, four waves; each wave takes rows
+//                  wave, wave + 4, ... of the cluster's cluster-major head rows, all loads of a
+//                  batch of rows issued first, fp32 dot with h (from LDS), wave sum.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tw_aux.h"
+#include "tw_device.h"
+#include "tw_internal.h"
+
+namespace tw {
+namespace {
+
+// int8 image of h (absmax) into LDS, and its scale; every thread of the workgroup takes part.
+template <int NT>
+__device__ __forceinline__ float head_quant_h(const uint16_t *__restrict__ h, int d, int8_t *s_q,
+                                              float *s_red)
+{
+    const int t = threadIdx.x;
+    float am = 0.0f;
+    for (int i = t; i < d; i += NT) am = fmaxf(am, fabsf(bf16_to_f32(h[i])));
+    am = wave_max(am);
+    if ((t & 63) == 0) s_red[t >> 6] = am;
+    __syncthreads();
+    am = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; w++) am = fmaxf(am, s_red[w]);
+    const float inv = 127.0f / am;
+    for (int i = t; i < d; i += NT) s_q[i] = am > 0.0f ? int8_quant(bf16_to_f32(h[i]), inv) : int8_t(0);
+    __syncthreads();
+    return am > 0.0f ? am / 127.0f : 0.0f;
+}
+
+__global__ __launch_bounds__(256) void k_head_score(const uint16_t *__restrict__ h, int d,
+                                                    const uint8_t *__restrict__ cent,
+                                                    const float *__restrict__ cscale, int ncl,
+                                                    float *__restrict__ scores)
+{
+    __shared__ int8_t s_q[kHeadMaxD];
+    __shared__ float s_red[4];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int nch = d / 32;   // 32-input chunks (16 centroid bytes) per row
+    const float sh = head_quant_h<256>(h, d, s_q, s_red);
+    // this lane's chunks (at most kHeadMaxD / 32 / 64 = 4): even and odd input words, and sum(q)
+    constexpr int MC = kHeadMaxD / 32 / 64;
+    uint32_t xe[MC][4], xo[MC][4];
+    int32_t sq = 0;
+#pragma unroll
+    for (int m = 0; m < MC; m++) {
+        const int c = lane + 64 * m;
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+            xe[m][w] = xo[m][w] = 0u;
+            if (c < nch) {
+                const int b = 32 * c + 8 * w;
+                int32_t e[4], o[4];
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    e[k] = s_q[b + 2 * k];
+                    o[k] = s_q[b + 2 * k + 1];
+                    sq += e[k] + o[k];
+                }
+                xe[m][w] = (uint32_t(uint8_t(e[0]))) | (uint32_t(uint8_t(e[1])) << 8) |
+                           (uint32_t(uint8_t(e[2])) << 16) | (uint32_t(uint8_t(e[3])) << 24);
+                xo[m][w] = (uint32_t(uint8_t(o[0]))) | (uint32_t(uint8_t(o[1])) << 8) |
+                           (uint32_t(uint8_t(o[2])) << 16) | (uint32_t(uint8_t(o[3])) << 24);
+            }
+        }
+    }
+    int32_t sqw[1] = {sq};
+    group_reduce<1>(sqw, 64);   // sum(q) over the row, in every lane
+    for (int c0 = blockIdx.x * 4 + wave; c0 < ncl; c0 += gridDim.x * 4) {
+        const uint4 *row = reinterpret_cast<const uint4 *>(cent + int64_t(c0) * (d / 2));
+        uint4 cv[MC];
+#pragma unroll
+        for (int m = 0; m < MC; m++) cv[m] = lane + 64 * m < nch ? row[lane + 64 * m] : make_uint4(0, 0, 0, 0);
+        int32_t acc[1] = {0};
+#pragma unroll
+        for (int m = 0; m < MC; m++) {
+            const uint32_t wd[4] = {cv[m].x, cv[m].y, cv[m].z, cv[m].w};
+#pragma unroll
+            for (int w = 0; w < 4; w++) {
+                acc[0] = __builtin_amdgcn_sdot4(int32_t(wd[w] & 0x0F0F0F0Fu), int32_t(xe[m][w]), acc[0], false);
+                acc[0] = __builtin_amdgcn_sdot4(int32_t((wd[w] >> 4) & 0x0F0F0F0Fu), int32_t(xo[m][w]), acc[0], false);
+            }
+        }
+        group_reduce<1>(acc, 64);
+        if (lane == 0) scores[c0] = (float(acc[0] - 8 * sqw[0]) * sh) * cscale[c0];
+    }
+}
+
+// Orderable key of an fp32 score (larger score, larger key; -0 taken as +0, so equal scores give
+// equal keys and the id decides).  Every real key is above 0, the key of the padding.
+__device__ __forceinline__ uint32_t score_key(float s)
+{
+    const uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__global__ __launch_bounds__(1024) void k_head_select(const float *__restrict__ scores, int ncl,
+                                                      int top, int32_t *__restrict__ sel)
+{
+    __shared__ uint32_t s_key[kHeadMaxClusters];
+    __shared__ uint16_t s_id[kHeadMaxClusters];
+    const int t = threadIdx.x;
+    int N = 1;
+    while (N < ncl) N <<= 1;
+    for (int i = t; i < N; i += 1024) {
+        s_key[i] = i < ncl ? score_key(scores[i]) : 0u;
+        s_id[i] = uint16_t(i < ncl ? i : 0xFFFF);
+    }
+    __syncthreads();
+    // bitonic sort, descending by (key, then lower id first)
+    for (int k = 2; k <= N; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = t; i < N; i += 1024) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const uint32_t ki = s_key[i], kl = s_key[l];
+                    const uint16_t ii = s_id[i], il = s_id[l];
+                    const bool l_first = kl > ki || (kl == ki && il < ii);   // l ranks before i
+                    const bool i_first = ki > kl || (ki == kl && ii < il);
+                    if (((i & k) == 0) ? l_first : i_first) {
+                        s_key[i] = kl;
+                        s_key[l] = ki;
+                        s_id[i] = il;
+                        s_id[l] = ii;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int i = t; i < top; i += 1024) sel[i] = int32_t(s_id[i]);
+}
+
+template <int M>   // M = d / 512: 8-input chunks per lane and row
+__global__ __launch_bounds__(256) void k_head_logits(const uint16_t *__restrict__ h, int d,
+                                                     const uint16_t *__restrict__ wc,
+                                                     const int32_t *__restrict__ members, int cs,
+                                                     const int32_t *__restrict__ sel,
+                                                     int32_t *__restrict__ ids,
+                                                     float *__restrict__ logits)
+{
+    constexpr int RB = 16 / M;   // rows per batch, all of a batch's loads in flight together
+    __shared__ float s_h[kHeadMaxD];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int j = blockIdx.x;
+    const int64_t c = sel[j];
+    for (int i = t; i < d; i += 256) s_h[i] = bf16_to_f32(h[i]);
+    __syncthreads();
+    for (int r0 = wave; r0 < cs; r0 += 4 * RB) {
+        uint4 buf[RB][M];
+#pragma unroll
+        for (int b = 0; b < RB; b++) {
+            const int r = r0 + 4 * b;
+            const uint4 *row = reinterpret_cast<const uint4 *>(wc + (c * cs + (r < cs ? r : 0)) * d);
+#pragma unroll
+            for (int m = 0; m < M; m++) buf[b][m] = row[lane + 64 * m];
+        }
+#pragma unroll
+        for (int b = 0; b < RB; b++) {
+            const int r = r0 + 4 * b;
+            float acc = 0.0f;
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+                const uint32_t wd[4] = {buf[b][m].x, buf[b][m].y, buf[b][m].z, buf[b][m].w};
+                const int e0 = 8 * (lane + 64 * m);
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    acc = acc + bf16_to_f32(uint16_t(wd[e >> 1] >> (16 * (e & 1)))) * s_h[e0 + e];
+            }
+            acc = wave_sum(acc);
+            if (lane == 0 && r < cs) {
+                logits[int64_t(j) * cs + r] = acc;
+                ids[int64_t(j) * cs + r] = members[c * cs + r];
+            }
+        }
+    }
+}
+
+}  // namespace
+
+int launch_flash_head(const void *h, int d, const uint8_t *cent, const float *cscale, int ncl,
+                      const void *wc, const int32_t *members, int cs, int top, int32_t *sel,
+                      int32_t *ids, float *logits, void *ws, void *stream)
+{
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    auto hp = static_cast<const uint16_t *>(h);
+    float *scores = static_cast<float *>(ws);
+    const int nb = (ncl + 3) / 4 < 1024 ? (ncl + 3) / 4 : 1024;
+    k_head_score<<<nb, 256, 0, st>>>(hp, d, cent, cscale, ncl, scores);
+    k_head_select<<<1, 1024, 0, st>>>(scores, ncl, top, sel);
+    auto wp = static_cast<const uint16_t *>(wc);
+    switch (d / 512) {
+    case 1: k_head_logits<1><<<top, 256, 0, st>>>(hp, d, wp, members, cs, sel, ids, logits); break;
+    case 2: k_head_logits<2><<<top, 256, 0, st>>>(hp, d, wp, members, cs, sel, ids, logits); break;
+    case 4: k_head_logits<4><<<top, 256, 0, st>>>(hp, d, wp, members, cs, sel, ids, logits); break;
+    case 8: k_head_logits<8><<<top, 256, 0, st>>>(hp, d, wp, members, cs, sel, ids, logits); break;
+    default: return int(hipErrorInvalidValue);
+    }
+    return int(hipGetLastError());
+}
+
+}  // namespace tw

@@ -211,6 +211,52 @@ tw_status attention_decode(const void *q, const void *k_cache, const void *v_cac
                : TW_OK;
 }
 
+size_t flash_head_workspace_bytes(int32_t n_clusters)
+{
+    if (n_clusters < 1 || n_clusters > tw::kHeadMaxClusters) return 0;
+    return tw::head_ws_bytes(n_clusters);
+}
+
+tw_status flash_head(const void *h, int32_t d, const uint8_t *centroids,
+                     const float *centroid_scales, int32_t n_clusters, const void *w_clustered,
+                     const int32_t *member_ids, int32_t cluster_size, int32_t top,
+                     int32_t *sel_clusters, int32_t *token_ids, float *logits, void *workspace,
+                     size_t workspace_bytes, void *stream)
+{
+    if (d < 1 || n_clusters < 1 || n_clusters > tw::kHeadMaxClusters || cluster_size < 1 ||
+        cluster_size > 1024 || top < 1 || top > n_clusters)
+        return TW_E_SHAPE;
+    if (d != 512 && d != 1024 && d != 2048 && d != 4096) return TW_E_UNSUPPORTED;
+    if (!h || !centroids || !centroid_scales || !w_clustered || !member_ids || !sel_clusters ||
+        !token_ids || !logits || !workspace)
+        return TW_E_NULL;
+    if ((((uintptr_t)centroids | (uintptr_t)w_clustered) & 15) || ((uintptr_t)h & 1) ||
+        (((uintptr_t)centroid_scales | (uintptr_t)member_ids | (uintptr_t)sel_clusters |
+          (uintptr_t)token_ids | (uintptr_t)logits) & 3) ||
+        ((uintptr_t)workspace & 255))
+        return TW_E_UNSUPPORTED;
+    const size_t need = tw::head_ws_bytes(n_clusters);
+    if (workspace_bytes < need) return TW_E_WORKSPACE;
+    const size_t nsel = size_t(top) * 4, nout = size_t(top) * cluster_size * 4;
+    const void *ins[5] = {h, centroids, centroid_scales, w_clustered, member_ids};
+    const size_t nin[5] = {size_t(d) * 2, size_t(n_clusters) * d / 2, size_t(n_clusters) * 4,
+                           size_t(n_clusters) * cluster_size * d * 2,
+                           size_t(n_clusters) * cluster_size * 4};
+    const void *outs[4] = {sel_clusters, token_ids, logits, workspace};
+    const size_t nouts[4] = {nsel, nout, nout, need};
+    for (int o = 0; o < 4; o++) {
+        for (int i = 0; i < 5; i++)
+            if (overlap(outs[o], nouts[o], ins[i], nin[i])) return TW_E_ALIAS;
+        for (int p = o + 1; p < 4; p++)
+            if (overlap(outs[o], nouts[o], outs[p], nouts[p])) return TW_E_ALIAS;
+    }
+    return tw::launch_flash_head(h, d, centroids, centroid_scales, n_clusters, w_clustered,
+                                 member_ids, cluster_size, top, sel_clusters, token_ids, logits,
+                                 workspace, stream)
+               ? TW_E_HIP
+               : TW_OK;
+}
+
 tw_status moe_route_topk(const void *x, int32_t x_dtype, const void *w_router, int32_t w_dtype,
                          int64_t n_tokens, int32_t d_model, int32_t n_experts, int32_t top_k,
                          int32_t pre_rmsnorm, float *logits, int32_t *expert_ids, float *gate_w,

@@ -244,3 +244,32 @@ def test_attention_decode_workspace_and_errors(L):
     assert a(A[0], A[1], A[2], 640, 16, 4, 128, A[0], A[4], big, s) == E_ALIAS
     assert a(A[0], A[1], A[2], 640, 16, 4, 128, A[3], A[2] + 1024, big, s) == E_ALIAS   # ws in v
     assert a(A[0], A[1], A[2], 640, 16, 4, 128, A[4] + 512, A[4], big, s) == E_ALIAS    # out in ws
+
+
+def test_flash_head_workspace_and_errors(L):
+    assert L.flash_head_workspace_bytes(4748) == (4748 * 4 + 255) // 256 * 256
+    assert L.flash_head_workspace_bytes(0) == 0 and L.flash_head_workspace_bytes(8193) == 0
+    f = L.flash_head
+    big = 1 << 30
+    ok = [A[0], 2048, A[1], A[2], 4748, A[15], A[4], 32, 512, A[5], A[6], A[7], A[8], big, None]
+
+    def call(**kw):
+        a = list(ok)
+        names = ["h", "d", "cent", "cs_", "ncl", "w", "mem", "csz", "top", "sel", "ids", "lg", "ws",
+                 "wsb", "s"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+    assert call(ncl=0) == E_SHAPE and call(ncl=8193) == E_SHAPE
+    assert call(csz=0) == E_SHAPE and call(csz=1025) == E_SHAPE
+    assert call(top=0) == E_SHAPE and call(top=4749) == E_SHAPE
+    assert call(d=0) == E_SHAPE
+    assert call(d=1536) == E_UNSUP and call(d=8192) == E_UNSUP
+    for k in ["h", "cent", "cs_", "w", "mem", "sel", "ids", "lg", "ws"]:
+        assert call(**{k: None}) == E_NULL, k
+    assert call(cent=A[1] + 8) == E_UNSUP and call(w=A[15] + 8) == E_UNSUP
+    assert call(h=A[0] + 1) == E_UNSUP and call(lg=A[7] + 2) == E_UNSUP and call(ws=A[8] + 64) == E_UNSUP
+    assert call(wsb=L.flash_head_workspace_bytes(4748) - 1) == E_WS
+    assert call(lg=A[15] + 4096) == E_ALIAS       # logits inside the head rows
+    assert call(ids=A[7] + 4) == E_ALIAS          # ids overlapping logits
+    assert call(ws=A[5]) == E_ALIAS               # workspace over sel

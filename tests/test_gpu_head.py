@@ -1,0 +1,91 @@
+"""Approximate output head on the GPU through the C ABI, against the CPU oracle: the selected
+clusters and token ids exactly (the scores are exact integer sums scaled by the same two fp32
+roundings, so both sides rank identically), the logits within a bound derived from fp32 summation:
+|logit - exact| <= 2^-22 * d * sum_i |w_i h_i| (d products, each partial sum rounding at most
+2^-24 relative; the factor 4 covers the lane partials and the wave tree)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import ternary_weight_moe_amd as tw
+from parity_util import require_gpu, step
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def check_logits(f, h, sel, ids, logits, rows=None):
+    w = f["w_clustered"]
+    s = sel.cpu().numpy()
+    lg = logits.cpu().numpy().astype(np.float64)
+    hv = h.float().cpu().numpy().astype(np.float64)
+    d = hv.size
+    idx = [(j, m) for j in range(len(s)) for m in range(lg.shape[1])] if rows is None else rows
+    W = w[torch.as_tensor([s[j] for j, _ in idx], device=w.device),
+          torch.as_tensor([m for _, m in idx], device=w.device)].float().cpu().numpy().astype(np.float64)
+    exact = W @ hv                                  # the oracle's logits are this product (pinned)
+    bound = 2.0 ** -22 * d * (np.abs(W) @ np.abs(hv)) + 1e-30
+    got = np.array([lg[j, m] for j, m in idx])
+    assert np.all(np.abs(got - exact) <= bound), float(np.max(np.abs(got - exact) / bound))
+
+
+@pytest.mark.parametrize("d,ncl,cs,top", [(512, 100, 8, 10), (1024, 37, 3, 37), (2048, 1000, 32, 512),
+                                          (4096, 300, 16, 64), (2048, 1, 32, 1)])
+def test_flash_head_matches_oracle(d, ncl, cs, top):
+    step("flash_head d=%d ncl=%d cs=%d top=%d" % (d, ncl, cs, top))
+    f = synth.head_inputs(ncl, cs, d, "cuda", seed=50 + ncl % 7)
+    h = synth.head_hidden(d, "cuda", seed=50)
+    sel, ids, logits = tw.flash_head(h, f["centroids"], f["centroid_scales"], f["w_clustered"],
+                                     f["member_ids"], top)
+    torch.cuda.synchronize()
+    rsel, rids, rlg, _ = oracle.flash_head(h.float().cpu(), f["centroids"].cpu(),
+                                           f["centroid_scales"].cpu(), f["w_clustered"].float().cpu(),
+                                           f["member_ids"].cpu(), top)
+    assert np.array_equal(sel.cpu().numpy(), rsel)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    bound = 2.0 ** -22 * d * np.abs(f["w_clustered"].float().cpu().numpy()[rsel]) @ np.abs(h.float().cpu().numpy())
+    assert np.all(np.abs(logits.cpu().numpy() - rlg) <= bound + 1e-30)
+
+
+def test_flash_head_ties_go_to_the_lower_cluster():
+    step("flash_head ties")
+    f = synth.head_inputs(64, 4, 512, "cuda", seed=60)
+    f["centroids"][40] = f["centroids"][9]
+    f["centroid_scales"][40] = f["centroid_scales"][9]
+    f["centroids"][9:10] = 0x77              # values -1 everywhere: tie both at a known score
+    f["centroids"][40:41] = 0x77
+    h = synth.head_hidden(512, "cuda", seed=60)
+    sel, ids, logits = tw.flash_head(h, f["centroids"], f["centroid_scales"], f["w_clustered"],
+                                     f["member_ids"], 64)
+    torch.cuda.synchronize()
+    s = sel.cpu().numpy().tolist()
+    assert sorted(s) == list(range(64)) and s.index(9) < s.index(40)
+    rsel = oracle.flash_head(h.float().cpu(), f["centroids"].cpu(), f["centroid_scales"].cpu(),
+                             f["w_clustered"].float().cpu(), f["member_ids"].cpu(), 64)[0]
+    assert np.array_equal(sel.cpu().numpy(), rsel)
+
+
+def test_flash_head_full_size():
+    # the pages' sizes: 151,936 tokens in 4,748 clusters of 32, the top 512; selection checked
+    # against the oracle's scores (cluster rows replaced by one zero row each, which the scores do
+    # not read), logits on sampled rows
+    ncl, cs, d, top = synth.HEAD_CLUSTERS, synth.HEAD_CLUSTER_SIZE, synth.HEAD_D, synth.HEAD_TOP
+    step("flash_head full size")
+    f = synth.head_inputs(ncl, cs, d, "cuda", seed=70)
+    h = synth.head_hidden(d, "cuda", seed=70)
+    sel, ids, logits = tw.flash_head(h, f["centroids"], f["centroid_scales"], f["w_clustered"],
+                                     f["member_ids"], top)
+    torch.cuda.synchronize()
+    rsel = oracle.flash_head(h.float().cpu(), f["centroids"].cpu(), f["centroid_scales"].cpu(),
+                             np.zeros((ncl, 1, d), np.float32), np.zeros((ncl, 1), np.int32), top)[0]
+    assert np.array_equal(sel.cpu().numpy(), rsel)
+    assert np.array_equal(ids.cpu().numpy(), f["member_ids"].cpu().numpy()[rsel])
+    r = np.random.default_rng(5)
+    rows = [(int(j), int(m)) for j, m in zip(r.integers(0, top, 256), r.integers(0, cs, 256))]
+    check_logits(f, h, sel, ids, logits, rows)
