@@ -10,9 +10,10 @@
 //                  offset-binary nibbles (value + 8) of the centroid are masked into int8x4 words
 //                  for v_dot4; the exact sum is corrected by -8 sum(q) and scaled,
 //                  score = (float(acc) * s_h) * scale (two fp32 roundings);
-//   k_head_select  one 1024-thread workgroup: a bitonic sort in LDS of (orderable score key,
-//                  cluster id) pairs, descending by score and ascending by id, then the first
-//                  `top` ids;
+//   k_head_select  one 1024-thread workgroup: the threshold key of the `top`-th cluster by four
+//                  8-bit radix passes (LDS histograms), the clusters above it plus the lowest ids
+//                  at it, then a bitonic sort in LDS of those `top` (orderable score key, cluster
+//                  id) pairs, descending by score and ascending by id;
 //   k_head_logits  one workgroup per selected cluster, four waves; each wave takes rows
 //                  wave, wave + 4, ... of the cluster's cluster-major head rows, all loads of a
 //                  batch of rows issued first, fp32 dot with h (from LDS), wave sum.
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(256) void k_head_score(const uint16_t *__restrict__
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int nch = d / 32;   // 32-input chunks (16 centroid bytes) per row
     const float sh = head_quant_h<256>(h, d, s_q, s_red);
-    // this lane's chunks (at most kHeadMaxD / 32 / 64 = 4): even and odd input words, and sum(q)
+    // this lane's chunks (at most kHeadMaxD / 2048 = 2): even and odd input words, and sum(q)
     constexpr int MC = kHeadMaxD / 32 / 64;
     uint32_t xe[MC][4], xo[MC][4];
     int32_t sq = 0;
@@ -115,17 +116,102 @@ __device__ __forceinline__ uint32_t score_key(float s)
 __global__ __launch_bounds__(1024) void k_head_select(const float *__restrict__ scores, int ncl,
                                                       int top, int32_t *__restrict__ sel)
 {
+    constexpr int PER = kHeadMaxClusters / 1024;
     __shared__ uint32_t s_key[kHeadMaxClusters];
     __shared__ uint16_t s_id[kHeadMaxClusters];
-    const int t = threadIdx.x;
+    __shared__ int s_hist[256];
+    __shared__ int s_wc[16];
+    __shared__ uint32_t s_prefix;
+    __shared__ int s_above, s_cnt;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    uint32_t key[PER];
+#pragma unroll
+    for (int m = 0; m < PER; m++) {
+        const int i = t + 1024 * m;
+        key[m] = i < ncl ? score_key(scores[i]) : 0u;
+    }
+    // 1. the threshold key T (count(key > T) < top <= count(key >= T)) by four 8-bit radix passes
+    //    from the top byte down; `above` counts the keys above the current bucket
+    uint32_t prefix = 0, mask = 0;
+    int above = 0;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        if (t < 256) s_hist[t] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < PER; m++)
+            if (t + 1024 * m < ncl && (key[m] & mask) == prefix) atomicAdd(&s_hist[(key[m] >> shift) & 255], 1);
+        __syncthreads();
+        if (wave == 0) {
+            // lane l holds bins 255 - 4l .. 252 - 4l; counts accumulate from the highest bin down
+            int c[4], tot = 0;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                c[q] = s_hist[255 - 4 * lane - q];
+                tot += c[q];
+            }
+            int inc = tot;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int v = __shfl_up(inc, off);
+                if (lane >= off) inc += v;
+            }
+            int run = above + inc - tot, found = -1, found_above = 0;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                if (found < 0 && run + c[q] >= top) {
+                    found = 255 - 4 * lane - q;
+                    found_above = run;
+                }
+                run += c[q];
+            }
+            const uint64_t bal = __ballot(found >= 0);
+            if (lane == __ffsll((unsigned long long)bal) - 1) {
+                s_prefix = prefix | (uint32_t(found) << shift);
+                s_above = found_above;
+            }
+        }
+        __syncthreads();
+        prefix = s_prefix;
+        above = s_above;
+        mask |= 255u << shift;
+        __syncthreads();
+    }
+    // 2. the selected clusters: every key above T, and the (top - above) lowest ids with key T
+    //    (ranked in id order, 1024 ids at a time), collected in LDS in any order
+    const int need = top - above;
+    if (t == 0) s_cnt = 0;
+    int eq_before = 0;
+    for (int m = 0; m < PER; m++) {
+        const int i = t + 1024 * m;
+        const bool valid = i < ncl;
+        const bool gt = valid && key[m] > prefix, eq = valid && key[m] == prefix;
+        const uint64_t b = __ballot(eq);
+        const int r = __popcll(b & ((uint64_t(1) << lane) - 1));
+        if (lane == 0) s_wc[wave] = __popcll(b);
+        __syncthreads();
+        int before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < 16; w++) {
+            before += w < wave ? s_wc[w] : 0;
+            total += s_wc[w];
+        }
+        if (gt || (eq && eq_before + before + r < need)) {
+            const int pos = atomicAdd(&s_cnt, 1);
+            s_key[pos] = key[m];
+            s_id[pos] = uint16_t(i);
+        }
+        eq_before += total;
+        __syncthreads();
+    }
+    // 3. bitonic sort of the `top` selected (padded to a power of two), descending by key, then
+    //    lower id first
     int N = 1;
-    while (N < ncl) N <<= 1;
-    for (int i = t; i < N; i += 1024) {
-        s_key[i] = i < ncl ? score_key(scores[i]) : 0u;
-        s_id[i] = uint16_t(i < ncl ? i : 0xFFFF);
+    while (N < top) N <<= 1;
+    for (int i = top + t; i < N; i += 1024) {
+        s_key[i] = 0u;
+        s_id[i] = 0xFFFF;
     }
     __syncthreads();
-    // bitonic sort, descending by (key, then lower id first)
     for (int k = 2; k <= N; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
             for (int i = t; i < N; i += 1024) {
