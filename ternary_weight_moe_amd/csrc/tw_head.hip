@@ -120,7 +120,7 @@ __global__ __launch_bounds__(1024) void k_head_select(const float *__restrict__ 
     __shared__ uint32_t s_key[kHeadMaxClusters];
     __shared__ uint16_t s_id[kHeadMaxClusters];
     __shared__ int s_hist[256];
-    __shared__ int s_wc[16];
+    __shared__ int s_wc[kHeadMaxClusters / 1024][16];
     __shared__ uint32_t s_prefix;
     __shared__ int s_above, s_cnt;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -177,36 +177,75 @@ __global__ __launch_bounds__(1024) void k_head_select(const float *__restrict__ 
         __syncthreads();
     }
     // 2. the selected clusters: every key above T, and the (top - above) lowest ids with key T
-    //    (ranked in id order, 1024 ids at a time), collected in LDS in any order
+    //    (ranked in id order: row m of 1024 ids before row m + 1, waves in order inside a row),
+    //    collected in LDS in any order; one barrier for the per-wave counts of all rows
     const int need = top - above;
     if (t == 0) s_cnt = 0;
+    uint64_t eqb[PER];
+#pragma unroll
+    for (int m = 0; m < PER; m++) {
+        const int i = t + 1024 * m;
+        eqb[m] = __ballot(i < ncl && key[m] == prefix);
+        if (lane == 0) s_wc[m][wave] = __popcll(eqb[m]);
+    }
+    __syncthreads();
     int eq_before = 0;
+#pragma unroll
     for (int m = 0; m < PER; m++) {
         const int i = t + 1024 * m;
         const bool valid = i < ncl;
         const bool gt = valid && key[m] > prefix, eq = valid && key[m] == prefix;
-        const uint64_t b = __ballot(eq);
-        const int r = __popcll(b & ((uint64_t(1) << lane) - 1));
-        if (lane == 0) s_wc[wave] = __popcll(b);
-        __syncthreads();
         int before = 0, total = 0;
 #pragma unroll
         for (int w = 0; w < 16; w++) {
-            before += w < wave ? s_wc[w] : 0;
-            total += s_wc[w];
+            before += w < wave ? s_wc[m][w] : 0;
+            total += s_wc[m][w];
         }
+        const int r = __popcll(eqb[m] & ((uint64_t(1) << lane) - 1));
         if (gt || (eq && eq_before + before + r < need)) {
             const int pos = atomicAdd(&s_cnt, 1);
             s_key[pos] = key[m];
             s_id[pos] = uint16_t(i);
         }
         eq_before += total;
-        __syncthreads();
     }
-    // 3. bitonic sort of the `top` selected (padded to a power of two), descending by key, then
-    //    lower id first
+    __syncthreads();
+    // 3. bitonic sort of the `top` selected (padded to a power of two N), descending by key, then
+    //    lower id first.  Up to 1024 of them: one per thread in registers, partners at distance
+    //    below 64 exchanged by lane shuffles, farther ones through LDS (5 barrier stages for 512);
+    //    more than 1024: the same network entirely in LDS.
     int N = 1;
     while (N < top) N <<= 1;
+    if (N <= 1024) {
+        uint32_t kk = t < top ? s_key[t] : 0u;
+        uint32_t ii = t < top ? uint32_t(s_id[t]) : 0xFFFFu;
+        for (int k = 2; k <= N; k <<= 1) {
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                uint32_t kp, ip;
+                if (j >= 64) {
+                    __syncthreads();   // every read of the previous exchange is done
+                    if (t < N) {
+                        s_key[t] = kk;
+                        s_id[t] = uint16_t(ii);
+                    }
+                    __syncthreads();
+                    kp = t < N ? s_key[t ^ j] : 0u;
+                    ip = t < N ? uint32_t(s_id[t ^ j]) : 0xFFFFu;
+                } else {
+                    kp = uint32_t(__shfl_xor(int(kk), j));
+                    ip = uint32_t(__shfl_xor(int(ii), j));
+                }
+                const bool mine_first = kk > kp || (kk == kp && ii < ip);
+                const bool keep_first = ((t & j) == 0) == ((t & k) == 0);
+                if (keep_first != mine_first) {
+                    kk = kp;
+                    ii = ip;
+                }
+            }
+        }
+        if (t < top) sel[t] = int32_t(ii);
+        return;
+    }
     for (int i = top + t; i < N; i += 1024) {
         s_key[i] = 0u;
         s_id[i] = 0xFFFF;

@@ -36,7 +36,8 @@ def check_logits(f, h, sel, ids, logits, rows=None):
 
 
 @pytest.mark.parametrize("d,ncl,cs,top", [(512, 100, 8, 10), (1024, 37, 3, 37), (2048, 1000, 32, 512),
-                                          (4096, 300, 16, 64), (2048, 1, 32, 1)])
+                                          (4096, 300, 16, 64), (2048, 1, 32, 1), (512, 1500, 2, 1024),
+                                          (512, 3000, 2, 2000), (512, 8192, 1, 8192)])
 def test_flash_head_matches_oracle(d, ncl, cs, top):
     step("flash_head d=%d ncl=%d cs=%d top=%d" % (d, ncl, cs, top))
     f = synth.head_inputs(ncl, cs, d, "cuda", seed=50 + ncl % 7)
