@@ -10,8 +10,8 @@
 //                  offset-binary nibbles (value + 8) of the centroid are masked into int8x4 words
 //                  for v_dot4; the exact sum is corrected by -8 sum(q) and scaled,
 //                  score = (float(acc) * s_h) * scale (two fp32 roundings);
-//   k_head_select  one 1024-thread workgroup: the threshold key of the `top`-th cluster by four
-//                  8-bit radix passes (LDS histograms), the clusters above it plus the lowest ids
+//   k_head_select  one 1024-thread workgroup: the threshold key of the `top`-th cluster by three
+//                  radix passes of 11, 11 and 10 bits (LDS histograms), the clusters above it plus the lowest ids
 //                  at it, then a bitonic sort in LDS of those `top` (orderable score key, cluster
 //                  id) pairs, descending by score and ascending by id;
 //   k_head_logits  one workgroup per selected cluster, four waves; each wave takes rows
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(1024) void k_head_select(const float *__restrict__ 
     constexpr int PER = kHeadMaxClusters / 1024;
     __shared__ uint32_t s_key[kHeadMaxClusters];
     __shared__ uint16_t s_id[kHeadMaxClusters];
-    __shared__ int s_hist[256];
+    __shared__ int s_hist[2048];
     __shared__ int s_wc[kHeadMaxClusters / 1024][16];
     __shared__ uint32_t s_prefix;
     __shared__ int s_above, s_cnt;
@@ -130,25 +130,25 @@ __global__ __launch_bounds__(1024) void k_head_select(const float *__restrict__ 
         const int i = t + 1024 * m;
         key[m] = i < ncl ? score_key(scores[i]) : 0u;
     }
-    // 1. the threshold key T (count(key > T) < top <= count(key >= T)) by four 8-bit radix passes
-    //    from the top byte down; `above` counts the keys above the current bucket
+    // 1. the threshold key T (count(key > T) < top <= count(key >= T)) by three radix passes of
+    //    11, 11 and 10 bits from the top down; `above` counts the keys above the current bucket
     uint32_t prefix = 0, mask = 0;
     int above = 0;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        if (t < 256) s_hist[t] = 0;
+#pragma unroll
+    for (int pass = 0; pass < 3; pass++) {
+        const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0, bits = pass == 2 ? 10 : 11;
+        const int nbins = 1 << bits, per = nbins / 64;
+        for (int i = t; i < nbins; i += 1024) s_hist[i] = 0;
         __syncthreads();
 #pragma unroll
         for (int m = 0; m < PER; m++)
-            if (t + 1024 * m < ncl && (key[m] & mask) == prefix) atomicAdd(&s_hist[(key[m] >> shift) & 255], 1);
+            if (t + 1024 * m < ncl && (key[m] & mask) == prefix)
+                atomicAdd(&s_hist[(key[m] >> shift) & uint32_t(nbins - 1)], 1);
         __syncthreads();
         if (wave == 0) {
-            // lane l holds bins 255 - 4l .. 252 - 4l; counts accumulate from the highest bin down
-            int c[4], tot = 0;
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                c[q] = s_hist[255 - 4 * lane - q];
-                tot += c[q];
-            }
+            // lane l holds bins nbins-1-per*l .. down; counts accumulate from the highest bin down
+            int tot = 0;
+            for (int q = 0; q < per; q++) tot += s_hist[nbins - 1 - per * lane - q];
             int inc = tot;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
@@ -156,13 +156,13 @@ __global__ __launch_bounds__(1024) void k_head_select(const float *__restrict__ 
                 if (lane >= off) inc += v;
             }
             int run = above + inc - tot, found = -1, found_above = 0;
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                if (found < 0 && run + c[q] >= top) {
-                    found = 255 - 4 * lane - q;
+            for (int q = 0; q < per; q++) {
+                const int c = s_hist[nbins - 1 - per * lane - q];
+                if (found < 0 && run + c >= top) {
+                    found = nbins - 1 - per * lane - q;
                     found_above = run;
                 }
-                run += c[q];
+                run += c;
             }
             const uint64_t bal = __ballot(found >= 0);
             if (lane == __ffsll((unsigned long long)bal) - 1) {
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(1024) void k_head_select(const float *__restrict__ 
         __syncthreads();
         prefix = s_prefix;
         above = s_above;
-        mask |= 255u << shift;
+        mask |= uint32_t(nbins - 1) << shift;
         __syncthreads();
     }
     // 2. the selected clusters: every key above T, and the (top - above) lowest ids with key T
