@@ -598,39 +598,18 @@ void or_ffn_batch_i8(const or_layer_i8 *L, const float *x, int64_t n_tokens, con
  * is the per-row absmean rule: g = mean_i |w_i| over the row, t_i = clamp(rint(w_i / g), -1, 1)
  * (rint: to nearest, ties to even), and g is the row's scale, so that g * t approximates w.  A row
  * of zeros gives t = 0 and g = 0.
- * Because g decides integer codes, the sum of |w_i| is taken in one fixed fp32 order: the row is
- * cut into 8-element chunks; partial p (p < 256) adds, in increasing order, the elements of chunks
- * p, p + 256, p + 512, ... (elements of a chunk in order), starting from 0; partials 64m .. 64m+63
- * are added by a balanced pairwise tree (neighbours first) into s_m; the sum is (s_0 + s_1) +
- * (s_2 + s_3).  g = sum / cols and q_i = w_i / g are single fp32 divisions.  cols must be a
- * multiple of 8.  Returns 0, or -1 when cols is not a multiple of 8. */
-
-static float pairwise_tree64(const float *v)
-{
-    float t[64];
-    for (int i = 0; i < 64; i++) t[i] = v[i];
-    for (int n = 64; n > 1; n /= 2)
-        for (int i = 0; i < n / 2; i++) t[i] = t[2 * i] + t[2 * i + 1];
-    return t[0];
-}
+ * The mean is the plain one: |w_i| summed in double (each fp32 value is exact in double), divided
+ * by cols in double and rounded once to fp32; q_i = w_i / g is one fp32 division.  No summation
+ * order is implied by the pages, so none is imitated here. */
 
 int or_quantize_absmean(const float *w, int64_t rows, int64_t cols, int8_t *t, float *scale)
 {
-    if (cols % 8 != 0) return -1;
-    int64_t nch = cols / 8;
+    if (cols <= 0) return cols == 0 ? 0 : -1;
     for (int64_t r = 0; r < rows; r++) {
         const float *row = w + r * cols;
-        float part[256];
-        for (int p = 0; p < 256; p++) {
-            float acc = 0.0f;
-            for (int64_t c = p; c < nch; c += 256)
-                for (int j = 0; j < 8; j++) acc = acc + fabsf(row[8 * c + j]);
-            part[p] = acc;
-        }
-        float s0 = pairwise_tree64(part), s1 = pairwise_tree64(part + 64);
-        float s2 = pairwise_tree64(part + 128), s3 = pairwise_tree64(part + 192);
-        float sum = (s0 + s1) + (s2 + s3);
-        float g = sum / (float)cols;
+        double sum = 0.0;
+        for (int64_t i = 0; i < cols; i++) sum += fabs((double)row[i]);
+        float g = (float)(sum / (double)cols);
         int8_t *tr = t + r * cols;
         if (g == 0.0f) {
             for (int64_t i = 0; i < cols; i++) tr[i] = 0;

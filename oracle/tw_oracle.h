@@ -151,8 +151,8 @@ void or_dense_ffn_token(const or_layer *L, const double *x, const int32_t *ids,
                         const double *gates, double *out);
 
 /* ---- float -> ternary quantisation ----------------------------------------------------------
- * Per row: g = mean |w| (fp32, in the fixed order given in tw_oracle.c), t = clamp(rint(w / g),
- * -1, 1), scale = g; zero rows give t = 0, g = 0.  cols must be a multiple of 8 (else -1). */
+ * Per row: g = mean |w| (summed in double, rounded once to fp32), t = clamp(rint(w / g), -1, 1)
+ * with one fp32 division, scale = g; zero rows give t = 0, g = 0.  Returns 0 (-1 if cols < 0). */
 int or_quantize_absmean(const float *w, int64_t rows, int64_t cols, int8_t *t, float *scale);
 
 /* ---- int8 spec mode ----------------------------------------------------------------------- */

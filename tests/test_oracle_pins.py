@@ -319,14 +319,45 @@ def test_bf16_rounding_matches_library_on_fp32_values_and_avoids_double_rounding
 
 # ---- int8 spec mode ---------------------------------------------------------------------------------
 
-def test_spec_exp_accuracy_and_special_values():
-    z = np.linspace(-80, 80, 20001).astype(np.float32)
-    e = oracle.spec_expf(z).astype(np.float64)
-    ref = np.exp(z.astype(np.float64))
+def _exp_ulp_error(e, z):
+    """Largest error of fp32 results e against the exponential of the fp32 arguments z, in units
+    of the fp32 spacing at the exact value."""
+    ref = np.exp(np.asarray(z, np.float64))
     ulp = np.spacing(ref.astype(np.float32)).astype(np.float64)
-    assert np.max(np.abs(e - ref) / ulp) < 3.0
+    return float(np.max(np.abs(np.asarray(e, np.float64) - ref) / ulp))
+
+
+def _degree6_expf(z):
+    """A planted mistake, for the pin below to reject: the spec exp's steps with the r^7 term of
+    the Taylor polynomial dropped (numpy fp32 operations, one rounding each)."""
+    f = np.float32
+    z = np.asarray(z, f)
+    n = np.rint(z * f(1.4426950408889634))
+    r = (z - n * f(0.693145751953125)) - n * f(0.6931471805599453 - 0.693145751953125)
+    p = f(1.0 / 720.0)
+    for c in (1.0 / 120.0, 1.0 / 24.0, 1.0 / 6.0, 0.5, 1.0, 1.0):
+        p = p * r + f(c)
+    return np.ldexp(p, n.astype(np.int32)).astype(f)
+
+
+def test_spec_exp_accuracy_and_special_values():
+    # a degree-7 Taylor polynomial after Cody-Waite reduction to |r| <= ln2/2 is within about one
+    # ulp of e^z; 1.5 ulp is the pin.  Dropping the r^7 term (the planted variant) gives ~2.9 ulp
+    # on this grid, so a lost Taylor term fails here.
+    z = np.linspace(-80, 80, 200001).astype(np.float32)
+    e = oracle.spec_expf(z).astype(np.float64)
+    assert _exp_ulp_error(e, z) <= 1.5
+    assert _exp_ulp_error(_degree6_expf(z), z) > 1.5
     assert oracle.spec_expf([0.0])[0] == 1.0
     assert np.all(np.diff(e) >= 0)
+    # the reading's cutoffs: arguments above 80 give +inf, below -80 give 0 (no subnormal result);
+    # 80 and -80 themselves are in range
+    up = np.nextafter(np.float32(80), np.float32(np.inf))
+    dn = np.nextafter(np.float32(-80), np.float32(-np.inf))
+    big, small = oracle.spec_expf([80.0, -80.0])
+    assert np.isfinite(big) and math.isclose(float(big), math.exp(80.0), rel_tol=2e-7)
+    assert small > 0 and math.isclose(float(small), math.exp(-80.0), rel_tol=2e-7)
+    assert oracle.spec_expf([up])[0] == np.inf and oracle.spec_expf([dn])[0] == 0.0
     assert oracle.spec_expf([81.0])[0] == np.inf and oracle.spec_expf([-81.0])[0] == 0.0
     for n in range(-100, 101, 7):
         zf = np.float32(n * math.log(2))              # the argument itself is rounded to fp32
@@ -462,21 +493,40 @@ def test_quantize_threshold_and_ties_to_even():
     assert s.tolist() == [14.0, 14.0, 3.734375, 3.71875, 3.5, 3.5]
 
 
-def test_quantize_scale_is_the_mean_magnitude():
-    # against the fp64 mean: the fp32 sum of n terms is within n * 2^-24 relative of it
+def test_quantize_scale_is_the_correctly_rounded_mean_magnitude():
+    # the exact mean of |w| (rational arithmetic) rounded once to fp32: the scale is within half an
+    # fp32 ulp of it (a slack of 2^-28 ulp covers the double-precision sum)
+    from fractions import Fraction
     w = (rng.normal(0, 0.02, (16, 2048))).astype(np.float32)
+    w[3] *= 1e-20
     _, s = oracle.quantize_absmean(w)
-    ref = np.mean(np.abs(w.astype(np.float64)), axis=1)
-    assert np.all(np.abs(s - ref) <= ref * 2048 * 2.0 ** -24)
+    for r in range(w.shape[0]):
+        exact = sum((Fraction(float(v)) for v in np.abs(w[r])), Fraction(0)) / w.shape[1]
+        err = abs(Fraction(float(s[r])) - exact)
+        half_ulp = Fraction(float(np.spacing(np.float32(float(exact))))) / 2
+        assert err <= half_ulp * (1 + Fraction(1, 2 ** 28)), r
 
 
-def test_quantize_rejects_ragged_rows():
-    with pytest.raises(ValueError):
-        oracle.quantize_absmean(np.ones((1, 12), np.float32))
+def test_quantize_is_independent_of_column_order():
+    # a mean has no order: permuting a row's weights permutes its codes and keeps its scale
+    w = (rng.normal(0, 0.02, (8, 2048))).astype(np.float32)
+    perm = rng.permutation(2048)
+    t, s = oracle.quantize_absmean(w)
+    tp, sp = oracle.quantize_absmean(w[:, perm])
+    assert np.array_equal(s, sp) and np.array_equal(tp, t[:, perm])
+
+
+def test_quantize_rows_of_any_length():
+    # rows that are not a multiple of 8: three weights 3, -1, 0.5 -> g = 1.5; 3/1.5 = 2 -> 1,
+    # -1/1.5 -> -0.67 -> -1, 0.5/1.5 = 0.33 -> 0; an empty row set is a no-op
+    t, s = oracle.quantize_absmean(np.array([[3.0, -1.0, 0.5]], np.float32))
+    assert t.tolist() == [[1, -1, 0]] and s.tolist() == [1.5]
+    t, s = oracle.quantize_absmean(np.zeros((0, 5), np.float32))
+    assert t.shape == (0, 5) and s.shape == (0,)
 
 
 def test_quantize_neighbours_of_the_half_scale():
-    # seven 15s and v = 7 (1 ulp up/down): the fp32 sum 105 + v rounds to 112 either way, g = 14,
+    # seven 15s and v = 7 (1 ulp up/down): the mean (105 + v) / 8 rounds to 14 either way, g = 14,
     # and v / g rounds above 1/2 (code 1) for the next float above 7, to 1/2 exactly (code 0, ties
     # to even) for 7, below 1/2 (code 0) for the float below 7
     up, dn = np.nextafter(np.float32(7), np.float32(8)), np.nextafter(np.float32(7), np.float32(6))
