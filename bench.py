@@ -3,8 +3,11 @@
 
 Default workload (stack24_b1): batch-1 decode through 24 stacked ternary MoE FFN layers
 (d_model 2048, 256 experts, expert width 512, top-8, pre-RMSNorm, residual between layers,
-attention replaced by identity), steps chained (step t+1 decodes step t's output), captured as a
-hipGraph of 256 consecutive steps and replayed.  A step is one token through all 24 layers.
+attention replaced by identity), steps chained (step t+1 decodes step t's output).  A step is one
+token through all 24 layers.  Graphs of min(--steps, 256) consecutive steps are captured and
+replayed at least 20 times in the timed region (each replay a sample; the steps actually timed are
+reported).  The decode health word is checked after the timed replays, and one more replay must
+equal the same steps run eagerly from the same state, bit for bit.
 
 Prints ONE JSON line: tokens/s of the whole job, the roofline view of the step (algorithmic HBM
 bytes per step / measured time per step against the 8 TB/s HBM peak) and the CPU oracle's rate on a
@@ -73,9 +76,8 @@ def build_layer(wl, l, device="cuda", keep_cpu=False, pre=None):
     return layer, cpu
 
 
-def time_graph(step_fn, n_graph, warmup, steps):
-    """Captures n_graph consecutive steps in one graph; replays warmup/n_graph times untimed and
-    steps/n_graph times timed.  Returns (total seconds, per-replay seconds list)."""
+def side_warmup(step_fn):
+    """Two eager steps on a side stream (warms up the allocator and the library before capture)."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -83,41 +85,116 @@ def time_graph(step_fn, n_graph, warmup, steps):
             step_fn(t)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
+
+
+def capture(step_fn, n_graph, first=0):
+    """Captures steps first .. first + n_graph - 1 as one graph (after two eager warm-up steps)."""
+    side_warmup(step_fn)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for t in range(n_graph):
+        for t in range(first, first + n_graph):
             step_fn(t)
     torch.cuda.synchronize()
+    return g
+
+
+class Replayer:
+    """Graphs of n_graph consecutive steps, replayed in order.  Steps alternate between two
+    buffers by the parity of their index, so for an odd n_graph two graphs (steps 0 .. n-1 and
+    n .. 2n-1) alternate and the chain stays serial: step t + 1 always reads step t's output."""
+
+    def __init__(self, step_fn, n_graph):
+        self.n = n_graph
+        self.graphs = [capture(step_fn, n_graph)]
+        if n_graph % 2:
+            self.graphs.append(capture(step_fn, n_graph, first=n_graph))
+        self.done = 0   # replays so far
+
+    def replay(self):
+        self.graphs[self.done % len(self.graphs)].replay()
+        self.done += 1
+
+    def next_first_step(self):
+        """Index (mod 2 significant) of the first step of the next replay."""
+        return self.done * self.n
+
+
+def time_graph(step_fn, n_graph, warmup, steps, rep=None):
+    """Replays graphs of n_graph consecutive steps for about `warmup` steps untimed, then
+    steps/n_graph times timed, HIP events between replays on the replay stream.  Returns
+    (total seconds, per-replay seconds list, the Replayer)."""
+    rep = rep if rep is not None else Replayer(step_fn, n_graph)
     for _ in range(max(1, warmup // n_graph)):
-        g.replay()
+        rep.replay()
     torch.cuda.synchronize()
     reps = steps // n_graph
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     torch.cuda.synchronize()
     ev[0].record()
     for r in range(reps):
-        g.replay()
+        rep.replay()
         ev[r + 1].record()
     torch.cuda.synchronize()
     per = [ev[r].elapsed_time(ev[r + 1]) / 1e3 for r in range(reps)]
-    return ev[0].elapsed_time(ev[reps]) / 1e3, per
+    return ev[0].elapsed_time(ev[reps]) / 1e3, per, rep
+
+
+def cpu_info():
+    """(CPU model name, threads this process may use) of the host the bench runs on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return model, n
+
+
+def baseline(v1, s1, vn, sn, n, unit):
+    """cpu_baseline object: the oracle on all usable cores (value, cores) with the one-core run
+    beside it, and the host's CPU model."""
+    model, _ = cpu_info()
+    return dict(value=vn, unit=unit, cores=n, kind="oracle", sample=sn, cpu_model=model,
+                one_core=dict(value=v1, unit=unit, cores=1, sample=s1))
 
 
 def cpu_baseline_stack(cpu_layers, wl, n_tokens):
+    """The oracle (fp64 truth mode) through the first layers of the stack: one thread on n_tokens
+    chained tokens, and all usable cores on independent sequences (one token each per layer call,
+    outputs rounded to bf16 between layers as in the stack)."""
     import oracle
     ors = [oracle.Layer(c["w_router"], c["t_gate"], c["t_up"], c["t_down"], c["s_gate"],
                         c["s_up"], c["s_down"], pre_rmsnorm=wl.pre_rmsnorm, top_k=wl.top_k)
            for c in cpu_layers]
+    scale = wl.n_layers / len(ors)
     x = synth.activations(wl, n_tokens, seed=4242)
     t0 = time.perf_counter()
     for t in range(n_tokens):
         oracle.decode_stack(ors, x[t].double().numpy(), 1)
-    dt = time.perf_counter() - t0
-    per_token_full = dt / n_tokens * wl.n_layers / len(ors)
-    return dict(value=1.0 / per_token_full, unit="tok/s", cores=1, kind="oracle",
-                sample="%d tokens through %d of the %d layers (fp64 truth mode, one thread), "
-                       "%.1f s; rate scaled to %d layers" % (n_tokens, len(ors), wl.n_layers, dt,
-                                                             wl.n_layers))
+    dt1 = time.perf_counter() - t0
+    _, n = cpu_info()
+    T = 4 * n
+    xs = synth.activations(wl, T, seed=4243).double().numpy()
+    t0 = time.perf_counter()
+    cur = xs
+    for layer in ors:
+        out, _, _, _ = oracle.moe_layer(layer, cur, n_threads=n)
+        cur = oracle.round_bf16(out)
+    dtn = time.perf_counter() - t0
+    return baseline(
+        n_tokens / (dt1 * scale),
+        "%d chained tokens through %d of the %d layers, one thread, %.1f s; rate scaled to %d layers"
+        % (n_tokens, len(ors), wl.n_layers, dt1, wl.n_layers),
+        T / (dtn * scale),
+        "%d independent sequences, one step through %d of the %d layers, %d threads, %.1f s; rate "
+        "scaled to %d layers" % (T, len(ors), wl.n_layers, n, dtn, wl.n_layers),
+        n, "tok/s")
 
 
 def run_stack(args):
@@ -138,8 +215,36 @@ def run_stack(args):
     def step(t):
         tw.ternary_moe_ffn_decode(layers, bufs[t % 2], out=bufs[(t + 1) % 2], workspace=ws)
 
-    G = args.graph_steps
-    total, per = time_graph(step, G, args.warmup, args.steps)
+    # graphs of G = min(--steps, 256) consecutive steps, replayed at least 20 times in the timed
+    # region (every replay is a sample); the steps actually timed are reported
+    G = min(args.steps, args.graph_steps)
+    reps = max(20, -(-args.steps // G))
+    steps = reps * G
+    total, per, rep = time_graph(step, G, args.warmup, steps)
+    # the health word after the timed replays: a hand-off wait that ran out would have ended a
+    # launch early (and made it look fast)
+    health = tw.decode_error_flag(layers, ws)
+    if health != 0:
+        log("stack24_b1: decode health word %#x after the timed replays" % health)
+        sys.exit(3)
+    # one more replay against the same G steps run eagerly from the same state, bit for bit
+    first = rep.next_first_step()
+    src, dst = bufs[first % 2], bufs[(first + G) % 2]
+    start = src.clone()
+    rep.replay()
+    torch.cuda.synchronize()
+    replayed = dst.clone()
+    health = tw.decode_error_flag(layers, ws)
+    src.copy_(start)
+    for t in range(first, first + G):
+        step(t)
+    torch.cuda.synchronize()
+    if health != 0 or tw.decode_error_flag(layers, ws) != 0 or \
+            not torch.equal(replayed.view(torch.int16), dst.view(torch.int16)):
+        log("stack24_b1: graph replay differs from the eager chain of the same %d steps" % G)
+        sys.exit(3)
+    requested = args.steps
+    args.steps = steps
     ms_per_step = total / args.steps * 1e3
     bytes_per_step = accounting.stack_bytes_per_token(wl)
     tok_s = args.steps / total
@@ -153,18 +258,23 @@ def run_stack(args):
     return dict(
         metric=METRIC, value=tok_s, unit="tok/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=ms_per_step, higher_is_better=True, scaling="weak",
-        vs_baseline=None, dtype="int8xint8->int32, fp32 (bf16 I/O)", data="synthetic",
+        vs_baseline=None,
+        dtype="int8 digit planes x ternary -> exact int32 sums (activations kept to 14 bits below "
+              "their max |x|), fp32 scales/SiLU/gates/combine, bf16 I/O",
+        data="synthetic",
         config=dict(workload="stack24_b1", layers=wl.n_layers, d_model=wl.d_model,
                     n_experts=wl.n_experts, d_ff=wl.d_ff, top_k=wl.top_k, batch=1,
-                    graph_steps=G, bytes_per_token=bytes_per_step,
+                    graph_steps=G, replays=len(per), requested_steps=requested,
+                    bytes_per_token=bytes_per_step,
                     us_per_token_median=per_tok_us[len(per_tok_us) // 2],
                     us_per_token_min=per_tok_us[0],
-                    us_per_token_p90=per_tok_us[int(0.9 * (len(per_tok_us) - 1))]),
+                    us_per_token_p90=per_tok_us[int(0.9 * (len(per_tok_us) - 1))],
+                    health_word=0, replay_equals_eager=True),
         roofline=dict(bound="hbm", achieved=achieved, peak=accounting.HBM_PEAK_BPS / 1e9,
                       unit="GB/s", frac=achieved * 1e9 / accounting.HBM_PEAK_BPS,
                       traffic=traffic,
                       kernel="k_persist<2048,512,8>: one launch per step runs all 24 layers "
-                             "(plus its 2 us word-clearing kernel)",
+                             "(timed with the small word-clearing kernel launched before it)",
                       bytes_per_launch=bytes_per_step,
                       us_per_launch=total / args.steps * 1e6),
         cpu_baseline=cpu,
@@ -176,10 +286,11 @@ def run_single_layer(args, name):
     n_copies = 8
     T = wl.batch
     act = wl.act
-    layers = []
+    layers, cpu0 = [], None
     for c in range(n_copies):
-        layer, _ = build_layer(wl, c)
+        layer, cpu = build_layer(wl, c, keep_cpu=(c == 0 and not args.no_cpu_baseline))
         layers.append(layer)
+        cpu0 = cpu0 if cpu is None else cpu
     xs = [synth.activations(wl, T, device="cuda", stream=c) for c in range(n_copies)]
     outs = [torch.empty((T, wl.d_model), dtype=torch.bfloat16 if wl.out_dtype == "bf16"
                         else torch.float32, device="cuda") for _ in range(n_copies)]
@@ -206,7 +317,9 @@ def run_single_layer(args, name):
                                        expert_ids=routing[c][0], gate_w=routing[c][1])
 
     G = args.graph_steps
-    total, per = time_graph(step, G, args.warmup, args.steps)
+    steps = max(1, round(args.steps / G)) * G   # whole replays; every replay rotates all copies
+    total, per, _ = time_graph(step, G, args.warmup, steps)
+    args.steps = steps
     bytes_per_step = sum(accounting.layer_bytes(wl, T, distinct[t % n_copies])
                          for t in range(G)) / G
     achieved = bytes_per_step / (total / args.steps) / 1e9
@@ -229,8 +342,37 @@ def run_single_layer(args, name):
         config=dict(workload=name, batch=T, act=act, layer_copies=n_copies,
                     distinct_experts=distinct, bytes_per_step=bytes_per_step),
         roofline=roof,
-        cpu_baseline=None,
+        cpu_baseline=cpu_baseline_layer(cpu0, wl, name) if cpu0 is not None else None,
     )
+
+
+def cpu_baseline_layer(cpu, wl, name):
+    """The oracle on a bounded sample of one single-layer workload: truth mode (fp64) for the
+    float paths, the int8 spec mode (routing from the oracle's own router) for int8 activations;
+    one thread on a few tokens, and all usable cores on more."""
+    import oracle
+    lay = oracle.Layer(cpu["w_router"], cpu["t_gate"], cpu["t_up"], cpu["t_down"], cpu["s_gate"],
+                       cpu["s_up"], cpu["s_down"], pre_rmsnorm=wl.pre_rmsnorm, top_k=wl.top_k)
+    _, n = cpu_info()
+    int8 = wl.act == "int8"
+    n1 = 8 if wl.batch > 1 else 4
+    nn = min(wl.batch, 32 * n) if int8 else max(wl.batch, 8 * n)
+
+    def run(T, threads):
+        x = synth.activations(wl, T, seed=4244).double().numpy()
+        t0 = time.perf_counter()
+        if int8:
+            ids, g, _ = oracle.route(lay, x, n_threads=threads)
+            oracle.ffn_batch_i8(lay, x.astype("float32"), ids, g.astype("float32"), n_threads=threads)
+        else:
+            oracle.moe_layer(lay, x, n_threads=threads)
+        return time.perf_counter() - t0
+
+    d1, dn = run(n1, 1), run(nn, n)
+    mode = "int8 spec mode, oracle routing" if int8 else "fp64 truth mode"
+    return baseline(n1 / d1, "%d tokens of %s (%s), one thread, %.1f s" % (n1, name, mode, d1),
+                    nn / dn, "%d tokens of %s (%s), %d threads, %.1f s" % (nn, name, mode, n, dn),
+                    n, "tok/s")
 
 
 def run_quantize(args):
@@ -249,7 +391,7 @@ def run_quantize(args):
 
     G = min(args.graph_steps, 16)
     steps = max(G, (args.steps // 10) // G * G)
-    total, _ = time_graph(step, G, min(args.warmup, 4 * G), steps)
+    total, _, _ = time_graph(step, G, min(args.warmup, 4 * G), steps)
     sec = total / steps
     n_w = sum(m.numel() for m in mats)
     bytes_per_step = accounting.quantize_bytes(wl)
@@ -300,7 +442,7 @@ def run_gemv(args, layout):
 
     G = min(args.graph_steps, 64)
     steps = max(G, (args.steps // 4) // G * G)
-    total, _ = time_graph(step, G, min(args.warmup, 4 * G), steps)
+    total, _, _ = time_graph(step, G, min(args.warmup, 4 * G), steps)
     sec = total / steps
     bytes_per_step = accounting.gemv_bytes(rows, cols, layout)
     achieved = bytes_per_step / sec / 1e9
@@ -346,7 +488,7 @@ def run_attention(args):
 
     G = min(args.graph_steps, 48)
     steps = max(G, (args.steps // 8) // G * G)
-    total, _ = time_graph(step, G, min(args.warmup, 4 * G), steps)
+    total, _, _ = time_graph(step, G, min(args.warmup, 4 * G), steps)
     sec = total / steps
     bytes_per_step = sum(2 * n * Hkv * dh * 2 + 2 * H * dh + 4 * H * dh for n in slots)
     achieved = bytes_per_step / sec / 1e9
@@ -383,7 +525,7 @@ def run_flash_head(args):
 
     G = min(args.graph_steps, 64)
     steps = max(G, (args.steps // 4) // G * G)
-    total, _ = time_graph(step, G, min(args.warmup, 4 * G), steps)
+    total, _, _ = time_graph(step, G, min(args.warmup, 4 * G), steps)
     sec = total / steps
     bytes_per_step = (ncl * d // 2 + 4 * ncl + 2 * d + top * cs * d * 2 + top * cs * 4
                       + top * cs * 8 + 4 * top)
@@ -400,6 +542,68 @@ def run_flash_head(args):
                       kernel="k_head_score + k_head_select + k_head_logits<4>"),
         cpu_baseline=None,
     )
+
+
+PHASE_NAMES = ["x gather + router (to the router barrier)", "logit gather (wave 0)", "top-k (wave 0)",
+               "top-k to its barrier", "gate/up loads + dots (to the h-publish barrier)",
+               "h publish + h gather (wave 0)", "down + max + digit planes (to the combine barrier)",
+               "combine + publish (to the end of the layer)"]
+
+
+def run_phases(args):
+    """Per-layer phase breakdown of the stacked decode from the measurement build
+    (libternary_moe_phases.so, -DTW_PHASE_TIMES): thread 0 of every workgroup stores the 100 MHz
+    wall clock at each phase boundary of every layer; means over workgroups, layers 1..23 and
+    20 steps.  The stores add a little time to every layer, so the total is above the product
+    build's."""
+    import numpy as np
+    wl = synth.STACK24_B1
+    layers = [build_layer(wl, l)[0] for l in range(wl.n_layers)]
+    x = synth.activations(wl, 1, device="cuda")[0]
+    ws = torch.zeros(tw.decode_workspace_bytes(layers), dtype=torch.uint8, device="cuda")
+    off = tw.lib().ternary_moe_decode_error_offset((tw.TwLayer * len(layers))(*[l.c for l in layers]),
+                                                   len(layers)) + 256
+    nwg, nl, ns = 256, 32, 10
+    bufs = [x.clone(), torch.empty_like(x)]
+    runs = []
+    for it in range(40):
+        tw.ternary_moe_ffn_decode(layers, bufs[it % 2], out=bufs[(it + 1) % 2], workspace=ws)
+        if it >= 20:
+            torch.cuda.synchronize()
+            assert tw.decode_error_flag(layers, ws) == 0
+            raw = ws[off:off + nwg * nl * ns * 8].cpu().view(torch.int64).numpy()
+            runs.append(raw.reshape(nwg, nl, ns)[:, :wl.n_layers, :].astype(np.float64) / 100.0)
+    ts = np.stack(runs)                       # [run, workgroup, layer, stamp] in us
+    L = slice(1, wl.n_layers)
+    order = [0, 1, 7, 8, 2, 3, 4, 5, 6]       # the stamps in time order within a layer
+    d = np.diff(ts[..., order], axis=3)[:, :, L, :]
+    phases = {n: round(float(d[..., i].mean()), 3) for i, n in enumerate(PHASE_NAMES)}
+    period = float((ts[:, :, 2:wl.n_layers, 0] - ts[:, :, 1:wl.n_layers - 1, 0]).mean())
+    skew = {str(p): round(float((ts[:, :, L, p].max(axis=1) - ts[:, :, L, p].min(axis=1)).mean()), 3)
+            for p in order}
+    lastpub = ts[:, :, 0:wl.n_layers - 1, 6].max(axis=1)
+    handoffs = {
+        "last residual published -> first / last router done":
+            [round(float((ts[:, :, 1:, 1].min(axis=1) - lastpub).mean()), 3),
+             round(float((ts[:, :, 1:, 1].max(axis=1) - lastpub).mean()), 3)],
+        "last logit published -> first / last top-k done":
+            [round(float((ts[:, :, L, 2].min(axis=1) - ts[:, :, L, 1].max(axis=1)).mean()), 3),
+             round(float((ts[:, :, L, 2].max(axis=1) - ts[:, :, L, 1].max(axis=1)).mean()), 3)],
+        "last h published -> first / last h gathered":
+            [round(float((ts[:, :, L, 4].min(axis=1) - ts[:, :, L, 3].max(axis=1)).mean()), 3),
+             round(float((ts[:, :, L, 4].max(axis=1) - ts[:, :, L, 3].max(axis=1)).mean()), 3)],
+    }
+    for n, v in phases.items():
+        log("  %-52s %.3f us" % (n, v))
+    log("  layer period %.3f us" % period)
+    return dict(metric="stack24_b1 per-layer phase breakdown (measurement build)", value=period,
+                unit="us per layer", n_gpus=1, steps=20, warmup=20, ms_per_step=None,
+                higher_is_better=False, scaling="weak", vs_baseline=None, dtype="as stack24_b1",
+                data="synthetic",
+                config=dict(workload="stack24_phases", layers=wl.n_layers, layers_averaged="1..23",
+                            workgroups=nwg, phases_us=phases, stamp_skew_us=skew,
+                            handoffs_us=handoffs),
+                roofline=None, cpu_baseline=None)
 
 
 def run_copy_calib(args):
@@ -429,24 +633,27 @@ def main():
     ap.add_argument("--warmup", type=int, default=512)
     ap.add_argument("--graph-steps", type=int, default=256)
     ap.add_argument("--workload", default="stack24_b1",
-                    choices=["stack24_b1", "layer_b1", "batched_b64", "batched_b64_int8",
+                    choices=["stack24_b1", "stack24_phases", "layer_b1", "batched_b64", "batched_b64_int8",
                              "prefill_4096", "quantize_layer", "gemv_2bit", "gemv_base3",
                              "attention_24l", "flash_head", "copy_calib"])
-    ap.add_argument("--cpu-tokens", type=int, default=36)
+    ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
-    if args.steps % args.graph_steps:
-        args.steps = max(1, round(args.steps / args.graph_steps)) * args.graph_steps
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "stack24_phases":
+        from ternary_weight_moe_amd import build as twb
+        tw.LIB_PATH = twb.PHASES_LIB   # the measurement build, before the library is loaded
     tw.lib()
     if args.workload == "stack24_b1":
         res = run_stack(args)
+    elif args.workload == "stack24_phases":
+        res = run_phases(args)
     elif args.workload == "copy_calib":
         res = run_copy_calib(args)
     elif args.workload == "quantize_layer":

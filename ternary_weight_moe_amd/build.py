@@ -7,6 +7,7 @@ correctly rounded fp32 division and square root.  Packed-fp32 instructions are d
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -35,25 +36,35 @@ def _run(cmd):
     return r
 
 
-def build(verbose: bool = False) -> str:
+# The measurement build: the same sources with -DTW_PHASE_TIMES, whose stacked decode kernel also
+# stores per-layer phase timestamps into its workspace (read by phase_times.py).
+PHASES_LIB = os.path.join(HERE, "libternary_moe_phases.so")
+
+
+def build(verbose: bool = False, phases: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    bdir = os.path.join(HERE, "_build")
+    bdir = os.path.join(HERE, "_build_phases" if phases else "_build")
+    out = PHASES_LIB if phases else LIB
+    extra = ["-DTW_PHASE_TIMES"] if phases else []
     os.makedirs(bdir, exist_ok=True)
     host_o = os.path.join(bdir, "tw_host.o")
-    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-c",
-          os.path.join(CSRC, "tw_host.cpp"), "-o", host_o])
-    objs = [host_o]
-    for src in HIP_SOURCES:
-        o = os.path.join(bdir, src.replace(".hip", ".o"))
-        _run([hipcc] + HIP_FLAGS + ["-c", os.path.join(CSRC, src), "-o", o])
-        objs.append(o)
-    tmp = LIB + ".tmp%d" % os.getpid()
+    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE] + extra +
+         ["-c", os.path.join(CSRC, "tw_host.cpp"), "-o", host_o])
+    objs = [os.path.join(bdir, src.replace(".hip", ".o")) for src in HIP_SOURCES]
+    jobs = [[hipcc] + HIP_FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", o]
+            for src, o in zip(HIP_SOURCES, objs)]
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        list(ex.map(_run, jobs))
+    objs = [host_o] + objs
+    tmp = out + ".tmp%d" % os.getpid()
     _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp])
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", out)
+    return out
 
 
 if __name__ == "__main__":
     build(verbose=True)
+    build(verbose=True, phases=True)

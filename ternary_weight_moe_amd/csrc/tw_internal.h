@@ -32,8 +32,12 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // ---- decode (batch 1) workspace -------------------------------------------------------------
 struct DecodeWs {
-    size_t ctrl, logits, ids, gates, xinfo, xdig, h, xbuf, ll, err, total;
+    size_t ctrl, logits, ids, gates, xinfo, xdig, h, xbuf, ll, err, ts, total;
 };
+// Phase timestamps of the one-launch stacked decode, kept only by a library built with
+// TW_PHASE_TIMES (a measurement build): per workgroup and layer, kPhaseStamps 64-bit clock values.
+constexpr int kPhaseStamps = 10;
+constexpr int kPhaseWorkgroups = 256;
 // Tagged words of the one-launch stacked decode: two parities of kLlCopies copies of one set of
 // (E logits, k*F fp32 h values, d/2 packed bf16 residual pairs).  Every word is stored into each
 // copy and each workgroup polls the copy of its own XCD, so that the polls of all 256 workgroups do
@@ -59,6 +63,9 @@ inline DecodeWs decode_ws_layout(const Dims &dm) {
     w.xbuf = o;   o += align256(sizeof(float) * 2 * size_t(dm.d));
     w.ll = o;     o += align256(sizeof(uint64_t) * persist_words(dm));
     w.err = o;    o += align256(sizeof(uint32_t) * 4);
+#ifdef TW_PHASE_TIMES
+    w.ts = o;     o += align256(sizeof(uint64_t) * kPhaseWorkgroups * kMaxPersistLayers * kPhaseStamps);
+#endif
     w.total = o;
     return w;
 }

@@ -51,6 +51,16 @@
 #include "tw_device.h"
 #include "tw_internal.h"
 
+// A measurement build (-DTW_PHASE_TIMES, made by phase_times.py) stores the 100 MHz wall clock at
+// the phase boundaries of every layer from thread 0 of every workgroup into the workspace, for a
+// per-layer time breakdown; the product build compiles these stores out.
+#ifdef TW_PHASE_TIMES
+#define TW_STAMP(P) \
+    if (t == 0 && a.ts) a.ts[(size_t(b) * kMaxPersistLayers + l) * kPhaseStamps + (P)] = wall_clock64()
+#else
+#define TW_STAMP(P) ((void)0)
+#endif
+
 namespace tw {
 namespace {
 
@@ -80,7 +90,9 @@ struct PArgs {
     uint16_t *x_out;
     uint64_t *ll;      // tagged words (2 parities)
     uint32_t *err;     // error slot: nonzero after a wait timed out
+    uint64_t *ts;      // phase timestamps (measurement build only)
     int E, n_layers, pre_norm;
+    int cont;          // 1: a later launch of one call (reads the health word first)
     PLayer L[kMaxPersistLayers];
 };
 
@@ -174,7 +186,10 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
     __shared__ int s_xsh;
     __shared__ float s_inv;
     __shared__ int s_abort;
-    if (t == 0) s_abort = 0;
+    // a launch that continues a call (more layers than one launch holds) starts aborted if a wait
+    // of an earlier launch ran out: its input is undefined, and the health word already reports it
+    // (the first launch of a call does not read the word: it was just cleared)
+    if (t == 0) s_abort = a.cont ? *reinterpret_cast<volatile uint32_t *>(a.err) != 0u : 0;
 
     int4 rw[kEM][C::NRC];
     load_router<C::NRC>(rw, a.L[0].w_router, b, E, D);
@@ -188,6 +203,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
     for (int l = 0; l < a.n_layers; l++) {
         const PLayer &P = a.L[l];
         const uint32_t tag = uint32_t(l + 1);
+        TW_STAMP(0);
         // copy 0 of this layer's parity (stores go to every copy) and the copy read here
         uint64_t *set0 = a.ll + size_t(l & 1) * kLlCopies * lls;
         const uint64_t *lgw = set0 + own, *hw = lgw + E * kLgStride;
@@ -267,6 +283,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
             }
         }
         __syncthreads();
+        TW_STAMP(1);
         {
             const float am = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
             const float ss = (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]);
@@ -304,9 +321,12 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
             wait_words<S>(lgw, lane * kLgStride, 64 * kLgStride, E * kLgStride, tag, v, &s_abort, a.err);
 #pragma unroll
             for (int q = 0; q < S; q++) lv[q] = __uint_as_float(uint32_t(v[q]));
+            TW_STAMP(7);
             topk_softmax_wave_regs<S, false>(lv, E, K, s_ids, s_gates, lane);
+            TW_STAMP(8);
         }
         __syncthreads();
+        TW_STAMP(2);
 
         // 4. request the gate/up rows of this workgroup's share at once (the down rows follow once
         //    these have arrived and the next router rows after the combine, so that these, on the
@@ -366,6 +386,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
             }
         }
         __syncthreads();
+        TW_STAMP(3);
         if (t < C::Q * kLlCopies) {   // thread t: value t % Q into copy t / Q
             const int i = t % C::Q;
             // (sum * scale) * inverse RMS, as the other kernels form a gate or up value
@@ -394,6 +415,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_sleep(kSleepH);
             wait_words<M>(hw + j * F, lane, 64, F, tag, v, &s_abort, a.err);
+            TW_STAMP(4);
             float am = 0.0f;
 #pragma unroll
             for (int m = 0; m < M; m++) {
@@ -425,6 +447,7 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
             if (c_d == 0 && lane < C::DL) ys[j * C::RD + lane / C::LPRD] = float_value<2>(acc, sh) * sd;
         }
         __syncthreads();
+        TW_STAMP(5);
         if (t < (C::RD / 2) * kLlCopies) {   // thread t: row pair t % (RD/2) into copy t / (RD/2)
             const int i = t % (C::RD / 2), c = t / (C::RD / 2);
             const int R0 = b * C::RD + 2 * i;
@@ -446,15 +469,19 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
         // the residual is gathered (requested with the down rows, a token took 193.6 us; here 192.1)
         if (l + 1 < a.n_layers) load_router<C::NRC>(rw, a.L[l + 1].w_router, b, E, D);
         __syncthreads();
+        TW_STAMP(6);
     }
 }
 
+// Clears the tagged words before a launch; the health word only before the first launch of a call
+// (err == nullptr for the later ones), so that a wait that ran out in an earlier launch stays
+// reported.
 __global__ void k_persist_zero(uint64_t *ll, int64_t n, uint32_t *err)
 {
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
          i += int64_t(gridDim.x) * blockDim.x)
         ll[i] = 0;
-    if (blockIdx.x == 0 && threadIdx.x < 4) err[threadIdx.x] = 0;
+    if (err && blockIdx.x == 0 && threadIdx.x < 4) err[threadIdx.x] = 0;
 }
 
 // Whether all kPB workgroups of an instantiation fit on the current device at once (cached).
@@ -500,15 +527,17 @@ int persist_run(const Dims &dm, const LayerPtrs *layers, int n, const void *x_in
         a.x_out = done + m == n ? static_cast<uint16_t *>(x_out) : xb[chunk & 1];
         a.ll = ll;
         a.err = err;
+        a.ts = L.ts && done == 0 ? reinterpret_cast<uint64_t *>(w + L.ts) : nullptr;   // first launch only
         a.E = dm.E;
         a.n_layers = m;
         a.pre_norm = dm.pre_norm;
+        a.cont = chunk > 0;
         for (int i = 0; i < m; i++) {
             const LayerPtrs &p = layers[done + i];
             a.L[i] = PLayer{static_cast<const uint16_t *>(p.w_router), p.w_gate, p.w_up, p.w_down,
                             p.s_gate, p.s_up, p.s_down};
         }
-        k_persist_zero<<<int((nw + 2047) / 2048), 256, 0, s>>>(ll, nw, err);
+        k_persist_zero<<<int((nw + 2047) / 2048), 256, 0, s>>>(ll, nw, chunk == 0 ? err : nullptr);
         k_persist<D, F, K><<<kPB, kPT, 0, s>>>(a);
         done += m;
         chunk++;

@@ -100,6 +100,37 @@ def test_route_topk(which, T, pre, small, full):
     ties = check_routing(ids.cpu().numpy(), g.cpu().numpy(), olg, oids, og, L.k)
     assert ties <= max(1, T // 100)
     assert np.allclose(g.sum(1).cpu().numpy(), 1.0, atol=L.k * 2.0 ** -23)
+    assert_selection_of_own_logits(lg, ids, L.k)
+
+
+def assert_selection_of_own_logits(lg, ids, k):
+    """The ids are exactly the top k of the logits the call returned, by (logit descending, id
+    ascending): the selection is unique given those logits, whatever reduction formed them."""
+    lg, ids = lg.cpu().numpy(), ids.cpu().numpy()
+    for t in range(lg.shape[0]):
+        order = np.lexsort((np.arange(lg.shape[1]), -lg[t].astype(np.float64)))
+        assert np.array_equal(ids[t], order[:k]), (t, ids[t], order[:k])
+
+
+@pytest.mark.parametrize("classes,k", [(16, 8), (128, 8), (4, 8), (64, 4), (2, 16), (256, 32)])
+def test_route_topk_tied_logits(classes, k):
+    # router rows repeat every `classes` experts, so each distinct logit is shared by 256 / classes
+    # experts and the top k is decided by ids among equal logits: ties inside the candidate set of
+    # the selection (and, with 2 classes, more candidates than one wave holds)
+    step("moe_route_topk tied logits: %d classes, k %d" % (classes, k))
+    g = torch.Generator().manual_seed(classes)
+    base = (torch.randn((classes, 2048), generator=g) * 0.02).to(torch.bfloat16)
+    wr = base[torch.arange(256) % classes].contiguous()
+    x = (torch.randn((12, 2048), generator=g)).to(torch.bfloat16)
+    lg, ids, gw = tw.moe_route_topk(x.cuda(), wr.cuda(), k)
+    torch.cuda.synchronize()
+    L = oracle.Layer(wr, np.zeros((256, 8, 2048), np.int8), np.zeros((256, 8, 2048), np.int8),
+                     np.zeros((256, 2048, 8), np.int8), np.ones((256, 8), np.float32),
+                     np.ones((256, 8), np.float32), np.ones((256, 2048), np.float32), top_k=k)
+    oids, og, olg = oracle.route(L, x, n_threads=4)
+    ties = check_routing(ids.cpu().numpy(), gw.cpu().numpy(), olg, oids, og, k)
+    assert ties <= 1
+    assert_selection_of_own_logits(lg, ids, k)
 
 
 def test_route_zero_input_goes_to_lowest_ids(full):
@@ -298,7 +329,10 @@ def test_decode_more_layers_than_one_launch_holds(mid3):
     seq = [p.gpu for p in mid3] * 12
     x0 = synth.activations(synth.MID_STACK_B1, 1, seed=29)[0].cuda()
     step("decode 36 layers fused")
-    fused = tw.ternary_moe_ffn_decode(seq, x0)
+    ws = torch.empty(tw.decode_workspace_bytes(seq), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xAB)   # the call clears the health word itself
+    fused = tw.ternary_moe_ffn_decode(seq, x0, workspace=ws)
+    assert tw.decode_error_flag(seq, ws) == 0   # no wait ran out in either launch
     step("decode 36 layers chained")
     cur = x0
     for layer in seq:
