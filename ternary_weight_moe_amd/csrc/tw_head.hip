@@ -10,10 +10,9 @@
 //                  offset-binary nibbles (value + 8) of the centroid are masked into int8x4 words
 //                  for v_dot4; the exact sum is corrected by -8 sum(q) and scaled,
 //                  score = (float(acc) * s_h) * scale (two fp32 roundings);
-//   k_head_select  one 1024-thread workgroup: the threshold key of the `top`-th cluster by three
-//                  radix passes of 11, 11 and 10 bits (LDS histograms), the clusters above it plus the lowest ids
-//                  at it, then a bitonic sort in LDS of those `top` (orderable score key, cluster
-//                  id) pairs, descending by score and ascending by id;
+//   k_head_rank    every cluster's rank (the clusters with a higher score, or the same score and a
+//                  lower id) by one 16-lane group per cluster over all keys in LDS; the clusters of
+//                  rank < top write their id at that rank;
 //   k_head_logits  one workgroup per selected cluster, four waves; each wave takes rows
 //                  wave, wave + 4, ... of the cluster's cluster-major head rows, all loads of a
 //                  batch of rows issued first, fp32 dot with h (from LDS), wave sum.
@@ -113,165 +112,29 @@ __device__ __forceinline__ uint32_t score_key(float s)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__global__ __launch_bounds__(1024) void k_head_select(const float *__restrict__ scores, int ncl,
-                                                      int top, int32_t *__restrict__ sel)
+// Rank selection: a cluster's place in the output is the number of clusters that come before it
+// (higher score key, or the same key and a lower id).  Each 16-lane group of a workgroup counts
+// that for one cluster against every cluster's key (the keys of all clusters are first copied
+// into LDS as 64-bit composites key << 32 | ~id, so that "comes before" is one unsigned compare and
+// every composite is distinct), and the clusters of rank < top write their id to sel[rank].  The
+// ranks are exact integer counts, so the selection and its order do not depend on the launch
+// shape; no threshold search, no sort and no single-workgroup step.
+__global__ __launch_bounds__(256) void k_head_rank(const float *__restrict__ scores, int ncl, int top,
+                                                   int32_t *__restrict__ sel)
 {
-    constexpr int PER = kHeadMaxClusters / 1024;
-    __shared__ uint32_t s_key[kHeadMaxClusters];
-    __shared__ uint16_t s_id[kHeadMaxClusters];
-    __shared__ int s_hist[2048];
-    __shared__ int s_wc[kHeadMaxClusters / 1024][16];
-    __shared__ uint32_t s_prefix;
-    __shared__ int s_above, s_cnt;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    uint32_t key[PER];
-#pragma unroll
-    for (int m = 0; m < PER; m++) {
-        const int i = t + 1024 * m;
-        key[m] = i < ncl ? score_key(scores[i]) : 0u;
-    }
-    // 1. the threshold key T (count(key > T) < top <= count(key >= T)) by three radix passes of
-    //    11, 11 and 10 bits from the top down; `above` counts the keys above the current bucket
-    uint32_t prefix = 0, mask = 0;
-    int above = 0;
-#pragma unroll
-    for (int pass = 0; pass < 3; pass++) {
-        const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0, bits = pass == 2 ? 10 : 11;
-        const int nbins = 1 << bits, per = nbins / 64;
-        for (int i = t; i < nbins; i += 1024) s_hist[i] = 0;
-        __syncthreads();
-#pragma unroll
-        for (int m = 0; m < PER; m++)
-            if (t + 1024 * m < ncl && (key[m] & mask) == prefix)
-                atomicAdd(&s_hist[(key[m] >> shift) & uint32_t(nbins - 1)], 1);
-        __syncthreads();
-        if (wave == 0) {
-            // lane l holds bins nbins-1-per*l .. down; counts accumulate from the highest bin down
-            int tot = 0;
-            for (int q = 0; q < per; q++) tot += s_hist[nbins - 1 - per * lane - q];
-            int inc = tot;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int v = __shfl_up(inc, off);
-                if (lane >= off) inc += v;
-            }
-            int run = above + inc - tot, found = -1, found_above = 0;
-            for (int q = 0; q < per; q++) {
-                const int c = s_hist[nbins - 1 - per * lane - q];
-                if (found < 0 && run + c >= top) {
-                    found = nbins - 1 - per * lane - q;
-                    found_above = run;
-                }
-                run += c;
-            }
-            const uint64_t bal = __ballot(found >= 0);
-            if (lane == __ffsll((unsigned long long)bal) - 1) {
-                s_prefix = prefix | (uint32_t(found) << shift);
-                s_above = found_above;
-            }
-        }
-        __syncthreads();
-        prefix = s_prefix;
-        above = s_above;
-        mask |= uint32_t(nbins - 1) << shift;
-        __syncthreads();
-    }
-    // 2. the selected clusters: every key above T, and the (top - above) lowest ids with key T
-    //    (ranked in id order: row m of 1024 ids before row m + 1, waves in order inside a row),
-    //    collected in LDS in any order; one barrier for the per-wave counts of all rows
-    const int need = top - above;
-    if (t == 0) s_cnt = 0;
-    uint64_t eqb[PER];
-#pragma unroll
-    for (int m = 0; m < PER; m++) {
-        const int i = t + 1024 * m;
-        eqb[m] = __ballot(i < ncl && key[m] == prefix);
-        if (lane == 0) s_wc[m][wave] = __popcll(eqb[m]);
-    }
+    extern __shared__ uint64_t s_c[];   // ncl composites
+    const int t = threadIdx.x;
+    for (int i = t; i < ncl; i += 256)
+        s_c[i] = (uint64_t(score_key(scores[i])) << 32) | uint64_t(~uint32_t(i));
     __syncthreads();
-    int eq_before = 0;
-#pragma unroll
-    for (int m = 0; m < PER; m++) {
-        const int i = t + 1024 * m;
-        const bool valid = i < ncl;
-        const bool gt = valid && key[m] > prefix, eq = valid && key[m] == prefix;
-        int before = 0, total = 0;
-#pragma unroll
-        for (int w = 0; w < 16; w++) {
-            before += w < wave ? s_wc[m][w] : 0;
-            total += s_wc[m][w];
-        }
-        const int r = __popcll(eqb[m] & ((uint64_t(1) << lane) - 1));
-        if (gt || (eq && eq_before + before + r < need)) {
-            const int pos = atomicAdd(&s_cnt, 1);
-            s_key[pos] = key[m];
-            s_id[pos] = uint16_t(i);
-        }
-        eq_before += total;
-    }
-    __syncthreads();
-    // 3. bitonic sort of the `top` selected (padded to a power of two N), descending by key, then
-    //    lower id first.  Up to 1024 of them: one per thread in registers, partners at distance
-    //    below 64 exchanged by lane shuffles, farther ones through LDS (5 barrier stages for 512);
-    //    more than 1024: the same network entirely in LDS.
-    int N = 1;
-    while (N < top) N <<= 1;
-    if (N <= 1024) {
-        uint32_t kk = t < top ? s_key[t] : 0u;
-        uint32_t ii = t < top ? uint32_t(s_id[t]) : 0xFFFFu;
-        for (int k = 2; k <= N; k <<= 1) {
-            for (int j = k >> 1; j > 0; j >>= 1) {
-                uint32_t kp, ip;
-                if (j >= 64) {
-                    __syncthreads();   // every read of the previous exchange is done
-                    if (t < N) {
-                        s_key[t] = kk;
-                        s_id[t] = uint16_t(ii);
-                    }
-                    __syncthreads();
-                    kp = t < N ? s_key[t ^ j] : 0u;
-                    ip = t < N ? uint32_t(s_id[t ^ j]) : 0xFFFFu;
-                } else {
-                    kp = uint32_t(__shfl_xor(int(kk), j));
-                    ip = uint32_t(__shfl_xor(int(ii), j));
-                }
-                const bool mine_first = kk > kp || (kk == kp && ii < ip);
-                const bool keep_first = ((t & j) == 0) == ((t & k) == 0);
-                if (keep_first != mine_first) {
-                    kk = kp;
-                    ii = ip;
-                }
-            }
-        }
-        if (t < top) sel[t] = int32_t(ii);
-        return;
-    }
-    for (int i = top + t; i < N; i += 1024) {
-        s_key[i] = 0u;
-        s_id[i] = 0xFFFF;
-    }
-    __syncthreads();
-    for (int k = 2; k <= N; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = t; i < N; i += 1024) {
-                const int l = i ^ j;
-                if (l > i) {
-                    const uint32_t ki = s_key[i], kl = s_key[l];
-                    const uint16_t ii = s_id[i], il = s_id[l];
-                    const bool l_first = kl > ki || (kl == ki && il < ii);   // l ranks before i
-                    const bool i_first = ki > kl || (ki == kl && ii < il);
-                    if (((i & k) == 0) ? l_first : i_first) {
-                        s_key[i] = kl;
-                        s_key[l] = ki;
-                        s_id[i] = il;
-                        s_id[l] = ii;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
-    for (int i = t; i < top; i += 1024) sel[i] = int32_t(s_id[i]);
+    const int g = t & 15;                       // lane in the cluster's group of 16
+    const int i = blockIdx.x * 16 + (t >> 4);   // the cluster this group ranks
+    const uint64_t ci = i < ncl ? s_c[i] : ~uint64_t(0);
+    int32_t cnt[1] = {0};
+#pragma unroll 4
+    for (int j = g; j < ncl; j += 16) cnt[0] += int32_t(s_c[j] > ci);
+    group_reduce<1>(cnt, 16);
+    if (g == 0 && i < ncl && cnt[0] < top) sel[cnt[0]] = i;
 }
 
 template <int M>   // M = d / 512: 8-input chunks per lane and row
@@ -330,7 +193,7 @@ int launch_flash_head(const void *h, int d, const uint8_t *cent, const float *cs
     float *scores = static_cast<float *>(ws);
     const int nb = (ncl + 3) / 4 < 1024 ? (ncl + 3) / 4 : 1024;
     k_head_score<<<nb, 256, 0, st>>>(hp, d, cent, cscale, ncl, scores);
-    k_head_select<<<1, 1024, 0, st>>>(scores, ncl, top, sel);
+    k_head_rank<<<(ncl + 15) / 16, 256, size_t(ncl) * sizeof(uint64_t), st>>>(scores, ncl, top, sel);
     auto wp = static_cast<const uint16_t *>(wc);
     switch (d / 512) {
     case 1: k_head_logits<1><<<top, 256, 0, st>>>(hp, d, wp, members, cs, sel, ids, logits); break;

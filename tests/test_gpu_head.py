@@ -87,6 +87,46 @@ def test_flash_head_full_size():
                              np.zeros((ncl, 1, d), np.float32), np.zeros((ncl, 1), np.int32), top)[0]
     assert np.array_equal(sel.cpu().numpy(), rsel)
     assert np.array_equal(ids.cpu().numpy(), f["member_ids"].cpu().numpy()[rsel])
-    r = np.random.default_rng(5)
-    rows = [(int(j), int(m)) for j, m in zip(r.integers(0, top, 256), r.integers(0, cs, 256))]
-    check_logits(f, h, sel, ids, logits, rows)
+    # every logit against the oracle's: the oracle reads only the rows of the clusters it selects,
+    # so the others are left zero in its (double) copy of the head
+    step("flash_head full size: oracle logits of the selected clusters")
+    wv = np.zeros((ncl, cs, d), np.float64)
+    idx = torch.as_tensor(rsel, device=f["w_clustered"].device, dtype=torch.int64)
+    wv[rsel] = f["w_clustered"][idx].float().cpu().numpy()
+    o = oracle.flash_head(h.float().cpu(), f["centroids"].cpu(), f["centroid_scales"].cpu(), wv,
+                          f["member_ids"].cpu(), top)
+    assert np.array_equal(o[0], rsel) and np.array_equal(ids.cpu().numpy(), o[1])
+    bound = 2.0 ** -22 * d * (np.abs(wv[rsel]) @ np.abs(h.float().cpu().numpy().astype(np.float64)))
+    assert np.all(np.abs(logits.cpu().numpy().astype(np.float64) - o[2]) <= bound + 1e-30)
+
+
+def test_flash_head_tie_group_split_by_top():
+    # 3000 clusters, all of one score except six above it; top = 1500 falls inside the tie group,
+    # whose members span three 1024-id rows: the six first (by score), then the lowest 1494 tied ids
+    # in ascending order
+    step("flash_head tie group split by top")
+    ncl, cs, d, top = 3000, 2, 512, 1500
+    f = synth.head_inputs(ncl, cs, d, "cuda", seed=61)
+    h = synth.head_hidden(d, "cuda", seed=61)
+    # one centroid for all, of value +7 where h >= 0 and -8 elsewhere: a positive score
+    nib = torch.where(h.float().cpu() >= 0, 15, 0).to(torch.uint8)
+    row = (nib[0::2] | (nib[1::2] << 4)).to(torch.uint8)
+    f["centroids"][:] = row.cuda()
+    f["centroid_scales"][:] = f["centroid_scales"][0]
+    high = [2999, 17, 1024, 2048, 5, 1500]
+    for r, c in enumerate(high):
+        f["centroid_scales"][c] = f["centroid_scales"][0] * (2.0 + r)
+    sel, ids, logits = tw.flash_head(h, f["centroids"], f["centroid_scales"], f["w_clustered"],
+                                     f["member_ids"], top)
+    torch.cuda.synchronize()
+    rsel, rids, rlg, sc = oracle.flash_head(h.float().cpu(), f["centroids"].cpu(),
+                                            f["centroid_scales"].cpu(),
+                                            f["w_clustered"].float().cpu(), f["member_ids"].cpu(), top)
+    got = sel.cpu().numpy()
+    assert np.array_equal(got, rsel) and np.array_equal(ids.cpu().numpy(), rids)
+    # the expected order, independently of both: the high clusters by score (and id on ties),
+    # then the rest of the ids ascending
+    hi = sorted(high, key=lambda c: (-float(sc[c]), c))
+    assert sc[0] > 0 and sc[hi[-1]] > sc[0]
+    rest = [c for c in range(ncl) if c not in high][:top - len(high)]
+    assert got.tolist() == hi + rest
