@@ -286,6 +286,29 @@ size_t ternary_moe_decode_workspace_bytes(const tw_moe_layer *layers, int32_t n_
 size_t ternary_moe_decode_error_offset(const tw_moe_layer *layers, int32_t n_layers);
 
 /*
+ * ternary_moe_ffn_decode_static -- ternary_moe_ffn_decode without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  The call allocates nothing: its workspace is a scratch array of
+ * TW_STATIC_SCRATCH_BYTES (2 MiB) that the library holds in each device's memory from its first
+ * call on that device until the process ends; the 24-layer d_model 2048 / 256 experts / width 512
+ * / top-8 stack needs about 0.8 MiB of it.  Results equal ternary_moe_ffn_decode's bit for bit (the same
+ * kernels run).
+ *   layers, n_layers, x_in, x_out, io_dtype, stream: as ternary_moe_ffn_decode.
+ *   health     nullable device uint32 (4-byte aligned): receives the call's health word (see
+ *              ternary_moe_decode_error_offset) once the call completes in stream order.
+ *   Every call on one device shares that device's scratch, which keeps the last call's contents
+ *   (the call clears what it needs cleared): calls that overlap on one device race on it, so keep
+ *   these calls on one stream per device and do not run two at once.
+ *   Errors: as ternary_moe_ffn_decode, plus TW_E_WORKSPACE when the layers need a larger workspace
+ *   than TW_STATIC_SCRATCH_BYTES (ternary_moe_decode_workspace_bytes tells), TW_E_UNSUPPORTED
+ *   (health misaligned), TW_E_ALIAS (health overlapping x_in or x_out).
+ */
+#define TW_STATIC_SCRATCH_BYTES (2u << 20)
+tw_status ternary_moe_ffn_decode_static(const tw_moe_layer *layers, int32_t n_layers,
+                                        const void *x_in, void *x_out, int32_t io_dtype,
+                                        uint32_t *health, void *stream);
+
+/*
  * ternary_moe_ffn_batched -- one layer for n_tokens independent tokens, each expert's weights read
  * once per call: (token, slot) pairs are grouped by expert and each expert's rows are applied to
  * all of its tokens.

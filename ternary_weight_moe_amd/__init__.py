@@ -43,7 +43,7 @@ class TwLayer(C.Structure):
 EXPORTS = ("tw_status_str", "ternary_pack", "ternary_quantize", "ternary_pack3_row_bytes",
            "ternary_pack3", "ternary_gemv_i8", "attention_decode_workspace_bytes",
            "attention_decode", "flash_head_workspace_bytes", "flash_head", "moe_route_topk",
-           "ternary_moe_ffn_decode",
+           "ternary_moe_ffn_decode", "ternary_moe_ffn_decode_static",
            "ternary_moe_decode_workspace_bytes", "ternary_moe_decode_error_offset",
            "ternary_moe_ffn_batched",
            "ternary_moe_batched_workspace_bytes")
@@ -75,6 +75,7 @@ def lib():
                 "moe_route_topk": (i32, [vp, i32, vp, i32, i64, i32, i32, i32, i32, vp, vp, vp,
                                          vp]),
                 "ternary_moe_ffn_decode": (i32, [LP, i32, vp, vp, i32, vp, sz, vp]),
+                "ternary_moe_ffn_decode_static": (i32, [LP, i32, vp, vp, i32, vp, vp]),
                 "ternary_moe_decode_workspace_bytes": (sz, [LP, i32]),
                 "ternary_moe_decode_error_offset": (sz, [LP, i32]),
                 "ternary_moe_ffn_batched": (i32, [LP, i64, vp, i32, vp, i32, i32, vp, vp, vp, sz,
@@ -330,6 +331,26 @@ def ternary_moe_ffn_decode(layers, x: torch.Tensor, out: torch.Tensor | None = N
     _check(lib().ternary_moe_ffn_decode(arr, len(layers), _ptr(x), _ptr(out), _DT[x.dtype],
                                         _ptr(workspace), workspace.numel(), _stream(stream)),
            "ternary_moe_ffn_decode")
+    return out
+
+
+STATIC_SCRATCH_BYTES = 2 << 20   # TW_STATIC_SCRATCH_BYTES of include/ternary_moe.h
+
+
+def ternary_moe_ffn_decode_static(layers, x: torch.Tensor, out: torch.Tensor | None = None,
+                                  health: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """ternary_moe_ffn_decode with the library's static per-device scratch as its workspace (the C
+    call allocates nothing); health: optional int32 device tensor of one element that receives
+    the health word.  Calls that overlap on one device race on the shared scratch."""
+    layers = list(layers)
+    _need_cuda(x, out, health)
+    arr = (TwLayer * len(layers))(*[l.c for l in layers])
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib().ternary_moe_ffn_decode_static(arr, len(layers), _ptr(x), _ptr(out), _DT[x.dtype],
+                                               _ptr(health) if health is not None else None,
+                                               _stream(stream)),
+           "ternary_moe_ffn_decode_static")
     return out
 
 

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libternary_moe.so")
 ARCH = "gfx950"
 HIP_SOURCES = ("tw_kernels.hip", "tw_persist.hip", "tw_prefill.hip", "tw_base3.hip", "tw_attn.hip",
-               "tw_head.hip")
+               "tw_head.hip", "tw_static.hip")
 
 HIP_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

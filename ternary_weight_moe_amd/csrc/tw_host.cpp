@@ -296,9 +296,13 @@ size_t ternary_moe_decode_error_offset(const tw_moe_layer *layers, int32_t n_lay
     return tw::decode_ws_layout(dims_of(&layers[0])).err;
 }
 
-tw_status ternary_moe_ffn_decode(const tw_moe_layer *layers, int32_t n_layers, const void *x_in,
-                                 void *x_out, int32_t io_dtype, void *workspace, size_t ws_bytes,
-                                 void *stream)
+static_assert(TW_STATIC_SCRATCH_BYTES == tw::kStaticScratchBytes, "one size for the static scratch");
+
+namespace {
+
+// Checks shared by the two decode entry points (everything but the workspace); fills dm and ptrs.
+tw_status check_decode(const tw_moe_layer *layers, int32_t n_layers, const void *x_in,
+                       void *x_out, int32_t io_dtype, tw::Dims &dm, tw::LayerPtrs *ptrs)
 {
     if (!layers) return TW_E_NULL;
     if (n_layers < 1) return TW_E_SHAPE;
@@ -313,21 +317,53 @@ tw_status ternary_moe_ffn_decode(const tw_moe_layer *layers, int32_t n_layers, c
             return TW_E_SHAPE;
     }
     if (!valid_float(io_dtype)) return TW_E_DTYPE;
-    if (!x_in || !x_out || !workspace) return TW_E_NULL;
-    if ((uintptr_t)workspace & 255) return TW_E_UNSUPPORTED;   // its regions are 256-byte aligned
-    tw::Dims dm = dims_of(&layers[0]);
+    if (!x_in || !x_out) return TW_E_NULL;
+    dm = dims_of(&layers[0]);
     // the down kernel keeps the digit planes of all k expert activations in 64 KiB of LDS
     if (size_t(dm.k) * 3 * dm.F > 65536 - 1024) return TW_E_UNSUPPORTED;
+    size_t xb = size_t(dm.d) * fsize(io_dtype);
+    if (overlap(x_in, xb, x_out, xb)) return TW_E_ALIAS;
+    for (int i = 0; i < n_layers; i++) ptrs[i] = ptrs_of(&layers[i]);
+    return TW_OK;
+}
+
+}  // namespace
+
+tw_status ternary_moe_ffn_decode(const tw_moe_layer *layers, int32_t n_layers, const void *x_in,
+                                 void *x_out, int32_t io_dtype, void *workspace, size_t ws_bytes,
+                                 void *stream)
+{
+    tw::Dims dm{};
+    tw::LayerPtrs ptrs[tw::kMaxLayers];
+    tw_status s = check_decode(layers, n_layers, x_in, x_out, io_dtype, dm, ptrs);
+    if (s != TW_OK) return s;
+    if (!workspace) return TW_E_NULL;
+    if ((uintptr_t)workspace & 255) return TW_E_UNSUPPORTED;   // its regions are 256-byte aligned
     size_t need = tw::decode_ws_layout(dm).total;
     if (ws_bytes < need) return TW_E_WORKSPACE;
     size_t xb = size_t(dm.d) * fsize(io_dtype);
-    if (overlap(x_in, xb, x_out, xb)) return TW_E_ALIAS;
     if (overlap(workspace, ws_bytes, x_in, xb) || overlap(workspace, ws_bytes, x_out, xb))
         return TW_E_ALIAS;
-    tw::LayerPtrs ptrs[tw::kMaxLayers];
-    for (int i = 0; i < n_layers; i++) ptrs[i] = ptrs_of(&layers[i]);
     return tw::launch_decode(dm, ptrs, n_layers, x_in, x_out, io_dtype == TW_BF16, workspace,
                              stream)
+               ? TW_E_HIP
+               : TW_OK;
+}
+
+tw_status ternary_moe_ffn_decode_static(const tw_moe_layer *layers, int32_t n_layers,
+                                        const void *x_in, void *x_out, int32_t io_dtype,
+                                        uint32_t *health, void *stream)
+{
+    tw::Dims dm{};
+    tw::LayerPtrs ptrs[tw::kMaxLayers];
+    tw_status s = check_decode(layers, n_layers, x_in, x_out, io_dtype, dm, ptrs);
+    if (s != TW_OK) return s;
+    if (tw::decode_ws_layout(dm).total > tw::kStaticScratchBytes) return TW_E_WORKSPACE;
+    if ((uintptr_t)health & 3) return TW_E_UNSUPPORTED;
+    size_t xb = size_t(dm.d) * fsize(io_dtype);
+    if (overlap(health, 4, x_in, xb) || overlap(health, 4, x_out, xb)) return TW_E_ALIAS;
+    return tw::launch_decode_static(dm, ptrs, n_layers, x_in, x_out, io_dtype == TW_BF16, health,
+                                    stream)
                ? TW_E_HIP
                : TW_OK;
 }

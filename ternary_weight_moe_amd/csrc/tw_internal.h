@@ -121,6 +121,11 @@ int launch_decode_persist(const Dims &dm, const LayerPtrs *layers, int n_layers,
                           void *x_out, int io_bf16, void *ws, void *stream);
 int launch_decode(const Dims &dm, const LayerPtrs *layers, int n_layers, const void *x_in,
                   void *x_out, int io_bf16, void *ws, void *stream);
+// The same decode with the library's static scratch (tw_static.hip) as its workspace; health
+// (nullable, device) receives the health word after the call.
+constexpr size_t kStaticScratchBytes = size_t(2) << 20;
+int launch_decode_static(const Dims &dm, const LayerPtrs *layers, int n_layers, const void *x_in,
+                         void *x_out, int io_bf16, uint32_t *health, void *stream);
 // Grouped MFMA path of the batched FFN (after quantisation/digit planes): planes = 1 (int8
 // activations) or 2 (digit planes of bf16 inputs).  sel_ids == nullptr: tiles of `tile` tokens from
 // k_group's lists; else the T k expert ids themselves (one workgroup per expert finds its pairs,

@@ -273,3 +273,25 @@ def test_flash_head_workspace_and_errors(L):
     assert call(lg=A[15] + 4096) == E_ALIAS       # logits inside the head rows
     assert call(ids=A[7] + 4) == E_ALIAS          # ids overlapping logits
     assert call(ws=A[5]) == E_ALIAS               # workspace over sel
+
+
+def test_decode_static_errors(L):
+    s = C.c_void_p(0)
+    one = (tw.TwLayer * 1)(layer())
+    # the same argument checks as ternary_moe_ffn_decode (no workspace argument)
+    assert L.ternary_moe_ffn_decode_static(None, 1, A[8], A[9], 1, None, s) == E_NULL
+    assert L.ternary_moe_ffn_decode_static(one, 0, A[8], A[9], 1, None, s) == E_SHAPE
+    assert L.ternary_moe_ffn_decode_static(one, 1, None, A[9], 1, None, s) == E_NULL
+    assert L.ternary_moe_ffn_decode_static(one, 1, A[8], A[8] + 64, 1, None, s) == E_ALIAS
+    assert L.ternary_moe_ffn_decode_static(one, 1, A[8], A[9], 7, None, s) == E_DTYPE
+    # the health word: 4-byte aligned, not overlapping the activations
+    assert L.ternary_moe_ffn_decode_static(one, 1, A[8], A[9], 1, A[10] + 2, s) == E_UNSUP
+    assert L.ternary_moe_ffn_decode_static(one, 1, A[8], A[9], 1, A[9] + 8, s) == E_ALIAS
+    # layers whose workspace exceeds the static scratch are rejected before any HIP call
+    big = (tw.TwLayer * 1)(layer(d=4096, F=1024, E=1024, k=16))
+    need = L.ternary_moe_decode_workspace_bytes(big, 1)
+    assert need > tw.STATIC_SCRATCH_BYTES
+    assert L.ternary_moe_ffn_decode_static(big, 1, A[8], A[9], 1, None, s) == E_WS
+    # the full-size stack fits
+    stack = (tw.TwLayer * 24)(*[layer() for _ in range(24)])
+    assert L.ternary_moe_decode_workspace_bytes(stack, 24) <= tw.STATIC_SCRATCH_BYTES
