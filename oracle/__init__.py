@@ -19,7 +19,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "tw_oracle.c")
-_LIB = os.path.join(_HERE, "libtw_oracle.so")
+# TW_ORACLE_LIB: another build of the same source (for instance one with sanitizers)
+_LIB = os.environ.get("TW_ORACLE_LIB") or os.path.join(_HERE, "libtw_oracle.so")
 _lock = threading.Lock()
 _lib = None
 

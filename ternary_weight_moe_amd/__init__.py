@@ -13,7 +13,8 @@ import threading
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libternary_moe.so")
+# TW_LIB_PATH: another build of the same sources (for instance with sanitized host code)
+LIB_PATH = os.environ.get("TW_LIB_PATH") or os.path.join(_HERE, "libternary_moe.so")
 
 TW_F32, TW_BF16 = 0, 1
 ACT_FLOAT, ACT_INT8 = 0, 1
