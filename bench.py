@@ -539,7 +539,7 @@ def run_flash_head(args):
                     hidden_states=8, bytes_per_step=bytes_per_step),
         roofline=dict(bound="hbm", achieved=achieved, peak=accounting.HBM_PEAK_BPS / 1e9,
                       unit="GB/s", frac=achieved * 1e9 / accounting.HBM_PEAK_BPS, traffic=None,
-                      kernel="k_head_score + k_head_select + k_head_logits<4>"),
+                      kernel="k_head_score<1> + k_head_rank + k_head_logits<4>"),
         cpu_baseline=None,
     )
 

@@ -4,14 +4,15 @@
 // most relevant ones, and only their tokens get full-precision logits).
 //
 // Three launches on the caller's stream:
-//   k_head_score   one wave per centroid row: h is quantised to int8 by absmax in every workgroup
-//                  (the same fp32 steps as the int8 FFN path, so the codes are identical), each
-//                  lane holds the codes of its 32-input chunks as even/odd int8x4 words, and the
-//                  offset-binary nibbles (value + 8) of the centroid are masked into int8x4 words
-//                  for v_dot4; the exact sum is corrected by -8 sum(q) and scaled,
-//                  score = (float(acc) * s_h) * scale (two fp32 roundings);
+//   k_head_score   each wave scores up to eight centroid rows, all their loads issued before h
+//                  is quantised to int8 by absmax in the workgroup (the same fp32 steps as the int8
+//                  FFN path, so the codes are identical); each lane holds the codes of its
+//                  32-input chunks as even/odd int8x4 words, and the offset-binary nibbles
+//                  (value + 8) of the centroid are masked into int8x4 words for v_dot4; the exact
+//                  sum is corrected by -8 sum(q) and scaled, score = (float(acc) * s_h) * scale
+//                  (two fp32 roundings);
 //   k_head_rank    every cluster's rank (the clusters with a higher score, or the same score and a
-//                  lower id) by one 16-lane group per cluster over all keys in LDS; the clusters of
+//                  lower id) by one wave per two clusters over all keys in LDS; the clusters of
 //                  rank < top write their id at that rank;
 //   k_head_logits  one workgroup per selected cluster, four waves; each wave takes rows
 //                  wave, wave + 4, ... of the cluster's cluster-major head rows, all loads of a
@@ -32,8 +33,16 @@ __device__ __forceinline__ float head_quant_h(const uint16_t *__restrict__ h, in
                                               float *s_red)
 {
     const int t = threadIdx.x;
+    constexpr int PER = kHeadMaxD / NT;
+    float hv[PER];
+#pragma unroll
+    for (int m = 0; m < PER; m++) {   // every load issued before the first is used
+        const int i = t + NT * m;
+        hv[m] = i < d ? bf16_to_f32(h[i]) : 0.0f;
+    }
     float am = 0.0f;
-    for (int i = t; i < d; i += NT) am = fmaxf(am, fabsf(bf16_to_f32(h[i])));
+#pragma unroll
+    for (int m = 0; m < PER; m++) am = fmaxf(am, fabsf(hv[m]));
     am = wave_max(am);
     if ((t & 63) == 0) s_red[t >> 6] = am;
     __syncthreads();
@@ -41,11 +50,20 @@ __device__ __forceinline__ float head_quant_h(const uint16_t *__restrict__ h, in
 #pragma unroll
     for (int w = 0; w < NT / 64; w++) am = fmaxf(am, s_red[w]);
     const float inv = 127.0f / am;
-    for (int i = t; i < d; i += NT) s_q[i] = am > 0.0f ? int8_quant(bf16_to_f32(h[i]), inv) : int8_t(0);
+#pragma unroll
+    for (int m = 0; m < PER; m++) {
+        const int i = t + NT * m;
+        if (i < d) s_q[i] = am > 0.0f ? int8_quant(hv[m], inv) : int8_t(0);
+    }
     __syncthreads();
     return am > 0.0f ? am / 127.0f : 0.0f;
 }
 
+// Each wave scores up to kHeadRowsPerWave centroid rows (rows blockIdx.x * 4 + wave + k * gridDim.x
+// * 4); all of its row loads are issued first, so they are in flight while h is quantised.
+constexpr int kHeadRowsPerWave = 8;
+
+template <int MC>   // MC = d / 2048 rounded up: 16-byte centroid chunks per lane and row
 __global__ __launch_bounds__(256) void k_head_score(const uint16_t *__restrict__ h, int d,
                                                     const uint8_t *__restrict__ cent,
                                                     const float *__restrict__ cscale, int ncl,
@@ -55,9 +73,19 @@ __global__ __launch_bounds__(256) void k_head_score(const uint16_t *__restrict__
     __shared__ float s_red[4];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int nch = d / 32;   // 32-input chunks (16 centroid bytes) per row
+    uint4 cv[kHeadRowsPerWave][MC];
+    float csc[kHeadRowsPerWave];
+#pragma unroll
+    for (int k = 0; k < kHeadRowsPerWave; k++) {
+        const int c0 = blockIdx.x * 4 + wave + k * gridDim.x * 4;
+        const uint4 *row = reinterpret_cast<const uint4 *>(cent + int64_t(c0 < ncl ? c0 : 0) * (d / 2));
+#pragma unroll
+        for (int m = 0; m < MC; m++)
+            cv[k][m] = c0 < ncl && lane + 64 * m < nch ? row[lane + 64 * m] : make_uint4(0, 0, 0, 0);
+        csc[k] = c0 < ncl && lane == 0 ? cscale[c0] : 0.0f;
+    }
     const float sh = head_quant_h<256>(h, d, s_q, s_red);
-    // this lane's chunks (at most kHeadMaxD / 2048 = 2): even and odd input words, and sum(q)
-    constexpr int MC = kHeadMaxD / 32 / 64;
+    // this lane's chunks: even and odd input words, and sum(q)
     uint32_t xe[MC][4], xo[MC][4];
     int32_t sq = 0;
 #pragma unroll
@@ -84,15 +112,14 @@ __global__ __launch_bounds__(256) void k_head_score(const uint16_t *__restrict__
     }
     int32_t sqw[1] = {sq};
     group_reduce<1>(sqw, 64);   // sum(q) over the row, in every lane
-    for (int c0 = blockIdx.x * 4 + wave; c0 < ncl; c0 += gridDim.x * 4) {
-        const uint4 *row = reinterpret_cast<const uint4 *>(cent + int64_t(c0) * (d / 2));
-        uint4 cv[MC];
 #pragma unroll
-        for (int m = 0; m < MC; m++) cv[m] = lane + 64 * m < nch ? row[lane + 64 * m] : make_uint4(0, 0, 0, 0);
+    for (int k = 0; k < kHeadRowsPerWave; k++) {
+        const int c0 = blockIdx.x * 4 + wave + k * gridDim.x * 4;
+        if (c0 >= ncl) break;   // uniform over the wave
         int32_t acc[1] = {0};
 #pragma unroll
         for (int m = 0; m < MC; m++) {
-            const uint32_t wd[4] = {cv[m].x, cv[m].y, cv[m].z, cv[m].w};
+            const uint32_t wd[4] = {cv[k][m].x, cv[k][m].y, cv[k][m].z, cv[k][m].w};
 #pragma unroll
             for (int w = 0; w < 4; w++) {
                 acc[0] = __builtin_amdgcn_sdot4(int32_t(wd[w] & 0x0F0F0F0Fu), int32_t(xe[m][w]), acc[0], false);
@@ -100,7 +127,7 @@ __global__ __launch_bounds__(256) void k_head_score(const uint16_t *__restrict__
             }
         }
         group_reduce<1>(acc, 64);
-        if (lane == 0) scores[c0] = (float(acc[0] - 8 * sqw[0]) * sh) * cscale[c0];
+        if (lane == 0) scores[c0] = (float(acc[0] - 8 * sqw[0]) * sh) * csc[k];
     }
 }
 
@@ -113,8 +140,8 @@ __device__ __forceinline__ uint32_t score_key(float s)
 }
 
 // Rank selection: a cluster's place in the output is the number of clusters that come before it
-// (higher score key, or the same key and a lower id).  Each 16-lane group of a workgroup counts
-// that for one cluster against every cluster's key (the keys of all clusters are first copied
+// (higher score key, or the same key and a lower id).  Each wave counts that for two clusters
+// against every cluster's key (the keys of all clusters are first copied
 // into LDS as 64-bit composites key << 32 | ~id, so that "comes before" is one unsigned compare and
 // every composite is distinct), and the clusters of rank < top write their id to sel[rank].  The
 // ranks are exact integer counts, so the selection and its order do not depend on the launch
@@ -124,17 +151,33 @@ __global__ __launch_bounds__(256) void k_head_rank(const float *__restrict__ sco
 {
     extern __shared__ uint64_t s_c[];   // ncl composites
     const int t = threadIdx.x;
-    for (int i = t; i < ncl; i += 256)
-        s_c[i] = (uint64_t(score_key(scores[i])) << 32) | uint64_t(~uint32_t(i));
+    constexpr int PER = kHeadMaxClusters / 256;
+    float sv[PER];
+#pragma unroll
+    for (int m = 0; m < PER; m++) {   // every score load issued before the first is used
+        const int i = t + 256 * m;
+        sv[m] = i < ncl ? scores[i] : 0.0f;
+    }
+#pragma unroll
+    for (int m = 0; m < PER; m++) {
+        const int i = t + 256 * m;
+        if (i < ncl) s_c[i] = (uint64_t(score_key(sv[m])) << 32) | uint64_t(~uint32_t(i));
+    }
     __syncthreads();
-    const int g = t & 15;                       // lane in the cluster's group of 16
-    const int i = blockIdx.x * 16 + (t >> 4);   // the cluster this group ranks
-    const uint64_t ci = i < ncl ? s_c[i] : ~uint64_t(0);
-    int32_t cnt[1] = {0};
+    // each wave ranks two clusters: every key read from LDS is compared with both
+    const int lane = t & 63;
+    const int i0 = (blockIdx.x * 4 + (t >> 6)) * 2, i1 = i0 + 1;
+    const uint64_t c0 = i0 < ncl ? s_c[i0] : ~uint64_t(0), c1 = i1 < ncl ? s_c[i1] : ~uint64_t(0);
+    int32_t cnt[2] = {0, 0};
 #pragma unroll 4
-    for (int j = g; j < ncl; j += 16) cnt[0] += int32_t(s_c[j] > ci);
-    group_reduce<1>(cnt, 16);
-    if (g == 0 && i < ncl && cnt[0] < top) sel[cnt[0]] = i;
+    for (int j = lane; j < ncl; j += 64) {
+        const uint64_t cj = s_c[j];
+        cnt[0] += int32_t(cj > c0);
+        cnt[1] += int32_t(cj > c1);
+    }
+    group_reduce<2>(cnt, 64);
+    if (lane == 0 && i0 < ncl && cnt[0] < top) sel[cnt[0]] = i0;
+    if (lane == 1 && i1 < ncl && cnt[1] < top) sel[cnt[1]] = i1;
 }
 
 template <int M>   // M = d / 512: 8-input chunks per lane and row
@@ -150,7 +193,18 @@ __global__ __launch_bounds__(256) void k_head_logits(const uint16_t *__restrict_
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int j = blockIdx.x;
     const int64_t c = sel[j];
-    for (int i = t; i < d; i += 256) s_h[i] = bf16_to_f32(h[i]);
+    {
+        constexpr int PER = kHeadMaxD / 256;
+        float hv[PER];
+#pragma unroll
+        for (int m = 0; m < PER; m++) {   // every load issued before the first is used
+            const int i = t + 256 * m;
+            hv[m] = i < d ? bf16_to_f32(h[i]) : 0.0f;
+        }
+#pragma unroll
+        for (int m = 0; m < PER; m++)
+            if (t + 256 * m < d) s_h[t + 256 * m] = hv[m];
+    }
     __syncthreads();
     for (int r0 = wave; r0 < cs; r0 += 4 * RB) {
         uint4 buf[RB][M];
@@ -191,9 +245,14 @@ int launch_flash_head(const void *h, int d, const uint8_t *cent, const float *cs
     hipStream_t st = static_cast<hipStream_t>(stream);
     auto hp = static_cast<const uint16_t *>(h);
     float *scores = static_cast<float *>(ws);
-    const int nb = (ncl + 3) / 4 < 1024 ? (ncl + 3) / 4 : 1024;
-    k_head_score<<<nb, 256, 0, st>>>(hp, d, cent, cscale, ncl, scores);
-    k_head_rank<<<(ncl + 15) / 16, 256, size_t(ncl) * sizeof(uint64_t), st>>>(scores, ncl, top, sel);
+    // at most kHeadRowsPerWave rows per wave, and about 256 workgroups at the largest sizes
+    const int waves = (ncl + kHeadRowsPerWave - 1) / kHeadRowsPerWave;
+    const int nb = max((waves + 3) / 4, min((ncl + 3) / 4, 256));
+    if (d > 2048)
+        k_head_score<2><<<nb, 256, 0, st>>>(hp, d, cent, cscale, ncl, scores);
+    else
+        k_head_score<1><<<nb, 256, 0, st>>>(hp, d, cent, cscale, ncl, scores);
+    k_head_rank<<<(ncl + 7) / 8, 256, size_t(ncl) * sizeof(uint64_t), st>>>(scores, ncl, top, sel);
     auto wp = static_cast<const uint16_t *>(wc);
     switch (d / 512) {
     case 1: k_head_logits<1><<<top, 256, 0, st>>>(hp, d, wp, members, cs, sel, ids, logits); break;
