@@ -370,15 +370,15 @@ __device__ __forceinline__ void cvt_rows8(const int4 (&raw)[R][NCH][2], int bf16
         }
 }
 
-// Router logits.  Workgroup (experts 8 f .. 8 f + 7, tokens 8 g .. 8 g + 7), 256 threads: thread t
-// holds the 8-element chunks t + 256 i of the 8 tokens and of the 8 router rows (every load issued
+// Router logits.  Workgroup (experts 4 f .. 4 f + 3, tokens 8 g .. 8 g + 7), 256 threads: thread t
+// holds the 8-element chunks t + 256 i of the 8 tokens and of the 4 router rows (every load issued
 // at once) and forms the canonical partial of each (expert, token) pair and each token's sum of
 // squares; the partials go to LDS and each wave adds those of two tokens in the canonical tree
 // (4 partials per lane, then wave_sum), so the pre-RMSNorm factor multiplies the logits in the same
 // wave.  With QP > 0 the workgroups also write the tokens' activation codes (quantize_token) and
 // their scale words, token u of a group by expert group u: the router has every chunk of its
 // tokens in registers already.
-constexpr int kRouteExp = 8;
+constexpr int kRouteExp = 4;   // 8: a 64-token batched call 1.3 us slower (fewer, busier workgroups)
 
 template <int NCH, int QP>
 __global__ __launch_bounds__(256) void k_route(const void *__restrict__ x, int x_bf16,
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(256) void k_route(const void *__restrict__ x, int x
         }
     }
     __syncthreads();
-    // wave w: tokens 2w, 2w + 1 -- the sum of squares, then the 8 logits
+    // wave w: tokens 2w, 2w + 1 -- the sum of squares, then the kRouteExp logits
     float ssv[2];
 #pragma unroll
     for (int h = 0; h < 2; h++) {
@@ -1147,6 +1147,73 @@ __global__ __launch_bounds__(256) void k_bat_dn(BatchedArgs a, LayerPtrs lp, uin
 
 // out[t] = ((x[t] + g_0 y_0) + g_1 y_1) + ..., j in selection order.  Slots whose expert id is
 // outside [0, E) contribute nothing (the expert kernels do not compute them either).  Workgroup
+// out = x + sum_j g_j y_j over the slots j < k (in slot order) whose expert id is in [0, E), every
+// product and every sum one fp32 rounding, for the 8-element chunk c of token tok; x and out in bf16
+// (XB / OB) or fp32, y rows [T k][d] fp32.  Every load of the chunk is issued before the first is
+// used (the residual chunk, the y rows of eight slots, their ids and gates).  The y row of every slot
+// exists (unwritten for slots without a valid expert, and then unused).
+template <bool XB, bool OB>
+__device__ __forceinline__ void combine_chunk(const void *__restrict__ x, void *__restrict__ out,
+                                              const int32_t *__restrict__ ids,
+                                              const float *__restrict__ gates,
+                                              const float *__restrict__ ybuf, int64_t tok, int c,
+                                              int d, int k, int E)
+{
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    float o[8];
+    if constexpr (XB) {
+        const int4 q = reinterpret_cast<const int4 *>(static_cast<const uint16_t *>(x) + tok * d)[c];
+        const uint32_t w[4] = {uint32_t(q.x), uint32_t(q.y), uint32_t(q.z), uint32_t(q.w)};
+#pragma unroll
+        for (int jj = 0; jj < 8; jj++) o[jj] = bf16_to_f32(uint16_t(w[jj >> 1] >> (16 * (jj & 1))));
+    } else {
+        const f4 *p = reinterpret_cast<const f4 *>(static_cast<const float *>(x) + tok * d) + 2 * c;
+        const f4 p0 = p[0], p1 = p[1];
+        o[0] = p0.x; o[1] = p0.y; o[2] = p0.z; o[3] = p0.w;
+        o[4] = p1.x; o[5] = p1.y; o[6] = p1.z; o[7] = p1.w;
+    }
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        f4 yv[8][2];
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const int j = j0 + u < k ? j0 + u : k - 1;
+            const f4 *yp = reinterpret_cast<const f4 *>(ybuf + (tok * k + j) * d + 8 * c);
+            yv[u][0] = yp[0];
+            yv[u][1] = yp[1];
+        }
+        float g[8];
+        bool ok[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const int j = j0 + u < k ? j0 + u : k - 1;
+            const int id = ids[tok * k + j];
+            ok[u] = j0 + u < k && id >= 0 && id < E;
+            g[u] = gates[tok * k + j];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            if (ok[u]) {
+                const float yy[8] = {yv[u][0].x, yv[u][0].y, yv[u][0].z, yv[u][0].w,
+                                     yv[u][1].x, yv[u][1].y, yv[u][1].z, yv[u][1].w};
+#pragma unroll
+                for (int q = 0; q < 8; q++) o[q] = o[q] + g[u] * yy[q];
+            }
+        }
+    }
+    if constexpr (OB) {
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+            w[q] = uint32_t(f32_to_bf16(o[2 * q])) | (uint32_t(f32_to_bf16(o[2 * q + 1])) << 16);
+        reinterpret_cast<int4 *>(static_cast<uint16_t *>(out) + tok * d)[c] =
+            make_int4(int(w[0]), int(w[1]), int(w[2]), int(w[3]));
+    } else {
+        f4 *op = reinterpret_cast<f4 *>(static_cast<float *>(out) + tok * d) + 2 * c;
+        op[0] = f4{o[0], o[1], o[2], o[3]};
+        op[1] = f4{o[4], o[5], o[6], o[7]};
+    }
+}
+
 // (token, s) covers the 8-element chunks s * blockDim + i of the token, one per thread (a small
 // batch takes one-wave workgroups so that its few tokens still spread over the compute units);
 // every load of a chunk is issued at once.
@@ -1157,70 +1224,11 @@ __global__ __launch_bounds__(256) void k_bat_combine(BatchedArgs a, const void *
                                                      const float *__restrict__ gates,
                                                      uint8_t *__restrict__ ws)
 {
-    typedef float f4 __attribute__((ext_vector_type(4)));
-    const int d = a.dm.d, k = a.dm.k, E = a.dm.E, nch = d >> 3;
-    const int64_t tok = blockIdx.x;
-    const float *ybuf = reinterpret_cast<const float *>(ws + a.L.y);
-    {
-        const int c = int(blockIdx.y * blockDim.x + threadIdx.x);
-        if (c >= nch) return;
-        float o[8];
-        if constexpr (XB) {
-            const int4 q = reinterpret_cast<const int4 *>(static_cast<const uint16_t *>(x) + tok * d)[c];
-            const uint32_t w[4] = {uint32_t(q.x), uint32_t(q.y), uint32_t(q.z), uint32_t(q.w)};
-#pragma unroll
-            for (int jj = 0; jj < 8; jj++) o[jj] = bf16_to_f32(uint16_t(w[jj >> 1] >> (16 * (jj & 1))));
-        } else {
-            const f4 *p = reinterpret_cast<const f4 *>(static_cast<const float *>(x) + tok * d) + 2 * c;
-            const f4 p0 = p[0], p1 = p[1];
-            o[0] = p0.x; o[1] = p0.y; o[2] = p0.z; o[3] = p0.w;
-            o[4] = p1.x; o[5] = p1.y; o[6] = p1.z; o[7] = p1.w;
-        }
-        for (int j0 = 0; j0 < k; j0 += 8) {
-            // every load of the chunk is issued before the first is used: the residual chunk, the y
-            // rows of the slots (still in the last-level cache after the expert kernel, for the
-            // most part), the ids and the gates.  The y row of every slot exists (unwritten for
-            // slots without a valid expert, and then unused).
-            f4 yv[8][2];
-#pragma unroll
-            for (int u = 0; u < 8; u++) {
-                const int j = j0 + u < k ? j0 + u : k - 1;
-                const f4 *yp = reinterpret_cast<const f4 *>(ybuf + (tok * k + j) * d + 8 * c);
-                yv[u][0] = yp[0];
-                yv[u][1] = yp[1];
-            }
-            float g[8];
-            bool ok[8];
-#pragma unroll
-            for (int u = 0; u < 8; u++) {
-                const int j = j0 + u < k ? j0 + u : k - 1;
-                const int id = ids[tok * k + j];
-                ok[u] = j0 + u < k && id >= 0 && id < E;
-                g[u] = gates[tok * k + j];
-            }
-#pragma unroll
-            for (int u = 0; u < 8; u++) {
-                if (ok[u]) {
-                    const float yy[8] = {yv[u][0].x, yv[u][0].y, yv[u][0].z, yv[u][0].w,
-                                         yv[u][1].x, yv[u][1].y, yv[u][1].z, yv[u][1].w};
-#pragma unroll
-                    for (int q = 0; q < 8; q++) o[q] = o[q] + g[u] * yy[q];
-                }
-            }
-            if (j0 + 8 < k) continue;
-            if constexpr (OB) {
-                uint32_t w[4];
-#pragma unroll
-                for (int q = 0; q < 4; q++) w[q] = pack_bf16x2(o[2 * q], o[2 * q + 1]);
-                reinterpret_cast<int4 *>(static_cast<uint16_t *>(out) + tok * d)[c] =
-                    make_int4(int(w[0]), int(w[1]), int(w[2]), int(w[3]));
-            } else {
-                f4 *op = reinterpret_cast<f4 *>(static_cast<float *>(out) + tok * d) + 2 * c;
-                op[0] = f4{o[0], o[1], o[2], o[3]};
-                op[1] = f4{o[4], o[5], o[6], o[7]};
-            }
-        }
-    }
+    const int d = a.dm.d, nch = d >> 3;
+    const int c = int(blockIdx.y * blockDim.x + threadIdx.x);
+    if (c >= nch) return;
+    combine_chunk<XB, OB>(x, out, ids, gates, reinterpret_cast<const float *>(ws + a.L.y),
+                          int64_t(blockIdx.x), c, d, a.dm.k, a.dm.E);
 }
 
 void launch_combine(const BatchedArgs &a, const void *x, int in_bf16, void *out, int out_bf16,

@@ -157,3 +157,27 @@ def test_batched_fp32_input_served_by_dot4_kernels(full):
         o = oracle.ffn_token(full.ora, x[t].double().numpy(), oids[t], og[t])
         got = out[t].cpu().numpy()
         assert np.max(np.abs(got - o)) <= 1e-4 * np.max(np.abs(o)), t
+
+
+@pytest.mark.parametrize("T", [40, 300])
+def test_batched_int8_invalid_slots_contribute_nothing(full, T):
+    # slots whose expert id is outside [0, E) contribute nothing; a token with no valid slot gets
+    # out = x.  Expected: the oracle's int8 spec with those slots given gate 0 (an exact zero term)
+    # and a valid id.  T = 40: small tiles built in every workgroup; T = 300: k_group's tiles
+    x = synth.activations(synth.PREFILL_4096, T, seed=81).cuda()
+    _, ids, gates = tw.moe_route_topk(x, full.gpu.w_router, 8)
+    ids, gates = ids.clone(), gates.clone()
+    r = np.random.default_rng(T)
+    bad = torch.as_tensor(r.random(ids.shape) < 0.2, device=ids.device)
+    bad[5] = True                                   # token 5: no valid slot
+    bad[7] = False
+    badval = torch.as_tensor(r.choice([-1, 256, 1000, -7], ids.shape), device=ids.device,
+                             dtype=ids.dtype)
+    ids = torch.where(bad, badval, ids)
+    step("batched int8 with invalid slots, T=%d" % T)
+    out = run_int8(full.gpu, x, ids, gates)
+    ids_o = torch.where(bad, torch.zeros_like(ids), ids).cpu().numpy()
+    gates_o = torch.where(bad, torch.zeros_like(gates), gates).cpu().numpy()
+    ref = oracle.ffn_batch_i8(full.ora, x.cpu(), ids_o, gates_o, n_threads=NTH)
+    assert np.array_equal(bits(out), ref.view(np.uint32))
+    assert torch.equal(out[5], x[5].float())
