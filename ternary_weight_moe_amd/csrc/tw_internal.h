@@ -72,7 +72,10 @@ inline DecodeWs decode_ws_layout(const Dims &dm) {
 
 // ---- batched workspace ------------------------------------------------------------------------
 struct BatchedWs {
-    size_t ctrl, logits, ids, gates, tinfo, xdig, counts, offsets, pairs, tiles, tilemeta, h, y, total;
+    // y: fp32 y rows (v_dot4 path; float activations on the matrix cores), or with int8 activations
+    // on the matrix cores the int32 down sums that do not fit y16; y16 / shp (int8 activations
+    // only): 16-bit down sums and each pair's s_h (zero-size otherwise)
+    size_t ctrl, logits, ids, gates, tinfo, xdig, counts, offsets, pairs, tiles, tilemeta, h, y, y16, shp, total;
     int64_t spare_row;   // first of kSpareRows y rows behind the last pair: stores of padding
                          // tokens land there (workgroup b uses row spare_row + b % kSpareRows)
 };
@@ -103,6 +106,8 @@ inline BatchedWs batched_ws_layout(const Dims &dm, int64_t T, int planes) {
     w.tilemeta = o; o += align256(2 * sizeof(int32_t) * size_t(max_tiles(dm, T, kMinTile) + 16));
     w.h = o;       o += align256(sizeof(float) * pairs * dm.F);
     w.y = o;       o += align256(sizeof(float) * (pairs + kSpareRows) * dm.d);
+    w.y16 = o;     o += planes == 1 ? align256(sizeof(int16_t) * (pairs + kSpareRows) * dm.d) : 0;
+    w.shp = o;     o += planes == 1 ? align256(sizeof(float) * pairs) : 0;
     w.spare_row = int64_t(pairs);
     w.total = o;
     return w;

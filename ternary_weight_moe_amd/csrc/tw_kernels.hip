@@ -1145,19 +1145,31 @@ __global__ __launch_bounds__(256) void k_bat_dn(BatchedArgs a, LayerPtrs lp, uin
     }
 }
 
-// out[t] = ((x[t] + g_0 y_0) + g_1 y_1) + ..., j in selection order.  Slots whose expert id is
-// outside [0, E) contribute nothing (the expert kernels do not compute them either).  Workgroup
-// out = x + sum_j g_j y_j over the slots j < k (in slot order) whose expert id is in [0, E), every
-// product and every sum one fp32 rounding, for the 8-element chunk c of token tok; x and out in bf16
-// (XB / OB) or fp32, y rows [T k][d] fp32.  Every load of the chunk is issued before the first is
-// used (the residual chunk, the y rows of eight slots, their ids and gates).  The y row of every slot
-// exists (unwritten for slots without a valid expert, and then unused).
-template <bool XB, bool OB>
+// Rows of 16-bit down sums (int8 activations on the matrix cores): the down sum of a (pair, output)
+// is an int32 of at most 127 F in magnitude; it is kept as an int16 when it lies in
+// [-32767, 32767] and otherwise as the marker -32768, with the int32 itself in the same position of
+// the 32-bit rows.  y = (float(sum) * s_h) * s_down[e][r] is formed here, in the same fp32 operations
+// as the v_dot4 and batch-1 paths, from the pair's s_h and the expert's down scales.
+struct Y16Rows {
+    const int16_t *y16;     // [T k + spare][d]
+    const int32_t *ywide;   // [T k + spare][d], read only at markers
+    const float *s_h;       // [T k]
+    const float *s_down;    // the layer's [E][d]
+};
+
+// out[t] = ((x[t] + g_0 y_0) + g_1 y_1) + ..., over the slots j < k in selection order whose expert
+// id is in [0, E) (the others contribute nothing: the expert kernels do not compute them either);
+// every product and every sum is one fp32 rounding.  One call covers the 8-element chunk c of token
+// tok; x and out in bf16 (XB / OB) or fp32; y rows [T k][d] fp32, or 16-bit sums (Y16).  Every load
+// of the chunk is issued before the first is used (the residual chunk, the y rows of eight slots,
+// their ids and gates, and with Y16 the s_h and down scales).  The y row of every slot exists
+// (unwritten for slots without a valid expert, and then unused).
+template <bool XB, bool OB, bool Y16>
 __device__ __forceinline__ void combine_chunk(const void *__restrict__ x, void *__restrict__ out,
                                               const int32_t *__restrict__ ids,
                                               const float *__restrict__ gates,
-                                              const float *__restrict__ ybuf, int64_t tok, int c,
-                                              int d, int k, int E)
+                                              const float *__restrict__ ybuf, const Y16Rows &yr,
+                                              int64_t tok, int c, int d, int k, int E)
 {
     typedef float f4 __attribute__((ext_vector_type(4)));
     float o[8];
@@ -1173,30 +1185,66 @@ __device__ __forceinline__ void combine_chunk(const void *__restrict__ x, void *
         o[4] = p1.x; o[5] = p1.y; o[6] = p1.z; o[7] = p1.w;
     }
     for (int j0 = 0; j0 < k; j0 += 8) {
-        f4 yv[8][2];
-#pragma unroll
-        for (int u = 0; u < 8; u++) {
-            const int j = j0 + u < k ? j0 + u : k - 1;
-            const f4 *yp = reinterpret_cast<const f4 *>(ybuf + (tok * k + j) * d + 8 * c);
-            yv[u][0] = yp[0];
-            yv[u][1] = yp[1];
-        }
+        int id[8];
         float g[8];
         bool ok[8];
 #pragma unroll
         for (int u = 0; u < 8; u++) {
             const int j = j0 + u < k ? j0 + u : k - 1;
-            const int id = ids[tok * k + j];
-            ok[u] = j0 + u < k && id >= 0 && id < E;
+            id[u] = ids[tok * k + j];
+            ok[u] = j0 + u < k && id[u] >= 0 && id[u] < E;
             g[u] = gates[tok * k + j];
+        }
+        float yy[8][8];
+        if constexpr (Y16) {
+            int4 yq[8];
+            float sh[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                const int j = j0 + u < k ? j0 + u : k - 1;
+                yq[u] = reinterpret_cast<const int4 *>(yr.y16 + (tok * k + j) * d)[c];
+                sh[u] = yr.s_h[tok * k + j];
+            }
+            f4 sd[8][2];
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                const f4 *sp = reinterpret_cast<const f4 *>(yr.s_down + int64_t(ok[u] ? id[u] : 0) * d) + 2 * c;
+                sd[u][0] = sp[0];
+                sd[u][1] = sp[1];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                const int j = j0 + u < k ? j0 + u : k - 1;
+                const uint32_t w[4] = {uint32_t(yq[u].x), uint32_t(yq[u].y), uint32_t(yq[u].z), uint32_t(yq[u].w)};
+                const float sdv[8] = {sd[u][0].x, sd[u][0].y, sd[u][0].z, sd[u][0].w,
+                                      sd[u][1].x, sd[u][1].y, sd[u][1].z, sd[u][1].w};
+#pragma unroll
+                for (int q = 0; q < 8; q++) {
+                    int32_t v = int32_t(int16_t(uint16_t(w[q >> 1] >> (16 * (q & 1)))));
+                    if (v == -32768 && ok[u]) v = yr.ywide[(tok * k + j) * d + 8 * c + q];
+                    yy[u][q] = (float(v) * sh[u]) * sdv[q];
+                }
+            }
+        } else {
+            f4 yv[8][2];
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                const int j = j0 + u < k ? j0 + u : k - 1;
+                const f4 *yp = reinterpret_cast<const f4 *>(ybuf + (tok * k + j) * d + 8 * c);
+                yv[u][0] = yp[0];
+                yv[u][1] = yp[1];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                yy[u][0] = yv[u][0].x; yy[u][1] = yv[u][0].y; yy[u][2] = yv[u][0].z; yy[u][3] = yv[u][0].w;
+                yy[u][4] = yv[u][1].x; yy[u][5] = yv[u][1].y; yy[u][6] = yv[u][1].z; yy[u][7] = yv[u][1].w;
+            }
         }
 #pragma unroll
         for (int u = 0; u < 8; u++) {
             if (ok[u]) {
-                const float yy[8] = {yv[u][0].x, yv[u][0].y, yv[u][0].z, yv[u][0].w,
-                                     yv[u][1].x, yv[u][1].y, yv[u][1].z, yv[u][1].w};
 #pragma unroll
-                for (int q = 0; q < 8; q++) o[q] = o[q] + g[u] * yy[q];
+                for (int q = 0; q < 8; q++) o[q] = o[q] + g[u] * yy[u][q];
             }
         }
     }
@@ -1217,30 +1265,43 @@ __device__ __forceinline__ void combine_chunk(const void *__restrict__ x, void *
 // (token, s) covers the 8-element chunks s * blockDim + i of the token, one per thread (a small
 // batch takes one-wave workgroups so that its few tokens still spread over the compute units);
 // every load of a chunk is issued at once.
-template <bool XB, bool OB>
+template <bool XB, bool OB, bool Y16>
 __global__ __launch_bounds__(256) void k_bat_combine(BatchedArgs a, const void *__restrict__ x,
                                                      void *__restrict__ out,
                                                      const int32_t *__restrict__ ids,
                                                      const float *__restrict__ gates,
-                                                     uint8_t *__restrict__ ws)
+                                                     uint8_t *__restrict__ ws, const float *__restrict__ s_down)
 {
     const int d = a.dm.d, nch = d >> 3;
     const int c = int(blockIdx.y * blockDim.x + threadIdx.x);
     if (c >= nch) return;
-    combine_chunk<XB, OB>(x, out, ids, gates, reinterpret_cast<const float *>(ws + a.L.y),
-                          int64_t(blockIdx.x), c, d, a.dm.k, a.dm.E);
+    const Y16Rows yr{reinterpret_cast<const int16_t *>(ws + a.L.y16), reinterpret_cast<const int32_t *>(ws + a.L.y),
+                     reinterpret_cast<const float *>(ws + a.L.shp), s_down};
+    combine_chunk<XB, OB, Y16>(x, out, ids, gates, reinterpret_cast<const float *>(ws + a.L.y), yr,
+                               int64_t(blockIdx.x), c, d, a.dm.k, a.dm.E);
 }
 
+// s_down != nullptr: the y rows are 16-bit down sums (grouped MFMA path, int8 activations).
 void launch_combine(const BatchedArgs &a, const void *x, int in_bf16, void *out, int out_bf16,
-                    const int32_t *ids, const float *gates, uint8_t *ws, void *stream)
+                    const int32_t *ids, const float *gates, uint8_t *ws, const float *s_down,
+                    void *stream)
 {
     const int nt = a.T >= 1024 ? 256 : 64, nch = a.dm.d >> 3;
     const dim3 g(unsigned(a.T), unsigned((nch + nt - 1) / nt));
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (in_bf16 && out_bf16) k_bat_combine<true, true><<<g, nt, 0, st>>>(a, x, out, ids, gates, ws);
-    else if (in_bf16) k_bat_combine<true, false><<<g, nt, 0, st>>>(a, x, out, ids, gates, ws);
-    else if (out_bf16) k_bat_combine<false, true><<<g, nt, 0, st>>>(a, x, out, ids, gates, ws);
-    else k_bat_combine<false, false><<<g, nt, 0, st>>>(a, x, out, ids, gates, ws);
+#define TW_COMB(XB, OB, Y) k_bat_combine<XB, OB, Y><<<g, nt, 0, st>>>(a, x, out, ids, gates, ws, s_down)
+    if (s_down) {
+        if (in_bf16 && out_bf16) TW_COMB(true, true, true);
+        else if (in_bf16) TW_COMB(true, false, true);
+        else if (out_bf16) TW_COMB(false, true, true);
+        else TW_COMB(false, false, true);
+    } else {
+        if (in_bf16 && out_bf16) TW_COMB(true, true, false);
+        else if (in_bf16) TW_COMB(true, false, false);
+        else if (out_bf16) TW_COMB(false, true, false);
+        else TW_COMB(false, false, false);
+    }
+#undef TW_COMB
 }
 
 inline hipStream_t S(void *s) { return static_cast<hipStream_t>(s); }
@@ -1323,7 +1384,9 @@ int batched_p(const Dims &dm, const LayerPtrs &lp, int64_t T, const void *x_in, 
         if (r != 0) return r;
         r = launch_grouped_mfma(dm, lp, T, P, tile, a.L, w, self ? ids : nullptr, stream);
         if (r != 0) return r;
-        launch_combine(a, x_in, in_bf16, x_out, out_bf16, ids, gates, w, stream);
+        // int8 activations in 64-token tiles: the grouped kernel stored 16-bit down sums
+        launch_combine(a, x_in, in_bf16, x_out, out_bf16, ids, gates, w,
+                       INT8 && tile >= 64 ? lp.s_down : nullptr, stream);
         return last_error();
     }
     const int rg = launch_group(a, ids, w, kTileTokens, stream);
@@ -1337,7 +1400,7 @@ int batched_p(const Dims &dm, const LayerPtrs &lp, int64_t T, const void *x_in, 
         k_bat_dn<P, INT8, 2><<<kBatG, 256, size_t(td) * P * dm.F, S(stream)>>>(a, lp, w, td);
     else
         k_bat_dn<P, INT8, 16><<<kBatG, 256, size_t(td) * P * dm.F, S(stream)>>>(a, lp, w, td);
-    launch_combine(a, x_in, in_bf16, x_out, out_bf16, ids, gates, w, stream);
+    launch_combine(a, x_in, in_bf16, x_out, out_bf16, ids, gates, w, nullptr, stream);
     return last_error();
 }
 

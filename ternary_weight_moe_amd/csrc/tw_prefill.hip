@@ -22,9 +22,13 @@
 //      and h = SiLU(gate) * up in fp32 in the order of the specification, in registers;
 //   3. per token: max |h| over all F rows (registers, lane shuffles, LDS over waves), h re-quantised
 //      (int8 absmax) or split into digit planes into LDS;
-//   4. down: wave w owns d/W output rows; same scheme with the down codes; y in fp32, four
-//      consecutive outputs of a token per lane stored as one 16-byte vector per (token, slot) pair
-//      for the ordered combine.
+//   4. down: wave w owns d/W output rows; same scheme with the down codes; four consecutive outputs
+//      of a token per lane stored as one vector per (token, slot) pair for the ordered combine:
+//      y in fp32, except for int8 activations in 64-token tiles (prefill-shaped calls): there the
+//      int32 down sums themselves are stored as int16 (|sum| <= 127 F; a sum outside the int16
+//      range is marked and kept in 32-bit rows), and the combine forms y = (sum s_h) s_down from
+//      them, which halves the bytes of the y round trip.  Small tiles keep fp32 y: their y traffic
+//      is small and the combine's extra scale loads would cost more than it saves.
 // K order: lane group g of an MFMA at step (S, s) covers inputs 256 S + 64 g + 16 s .. +16 -- a
 // permutation of the inputs shared by both operands, so every int32 sum is the exact dot product.
 // Work items are mapped to workgroups so that pairs of consecutive tiles (usually one expert) run on
@@ -96,6 +100,8 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
     static_assert(D % 256 == 0 && F % 256 == 0 && F % (16 * W) == 0 && D % (16 * W) == 0, "shape");
     static_assert((P == 1 || P == 2) && (MT * P) % 16 == 0 && MT <= NT, "tile");
     constexpr bool INT8 = P == 1;
+    // int8 activations in large tiles: 16-bit down sums (the combine forms y); else fp32 y
+    constexpr bool Y16 = INT8 && MT >= 64;
     // The activation tile has MT * P rows (token m, plane pl at row m P + pl); an MFMA takes 16 of
     // them, so the 16 result columns of sub-tile rs are 16 / P tokens x P planes: column l16 is
     // token rs * TPS + l16 / P, plane l16 % P.  With two planes the two lanes of a token combine
@@ -212,7 +218,7 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
             const int n = u - NGU;
             slot[0] = *reinterpret_cast<const int4 *>(dbase + n * 16 * (F / 4) + dofs);
             if (SD > 1) slot[1] = *reinterpret_cast<const int4 *>(dbase + n * 16 * (F / 4) + 64 + dofs);
-            dsc[n] = *reinterpret_cast<const float4 *>(dsbase + n * 16 + sofs);
+            if constexpr (!Y16) dsc[n] = *reinterpret_cast<const float4 *>(dsbase + n * 16 + sofs);
         }
     };
 #pragma unroll
@@ -222,6 +228,9 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
     const float *tinfo = reinterpret_cast<const float *>(ws + L.tinfo);
     const int8_t *xdig = reinterpret_cast<const int8_t *>(ws + L.xdig);
     float *ybuf = reinterpret_cast<float *>(ws + L.y);
+    int16_t *y16 = reinterpret_cast<int16_t *>(ws + L.y16);    // int8 activations: 16-bit sums,
+    int32_t *ywide = reinterpret_cast<int32_t *>(ws + L.y);    // the sums that do not fit them,
+    float *shp = reinterpret_cast<float *>(ws + L.shp);        // and each pair's s_h
     const int k = dm.k;
     const int pl = l16 % P;                         // this lane's plane in every sub-tile
     const int nv = meta.y;                          // tokens in this tile (1 .. MT)
@@ -351,10 +360,12 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
 #pragma unroll
         for (int w = 0; w < W; w++) am = fmaxf(am, s_pam[w][t]);
         s_amx[t] = am;
-        if (INT8)
+        if (INT8) {
             s_hk[t] = am > 0.0f ? am / 127.0f : 0.0f;
-        else
+            if (Y16 && s_pair[t] >= 0) shp[s_pair[t]] = s_hk[t];   // the combine forms y from it
+        } else {
             s_hk[t] = __int_as_float(float_digit_shift(am, P));
+        }
     }
     __syncthreads();
 #pragma unroll
@@ -416,21 +427,39 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
         for (int rs = 0; rs < RS; rs++) {
             if (rs > 0 && rs >= rsv) break;
             const int m = rs * TPS + l16 / P, pr = s_pair[m];
-            const float hk = s_hk[m];
-            float y[4];
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                if constexpr (INT8) {
-                    y[r] = (float(acc[rs][r]) * hk) * comp(dsc[n], r);
-                } else {
-                    const int32_t o = dpp_i<kDppXor1>(acc[rs][r]);
-                    const int32_t ad[2] = {pl == 0 ? acc[rs][r] : o, pl == 0 ? o : acc[rs][r]};
-                    y[r] = float_value<2>(ad, __float_as_int(hk)) * comp(dsc[n], r);
-                }
-            }
             // the second lane of a two-plane token holds the same values: it writes a spare row
             const int64_t row = pr >= 0 && pl == 0 ? int64_t(pr) : L.spare_row + (blockIdx.x % kSpareRows);
-            *reinterpret_cast<f4 *>(ybuf + row * D + R0 + 4 * g4) = f4{y[0], y[1], y[2], y[3]};
+            if constexpr (Y16) {
+                // 16-bit sums; a sum outside [-32767, 32767] is stored as the marker -32768 and the
+                // four int32 sums of this lane go to the 32-bit rows as well
+                uint32_t hv[2] = {0u, 0u};
+                bool wide = false;
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int32_t v = acc[rs][r];
+                    const bool fits = v >= -32767 && v <= 32767;
+                    wide = wide || !fits;
+                    hv[r >> 1] |= (uint32_t(fits ? v : -32768) & 0xffffu) << (16 * (r & 1));
+                }
+                *reinterpret_cast<uint2 *>(y16 + row * D + R0 + 4 * g4) = make_uint2(hv[0], hv[1]);
+                if (wide)
+                    *reinterpret_cast<int4 *>(ywide + row * D + R0 + 4 * g4) =
+                        make_int4(acc[rs][0], acc[rs][1], acc[rs][2], acc[rs][3]);
+            } else {
+                const float hk = s_hk[m];
+                float y[4];
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    if constexpr (INT8) {
+                        y[r] = (float(acc[rs][r]) * hk) * comp(dsc[n], r);
+                    } else {
+                        const int32_t o = dpp_i<kDppXor1>(acc[rs][r]);
+                        const int32_t ad[2] = {pl == 0 ? acc[rs][r] : o, pl == 0 ? o : acc[rs][r]};
+                        y[r] = float_value<2>(ad, __float_as_int(hk)) * comp(dsc[n], r);
+                    }
+                }
+                *reinterpret_cast<f4 *>(ybuf + row * D + R0 + 4 * g4) = f4{y[0], y[1], y[2], y[3]};
+            }
         }
     }
 }

@@ -127,7 +127,7 @@ def test_batched_errors(L):
     l = layer()
     need = L.ternary_moe_batched_workspace_bytes(C.byref(l), 64, 0)
     need8 = L.ternary_moe_batched_workspace_bytes(C.byref(l), 64, 1)
-    assert need > need8 > 0
+    assert need > 0 and need8 > 0
     assert L.ternary_moe_batched_workspace_bytes(C.byref(l), 64, 7) == 0
     call = lambda T=64, xi=A[8], idt=1, xo=A[9], odt=1, act=0, ids=None, g=None, ws=A[10], wsb=need, ll=None: \
         L.ternary_moe_ffn_batched(C.byref(ll if ll is not None else l), T, xi, idt, xo, odt, act,
@@ -138,6 +138,7 @@ def test_batched_errors(L):
     assert call(ids=A[11]) == E_NULL                                  # ids without gates
     assert call(xi=None) == E_NULL
     assert call(wsb=need - 1) == E_WS
+    assert call(act=1, wsb=need8 - 1) == E_WS
     assert call(xo=A[8] + 64) == E_ALIAS
     assert call(T=0, xi=None, xo=None, ws=None) == OK
     assert call(act=1, ll=layer(pre=1), wsb=need8) == E_UNSUP         # int8 with pre-norm

@@ -12,7 +12,7 @@ import torch
 import oracle
 import synth
 import ternary_weight_moe_amd as tw
-from parity_util import make_pair, require_gpu, step
+from parity_util import LayerPair, make_pair, require_gpu, step
 
 pytestmark = pytest.mark.gpu
 
@@ -181,3 +181,37 @@ def test_batched_int8_invalid_slots_contribute_nothing(full, T):
     ref = oracle.ffn_batch_i8(full.ora, x.cpu(), ids_o, gates_o, n_threads=NTH)
     assert np.array_equal(bits(out), ref.view(np.uint32))
     assert torch.equal(out[5], x[5].float())
+
+
+@pytest.mark.parametrize("T", [40, 300])
+def test_int8_down_sums_outside_int16(T):
+    # With int8 activations in 64-token tiles the grouped kernel keeps each down sum as an int16 and
+    # marks the ones outside [-32767, 32767], which then come from 32-bit rows.  Expert 0 here has all-+1 gate and
+    # up rows with equal scales, and every input of the tokens is positive, so its h is the same
+    # value in all F rows and quantises to 127 everywhere; its down row r has +1 in the first
+    # r mod 513 positions and -1 after them, so the down sums are 127 (2 a - 512) for every a in
+    # 0 .. 512: from -65024 to 65024, with 32766 the largest that fits and 33020 the smallest that
+    # does not.  Expected: the oracle's int8 spec bit for bit.  T = 40: small self-grouped tiles
+    # (fp32 y rows); T = 300: 64-token tiles from the grouping kernel (16-bit sums).
+    wl = synth.PREFILL_4096
+    E, k, d, F = 8, 4, wl.d_model, wl.d_ff
+    w = synth.layer_weights(wl, 0, n_experts=E)
+    w["t_gate"][0] = 1
+    w["t_up"][0] = 1
+    w["s_gate"][0] = 0.03
+    w["s_up"][0] = 0.02
+    a = torch.arange(d).remainder(F + 1)
+    w["t_down"][0] = torch.where(torch.arange(F)[None, :] < a[:, None], 1, -1).to(torch.int8)
+    pair = LayerPair(w, k, False)
+    x = (synth.activations(wl, T, seed=83).float().abs() + 0.25).to(torch.bfloat16)
+    r = np.random.default_rng(T)
+    ids_np = np.stack([np.concatenate([[0], r.permutation(np.arange(1, E))[:k - 1]]) for _ in range(T)])
+    g = r.random((T, k)) + 0.05
+    gates_np = (g / g.sum(1, keepdims=True)).astype(np.float32)
+    sums = 127 * (2 * a.numpy() - F)
+    assert (np.abs(sums) > 32767).sum() > 500 and (np.abs(sums) <= 32767).sum() > 500
+    step("batched int8 with down sums outside int16, T=%d" % T)
+    out = run_int8(pair.gpu, x.cuda(), torch.from_numpy(ids_np.astype(np.int32)).cuda(),
+                   torch.from_numpy(gates_np).cuda())
+    ref = oracle.ffn_batch_i8(pair.ora, x, ids_np.astype(np.int32), gates_np, n_threads=NTH)
+    assert np.array_equal(bits(out), ref.view(np.uint32))
