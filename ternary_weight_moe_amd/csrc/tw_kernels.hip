@@ -1164,14 +1164,15 @@ struct Y16Rows {
 // of the chunk is issued before the first is used (the residual chunk, the y rows of eight slots,
 // their ids and gates, and with Y16 the s_h and down scales).  The y row of every slot exists
 // (unwritten for slots without a valid expert, and then unused).
-template <bool XB, bool OB, bool Y16>
+template <bool XB, bool OB, bool Y16, int KK>
 __device__ __forceinline__ void combine_chunk(const void *__restrict__ x, void *__restrict__ out,
                                               const int32_t *__restrict__ ids,
                                               const float *__restrict__ gates,
                                               const float *__restrict__ ybuf, const Y16Rows &yr,
-                                              int64_t tok, int c, int d, int k, int E)
+                                              int64_t tok, int c, int d, int k_rt, int E)
 {
     typedef float f4 __attribute__((ext_vector_type(4)));
+    const int k = KK > 0 ? KK : k_rt;   // KK: the slot count known when compiled
     float o[8];
     if constexpr (XB) {
         const int4 q = reinterpret_cast<const int4 *>(static_cast<const uint16_t *>(x) + tok * d)[c];
@@ -1185,27 +1186,27 @@ __device__ __forceinline__ void combine_chunk(const void *__restrict__ x, void *
         o[4] = p1.x; o[5] = p1.y; o[6] = p1.z; o[7] = p1.w;
     }
     for (int j0 = 0; j0 < k; j0 += 8) {
+        // per slot: the pair index, expert id, gate (and s_h), loaded before any row
+        int64_t pj[8];
         int id[8];
-        float g[8];
+        float g[8], sh[8];
         bool ok[8];
 #pragma unroll
+        for (int u = 0; u < 8; u++) pj[u] = tok * k + (j0 + u < k ? j0 + u : k - 1);
+#pragma unroll
         for (int u = 0; u < 8; u++) {
-            const int j = j0 + u < k ? j0 + u : k - 1;
-            id[u] = ids[tok * k + j];
-            ok[u] = j0 + u < k && id[u] >= 0 && id[u] < E;
-            g[u] = gates[tok * k + j];
+            id[u] = ids[pj[u]];
+            g[u] = gates[pj[u]];
+            if constexpr (Y16) sh[u] = yr.s_h[pj[u]];
         }
+#pragma unroll
+        for (int u = 0; u < 8; u++) ok[u] = j0 + u < k && id[u] >= 0 && id[u] < E;
         float yy[8][8];
         if constexpr (Y16) {
             int4 yq[8];
-            float sh[8];
-#pragma unroll
-            for (int u = 0; u < 8; u++) {
-                const int j = j0 + u < k ? j0 + u : k - 1;
-                yq[u] = reinterpret_cast<const int4 *>(yr.y16 + (tok * k + j) * d)[c];
-                sh[u] = yr.s_h[tok * k + j];
-            }
             f4 sd[8][2];
+#pragma unroll
+            for (int u = 0; u < 8; u++) yq[u] = reinterpret_cast<const int4 *>(yr.y16 + pj[u] * d)[c];
 #pragma unroll
             for (int u = 0; u < 8; u++) {
                 const f4 *sp = reinterpret_cast<const f4 *>(yr.s_down + int64_t(ok[u] ? id[u] : 0) * d) + 2 * c;
@@ -1214,23 +1215,31 @@ __device__ __forceinline__ void combine_chunk(const void *__restrict__ x, void *
             }
 #pragma unroll
             for (int u = 0; u < 8; u++) {
-                const int j = j0 + u < k ? j0 + u : k - 1;
                 const uint32_t w[4] = {uint32_t(yq[u].x), uint32_t(yq[u].y), uint32_t(yq[u].z), uint32_t(yq[u].w)};
+                int32_t v[8];
+                bool marked = false;
+#pragma unroll
+                for (int q = 0; q < 8; q++) {
+                    v[q] = int32_t(int16_t(uint16_t(w[q >> 1] >> (16 * (q & 1)))));
+                    marked = marked || v[q] == -32768;
+                }
+                if (marked && ok[u]) {   // a sum outside the int16 range: the 32-bit row holds it
+                    const int4 *wp = reinterpret_cast<const int4 *>(yr.ywide + pj[u] * d + 8 * c);
+                    const int4 w0 = wp[0], w1 = wp[1];
+                    const int32_t wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+                    for (int q = 0; q < 8; q++) v[q] = v[q] == -32768 ? wv[q] : v[q];
+                }
                 const float sdv[8] = {sd[u][0].x, sd[u][0].y, sd[u][0].z, sd[u][0].w,
                                       sd[u][1].x, sd[u][1].y, sd[u][1].z, sd[u][1].w};
 #pragma unroll
-                for (int q = 0; q < 8; q++) {
-                    int32_t v = int32_t(int16_t(uint16_t(w[q >> 1] >> (16 * (q & 1)))));
-                    if (v == -32768 && ok[u]) v = yr.ywide[(tok * k + j) * d + 8 * c + q];
-                    yy[u][q] = (float(v) * sh[u]) * sdv[q];
-                }
+                for (int q = 0; q < 8; q++) yy[u][q] = (float(v[q]) * sh[u]) * sdv[q];
             }
         } else {
             f4 yv[8][2];
 #pragma unroll
             for (int u = 0; u < 8; u++) {
-                const int j = j0 + u < k ? j0 + u : k - 1;
-                const f4 *yp = reinterpret_cast<const f4 *>(ybuf + (tok * k + j) * d + 8 * c);
+                const f4 *yp = reinterpret_cast<const f4 *>(ybuf + pj[u] * d + 8 * c);
                 yv[u][0] = yp[0];
                 yv[u][1] = yp[1];
             }
@@ -1265,7 +1274,7 @@ __device__ __forceinline__ void combine_chunk(const void *__restrict__ x, void *
 // (token, s) covers the 8-element chunks s * blockDim + i of the token, one per thread (a small
 // batch takes one-wave workgroups so that its few tokens still spread over the compute units);
 // every load of a chunk is issued at once.
-template <bool XB, bool OB, bool Y16>
+template <bool XB, bool OB, bool Y16, int KK>
 __global__ __launch_bounds__(256) void k_bat_combine(BatchedArgs a, const void *__restrict__ x,
                                                      void *__restrict__ out,
                                                      const int32_t *__restrict__ ids,
@@ -1277,7 +1286,7 @@ __global__ __launch_bounds__(256) void k_bat_combine(BatchedArgs a, const void *
     if (c >= nch) return;
     const Y16Rows yr{reinterpret_cast<const int16_t *>(ws + a.L.y16), reinterpret_cast<const int32_t *>(ws + a.L.y),
                      reinterpret_cast<const float *>(ws + a.L.shp), s_down};
-    combine_chunk<XB, OB, Y16>(x, out, ids, gates, reinterpret_cast<const float *>(ws + a.L.y), yr,
+    combine_chunk<XB, OB, Y16, KK>(x, out, ids, gates, reinterpret_cast<const float *>(ws + a.L.y), yr,
                                int64_t(blockIdx.x), c, d, a.dm.k, a.dm.E);
 }
 
@@ -1289,7 +1298,11 @@ void launch_combine(const BatchedArgs &a, const void *x, int in_bf16, void *out,
     const int nt = a.T >= 1024 ? 256 : 64, nch = a.dm.d >> 3;
     const dim3 g(unsigned(a.T), unsigned((nch + nt - 1) / nt));
     hipStream_t st = static_cast<hipStream_t>(stream);
-#define TW_COMB(XB, OB, Y) k_bat_combine<XB, OB, Y><<<g, nt, 0, st>>>(a, x, out, ids, gates, ws, s_down)
+#define TW_COMB(XB, OB, Y)                                                                        \
+    do {                                                                                          \
+        if (a.dm.k == 8) k_bat_combine<XB, OB, Y, 8><<<g, nt, 0, st>>>(a, x, out, ids, gates, ws, s_down); \
+        else k_bat_combine<XB, OB, Y, 0><<<g, nt, 0, st>>>(a, x, out, ids, gates, ws, s_down);    \
+    } while (0)
     if (s_down) {
         if (in_bf16 && out_bf16) TW_COMB(true, true, true);
         else if (in_bf16) TW_COMB(true, false, true);
