@@ -51,12 +51,14 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 // Waves per workgroup: 16 for 16-token tiles of at most two planes (at <= 128 VGPRs, four waves
 // per SIMD); 8 otherwise (256 VGPRs: the h values of a 64-token tile stay in registers).
 // AHEAD: code units (one 16-row block of gate and up codes over 256 inputs, or one 16-row block of
-// down codes) each wave keeps in flight ahead of the one it computes.
+// down codes) each wave keeps in flight ahead of the one it computes: 4 for the small tiles (3 and 4
+// measured the same, 5 slower), 2 for the large ones (4096 int8 tokens: 263.0 us per call against
+// 266.2 with 3, 267.7 with 4 (register spills), 285.4 with 1).
 template <int MT, int P>
 struct PfShape {
     static constexpr int W = MT * P <= 16 ? 16 : 8;
     static constexpr int T = 64 * W;
-    static constexpr int AHEAD = 4;
+    static constexpr int AHEAD = MT * P <= 16 ? 4 : 2;
 };
 
 // The 16 int8 weights of one 32-bit code word, in the transposed order of the activation digits.
