@@ -183,8 +183,8 @@ def test_batched_int8_invalid_slots_contribute_nothing(full, T):
     assert torch.equal(out[5], x[5].float())
 
 
-@pytest.mark.parametrize("T", [40, 300])
-def test_int8_down_sums_outside_int16(T):
+@pytest.mark.parametrize("T,E,k", [(40, 8, 4), (300, 8, 4), (300, 16, 8)])
+def test_int8_down_sums_outside_int16(T, E, k):
     # With int8 activations in 64-token tiles the grouped kernel keeps each down sum as an int16 and
     # marks the ones outside [-32767, 32767], which then come from 32-bit rows.  Expert 0 here has all-+1 gate and
     # up rows with equal scales, and every input of the tokens is positive, so its h is the same
@@ -192,9 +192,10 @@ def test_int8_down_sums_outside_int16(T):
     # r mod 513 positions and -1 after them, so the down sums are 127 (2 a - 512) for every a in
     # 0 .. 512: from -65024 to 65024, with 32766 the largest that fits and 33020 the smallest that
     # does not.  Expected: the oracle's int8 spec bit for bit.  T = 40: small self-grouped tiles
-    # (fp32 y rows); T = 300: 64-token tiles from the grouping kernel (16-bit sums).
+    # (fp32 y rows); T = 300: 64-token tiles from the grouping kernel (16-bit sums), top-4 (the
+    # combine's slot count given at run time) and top-8 (fixed when compiled).
     wl = synth.PREFILL_4096
-    E, k, d, F = 8, 4, wl.d_model, wl.d_ff
+    d, F = wl.d_model, wl.d_ff
     w = synth.layer_weights(wl, 0, n_experts=E)
     w["t_gate"][0] = 1
     w["t_up"][0] = 1
