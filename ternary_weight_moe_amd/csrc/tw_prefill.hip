@@ -10,7 +10,8 @@
 // planes and the two lanes of a token combine their sums with one DPP exchange.  Every result is
 // bit-identical to the per-pair v_dot4 path and to the batch-1 decode.
 //
-// One workgroup (8 or 16 waves) takes one (expert e, tile of MT tokens) work item:
+// One workgroup (8 or 16 waves) takes one (expert e, tile of MT tokens) work item (with 64-token
+// tiles, an expert's last tile of at most 32 tokens runs the same steps compiled for 32):
 //   1. the tile's MT x P rows of activation digits (d bytes each, 4x4-transposed inside groups of
 //      16 as in tw_device.h) are copied into LDS, rows padded by 16 bytes so that the 16 rows read
 //      by one MFMA operand fetch spread over the banks;
@@ -94,20 +95,17 @@ __device__ __forceinline__ v4i mfma8(const v4i &w, const v4i &x, const v4i &c)
 // tile, and the tile's pairs (the expert's pairs in ascending order).  The list is the one k_group
 // writes (the same tiles in the same order; inside a tile k_group's order may differ, which changes
 // nothing), so no grouping kernel runs.  Otherwise the work item comes from k_group's lists.
-template <int D, int F, int P, int MT, bool SELF>
-__global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, BatchedWs L, LayerPtrs lp, uint8_t *ws, int nb,
-                                                               const int32_t *__restrict__ sel_ids, int npairs)
+// The work of one (expert e, tile) item after the tile lookup: meta = (position of the tile's first
+// pair in the pair list: k_group's pairs[] or, SELF, the expert's list in LDS, s_list), tokens).
+// MT: tokens the body is compiled for (the kernel's tile size, or half of it for an expert's last
+// tile when that holds at most half); Y16: the call keeps 16-bit down sums (decided per call, so
+// that a half-size tile stores the same form as the full ones).
+template <int D, int F, int P, int MT, bool SELF, bool Y16>
+__device__ __forceinline__ void pf_work(const Dims &dm, const BatchedWs &L, const LayerPtrs &lp, uint8_t *ws,
+                                        int e, int2 meta, const int32_t *s_list, int8_t *sm)
 {
     constexpr int W = PfShape<MT, P>::W, NT = PfShape<MT, P>::T;
-    static_assert(D % 256 == 0 && F % 256 == 0 && F % (16 * W) == 0 && D % (16 * W) == 0, "shape");
-    static_assert((P == 1 || P == 2) && (MT * P) % 16 == 0 && MT <= NT, "tile");
     constexpr bool INT8 = P == 1;
-    // int8 activations in large tiles: 16-bit down sums (the combine forms y); else fp32 y
-    constexpr bool Y16 = INT8 && MT >= 64;
-    // The activation tile has MT * P rows (token m, plane pl at row m P + pl); an MFMA takes 16 of
-    // them, so the 16 result columns of sub-tile rs are 16 / P tokens x P planes: column l16 is
-    // token rs * TPS + l16 / P, plane l16 % P.  With two planes the two lanes of a token combine
-    // their sums with one DPP exchange.
     constexpr int RS = MT * P / 16;       // row sub-tiles
     constexpr int TPS = 16 / P;           // tokens per row sub-tile
     constexpr int GPW = F / 16 / W;       // h-row groups of 16 per wave
@@ -117,77 +115,18 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
     constexpr int kPfAhead = PfShape<MT, P>::AHEAD;
     constexpr int NU = NGU + NSD, RING = kPfAhead + 1;
     static_assert(SD <= 2, "a down unit is at most two 16-byte chunks per lane");
-    extern __shared__ __attribute__((aligned(16))) int8_t sm[];   // [MT][P] rows of D, later of F
+    static_assert(!Y16 || INT8, "16-bit down sums need int8 activations");
     __shared__ int32_t s_pair[MT];
     __shared__ float s_tk[MT][2];         // per token: s_x (int8) or digit shift bits; 1/rms
     __shared__ float s_hk[MT];            // per token: s_h (int8) or digit shift bits of h
     __shared__ float s_amx[MT];
     __shared__ float s_pam[W][MT];
-    __shared__ int32_t s_cnt[SELF ? NT : 1];    // SELF: pairs per expert, then the expert's pairs
-    __shared__ int32_t s_wcnt[W], s_wtil[W];
-    __shared__ int32_t s_sel[2];
-
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l16 = lane & 15, g4 = lane >> 4;
-    // workgroups b and b + 8 run on the same XCD: they take consecutive tiles (usually one expert),
-    // and every 16 workgroups cover 16 consecutive tiles, so work spreads evenly over the XCDs
-    const int b = blockIdx.x;
-    const int ti = (b / 16) * 16 + (b % 8) * 2 + ((b / 8) & 1);
-    int e;
-    int2 meta;   // first pair position (k_group lists) or tile (SELF), tokens of the tile
-    if constexpr (SELF) {
-        const int E = dm.E;
-        const int id = t < npairs ? sel_ids[t] : -1;
-        const bool valid = id >= 0 && id < E;
-        if (t < E) s_cnt[t] = 0;
-        __syncthreads();
-        if (valid) atomicAdd(&s_cnt[id], 1);
-        __syncthreads();
-        // exclusive scan of the tiles per expert (expert t per thread), inside each wave and then
-        // over the wave totals
-        const int c = t < E ? s_cnt[t] : 0, nt = (c + MT - 1) / MT;
-        int it = nt;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int u = __shfl_up(it, off);
-            if (lane >= off) it += u;
-        }
-        if (lane == 63) s_wtil[wave] = it;
-        if (t < 2) s_sel[t] = -1;
-        __syncthreads();
-        int bt = 0;
-#pragma unroll
-        for (int w = 0; w < W; w++) bt += w < wave ? s_wtil[w] : 0;
-        const int tile0 = bt + it - nt;
-        if (ti >= tile0 && ti < tile0 + nt) {   // this workgroup's tile belongs to expert t
-            s_sel[0] = t;
-            s_sel[1] = ti - tile0;
-        }
-        __syncthreads();
-        e = s_sel[0];
-        if (e < 0) return;   // past the last tile (uniform over the workgroup)
-        const int tl = s_sel[1];
-        // the expert's pairs in ascending order: a ballot per wave, then the waves' counts
-        const uint64_t hit = __ballot(id == e);
-        const int rank = __popcll(hit & ((uint64_t(1) << lane) - 1));
-        if (lane == 0) s_wcnt[wave] = __popcll(hit);
-        __syncthreads();   // every read of s_cnt is done
-        int before = 0, total = 0;
-#pragma unroll
-        for (int w = 0; w < W; w++) {
-            before += w < wave ? s_wcnt[w] : 0;
-            total += s_wcnt[w];
-        }
-        if (id == e) s_cnt[before + rank] = t;
-        meta = make_int2(tl * MT, min(MT, total - tl * MT));
-    } else {
-        const int32_t *tiles = reinterpret_cast<const int32_t *>(ws + L.tiles);
-        const int2 *tmeta = reinterpret_cast<const int2 *>(ws + L.tilemeta);
-        // ti < nb: inside the tile lists' storage (read before the count is known, then checked)
-        const int ntiles = tiles[0], tile = tiles[1 + ti];
-        meta = tmeta[ti];
-        if (ti >= ntiles) return;
-        e = tile & 1023;
-    }
+    (void)NT;
+    // The activation tile has MT * P rows (token m, plane pl at row m P + pl); an MFMA takes 16 of
+    // them, so the 16 result columns of sub-tile rs are 16 / P tokens x P planes: column l16 is
+    // token rs * TPS + l16 / P, plane l16 % P.  With two planes the two lanes of a token combine
+    // their sums with one DPP exchange.
 
     // Code units of this wave, in the order they are computed.  Unit u < NGU: gate and up chunk
     // u % SG of h-row group u / SG (plus, with the first chunk, the group's gate and up scales);
@@ -238,7 +177,7 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
     const int nv = meta.y;                          // tokens in this tile (1 .. MT)
     const int rsv = (nv + TPS - 1) / TPS;           // row sub-tiles holding any of them
     if constexpr (SELF) __syncthreads();            // the expert's pair list is complete
-    if (t < MT) s_pair[t] = t < nv ? (SELF ? s_cnt[meta.x + t] : pairs[meta.x + t]) : -1;
+    if (t < MT) s_pair[t] = t < nv ? (SELF ? s_list[meta.x + t] : pairs[meta.x + t]) : -1;
     __syncthreads();
     // 1. activation tile: row (m, plane) = plane of token m, and each token's scale words; every
     //    load is issued before the first LDS store (padding tokens re-read token 0's row, which
@@ -464,6 +403,93 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
             }
         }
     }
+}
+
+template <int D, int F, int P, int MT, bool SELF>
+__global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, BatchedWs L, LayerPtrs lp, uint8_t *ws, int nb,
+                                                               const int32_t *__restrict__ sel_ids, int npairs)
+{
+    constexpr int W = PfShape<MT, P>::W, NT = PfShape<MT, P>::T;
+    static_assert(D % 256 == 0 && F % 256 == 0 && F % (16 * W) == 0 && D % (16 * W) == 0, "shape");
+    static_assert((P == 1 || P == 2) && (MT * P) % 16 == 0 && MT <= NT, "tile");
+    // int8 activations in large tiles: 16-bit down sums (the combine forms y); else fp32 y
+    constexpr bool Y16 = P == 1 && MT >= 64;
+    extern __shared__ __attribute__((aligned(16))) int8_t sm[];   // [MT][P] rows of D, later of F
+    __shared__ int32_t s_cnt[SELF ? NT : 1];    // SELF: pairs per expert, then the expert's pairs
+    __shared__ int32_t s_wcnt[W], s_wtil[W];
+    __shared__ int32_t s_sel[2];
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    // workgroups b and b + 8 run on the same XCD: they take consecutive tiles (usually one expert),
+    // and every 16 workgroups cover 16 consecutive tiles, so work spreads evenly over the XCDs
+    const int b = blockIdx.x;
+    const int ti = (b / 16) * 16 + (b % 8) * 2 + ((b / 8) & 1);
+    int e;
+    int2 meta;   // first pair position (k_group lists) or tile (SELF), tokens of the tile
+    if constexpr (SELF) {
+        const int E = dm.E;
+        const int id = t < npairs ? sel_ids[t] : -1;
+        const bool valid = id >= 0 && id < E;
+        if (t < E) s_cnt[t] = 0;
+        __syncthreads();
+        if (valid) atomicAdd(&s_cnt[id], 1);
+        __syncthreads();
+        // exclusive scan of the tiles per expert (expert t per thread), inside each wave and then
+        // over the wave totals
+        const int c = t < E ? s_cnt[t] : 0, nt = (c + MT - 1) / MT;
+        int it = nt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int u = __shfl_up(it, off);
+            if (lane >= off) it += u;
+        }
+        if (lane == 63) s_wtil[wave] = it;
+        if (t < 2) s_sel[t] = -1;
+        __syncthreads();
+        int bt = 0;
+#pragma unroll
+        for (int w = 0; w < W; w++) bt += w < wave ? s_wtil[w] : 0;
+        const int tile0 = bt + it - nt;
+        if (ti >= tile0 && ti < tile0 + nt) {   // this workgroup's tile belongs to expert t
+            s_sel[0] = t;
+            s_sel[1] = ti - tile0;
+        }
+        __syncthreads();
+        e = s_sel[0];
+        if (e < 0) return;   // past the last tile (uniform over the workgroup)
+        const int tl = s_sel[1];
+        // the expert's pairs in ascending order: a ballot per wave, then the waves' counts
+        const uint64_t hit = __ballot(id == e);
+        const int rank = __popcll(hit & ((uint64_t(1) << lane) - 1));
+        if (lane == 0) s_wcnt[wave] = __popcll(hit);
+        __syncthreads();   // every read of s_cnt is done
+        int before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < W; w++) {
+            before += w < wave ? s_wcnt[w] : 0;
+            total += s_wcnt[w];
+        }
+        if (id == e) s_cnt[before + rank] = t;
+        meta = make_int2(tl * MT, min(MT, total - tl * MT));
+    } else {
+        const int32_t *tiles = reinterpret_cast<const int32_t *>(ws + L.tiles);
+        const int2 *tmeta = reinterpret_cast<const int2 *>(ws + L.tilemeta);
+        // ti < nb: inside the tile lists' storage (read before the count is known, then checked)
+        const int ntiles = tiles[0], tile = tiles[1 + ti];
+        meta = tmeta[ti];
+        if (ti >= ntiles) return;
+        e = tile & 1023;
+    }
+
+    // an expert's last tile with at most half the tokens takes the half-size body (half the matrix
+    // operations and epilogues; same code stream)
+    if constexpr (!SELF && MT >= 64) {
+        if (meta.y <= MT / 2) {
+            pf_work<D, F, P, MT / 2, SELF, Y16>(dm, L, lp, ws, e, meta, s_cnt, sm);
+            return;
+        }
+    }
+    pf_work<D, F, P, MT, SELF, Y16>(dm, L, lp, ws, e, meta, s_cnt, sm);
 }
 
 // One workgroup per tile slot; sel_ids != nullptr: the workgroups build the tile list themselves

@@ -99,11 +99,13 @@ def test_prefill_int8_one_hot_experts_ragged_tiles(full):
     assert np.array_equal(bits(out)[sample], ref.view(np.uint32))
 
 
-def test_prefill_int8_second_shape():
-    # d=1024, 64 experts, F=256, top-4: the second instantiation of the MFMA path
+@pytest.mark.parametrize("T", [256, 1024])
+def test_prefill_int8_second_shape(T):
+    # d=1024, 64 experts, F=256, top-4: the second instantiation of the MFMA path; 256 tokens take
+    # the small self-grouped tiles, 1024 tokens (64 pairs per expert) the 64-token tiles, whose
+    # ragged last tiles of at most 32 tokens take the half-size body
     wl = synth.MID_STACK_B1
     pair = make_pair(wl, pre=False)
-    T = 256
     x = synth.activations(wl, T, seed=75).cuda()
     _, ids, gates = tw.moe_route_topk(x, pair.gpu.w_router, wl.top_k)
     step("prefill int8 mid shape T=%d" % T)
