@@ -271,12 +271,12 @@ __device__ __forceinline__ void store_chunk_digits(int8_t *plane, int c, const i
 }
 
 // Digit planes (QP = 2, 3) or int8 absmax codes (QP = 1) of a token whose chunks c = t + 256 i
-// this thread holds, given the token's max |x| and canonical sum of squares.
+// this thread (t: its index among the token's 256 threads) holds, given the token's max |x| and
+// canonical sum of squares.
 template <int QP, int NCH>
 __device__ __forceinline__ void quantize_token(const float (&v)[NCH][8], int nch, float am, float ss, int d,
-                                               int pre_norm, int8_t *xd, float *ti)
+                                               int pre_norm, int8_t *xd, float *ti, int t)
 {
-    const int t = threadIdx.x;
     if constexpr (QP == 1) {
         const float inv = am > 0.0f ? 127.0f / am : 0.0f;
 #pragma unroll
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(256) void k_route(const void *__restrict__ x, int x
             if (!mine(u)) continue;
             const float am = fmaxf(fmaxf(s_am[0][u], s_am[1][u]), fmaxf(s_am[2][u], s_am[3][u]));
             quantize_token<QP, NCH>(xv[u], nch, am, s_ss[u], d, pre_norm,
-                                    xdig + (tb + u) * int64_t(QP) * d, tinfo + 2 * (tb + u));
+                                    xdig + (tb + u) * int64_t(QP) * d, tinfo + 2 * (tb + u), t);
         }
     }
 }
@@ -697,21 +697,23 @@ struct BatchedArgs {
     int int8_act;
 };
 
-// Digit planes of every token (int8 mode: one plane, scale amax/127; float mode: P planes, shift).
+// Digit planes of one token (int8 mode: one plane, scale amax/127; float mode: P planes, shift) by
+// 256 threads: thread q of the group holds the 8-element chunks q, q + 256 of the token; red is the
+// group's [4][2] LDS scratch.  Contains one workgroup barrier, which every thread of the workgroup
+// reaches (tok >= T: no loads, no stores).
 template <int P, bool INT8>
-__global__ __launch_bounds__(256) void k_bat_quant_x(BatchedArgs a, const void *__restrict__ x,
-                                                     int x_bf16, uint8_t *__restrict__ ws)
+__device__ __forceinline__ void quant_token256(const BatchedArgs &a, const void *__restrict__ x, int x_bf16,
+                                               uint8_t *__restrict__ ws, int64_t tok, int q, float (*red)[2])
 {
-    // one workgroup per token; thread t holds the 8-element chunks t, t + 256 of the token
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int64_t tok = blockIdx.x;
+    const int lane = q & 63, wave = q >> 6;
     const int d = a.dm.d, nch = d >> 3;
+    const bool live = tok < a.T;
     float v[2][8] = {};
     float am = 0.0f, ss = 0.0f;
 #pragma unroll
     for (int i = 0; i < 2; i++) {
-        const int c = t + 256 * i;
-        if (c < nch) {
+        const int c = q + 256 * i;
+        if (live && c < nch) {
             load_chunk8(x, tok, d, c, x_bf16, v[i]);
 #pragma unroll
             for (int j = 0; j < 8; j++) {
@@ -720,7 +722,6 @@ __global__ __launch_bounds__(256) void k_bat_quant_x(BatchedArgs a, const void *
             }
         }
     }
-    __shared__ float red[4][2];
     am = wave_max(am);
     if (!INT8 && a.dm.pre_norm) ss = wave_sum(ss);
     if (lane == 0) {
@@ -728,12 +729,22 @@ __global__ __launch_bounds__(256) void k_bat_quant_x(BatchedArgs a, const void *
         red[wave][1] = ss;
     }
     __syncthreads();
+    if (!live) return;
     am = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
     // the pre-RMSNorm sum of squares in the canonical order (partials t, waves in pairs)
     const float tot = (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]);
     quantize_token<INT8 ? 1 : P, 2>(v, nch, am, tot, d, a.dm.pre_norm,
                                     reinterpret_cast<int8_t *>(ws + a.L.xdig) + tok * int64_t(P) * d,
-                                    reinterpret_cast<float *>(ws + a.L.tinfo) + 2 * tok);
+                                    reinterpret_cast<float *>(ws + a.L.tinfo) + 2 * tok, q);
+}
+
+// One workgroup per token.
+template <int P, bool INT8>
+__global__ __launch_bounds__(256) void k_bat_quant_x(BatchedArgs a, const void *__restrict__ x,
+                                                     int x_bf16, uint8_t *__restrict__ ws)
+{
+    __shared__ float red[4][2];
+    quant_token256<P, INT8>(a, x, x_bf16, ws, int64_t(blockIdx.x), int(threadIdx.x), red);
 }
 
 // Groups the T*k (token, slot) pairs by expert: counts[e], offsets[E+1] and pairs[] (the pairs of
@@ -750,10 +761,9 @@ constexpr int kGrpPer = 32;                    // ids per thread per pass
 constexpr int kGrpPass = 1024 * kGrpPer;       // pairs per pass
 constexpr int kGrpStage = kGrpPass;            // pairs staged in LDS (128 KiB)
 
-__global__ __launch_bounds__(1024) void k_group(BatchedArgs a, const int32_t *__restrict__ ids,
-                                                uint8_t *__restrict__ ws, int tt)
+__device__ __forceinline__ void group_pairs(const BatchedArgs &a, const int32_t *__restrict__ ids,
+                                            uint8_t *__restrict__ ws, int tt, int32_t *stage)
 {
-    extern __shared__ __attribute__((aligned(16))) int32_t stage[];   // [npairs] when staged
     const int E = a.dm.E, t = threadIdx.x;
     const int64_t npairs = a.T * a.dm.k;
     const bool staged = npairs <= kGrpStage;
@@ -847,6 +857,50 @@ __global__ __launch_bounds__(1024) void k_group(BatchedArgs a, const int32_t *__
         else
             for (int j = 4 * i; j < placed; j++) pairs[j] = stage[j];
     }
+}
+
+__global__ __launch_bounds__(1024) void k_group(BatchedArgs a, const int32_t *__restrict__ ids,
+                                                uint8_t *__restrict__ ws, int tt)
+{
+    extern __shared__ __attribute__((aligned(16))) int32_t stage[];   // [npairs] when staged
+    group_pairs(a, ids, ws, tt, stage);
+}
+
+// The quantisation of the tokens and the grouping of the pairs in one launch (they are
+// independent): workgroup 0 groups, workgroup 1 + j quantises tokens 4 j .. 4 j + 3, one per
+// 256-thread quarter, so the grouping runs beside the quantisation instead of after it.
+template <int P, bool INT8>
+__global__ __launch_bounds__(1024) void k_quant_group(BatchedArgs a, const void *__restrict__ x, int x_bf16,
+                                                      const int32_t *__restrict__ ids,
+                                                      uint8_t *__restrict__ ws, int tt)
+{
+    extern __shared__ __attribute__((aligned(16))) int32_t stage[];   // [npairs] when staged
+    __shared__ float red[4][4][2];
+    if (blockIdx.x == 0) {
+        group_pairs(a, ids, ws, tt, stage);
+        return;
+    }
+    const int q = int(threadIdx.x) >> 8;
+    quant_token256<P, INT8>(a, x, x_bf16, ws, int64_t(blockIdx.x - 1) * 4 + q, int(threadIdx.x) & 255, red[q]);
+}
+
+template <int P, bool INT8>
+int launch_quant_group(const BatchedArgs &a, const void *x, int x_bf16, const int32_t *ids, uint8_t *ws,
+                       int tt, void *stream)
+{
+    const int64_t npairs = a.T * a.dm.k;
+    const size_t lds = npairs <= kGrpStage ? size_t(npairs) * sizeof(int32_t) : 0;
+    static std::atomic<int> attr_set{0};
+    if (lds > 0 && !attr_set.load(std::memory_order_relaxed)) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_quant_group<P, INT8>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                int(kGrpStage * sizeof(int32_t))) != hipSuccess)
+            return int(hipErrorInvalidValue);
+        attr_set.store(1, std::memory_order_relaxed);
+    }
+    k_quant_group<P, INT8><<<unsigned(1 + (a.T + 3) / 4), 1024, lds, static_cast<hipStream_t>(stream)>>>(
+        a, x, x_bf16, ids, ws, tt);
+    return 0;
 }
 
 // Launches k_group (one workgroup) with the LDS staging area when the pairs fit in it.
@@ -1376,6 +1430,7 @@ int batched_p(const Dims &dm, const LayerPtrs &lp, int64_t T, const void *x_in, 
 {
     BatchedArgs a{dm, batched_ws_layout(dm, T, INT8 ? 1 : 3), T, INT8};
     uint8_t *w = static_cast<uint8_t *>(ws);
+    const bool routed = ids != nullptr;   // routing passed in: the activation codes are made here
     if (!ids) {
         // routing inside: the router also writes the activation codes
         float *logits = reinterpret_cast<float *>(w + a.L.logits);
@@ -1386,14 +1441,24 @@ int batched_p(const Dims &dm, const LayerPtrs &lp, int64_t T, const void *x_in, 
         launch_topk(logits, T, dm.E, dm.k, wid, wg, stream);
         ids = wid;
         gates = wg;
-    } else {
-        k_bat_quant_x<P, INT8><<<unsigned(T), 256, 0, S(stream)>>>(a, x_in, in_bf16, w);
     }
     int tile = kTileTokens;
-    if (grouped_mfma_serves(dm, T, P, &tile)) {
-        // small batches: each expert's workgroup finds its own tokens, no grouping kernel
-        const bool self = grouped_mfma_self(dm, T, tile);
-        int r = self ? 0 : launch_group(a, ids, w, tile, stream);
+    const bool mfma = grouped_mfma_serves(dm, T, P, &tile);
+    // small batches on the matrix cores: each expert's workgroup finds its own tokens, no grouping
+    const bool self = mfma && grouped_mfma_self(dm, T, tile);
+    const int tt = mfma ? tile : kTileTokens;
+    bool grouped = false;
+    if (routed) {
+        if (self) {
+            k_bat_quant_x<P, INT8><<<unsigned(T), 256, 0, S(stream)>>>(a, x_in, in_bf16, w);
+        } else {
+            const int r = launch_quant_group<P, INT8>(a, x_in, in_bf16, ids, w, tt, stream);
+            if (r != 0) return r;
+            grouped = true;
+        }
+    }
+    if (mfma) {
+        int r = self || grouped ? 0 : launch_group(a, ids, w, tile, stream);
         if (r != 0) return r;
         r = launch_grouped_mfma(dm, lp, T, P, tile, a.L, w, self ? ids : nullptr, stream);
         if (r != 0) return r;
@@ -1402,7 +1467,7 @@ int batched_p(const Dims &dm, const LayerPtrs &lp, int64_t T, const void *x_in, 
                        INT8 && tile >= 64 ? lp.s_down : nullptr, stream);
         return last_error();
     }
-    const int rg = launch_group(a, ids, w, kTileTokens, stream);
+    const int rg = grouped ? 0 : launch_group(a, ids, w, kTileTokens, stream);
     if (rg != 0) return rg;
     const int tg = tokens_per_round(P * dm.d), td = tokens_per_round(P * dm.F);
     if (dm.d <= 2048)
