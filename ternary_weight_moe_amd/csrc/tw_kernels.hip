@@ -1216,7 +1216,9 @@ struct Y16Rows {
 // every product and every sum is one fp32 rounding.  One call covers the 8-element chunk c of token
 // tok; x and out in bf16 (XB / OB) or fp32; y rows [T k][d] fp32, or 16-bit sums (Y16).  Every load
 // of the chunk is issued before the first is used (the residual chunk, the y rows of eight slots,
-// their ids and gates, and with Y16 the s_h and down scales).  The y row of every slot exists
+// their ids and gates, and with Y16 the s_h and down scales); the residual and the y rows are read
+// once, with non-temporal loads, so that they do not push the down scales (read by every token)
+// out of L2 (4096 int8 tokens: 253.2 -> 250.3 us per call).  The y row of every slot exists
 // (unwritten for slots without a valid expert, and then unused).
 template <bool XB, bool OB, bool Y16, int KK>
 __device__ __forceinline__ void combine_chunk(const void *__restrict__ x, void *__restrict__ out,
@@ -1226,16 +1228,17 @@ __device__ __forceinline__ void combine_chunk(const void *__restrict__ x, void *
                                               int64_t tok, int c, int d, int k_rt, int E)
 {
     typedef float f4 __attribute__((ext_vector_type(4)));
+    typedef int i4v __attribute__((ext_vector_type(4)));
     const int k = KK > 0 ? KK : k_rt;   // KK: the slot count known when compiled
     float o[8];
     if constexpr (XB) {
-        const int4 q = reinterpret_cast<const int4 *>(static_cast<const uint16_t *>(x) + tok * d)[c];
+        const i4v q = __builtin_nontemporal_load(reinterpret_cast<const i4v *>(static_cast<const uint16_t *>(x) + tok * d) + c);
         const uint32_t w[4] = {uint32_t(q.x), uint32_t(q.y), uint32_t(q.z), uint32_t(q.w)};
 #pragma unroll
         for (int jj = 0; jj < 8; jj++) o[jj] = bf16_to_f32(uint16_t(w[jj >> 1] >> (16 * (jj & 1))));
     } else {
         const f4 *p = reinterpret_cast<const f4 *>(static_cast<const float *>(x) + tok * d) + 2 * c;
-        const f4 p0 = p[0], p1 = p[1];
+        const f4 p0 = __builtin_nontemporal_load(p), p1 = __builtin_nontemporal_load(p + 1);
         o[0] = p0.x; o[1] = p0.y; o[2] = p0.z; o[3] = p0.w;
         o[4] = p1.x; o[5] = p1.y; o[6] = p1.z; o[7] = p1.w;
     }
@@ -1260,7 +1263,10 @@ __device__ __forceinline__ void combine_chunk(const void *__restrict__ x, void *
             int4 yq[8];
             f4 sd[8][2];
 #pragma unroll
-            for (int u = 0; u < 8; u++) yq[u] = reinterpret_cast<const int4 *>(yr.y16 + pj[u] * d)[c];
+            for (int u = 0; u < 8; u++) {
+                const i4v q = __builtin_nontemporal_load(reinterpret_cast<const i4v *>(yr.y16 + pj[u] * d) + c);
+                yq[u] = make_int4(q.x, q.y, q.z, q.w);
+            }
 #pragma unroll
             for (int u = 0; u < 8; u++) {
                 const f4 *sp = reinterpret_cast<const f4 *>(yr.s_down + int64_t(ok[u] ? id[u] : 0) * d) + 2 * c;
@@ -1294,8 +1300,8 @@ __device__ __forceinline__ void combine_chunk(const void *__restrict__ x, void *
 #pragma unroll
             for (int u = 0; u < 8; u++) {
                 const f4 *yp = reinterpret_cast<const f4 *>(ybuf + pj[u] * d + 8 * c);
-                yv[u][0] = yp[0];
-                yv[u][1] = yp[1];
+                yv[u][0] = __builtin_nontemporal_load(yp);
+                yv[u][1] = __builtin_nontemporal_load(yp + 1);
             }
 #pragma unroll
             for (int u = 0; u < 8; u++) {
