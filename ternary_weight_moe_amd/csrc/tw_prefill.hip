@@ -90,11 +90,6 @@ __device__ __forceinline__ v4i mfma8(const v4i &w, const v4i &x, const v4i &c)
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(w, x, c, 0, 0, 0);
 }
 
-// SELF: every workgroup builds the tile list itself from the T k expert ids (at most one id per
-// thread): per-expert counts, the tiles of MT tokens per expert in expert order, this workgroup's
-// tile, and the tile's pairs (the expert's pairs in ascending order).  The list is the one k_group
-// writes (the same tiles in the same order; inside a tile k_group's order may differ, which changes
-// nothing), so no grouping kernel runs.  Otherwise the work item comes from k_group's lists.
 // The work of one (expert e, tile) item after the tile lookup: meta = (position of the tile's first
 // pair in the pair list: k_group's pairs[] or, SELF, the expert's list in LDS, s_list), tokens).
 // MT: tokens the body is compiled for (the kernel's tile size, or half of it for an expert's last
@@ -405,6 +400,11 @@ __device__ __forceinline__ void pf_work(const Dims &dm, const BatchedWs &L, cons
     }
 }
 
+// SELF: every workgroup builds the tile list itself from the T k expert ids (at most one id per
+// thread): per-expert counts, the tiles of MT tokens per expert in expert order, this workgroup's
+// tile, and the tile's pairs (the expert's pairs in ascending order).  The list is the one k_group
+// writes (the same tiles in the same order; inside a tile k_group's order may differ, which changes
+// nothing), so no grouping kernel runs.  Otherwise the work item comes from k_group's lists.
 template <int D, int F, int P, int MT, bool SELF>
 __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, BatchedWs L, LayerPtrs lp, uint8_t *ws, int nb,
                                                                const int32_t *__restrict__ sel_ids, int npairs)
