@@ -322,7 +322,8 @@ __global__ __launch_bounds__(kPT) void k_persist(PArgs a)
 #pragma unroll
             for (int q = 0; q < S; q++) lv[q] = __uint_as_float(uint32_t(v[q]));
             TW_STAMP(7);
-            topk_softmax_wave_regs<S, false>(lv, E, K, s_ids, s_gates, lane);
+            if (!topk_wave_composite_to<S>(lv, E, K, s_ids, s_gates, lane))
+                topk_softmax_wave_regs<S, false>(lv, E, K, s_ids, s_gates, lane);
             TW_STAMP(8);
         }
         __syncthreads();

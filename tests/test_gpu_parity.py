@@ -133,6 +133,47 @@ def test_route_topk_tied_logits(classes, k):
     assert_selection_of_own_logits(lg, ids, k)
 
 
+def near_copy_router(seed):
+    """Router rows 0 .. 127 drawn at random; rows 128 .. 255 copies of row 0 whose element 0 is
+    (e - 128) 2^-24 (exact in bf16), with row 0's element 0 set to 0: for an input with x_0 = 1 the
+    129 experts' logits lie within ~1e-5 of each other, a few fp32 ulps apart or equal."""
+    g = torch.Generator().manual_seed(seed)
+    wr = torch.randn((256, 2048), generator=g) * 0.02
+    wr[128:] = wr[0]
+    wr[0, 0] = 0.0
+    wr[128:, 0] = torch.arange(128, dtype=torch.float32) * 2.0 ** -24
+    return wr.to(torch.bfloat16), g
+
+
+@pytest.mark.parametrize("k", [8, 32])
+def test_route_topk_near_tied_logits(k):
+    # The selection runs on 32-bit composites (upper 24 bits of each logit's order key, then the
+    # id) and hands over to the exact form where those cannot decide it.  Tokens 0 .. 31 lean
+    # towards row 0, so their top k + 1 are near-copies a few ulps apart (or equal); tokens 32 .. 63
+    # select among the random rows.  Exact against the logits the call returned; gates
+    # against a softmax of those logits.
+    wr, g = near_copy_router(300 + k)
+    x = torch.randn((64, 2048), generator=g)
+    x[:32] += 0.1 * torch.where(wr[0].float() >= 0, 1.0, -1.0)   # near-copy logits ~3 above the rest
+    x[:, 0] = 1.0
+    x = x.to(torch.bfloat16)
+    step("moe_route_topk near-tied logits, k %d" % k)
+    lg, ids, gw = tw.moe_route_topk(x.cuda(), wr.cuda(), k)
+    torch.cuda.synchronize()
+    assert_selection_of_own_logits(lg, ids, k)
+    l = lg.cpu().numpy().astype(np.float64)
+    sel = np.take_along_axis(l, ids.cpu().numpy().astype(np.int64), axis=1)
+    ref = np.exp(sel - sel[:, :1])
+    assert np.allclose(gw.cpu().numpy(), ref / ref.sum(1, keepdims=True), rtol=2e-6, atol=1e-8)
+    near = np.isin(ids.cpu().numpy(), np.r_[0, 128:256]).sum(1)
+    assert (near[:32] >= 2).sum() >= 24 and (near[32:] == 0).sum() >= 16   # both kinds of token occur
+    L = oracle.Layer(wr, np.zeros((256, 8, 2048), np.int8), np.zeros((256, 8, 2048), np.int8),
+                     np.zeros((256, 2048, 8), np.int8), np.ones((256, 8), np.float32),
+                     np.ones((256, 8), np.float32), np.ones((256, 2048), np.float32), top_k=k)
+    oids, og, olg = oracle.route(L, x, n_threads=4)
+    check_routing(ids.cpu().numpy(), gw.cpu().numpy(), olg, oids, og, k)
+
+
 def test_route_zero_input_goes_to_lowest_ids(full):
     step("moe_route_topk zero input")
     x = torch.zeros((3, 2048), dtype=torch.bfloat16, device="cuda")
@@ -340,6 +381,44 @@ def test_decode_more_layers_than_one_launch_holds(mid3):
     torch.cuda.synchronize()
     assert torch.equal(fused.view(torch.int16), cur.view(torch.int16))
     assert torch.isfinite(fused.float()).all()
+
+
+@pytest.mark.parametrize("kind", ["repeated", "near_copies"])
+def test_decode_one_launch_tied_router_logits(kind):
+    # The one-launch decode selects by 32-bit composites (upper 24 bits of each logit's order key,
+    # then the id) and hands over to the exact form on equal or near-equal logits.  "repeated":
+    # router rows repeat every 64 experts, so each logit is shared by 4 experts and the top 8 holds
+    # equal logits (decided by the lower id, in the kernel and in the oracle).  "near_copies": rows
+    # 128 .. 255 are row 0 with element 0 set to (e - 128) 2^-13 and the input is the sign pattern
+    # of row 0, so the top 9 are near-copies with logits near 32 and 1.2e-4 apart: closer than the
+    # 24-bit parts resolve (~1e-3 there), far apart for fp32 sums and the near-tie tolerance, so
+    # the oracle's routing must be met exactly.  Output against the oracle.
+    wl = synth.LAYER_B1
+    w = {k: v.cpu() for k, v in synth.layer_weights(wl, 0, device="cuda").items()}
+    if kind == "repeated":
+        w["w_router"] = w["w_router"][torch.arange(256) % 64].contiguous()
+        x = synth.activations(wl, 4, seed=41)
+    else:
+        g = torch.Generator().manual_seed(45)
+        wr = torch.randn((256, 2048), generator=g) * 0.02
+        wr[128:] = wr[0]
+        wr[:, 0] = 0.0
+        wr[128:, 0] = torch.arange(128, dtype=torch.float32) * 2.0 ** -13
+        w["w_router"] = wr.to(torch.bfloat16)
+        sgn = torch.where(w["w_router"][0].float() >= 0, 1.0, -1.0)
+        x = torch.stack([sgn * s for s in (1.0, 0.5, 2.0)])
+        x[:, 0] = 1.0
+        x = x.to(torch.bfloat16)
+    pair = LayerPair(w, wl.top_k, wl.pre_rmsnorm)
+    for t in range(x.shape[0]):
+        step("one-launch decode, %s router rows, token %d" % (kind, t))
+        got = to_np(tw.ternary_moe_ffn_decode([pair.gpu], x[t].cuda()))
+        cands = oracle_decode_expect(pair.ora, x[t].double().numpy())
+        if kind == "near_copies":
+            _, oids, _, olg = oracle.moe_layer(pair.ora, x[t].double().numpy()[None])
+            assert np.all(oids[0] >= 128) and len(cands) == 1
+        errs = [normwise(got, c) for c in cands]
+        assert_bf16_close(got, cands[int(np.argmin(errs))], "%s token %d" % (kind, t))
 
 
 def test_decode_bf16_shape_served_by_per_layer_kernels():
