@@ -462,11 +462,12 @@ def run_gemv(args, layout):
     )
 
 
-def run_attention(args):
+def run_attention(args, one=False):
     """Decode attention of one token through the 24 layers' caches: 6 global layers over the pages'
     640-token context and 18 windowed layers over their 512-slot rings (16 query heads over 4 KV
     heads of 128, bf16).  12 step copies of all 24 caches (320 MB) are rotated, so that the caches
-    come from HBM rather than the 256 MB last-level cache."""
+    come from HBM rather than the 256 MB last-level cache.  one: attention_decode_one (one launch
+    per layer) instead of attention_decode (two)."""
     H, Hkv, dh = synth.ATTN_HEADS, synth.ATTN_KV_HEADS, synth.ATTN_HEAD_DIM
     n_layers = synth.ATTN_GLOBAL_LAYERS + synth.ATTN_WINDOW_LAYERS
     slots = [synth.ATTN_CONTEXT if (l % 4) == 3 else synth.ATTN_WINDOW for l in range(n_layers)]
@@ -476,15 +477,21 @@ def run_attention(args):
         caches.append([synth.attention_inputs(slots[l], "cuda", seed=2000 + c, layer=l)
                        for l in range(n_layers)])
     outs = [torch.empty((H, dh), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
-    ws = torch.empty(tw.attention_decode_workspace_bytes(H, dh, max(slots)), dtype=torch.uint8,
-                     device="cuda")
+    if one:
+        ws = tw.attention_decode_one_workspace(H, dh, max(slots))
+    else:
+        ws = torch.empty(tw.attention_decode_workspace_bytes(H, dh, max(slots)), dtype=torch.uint8,
+                         device="cuda")
     torch.cuda.synchronize()
 
     def step(t):
         c = t % n_copies
         for l in range(n_layers):
             q, k, v = caches[c][l]
-            tw.attention_decode(q, k, v, out=outs[l], workspace=ws)
+            if one:
+                tw.attention_decode_one(q, k, v, ws, out=outs[l])
+            else:
+                tw.attention_decode(q, k, v, out=outs[l], workspace=ws)
 
     G = min(args.graph_steps, 48)
     steps = max(G, (args.steps // 8) // G * G)
@@ -497,13 +504,13 @@ def run_attention(args):
         value=1.0 / sec, unit="tok/s", n_gpus=1, steps=steps, warmup=args.warmup,
         ms_per_step=sec * 1e3, higher_is_better=True, scaling="weak", vs_baseline=None,
         dtype="bf16 in, fp32 sums and out", data="synthetic",
-        config=dict(workload="attention_24l", heads=H, kv_heads=Hkv, head_dim=dh,
+        config=dict(workload="attention_24l_one" if one else "attention_24l", heads=H, kv_heads=Hkv, head_dim=dh,
                     global_layers=synth.ATTN_GLOBAL_LAYERS, global_slots=synth.ATTN_CONTEXT,
                     window_layers=synth.ATTN_WINDOW_LAYERS, window_slots=synth.ATTN_WINDOW,
                     step_copies=n_copies, bytes_per_step=bytes_per_step),
         roofline=dict(bound="hbm", achieved=achieved, peak=accounting.HBM_PEAK_BPS / 1e9,
                       unit="GB/s", frac=achieved * 1e9 / accounting.HBM_PEAK_BPS, traffic=None,
-                      kernel="k_attn_part<4> + k_attn_merge, 24 layer calls per step"),
+                      kernel=("k_attn_one<4>" if one else "k_attn_part<4> + k_attn_merge") + ", 24 layer calls per step"),
         cpu_baseline=None,
     )
 
@@ -635,7 +642,7 @@ def main():
     ap.add_argument("--workload", default="stack24_b1",
                     choices=["stack24_b1", "stack24_phases", "layer_b1", "batched_b64", "batched_b64_int8",
                              "prefill_4096", "quantize_layer", "gemv_2bit", "gemv_base3",
-                             "attention_24l", "flash_head", "copy_calib"])
+                             "attention_24l", "attention_24l_one", "flash_head", "copy_calib"])
     ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -660,6 +667,8 @@ def main():
         res = run_quantize(args)
     elif args.workload == "attention_24l":
         res = run_attention(args)
+    elif args.workload == "attention_24l_one":
+        res = run_attention(args, one=True)
     elif args.workload == "flash_head":
         res = run_flash_head(args)
     elif args.workload in ("gemv_2bit", "gemv_base3"):

@@ -201,6 +201,27 @@ tw_status attention_decode(const void *q, const void *k_cache, const void *v_cac
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * attention_decode_one_workspace_bytes -- workspace bytes of attention_decode_one (0 when the
+ *   arguments are invalid or n_slots is above 1024).
+ * attention_decode_one -- the operation of attention_decode in one kernel launch instead of two,
+ *   for at most 1024 cached slots (64 splits of 16).  The split workgroups publish their partial
+ *   (max, sum, 128 outputs) per query head as 64-bit words, each an fp32 value beside a 32-bit tag
+ *   that names the call; one workgroup per query head, last in the grid, waits until its words carry
+ *   the call's tag and merges them in attention_decode's order, so the outputs are the same bits as
+ *   attention_decode's.  Arguments, layouts and errors as attention_decode, with the workspace size
+ *   of attention_decode_one_workspace_bytes and TW_E_UNSUPPORTED above 1024 slots.
+ *   Workspace contract (unlike the other calls): zero-filled before its first call (for example by
+ *   hipMemsetAsync) and used by no other call; every call that completes writes zeros back over the
+ *   words it used.  Calls on one workspace must not overlap.  A wait that runs out (only if a split
+ *   workgroup never ran) leaves NaN in that head's output and the head's words in place.
+ *   Source: as attention_decode.
+ */
+size_t attention_decode_one_workspace_bytes(int32_t n_heads, int32_t head_dim, int64_t n_slots);
+tw_status attention_decode_one(const void *q, const void *k_cache, const void *v_cache, int64_t n_slots,
+                               int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, float *out,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * flash_head_workspace_bytes -- workspace bytes of flash_head for n_clusters clusters (0 if invalid).
  * flash_head -- approximate output head over a clustered vocabulary: 4-bit centroid scores pick
  * the `top` most relevant clusters, and only their tokens get full-precision logits.

@@ -43,7 +43,8 @@ class TwLayer(C.Structure):
 
 EXPORTS = ("tw_status_str", "ternary_pack", "ternary_quantize", "ternary_pack3_row_bytes",
            "ternary_pack3", "ternary_gemv_i8", "attention_decode_workspace_bytes",
-           "attention_decode", "flash_head_workspace_bytes", "flash_head", "moe_route_topk",
+           "attention_decode", "attention_decode_one_workspace_bytes", "attention_decode_one",
+           "flash_head_workspace_bytes", "flash_head", "moe_route_topk",
            "ternary_moe_ffn_decode", "ternary_moe_ffn_decode_static",
            "ternary_moe_decode_workspace_bytes", "ternary_moe_decode_error_offset",
            "ternary_moe_ffn_batched",
@@ -70,6 +71,8 @@ def lib():
                 "ternary_gemv_i8": (i32, [vp, i32, vp, i64, i64, vp, vp, vp, vp]),
                 "attention_decode_workspace_bytes": (sz, [i32, i32, i64]),
                 "attention_decode": (i32, [vp, vp, vp, i64, i32, i32, i32, vp, vp, sz, vp]),
+                "attention_decode_one_workspace_bytes": (sz, [i32, i32, i64]),
+                "attention_decode_one": (i32, [vp, vp, vp, i64, i32, i32, i32, vp, vp, sz, vp]),
                 "flash_head_workspace_bytes": (sz, [i32]),
                 "flash_head": (i32, [vp, i32, vp, vp, i32, vp, vp, i32, i32, vp, vp, vp, vp, sz,
                                      vp]),
@@ -185,6 +188,34 @@ def attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
                                   _ptr(workspace), workspace.numel(), _stream(stream)),
            "attention_decode")
     return out
+
+
+def attention_decode_one(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         workspace: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """attention_decode in one launch (at most 1024 slots).  `workspace` must be zero-filled before
+    its first call (attention_decode_one_workspace) and used by this call only; each call leaves it
+    zero-filled."""
+    _need_cuda(q, k_cache, v_cache, out, workspace)
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise ValueError("attention_decode_one expects bf16 q, k_cache and v_cache")
+    H, dh = q.shape
+    n, Hkv, dh2 = k_cache.shape
+    if dh2 != dh or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((H, dh), dtype=torch.float32, device=q.device)
+    _check(lib().attention_decode_one(_ptr(q), _ptr(k_cache), _ptr(v_cache), n, H, Hkv, dh,
+                                      _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "attention_decode_one")
+    return out
+
+
+def attention_decode_one_workspace(n_heads: int, head_dim: int, n_slots: int, device="cuda"):
+    """A zero-filled workspace for attention_decode_one calls of up to n_slots slots."""
+    nbytes = int(lib().attention_decode_one_workspace_bytes(int(n_heads), int(head_dim), int(n_slots)))
+    if nbytes == 0:
+        raise ValueError("attention_decode_one: unsupported shape")
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 def flash_head(h: torch.Tensor, centroids: torch.Tensor, centroid_scales: torch.Tensor,

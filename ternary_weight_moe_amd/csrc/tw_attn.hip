@@ -22,6 +22,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "tw_device.h"
 #include "tw_aux.h"
 #include "tw_internal.h"
@@ -160,7 +162,224 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float *__restrict__ ws
     if (half == 0) out[int64_t(h) * DH + i] = (O + s_o[i]) / (L + s_red[0]);
 }
 
+// ---- one launch: the splits publish tagged words, a merge workgroup per query head waits for them
+//
+// Each partial value goes to the workspace as one 64-bit word, a 32-bit tag naming the call beside
+// the fp32 bits, stored and read with single 64-bit device-scope accesses: a word that carries the
+// call's tag holds this call's value, so no fence is needed between the splits and the merge.  The
+// merge workgroups come last in the grid: workgroups are dispatched in order, so every split's
+// workgroup has been dispatched when a merge workgroup starts waiting, and the splits never wait.
+// After merging, each merge workgroup writes zeros over the words it read, so the workspace is
+// zero-filled again between calls; stale words from a call that did not complete carry that
+// call's tag.
+
+// Splits of 16 slots: wave w of workgroup (KV head g, b) takes split 4 b + w.
+template <int G>
+__device__ __forceinline__ void attn_one_part(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                              const uint16_t *__restrict__ v, int64_t n, int Hkv, float scale,
+                                              uint64_t *__restrict__ ws, uint32_t tag, int g, int b)
+{
+    constexpr int DH = kAttnHeadDim, CH = kAttnChunk;
+    __shared__ float s_q[G][DH];
+    __shared__ float s_p[4][G][CH];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int H = Hkv * G;
+    const int64_t S = (n + CH - 1) / CH;
+    const int64_t sp = int64_t(4) * b + wave;
+    const bool act = sp < S;
+    const int64_t t0 = (act ? sp : 0) * CH;
+    const int slot = lane >> 2, qd = lane & 3;
+    const int64_t tt = t0 + slot;
+    const bool valid = act && tt < n;
+    const int nv = act ? int(n - t0 < CH ? n - t0 : CH) : 0;
+    uint4 kr[4];
+    const uint4 *kp = reinterpret_cast<const uint4 *>(k + (int64_t(valid ? tt : t0) * Hkv + g) * DH + 32 * qd);
+#pragma unroll
+    for (int c = 0; c < 4; c++) kr[c] = kp[c];
+    uint32_t vv[CH];
+    const uint16_t *vp = v + (t0 * Hkv + g) * DH + 2 * lane;
+#pragma unroll
+    for (int u = 0; u < CH; u++)
+        vv[u] = u < nv ? *reinterpret_cast<const uint32_t *>(vp + int64_t(u) * Hkv * DH) : 0u;
+    for (int i = t; i < G * DH; i += 256) s_q[i / DH][i % DH] = bf16_to_f32(q[int64_t(g) * G * DH + i]);
+    __syncthreads();
+    float sc[G];
+#pragma unroll
+    for (int j = 0; j < G; j++) sc[j] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        const uint32_t w[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const float kv = bf16_to_f32(uint16_t(w[e >> 1] >> (16 * (e & 1))));
+#pragma unroll
+            for (int j = 0; j < G; j++) sc[j] = sc[j] + s_q[j][32 * qd + 8 * c + e] * kv;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < G; j++) {
+        sc[j] = sc[j] + dpp_f<kDppXor1>(sc[j]);
+        sc[j] = sc[j] + dpp_f<kDppXor2>(sc[j]);
+    }
+    float m[G], l[G];
+#pragma unroll
+    for (int j = 0; j < G; j++) {
+        const float x = valid ? sc[j] * scale : -INFINITY;
+        m[j] = wave_max(x);
+        const float p = valid ? expf(x - m[j]) : 0.0f;
+        l[j] = wave_sum(qd == 0 ? p : 0.0f);
+        if (qd == 0) s_p[wave][j][slot] = p;
+    }
+    __syncthreads();
+    if (!act) return;
+    float o[G][2];
+#pragma unroll
+    for (int j = 0; j < G; j++) o[j][0] = o[j][1] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < CH; u++) {
+        if (u < nv) {
+            const float v0 = bf16_to_f32(uint16_t(vv[u])), v1 = bf16_to_f32(uint16_t(vv[u] >> 16));
+#pragma unroll
+            for (int j = 0; j < G; j++) {
+                o[j][0] = o[j][0] + s_p[wave][j][u] * v0;
+                o[j][1] = o[j][1] + s_p[wave][j][u] * v1;
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < G; j++) {
+        uint64_t *pw = ws + (sp * H + int64_t(g) * G + j) * (DH + 2);
+        st_tagged(pw + 2 * lane, tag, __float_as_uint(o[j][0]));
+        st_tagged(pw + 2 * lane + 1, tag, __float_as_uint(o[j][1]));
+        if (lane == 0) {
+            st_tagged(pw + DH, tag, __float_as_uint(m[j]));
+            st_tagged(pw + DH + 1, tag, __float_as_uint(l[j]));
+        }
+    }
+}
+
+constexpr uint32_t kAttnOneSpin = 1u << 22;
+
+// The merge of query head h: thread (i, half) sums the rescaled outputs of the splits s = half,
+// half + 2, ... in increasing order, as k_attn_merge does, so the results are the same bits.
+__device__ __forceinline__ void attn_one_merge(uint64_t *__restrict__ ws, int64_t S, int H, int h,
+                                               uint32_t tag, float *__restrict__ out)
+{
+    constexpr int DH = kAttnHeadDim, NO = kAttnOneMaxSplits / 2;
+    __shared__ float s_m[kAttnOneMaxSplits], s_l[kAttnOneMaxSplits];
+    __shared__ float s_red[4];
+    __shared__ float s_o[DH];
+    __shared__ int s_bad;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int i = t & (DH - 1), half = t >> 7;
+    const int ns = int((S - half + 1) / 2);   // splits of this thread's half
+    if (t == 0) s_bad = 0;
+    // words of this thread: o[i] of its half's splits, and (t < S) the max and sum of split t
+    uint64_t wo[NO], wm = 0, wl = 0;
+#pragma unroll
+    for (int u = 0; u < NO; u++) wo[u] = 0;
+    uint64_t pend = 0;
+#pragma unroll
+    for (int u = 0; u < NO; u++)
+        if (u < ns) pend |= uint64_t(1) << u;
+    const bool ml = t < S;
+    bool pml = ml;
+    const uint64_t *base = ws + int64_t(h) * (DH + 2);
+    const int64_t stride = int64_t(H) * (DH + 2);
+    uint32_t it = 0;
+    for (; (pend || pml) && it < kAttnOneSpin; ++it) {
+#pragma unroll
+        for (int u = 0; u < NO; u++)
+            if ((pend >> u) & 1u) wo[u] = ld_tagged(base + (half + 2 * u) * stride + i);
+        if (pml) {
+            wm = ld_tagged(base + t * stride + DH);
+            wl = ld_tagged(base + t * stride + DH + 1);
+        }
+#pragma unroll
+        for (int u = 0; u < NO; u++)
+            if (((pend >> u) & 1u) && uint32_t(wo[u] >> 32) == tag) pend &= ~(uint64_t(1) << u);
+        if (pml && uint32_t(wm >> 32) == tag && uint32_t(wl >> 32) == tag) pml = false;
+    }
+    __syncthreads();
+    if (pend || pml) s_bad = 1;
+    if (ml) {
+        s_m[t] = __uint_as_float(uint32_t(wm));
+        s_l[t] = __uint_as_float(uint32_t(wl));
+    }
+    float mx = ml ? __uint_as_float(uint32_t(wm)) : -INFINITY;
+    mx = wave_max(mx);
+    if (lane == 0) s_red[wave] = mx;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    float L = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int u = 0; u < NO; u++) {
+        if (u < ns) {
+            const int s = half + 2 * u;
+            const float e = expf(s_m[s] - M);
+            L = L + e * s_l[s];
+            O = O + e * __uint_as_float(uint32_t(wo[u]));
+        }
+    }
+    // zeros over the words read (the workspace is zero-filled again for the next call)
+    if (!s_bad) {
+#pragma unroll
+        for (int u = 0; u < NO; u++)
+            if (u < ns) st_tagged(const_cast<uint64_t *>(base) + (half + 2 * u) * stride + i, 0u, 0u);
+        if (ml) {
+            st_tagged(const_cast<uint64_t *>(base) + t * stride + DH, 0u, 0u);
+            st_tagged(const_cast<uint64_t *>(base) + t * stride + DH + 1, 0u, 0u);
+        }
+    }
+    __syncthreads();
+    if (half == 1) {
+        s_o[i] = O;
+        if (i == 0) s_red[0] = L;
+    }
+    __syncthreads();
+    if (half == 0) out[int64_t(h) * DH + i] = s_bad ? __uint_as_float(0x7fc00000u) : (O + s_o[i]) / (L + s_red[0]);
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void k_attn_one(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                                  const uint16_t *__restrict__ v, int64_t n, int Hkv, float scale,
+                                                  uint64_t *__restrict__ ws, uint32_t tag, float *__restrict__ out)
+{
+    const int64_t S = (n + kAttnChunk - 1) / kAttnChunk;
+    const int nb = int((S + 3) / 4);   // split workgroups per KV head
+    const int bid = blockIdx.x;
+    if (bid < nb * Hkv)
+        attn_one_part<G>(q, k, v, n, Hkv, scale, ws, tag, bid / nb, bid % nb);
+    else
+        attn_one_merge(ws, S, Hkv * G, bid - nb * Hkv, tag, out);
+}
+
 }  // namespace
+
+int launch_attn_decode_one(const void *q, const void *k, const void *v, int64_t n, int H, int Hkv,
+                           float *out, void *ws, void *stream)
+{
+    static std::atomic<uint32_t> calls{0};
+    uint32_t tag = calls.fetch_add(1, std::memory_order_relaxed) + 1;
+    if (tag == 0) tag = calls.fetch_add(1, std::memory_order_relaxed) + 1;   // 0 marks a cleared word
+    const int G = H / Hkv;
+    const int64_t S = attn_splits(n);
+    if (S > kAttnOneMaxSplits) return int(hipErrorInvalidValue);
+    const float scale = 1.0f / sqrtf(float(kAttnHeadDim));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const unsigned nbk = unsigned((S + 3) / 4 * Hkv + H);
+    auto qp = static_cast<const uint16_t *>(q), kp = static_cast<const uint16_t *>(k),
+         vp = static_cast<const uint16_t *>(v);
+    uint64_t *w = static_cast<uint64_t *>(ws);
+    switch (G) {
+    case 1: k_attn_one<1><<<nbk, 256, 0, st>>>(qp, kp, vp, n, Hkv, scale, w, tag, out); break;
+    case 2: k_attn_one<2><<<nbk, 256, 0, st>>>(qp, kp, vp, n, Hkv, scale, w, tag, out); break;
+    case 4: k_attn_one<4><<<nbk, 256, 0, st>>>(qp, kp, vp, n, Hkv, scale, w, tag, out); break;
+    case 8: k_attn_one<8><<<nbk, 256, 0, st>>>(qp, kp, vp, n, Hkv, scale, w, tag, out); break;
+    default: return int(hipErrorInvalidValue);
+    }
+    return int(hipGetLastError());
+}
 
 int launch_attn_decode(const void *q, const void *k, const void *v, int64_t n, int H, int Hkv,
                        float *out, void *ws, void *stream)

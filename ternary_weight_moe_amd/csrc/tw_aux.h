@@ -26,6 +26,12 @@ inline int64_t attn_splits(int64_t n) { return (n + kAttnChunk - 1) / kAttnChunk
 inline size_t attn_ws_bytes(int64_t n, int H) { return align256(sizeof(float) * size_t(attn_splits(n)) * H * (kAttnHeadDim + 2)); }
 int launch_attn_decode(const void *q, const void *k, const void *v, int64_t n, int H, int Hkv,
                        float *out, void *ws, void *stream);
+// The one-launch form: at most kAttnOneMaxSplits splits; the workspace holds one 64-bit tagged
+// word per (split, query head, value) and is zero-filled between calls.
+constexpr int kAttnOneMaxSplits = 64;
+inline size_t attn_one_ws_bytes(int64_t n, int H) { return align256(sizeof(uint64_t) * size_t(attn_splits(n)) * H * (kAttnHeadDim + 2)); }
+int launch_attn_decode_one(const void *q, const void *k, const void *v, int64_t n, int H, int Hkv,
+                           float *out, void *ws, void *stream);
 // Approximate output head (tw_head.hip): d in {512, 1024, 2048, 4096}, at most 8192 clusters; the
 // workspace holds the clusters' fp32 scores.
 constexpr int kHeadMaxD = 4096;

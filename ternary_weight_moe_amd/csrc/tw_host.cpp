@@ -211,6 +211,43 @@ tw_status attention_decode(const void *q, const void *k_cache, const void *v_cac
                : TW_OK;
 }
 
+size_t attention_decode_one_workspace_bytes(int32_t n_heads, int32_t head_dim, int64_t n_slots)
+{
+    if (n_heads < 1 || n_heads > 128 || head_dim != tw::kAttnHeadDim || n_slots < 1 ||
+        tw::attn_splits(n_slots) > tw::kAttnOneMaxSplits)
+        return 0;
+    return tw::attn_one_ws_bytes(n_slots, n_heads);
+}
+
+tw_status attention_decode_one(const void *q, const void *k_cache, const void *v_cache, int64_t n_slots,
+                               int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, float *out,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (n_slots < 1 || n_slots > (int64_t(1) << 21) || n_heads < 1 || n_kv_heads < 1 ||
+        n_heads % n_kv_heads != 0)
+        return TW_E_SHAPE;
+    const int G = n_heads / n_kv_heads;
+    if (head_dim != tw::kAttnHeadDim || n_heads > 128 || (G != 1 && G != 2 && G != 4 && G != 8) ||
+        tw::attn_splits(n_slots) > tw::kAttnOneMaxSplits)
+        return TW_E_UNSUPPORTED;
+    if (!q || !k_cache || !v_cache || !out || !workspace) return TW_E_NULL;
+    if ((((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15) || ((uintptr_t)out & 3) ||
+        ((uintptr_t)workspace & 255))
+        return TW_E_UNSUPPORTED;
+    const size_t need = tw::attn_one_ws_bytes(n_slots, n_heads);
+    if (workspace_bytes < need) return TW_E_WORKSPACE;
+    const size_t nq = size_t(n_heads) * head_dim * 2, nkv = size_t(n_slots) * n_kv_heads * head_dim * 2,
+                 no = size_t(n_heads) * head_dim * 4;
+    if (overlap(out, no, q, nq) || overlap(out, no, k_cache, nkv) || overlap(out, no, v_cache, nkv) ||
+        overlap(out, no, workspace, need) || overlap(workspace, need, q, nq) ||
+        overlap(workspace, need, k_cache, nkv) || overlap(workspace, need, v_cache, nkv))
+        return TW_E_ALIAS;
+    return tw::launch_attn_decode_one(q, k_cache, v_cache, n_slots, n_heads, n_kv_heads, out,
+                                      workspace, stream)
+               ? TW_E_HIP
+               : TW_OK;
+}
+
 size_t flash_head_workspace_bytes(int32_t n_clusters)
 {
     if (n_clusters < 1 || n_clusters > tw::kHeadMaxClusters) return 0;

@@ -247,6 +247,31 @@ def test_attention_decode_workspace_and_errors(L):
     assert a(A[0], A[1], A[2], 640, 16, 4, 128, A[4] + 512, A[4], big, s) == E_ALIAS    # out in ws
 
 
+def test_attention_decode_one_workspace_and_errors(L):
+    ws = L.attention_decode_one_workspace_bytes
+    assert ws(16, 128, 640) == ((640 + 15) // 16 * 16 * 130 * 8 + 255) // 256 * 256
+    assert ws(16, 128, 1024) > 0 and ws(16, 128, 1025) == 0      # at most 64 splits of 16
+    assert ws(16, 64, 640) == 0 and ws(0, 128, 640) == 0 and ws(16, 128, 0) == 0
+    s = None
+    a = L.attention_decode_one
+    big = 1 << 30
+    assert a(A[0], A[1], A[2], 0, 16, 4, 128, A[3], A[4], big, s) == E_SHAPE
+    assert a(A[0], A[1], A[2], 640, 16, 3, 128, A[3], A[4], big, s) == E_SHAPE
+    assert a(A[0], A[1], A[2], 1025, 16, 4, 128, A[3], A[4], big, s) == E_UNSUP    # > 64 splits
+    assert a(A[0], A[1], A[2], 640, 16, 4, 64, A[3], A[4], big, s) == E_UNSUP
+    assert a(A[0], A[1], A[2], 640, 12, 4, 128, A[3], A[4], big, s) == E_UNSUP     # group 3
+    for i in range(5):
+        args = [A[0], A[1], A[2], A[3], A[4]]
+        args[i] = None
+        assert a(args[0], args[1], args[2], 640, 16, 4, 128, args[3], args[4], big, s) == E_NULL
+    assert a(A[0] + 8, A[1], A[2], 640, 16, 4, 128, A[3], A[4], big, s) == E_UNSUP
+    assert a(A[0], A[1], A[2], 640, 16, 4, 128, A[3], A[4] + 16, big, s) == E_UNSUP
+    assert a(A[0], A[1], A[2], 640, 16, 4, 128, A[3], A[4], ws(16, 128, 640) - 1, s) == E_WS
+    assert a(A[0], A[1], A[2], 640, 16, 4, 128, A[1] + 4096, A[4], big, s) == E_ALIAS   # in k
+    assert a(A[0], A[1], A[2], 640, 16, 4, 128, A[3], A[2] + 1024, big, s) == E_ALIAS   # ws in v
+    assert a(A[0], A[1], A[2], 640, 16, 4, 128, A[4] + 512, A[4], big, s) == E_ALIAS    # out in ws
+
+
 def test_flash_head_workspace_and_errors(L):
     assert L.flash_head_workspace_bytes(4748) == (4748 * 4 + 255) // 256 * 256
     assert L.flash_head_workspace_bytes(0) == 0 and L.flash_head_workspace_bytes(8193) == 0

@@ -103,3 +103,51 @@ def test_attention_reuses_workspace_and_is_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     check(q2, k2, v2, c)
+
+
+# ---- the one-launch form ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,H,Hkv", [(1, 16, 4), (15, 16, 4), (16, 16, 4), (17, 16, 4), (100, 8, 8),
+                                     (512, 16, 4), (640, 16, 4), (1000, 16, 8), (1024, 2, 1),
+                                     (333, 64, 8)])
+def test_attention_one_launch_equals_two_launches(n, H, Hkv):
+    # the same partials merged in the same order: the same bits as attention_decode, and within
+    # the oracle tolerance; the workspace is zero-filled again after the call
+    step("attention one launch n=%d H=%d Hkv=%d" % (n, H, Hkv))
+    q, k, v = synth.attention_inputs(n, "cuda", seed=50 + n % 13, heads=H, kv_heads=Hkv)
+    ws = tw.attention_decode_one_workspace(H, 128, n)
+    one = tw.attention_decode_one(q, k, v, ws)
+    two = tw.attention_decode(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(one, two)
+    assert not torch.any(ws)
+    check(q, k, v, one)
+
+
+def test_attention_one_launch_reused_workspace():
+    # calls of several sizes and group shapes on one workspace (sized for the largest), each
+    # equal to attention_decode; between calls every word is zero again
+    ws = tw.attention_decode_one_workspace(64, 128, 1024)
+    for i, (n, H, Hkv) in enumerate([(1024, 64, 8), (640, 16, 4), (1, 16, 4), (1024, 16, 4),
+                                     (37, 64, 8), (640, 16, 4)]):
+        step("attention one launch, reused workspace, call %d (n=%d)" % (i, n))
+        q, k, v = synth.attention_inputs(n, "cuda", seed=60 + i, heads=H, kv_heads=Hkv)
+        one = tw.attention_decode_one(q, k, v, ws)
+        two = tw.attention_decode(q, k, v)
+        torch.cuda.synchronize()
+        assert torch.equal(one, two), i
+        assert not torch.any(ws), i
+
+
+def test_attention_one_launch_sharp_softmax_and_rejects_long_caches():
+    step("attention one launch, sharp softmax")
+    q, k, v = synth.attention_inputs(640, "cuda", seed=42)
+    q8 = (q.float() * 8).to(torch.bfloat16)
+    ws = tw.attention_decode_one_workspace(16, 128, 640)
+    out = tw.attention_decode_one(q8, k, v, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, tw.attention_decode(q8, k, v))
+    check(q8, k, v, out)
+    q2, k2, v2 = synth.attention_inputs(1025, "cuda", seed=43)
+    with pytest.raises(RuntimeError):
+        tw.attention_decode_one(q2, k2, v2, ws)

@@ -82,6 +82,8 @@ def test_graph_replay_gemv_attention_head():
     q, k, v = synth.attention_inputs(640, "cuda", seed=81)
     ao = torch.empty((16, 128), dtype=torch.float32, device="cuda")
     aws = torch.empty(tw.attention_decode_workspace_bytes(16, 128, 640), dtype=torch.uint8, device="cuda")
+    ao1 = torch.empty((16, 128), dtype=torch.float32, device="cuda")
+    aws1 = tw.attention_decode_one_workspace(16, 128, 640)   # every replay leaves it zero-filled
     f = synth.head_inputs(300, 8, 1024, "cuda", seed=82)
     h = synth.head_hidden(1024, "cuda", seed=82)
     hws = torch.empty(tw.lib().flash_head_workspace_bytes(300), dtype=torch.uint8, device="cuda")
@@ -90,12 +92,14 @@ def test_graph_replay_gemv_attention_head():
     def fn():
         tw.ternary_gemv_i8(c3, 3, sc, 2048, xq, xs, out=y)
         tw.attention_decode(q, k, v, out=ao, workspace=aws)
+        tw.attention_decode_one(q, k, v, aws1, out=ao1)
         res["head"] = tw.flash_head(h, f["centroids"], f["centroid_scales"], f["w_clustered"],
                                     f["member_ids"], 40, workspace=hws)
     fn()
     torch.cuda.synchronize()
     sel, ids, lg = res["head"]
-    ref = [y.clone(), ao.clone(), sel.clone(), ids.clone(), lg.clone()]
+    ref = [y.clone(), ao.clone(), sel.clone(), ids.clone(), lg.clone(), ao1.clone()]
+    assert torch.equal(ao1, ao)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -106,12 +110,14 @@ def test_graph_replay_gemv_attention_head():
     with torch.cuda.graph(g):
         fn()
     torch.cuda.synchronize()
-    outs = [y, ao, *res["head"]]            # the head's outputs allocated inside the capture
+    outs = [y, ao, *res["head"], ao1]       # the head's outputs allocated inside the capture
     for r in range(3):
         y.fill_(-7)
         ao.fill_(-7)
+        ao1.fill_(-7)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         for a, b in zip(outs, ref):
             assert torch.equal(a, b), r
+        assert not torch.any(aws1), r
