@@ -330,6 +330,17 @@ __device__ __forceinline__ void pf_work(const Dims &dm, const BatchedWs &L, cons
     //    ms * 16 + l16 and stores them as one 16-byte vector (padding tokens write a spare row
     //    behind the last pair, one per workgroup slot so that few workgroups share one; every store
     //    is unconditional, so the wait for a code unit never has to wait for a store)
+    // 16-bit sums: each row sub-tile's store offset (bytes from y16) is formed once, with this
+    // wave's first output row, so that a unit's store adds only a constant
+    uint32_t yoff[RS];
+    if constexpr (Y16) {
+#pragma unroll
+        for (int rs = 0; rs < RS; rs++) {
+            const int m = rs * TPS + l16 / P, pr = s_pair[m];
+            const int64_t row = pr >= 0 ? int64_t(pr) : L.spare_row + (blockIdx.x % kSpareRows);
+            yoff[rs] = uint32_t(row) * uint32_t(2 * D) + uint32_t(2 * (wave * NSD * 16 + 4 * g4));
+        }
+    }
 #pragma unroll
     for (int n = 0; n < NSD; n++) {
         const int u = NGU + n;
@@ -366,18 +377,20 @@ __device__ __forceinline__ void pf_work(const Dims &dm, const BatchedWs &L, cons
             // the second lane of a two-plane token holds the same values: it writes a spare row
             const int64_t row = pr >= 0 && pl == 0 ? int64_t(pr) : L.spare_row + (blockIdx.x % kSpareRows);
             if constexpr (Y16) {
-                // 16-bit sums; a sum outside [-32767, 32767] is stored as the marker -32768 and the
-                // four int32 sums of this lane go to the 32-bit rows as well
-                uint32_t hv[2] = {0u, 0u};
+                // 16-bit sums; a sum outside [-32767, 32767] is stored as the marker -32768 (the
+                // clamp to [-32768, 32768] maps every such sum to a value whose low 16 bits are
+                // 0x8000) and the four int32 sums of this lane go to the 32-bit rows as well
+                int32_t c[4];
                 bool wide = false;
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
                     const int32_t v = acc[rs][r];
-                    const bool fits = v >= -32767 && v <= 32767;
-                    wide = wide || !fits;
-                    hv[r >> 1] |= (uint32_t(fits ? v : -32768) & 0xffffu) << (16 * (r & 1));
+                    c[r] = min(max(v, -32768), 32768);
+                    wide = wide || uint32_t(v + 32767) > 65534u;
                 }
-                *reinterpret_cast<uint2 *>(y16 + row * D + R0 + 4 * g4) = make_uint2(hv[0], hv[1]);
+                const uint2 hv = make_uint2((uint32_t(c[0]) & 0xffffu) | (uint32_t(c[1]) << 16),
+                                            (uint32_t(c[2]) & 0xffffu) | (uint32_t(c[3]) << 16));
+                *reinterpret_cast<uint2 *>(reinterpret_cast<uint8_t *>(y16) + yoff[rs] + 32 * n) = hv;
                 if (wide)
                     *reinterpret_cast<int4 *>(ywide + row * D + R0 + 4 * g4) =
                         make_int4(acc[rs][0], acc[rs][1], acc[rs][2], acc[rs][3]);
