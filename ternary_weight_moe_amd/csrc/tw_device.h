@@ -453,10 +453,11 @@ __device__ __forceinline__ void topk_softmax_wave_regs(const float (&lv)[KPER], 
 
 // A shorter form of topk_softmax_wave_regs<KPER, false> for E <= 256.  Each candidate becomes one
 // 32-bit composite: the upper 24 bits of its order key, then 255 - id, so that a round is a single
-// 32-bit wave maximum with no tie step (composites are distinct).  It runs k + 1 rounds and accepts
-// the result when the 24-bit parts strictly decrease over them: a larger key never has a smaller
-// 24-bit part, so then the first k rounds selected the k largest keys in the exact order, and no
-// candidate outside them has a key as large as the k-th.  Returns false when they do not (near-equal
+// 32-bit wave maximum with no tie step (composites are distinct).  It runs k rounds and accepts the
+// result when the 24-bit parts of the k winners strictly decrease and no other candidate's 24-bit
+// part reaches the k-th winner's: a larger key never has a smaller 24-bit part, so then the k
+// rounds selected the k largest keys in the exact order, and no candidate outside them has a key as
+// large as the k-th.  Returns false when they do not (near-equal
 // or equal logits); the caller then runs the exact form.  On success lane j < k holds the id and
 // the logit selected in round j.  Measured alone (one wave, 8 of 256): 0.78 us against 0.95 for the
 // exact form.
@@ -483,7 +484,7 @@ __device__ __forceinline__ bool topk_wave_composite(const float (&lv)[KPER], int
     uint32_t mine = 0u;   // lane j: the composite selected in round j
     uint32_t prev = 0xffffffffu;
     bool ok = true;
-    for (int j = 0; j <= k; j++) {
+    for (int j = 0; j < k; j++) {
         const uint32_t m = wave_max_u32(c[0]);
         ok = ok && (j == 0 || (m >> 8) < (prev >> 8));
         prev = m;
@@ -494,6 +495,9 @@ __device__ __forceinline__ bool topk_wave_composite(const float (&lv)[KPER], int
             c[KPER - 1] = 0u;
         }
     }
+    // in place of round k + 1: no remaining candidate (each lane's head is its largest) reaches the
+    // 24-bit part of the k-th selected one
+    ok = ok && __ballot((c[0] >> 8) >= (prev >> 8)) == 0;
     if (!ok) return false;
     // lane j < k: its logit is in lane id % 64, slot id / 64
     const uint32_t id = 255u - (mine & 255u);
