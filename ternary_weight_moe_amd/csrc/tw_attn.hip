@@ -17,7 +17,8 @@
 // part: wave max and sum per head.  Values: lane = two dimensions; each slot's value row is one
 // coalesced 256-byte read.  The partial (max, sum, 128 outputs) per (split, head) goes to the
 // workspace, and a second kernel merges the splits of each head with the usual rescaling by
-// exp(m_s - M).
+// exp(m_s - M).  attention_decode_one does the same in one launch (up to 64 splits): the partials
+// go out as tagged words and merge workgroups at the end of the grid wait for them (below).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
