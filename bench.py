@@ -328,7 +328,7 @@ def run_single_layer(args, name):
         tops = ops / (total / args.steps) / 1e12
         roof = dict(bound="mfma", achieved=tops, peak=accounting.INT8_MFMA_PEAK_OPS / 1e12,
                     unit="TOP/s", frac=tops * 1e12 / accounting.INT8_MFMA_PEAK_OPS, traffic=None,
-                    kernel="one call: quantise x, group, k_pf_ffn<2048,512>, combine",
+                    kernel="one call: quantise x, group, k_pf_expert<2048,512>, combine",
                     ops_per_call=ops, hbm_gb_s=achieved)
     else:
         roof = dict(bound="hbm", achieved=achieved, peak=accounting.HBM_PEAK_BPS / 1e9,

@@ -35,10 +35,13 @@
 // Work items are mapped to workgroups so that pairs of consecutive tiles (usually one expert) run on
 // the same XCD at about the same time (workgroups b and b + 8 share an XCD): the second tile's code
 // bytes then come from that XCD's L2.
+// Prefill-shaped int8 calls (many tokens per expert) take k_pf_expert instead: one workgroup per
+// expert's tokens (up to 192), described where it is defined.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "tw_device.h"
 #include "tw_internal.h"
@@ -505,6 +508,453 @@ __global__ __launch_bounds__((PfShape<MT, P>::T)) void k_pf_ffn(Dims dm, Batched
     pf_work<D, F, P, MT, SELF, Y16>(dm, L, lp, ws, e, meta, s_cnt, sm);
 }
 
+// ---- prefill-shaped int8 calls: one workgroup per (expert, up to 192 tokens) ------------------
+//
+// A work item is one of k_group's tiles with tiles of kExMaxTok tokens: with many tokens per expert
+// usually one item per expert, so the 256 items of a 256-expert layer run as one round on 256
+// compute units.  The item's workgroup streams its expert's codes once and decodes every code word
+// once for half of its tokens (up to 6 row sub-tiles of 16 per decoded operand; the 64-token tiles
+// decode each expert in every tile):
+//   gate/up: four passes of 128 h rows; the item's activation rows stream through LDS in slices of
+//     256 inputs (loaded straight from memory into LDS, three buffers); h (fp32) goes to the
+//     workspace and max |h| per token is folded into LDS;
+//   h: re-read per (token, 16-row group) and re-quantised (int8 absmax over all F rows) into an int8
+//     tile in LDS, in the digit-plane byte order;
+//   down: the 16-bit sums of pf_work, two output blocks per step.
+// Per value the operations and their order are pf_work's (int8 activations), so the results are
+// the same bits.
+constexpr int kExW = 8, kExT = 64 * kExW;   // waves, threads
+constexpr int kExKS = 256;                  // inputs per activation slice
+constexpr int kExPD = 3;                    // LDS operand reads in flight ahead of the products
+constexpr int kExMaxRS = 12;
+constexpr int kExMaxTok = 16 * kExMaxRS;    // 192 tokens per work item
+
+template <int D, int F, int RS>
+constexpr size_t ex_lds()
+{
+    constexpr size_t slices = 3 * size_t(RS) * 16 * kExKS + 1024, htile = size_t(RS) * 16 * (F + 16);
+    return slices > htile ? slices : htile;
+}
+
+// One 16-byte load per lane from global memory straight into LDS: the wave's 64 lanes fill the 1024
+// bytes at lds (lane l at byte 16 l); lds is wave-uniform.
+__device__ __forceinline__ void load_lds16(const void *g, void *lds)
+{
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                     (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left alone)
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier for LDS hand-offs whose global-to-LDS loads the caller has already waited for
+// (wait_vm): this wave's LDS operations are complete, then s_barrier.  __syncthreads() would also
+// wait for every load still in flight (the loads straight into LDS make its fence wait for all
+// vector memory operations), including the ones requested ahead on purpose.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int D, int F, int RS>
+__device__ __forceinline__ void ex_work(const Dims &dm, const BatchedWs &L, const LayerPtrs &lp, uint8_t *ws,
+                                        int e, int2 meta, int8_t *sm, int32_t *s_pair, float *s_sx,
+                                        uint32_t *s_amax, const float *s_gs, const float *s_us)
+{
+    // Waves: row group rg = wave % 4 (two blocks of 16 h rows per pass and per down step), token
+    // half th = wave / 4 (row sub-tiles th, th + 2, ...).  Every activation operand read from LDS
+    // feeds four matrix products (two blocks, gate and up), every h operand two.
+    constexpr int HP = 16 * kExW;               // h rows per pass
+    constexpr int NPASS = F / HP;
+    constexpr int NSL = D / kExKS;              // activation slices per pass
+    constexpr int NG = NPASS * NSL;             // slice steps
+    constexpr int HS = RS / 2;                  // row sub-tiles per wave
+    constexpr int NTK = RS * 16;                // token rows, padded
+    constexpr int SLICE = NTK * kExKS;          // one slice buffer: unpadded rows of 256 bytes
+    constexpr int NJ = NTK / 4;                 // 1024-byte groups (4 rows) per slice
+    constexpr int JPW = (NJ + kExW - 1) / kExW; // groups per wave (at most)
+    constexpr int DB = D / 16 / 4;              // output row blocks per row group
+    constexpr int NDS = DB / 2;                 // down steps (two blocks each)
+    constexpr int SD = F / 256;
+    static_assert(RS % 2 == 0 && F % HP == 0 && D % kExKS == 0 && NSL % 2 == 0 && NG >= 2, "shape");
+    static_assert(DB % 2 == 0 && NDS % 2 == 0 && SD >= 1 && SD <= 2, "shape");
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l16 = lane & 15, g4 = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int rg = wv & 3, th = wv >> 2;
+    const int k = dm.k, nv = meta.y, rsv = (nv + 15) / 16;
+    const int32_t *pairs = reinterpret_cast<const int32_t *>(ws + L.pairs);
+    const float *tinfo = reinterpret_cast<const float *>(ws + L.tinfo);
+    const int8_t *xdig = reinterpret_cast<const int8_t *>(ws + L.xdig);
+    float *hbuf = reinterpret_cast<float *>(ws + L.h);
+    int16_t *y16 = reinterpret_cast<int16_t *>(ws + L.y16);
+    int32_t *ywide = reinterpret_cast<int32_t *>(ws + L.y);
+    float *shp = reinterpret_cast<float *>(ws + L.shp);
+    if (t < NTK) {
+        const int pr = t < nv ? pairs[meta.x + t] : -1;
+        s_pair[t] = pr;
+        s_sx[t] = pr >= 0 ? tinfo[2 * (pr / k)] : 0.0f;
+        s_amax[t] = 0u;
+    }
+
+    // gate/up code units: unit g = pass * NSL + slice holds, for both of the wave's row blocks, the
+    // 16 rows of gate and of up over the slice's 256 inputs (one 16-byte chunk per lane each).  Unit
+    // g sits in ring slot g % 2; a step decodes its unit and at once requests unit g + 2 into it.
+    int4 ring[2][4];
+    const uint32_t gofs = uint32_t(l16 * (D / 4) + 16 * g4);
+    const uint8_t *gbase = lp.w_gate + (int64_t(e) * F + rg * 32) * (D / 4);
+    const uint8_t *ubase = lp.w_up + (int64_t(e) * F + rg * 32) * (D / 4);
+    auto issue_gu = [&](int u, auto slot_c) __attribute__((always_inline)) {
+        constexpr int SLOT = decltype(slot_c)::value;
+        u = min(u, NG - 1);   // past the last unit: a harmless re-read (the slot is always refilled)
+        const int ps = u / NSL, sl = u % NSL;
+        const int64_t o = int64_t(ps) * HP * (D / 4) + 64 * sl + gofs;
+#pragma unroll
+        for (int bb = 0; bb < 2; bb++) {
+            ring[SLOT][2 * bb] = *reinterpret_cast<const int4 *>(gbase + o + bb * 16 * (D / 4));
+            ring[SLOT][2 * bb + 1] = *reinterpret_cast<const int4 *>(ubase + o + bb * 16 * (D / 4));
+        }
+    };
+    // activation slices, from memory straight into LDS (three buffers: step g computes slice g from
+    // buffer g % 3 while slices g + 1 and g + 2 arrive): chunk q (16 bytes) of row m sits at position
+    // q ^ (m % 16) of the row, so that the 16 rows an operand read takes hit 16 different bank
+    // groups.  Group j (rows 4 j .. 4 j + 3) is one wave-wide load: lane l fills row 4 j + l / 16,
+    // position l % 16.  A padding row holds the item's first token (its results are never stored).
+    // Every wave issues JPW loads per slice (a wave with fewer groups re-reads its first group into
+    // a spare kilobyte behind the buffers), so that each step has a fixed number of loads in flight.
+    uint32_t xoff[JPW];
+    auto load_slice = [&](int sl, int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < JPW; i++) {
+            const int j = wv + kExW * i;
+            const bool real = j < NJ;
+            load_lds16(xdig + (real ? xoff[i] : xoff[0]) + kExKS * sl,
+                       sm + (real ? buf * SLICE + 1024 * j : 3 * SLICE));
+        }
+    };
+    issue_gu(0, std::integral_constant<int, 0>{});
+    issue_gu(1, std::integral_constant<int, 1>{});
+    __syncthreads();   // s_pair, s_sx, s_amax and the expert's scales
+    {
+        const int pr0 = s_pair[0];
+#pragma unroll
+        for (int i = 0; i < JPW; i++) {
+            const int m = min(4 * (wv + kExW * i) + (lane >> 4), NTK - 1), q = (lane & 15) ^ (m & 15);
+            const int pr = s_pair[m] >= 0 ? s_pair[m] : pr0;
+            xoff[i] = uint32_t(pr / k) * uint32_t(D) + uint32_t(16 * q);
+        }
+    }
+    // the lane's operand reads: chunk 4 g4 + s of rows (2 i + th) * 16 + l16 (row % 16 = l16)
+    uint32_t aoff[4];
+#pragma unroll
+    for (int s = 0; s < 4; s++) aoff[s] = uint32_t((th * 16 + l16) * kExKS + 16 * ((4 * g4 + s) ^ l16));
+    load_slice(0, 0);
+    load_slice(1 % NSL, 1);
+    wait_vm<JPW>();   // slice 0 and the first two code units are in
+    lds_barrier();
+
+    int gb = 0;   // buffer of the current step
+    v4i wd[2][4];   // decoded weights (gate and up of both blocks) of two input steps
+#pragma unroll
+    for (int c = 0; c < 4; c++) wd[0][c] = decode16(word_of(ring[0][c], 0));
+    for (int ps = 0; ps < NPASS; ps++) {
+        v4i accg[2][HS], accu[2][HS];
+#pragma unroll
+        for (int i = 0; i < HS; i++)
+#pragma unroll
+            for (int bb = 0; bb < 2; bb++) accg[bb][i] = accu[bb][i] = v4i{0, 0, 0, 0};
+        auto slice_step = [&](int sl, auto slot_c) __attribute__((always_inline)) {
+            constexpr int SLOT = decltype(slot_c)::value;
+            const int g = ps * NSL + sl;
+            const int4 (&cq)[4] = ring[SLOT];
+            // slice g + 2 into buffer (g + 2) % 3 (past the last step: a harmless re-read into a
+            // buffer no step reads again), so that every step issues the same loads
+            load_slice((sl + 2) % NSL, gb == 0 ? 2 : gb - 1);
+            // fragments n = s * HS + i (input step s, sub-tile 2 i + th), read kExPD ahead of their
+            // products.  The weights of input step s + 1 are decoded while the products
+            // of step s run (those of step 0 at the end of the previous slice step); once the last
+            // words are decoded, unit g + 2 is requested into the same registers.
+            const int8_t *abase = sm + gb * SLICE;
+            v4i a[kExPD + 1];
+            auto aread = [&](int n) __attribute__((always_inline)) {
+                return *reinterpret_cast<const v4i *>(abase + (n % HS) * 32 * kExKS + aoff[n / HS]);
+            };
+#pragma unroll
+            for (int n = 0; n < kExPD; n++) a[n] = aread(n);
+#pragma unroll
+            for (int n = 0; n < 4 * HS; n++) {
+                const int s = n / HS, i = n % HS;
+                if (n + kExPD < 4 * HS) a[(n + kExPD) % (kExPD + 1)] = aread(n + kExPD);
+                __builtin_amdgcn_sched_barrier(0);   // the read stays ahead of this fragment's products
+                const v4i(&w)[4] = wd[s & 1];
+                const v4i &af = a[n % (kExPD + 1)];
+                accg[0][i] = mfma8(w[0], af, accg[0][i]);
+                accu[0][i] = mfma8(w[1], af, accu[0][i]);
+                accg[1][i] = mfma8(w[2], af, accg[1][i]);
+                accu[1][i] = mfma8(w[3], af, accu[1][i]);
+                if (i == 0 && s < 3) {
+#pragma unroll
+                    for (int c = 0; c < 4; c++) wd[(s + 1) & 1][c] = decode16(word_of(cq[c], s + 1));
+                    if (s == 2) {
+                        __builtin_amdgcn_sched_barrier(0);   // the unit's registers are free again
+                        issue_gu(g + 2, slot_c);
+                    }
+                }
+            }
+            // input step 0 of the next unit (past the last one: a harmless decode of the re-read)
+#pragma unroll
+            for (int c = 0; c < 4; c++) wd[0][c] = decode16(word_of(ring[1 - SLOT][c], 0));
+            // slice g + 1 is in LDS: everything but this step's requests has arrived
+            wait_vm<JPW + 4>();
+            lds_barrier();
+            gb = gb == 2 ? 0 : gb + 1;
+        };
+        for (int sl = 0; sl < NSL; sl += 2) {
+            slice_step(sl, std::integral_constant<int, 0>{});
+            slice_step(sl + 1, std::integral_constant<int, 1>{});
+        }
+        // epilogue of the pass: h = SiLU(gate) * up (pf_work's operations), stored in fp32; max |h|
+        // per token folded into LDS.  Sub-tiles past the item's tokens are skipped.
+        const int row0 = ps * HP + rg * 32 + 4 * g4;
+        f4 gsc[2], usc[2];
+#pragma unroll
+        for (int bb = 0; bb < 2; bb++) {
+            gsc[bb] = *reinterpret_cast<const f4 *>(s_gs + row0 + 16 * bb);
+            usc[bb] = *reinterpret_cast<const f4 *>(s_us + row0 + 16 * bb);
+        }
+        float mxs[HS];
+#pragma unroll
+        for (int i = 0; i < HS; i++) mxs[i] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < HS; i++) {
+            if (2 * i + th >= rsv && i > 0) break;
+            const int m = (2 * i + th) * 16 + l16;
+            const float sx = s_sx[m];
+            const int pr = s_pair[m];
+            float &mx = mxs[i];
+#pragma unroll
+            for (int bb = 0; bb < 2; bb++) {
+                float hv[4];
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const float gate = (float(accg[bb][i][r]) * sx) * gsc[bb][r];
+                    const float up = (float(accu[bb][i][r]) * sx) * usc[bb][r];
+                    hv[r] = tw_silu(gate) * up;
+                    mx = fmaxf(mx, fabsf(hv[r]));
+                }
+                if (pr >= 0)
+                    *reinterpret_cast<f4 *>(hbuf + int64_t(pr) * F + row0 + 16 * bb) = f4{hv[0], hv[1], hv[2], hv[3]};
+                __builtin_amdgcn_sched_barrier(0);   // four SiLUs at a time: bounded temporaries
+            }
+        }
+        // the per-token maxima after all SiLUs (an LDS atomic waits for the loads still in flight)
+#pragma unroll
+        for (int i = 0; i < HS; i++) {
+            const int m = (2 * i + th) * 16 + l16;
+            float mx = fmaxf(mxs[i], __shfl_xor(mxs[i], 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            if (g4 == 0 && s_pair[m] >= 0) atomicMax(&s_amax[m], __float_as_uint(mx));
+        }
+    }
+
+    // down code units: unit j (step j) holds the two 16-row output blocks 2 j, 2 j + 1 of the row
+    // group (rows rg * D / 4 + 32 j ..), SD 16-byte chunks per lane and block; unit j sits in slot
+    // j % 2, and step j requests unit j + 1 as it starts.  The first is requested before the
+    // re-quantisation.
+    const uint32_t dofs = uint32_t(l16 * (F / 4) + 16 * g4);
+    const uint8_t *dbase = lp.w_down + (int64_t(e) * D + rg * (D / 4)) * (F / 4);
+    int4 dring[2][2][SD];
+    auto issue_d = [&](int j, auto slot_c) __attribute__((always_inline)) {
+        constexpr int SLOT = decltype(slot_c)::value;
+        if (j >= NDS) return;
+#pragma unroll
+        for (int bb = 0; bb < 2; bb++)
+#pragma unroll
+            for (int S = 0; S < SD; S++)
+                dring[SLOT][bb][S] = *reinterpret_cast<const int4 *>(dbase + (2 * j + bb) * 16 * (F / 4) + 64 * S + dofs);
+    };
+    issue_d(0, std::integral_constant<int, 0>{});
+    __syncthreads();   // every h store and max of this item is done
+
+    // h: per (token, 16-row group) re-quantised against the token's max |h| into the int8 tile (byte
+    // j of a group's 16 rows goes to byte 4 (j % 4) + j / 4, the order of the decoded code words);
+    // the loads of QB items are in flight together (a padding row reads the item's first token)
+    {
+        constexpr int NQ = NTK * (F / 16), QPT = (NQ + kExT - 1) / kExT, QB = 4;
+        const int pr0 = s_pair[0];
+#pragma unroll
+        for (int j0 = 0; j0 < QPT; j0 += QB) {
+            f4 v[QB][4];
+            int mq[QB], gq[QB], pq[QB];
+#pragma unroll
+            for (int b = 0; b < QB; b++) {
+                const int i = t + kExT * (j0 + b);
+                mq[b] = min(i / (F / 16), NTK - 1);
+                gq[b] = i % (F / 16);
+                pq[b] = j0 + b < QPT && i < NQ ? s_pair[mq[b]] : -2;
+                const f4 *hp = reinterpret_cast<const f4 *>(hbuf + int64_t(pq[b] >= 0 ? pq[b] : pr0) * F + 16 * gq[b]);
+                if (j0 + b < QPT) {
+#pragma unroll
+                    for (int c = 0; c < 4; c++) v[b][c] = hp[c];
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < QB; b++) {
+                if (j0 + b >= QPT || pq[b] == -2) continue;
+                int4 packed = make_int4(0, 0, 0, 0);
+                if (pq[b] >= 0) {
+                    const float am = __uint_as_float(s_amax[mq[b]]);
+                    int8_t q[16];
+#pragma unroll
+                    for (int c = 0; c < 4; c++)
+#pragma unroll
+                        for (int j = 0; j < 4; j++)
+                            q[4 * c + j] = am > 0.0f ? int8_quant(v[b][c][j], 127.0f / am) : int8_t(0);
+                    uint32_t d[4];
+#pragma unroll
+                    for (int dd = 0; dd < 4; dd++)
+                        d[dd] = uint32_t(uint8_t(q[dd])) | (uint32_t(uint8_t(q[dd + 4])) << 8) |
+                                (uint32_t(uint8_t(q[dd + 8])) << 16) | (uint32_t(uint8_t(q[dd + 12])) << 24);
+                    packed = make_int4(int32_t(d[0]), int32_t(d[1]), int32_t(d[2]), int32_t(d[3]));
+                }
+                *reinterpret_cast<int4 *>(sm + mq[b] * (F + 16) + 16 * gq[b]) = packed;
+            }
+        }
+    }
+    if (t < NTK && s_pair[t] >= 0) {
+        const float am = __uint_as_float(s_amax[t]);
+        shp[s_pair[t]] = am > 0.0f ? am / 127.0f : 0.0f;   // the combine forms y from it
+    }
+    __syncthreads();
+
+    // down, two 16-row blocks per step (pf_work's sums and 16-bit stores); sub-tiles past the item's
+    // tokens store into spare rows
+    uint32_t yoff[HS];
+#pragma unroll
+    for (int i = 0; i < HS; i++) {
+        const int pr = s_pair[(2 * i + th) * 16 + l16];
+        const int64_t row = pr >= 0 ? int64_t(pr) : L.spare_row + (blockIdx.x % kSpareRows);
+        yoff[i] = uint32_t(row) * uint32_t(2 * D) + uint32_t(2 * (rg * (D / 4) + 4 * g4));
+    }
+    const int8_t *hbase = sm + tofs(th * 16 + l16, 4 * g4, F);
+    // 16-bit sums of block bb, sub-tile 2 i + th of down step j (a sum outside [-32767, 32767] is
+    // stored as the marker -32768, and the lane's four sums go to the 32-bit rows as well); padding
+    // tokens of a sub-tile that holds real ones write spare rows
+    auto emit = [&](const v4i &v4, int bb, int i, int j) __attribute__((always_inline)) {
+        if (i > 0 && 2 * i + th >= rsv) return;   // a sub-tile of padding rows only: nothing to keep
+        int32_t cl[4];
+        bool wide = false;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int32_t v = v4[r];
+            cl[r] = min(max(v, -32768), 32768);
+            wide = wide || uint32_t(v + 32767) > 65534u;
+        }
+        const uint2 hv2 = make_uint2((uint32_t(cl[0]) & 0xffffu) | (uint32_t(cl[1]) << 16),
+                                     (uint32_t(cl[2]) & 0xffffu) | (uint32_t(cl[3]) << 16));
+        *reinterpret_cast<uint2 *>(reinterpret_cast<uint8_t *>(y16) + yoff[i] + 64 * j + 32 * bb) = hv2;
+        // the same element in the 32-bit rows sits at twice the byte offset
+        if (wide)
+            *reinterpret_cast<int4 *>(reinterpret_cast<uint8_t *>(ywide) + 2 * size_t(yoff[i]) + 128 * j + 64 * bb) =
+                make_int4(v4[0], v4[1], v4[2], v4[3]);
+    };
+    // step j sums into acc[j % 2]; the sums of step j - 1 are stored piece by piece while the
+    // products of step j run (one (block, sub-tile) piece after every 2 SD fragments)
+    v4i acc[2][2][HS];
+    auto down_step = [&](int j, auto slot_c) __attribute__((always_inline)) {
+        constexpr int SLOT = decltype(slot_c)::value;
+        issue_d(j + 1, std::integral_constant<int, 1 - SLOT>{});
+        const int4 (&cq)[2][SD] = dring[SLOT];
+        v4i (&ac)[2][HS] = acc[SLOT];
+        const v4i (&ap)[2][HS] = acc[1 - SLOT];
+        // fragments n = c * HS + i (h chunk 16 (c / 4) + 4 g4 + c % 4, sub-tile 2 i + th), read
+        // kExPD ahead of their products; the two blocks' words of step c are decoded as it starts
+        v4i w[2], hv[kExPD + 1];
+        auto hread = [&](int n) __attribute__((always_inline)) {
+            const int c = n / HS, i = n % HS;
+            return *reinterpret_cast<const v4i *>(hbase + i * 32 * (F + 16) + 256 * (c >> 2) + 16 * (c & 3));
+        };
+#pragma unroll
+        for (int n = 0; n < kExPD; n++) hv[n] = hread(n);
+#pragma unroll
+        for (int n = 0; n < 4 * SD * HS; n++) {
+            const int c = n / HS, i = n % HS;
+            if (i == 0) {
+#pragma unroll
+                for (int bb = 0; bb < 2; bb++) w[bb] = decode16(word_of(cq[bb][c >> 2], c & 3));
+            }
+            if (n + kExPD < 4 * SD * HS) hv[(n + kExPD) % (kExPD + 1)] = hread(n + kExPD);
+            __builtin_amdgcn_sched_barrier(0);   // the read stays ahead of this fragment's products
+#pragma unroll
+            for (int bb = 0; bb < 2; bb++)   // the first product of a sum starts from zero
+                ac[bb][i] = mfma8(w[bb], hv[n % (kExPD + 1)], c == 0 ? v4i{0, 0, 0, 0} : ac[bb][i]);
+            if (j > 0 && n % (2 * SD) == 2 * SD - 1) {
+                const int pc = n / (2 * SD);   // 0 .. 2 HS - 1
+                emit(ap[pc & 1][pc >> 1], pc & 1, pc >> 1, j - 1);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int j = 0; j < NDS; j += 2) {
+        down_step(j, std::integral_constant<int, 0>{});
+        down_step(j + 1, std::integral_constant<int, 1>{});
+    }
+    // the last step's sums (NDS is even: they are in acc[1])
+#pragma unroll
+    for (int i = 0; i < HS; i++)
+#pragma unroll
+        for (int bb = 0; bb < 2; bb++) emit(acc[1][bb][i], bb, i, NDS - 1);
+}
+
+template <int D, int F>
+__global__ __launch_bounds__(kExT) void k_pf_expert(Dims dm, BatchedWs L, LayerPtrs lp, uint8_t *ws)
+{
+    extern __shared__ __attribute__((aligned(16))) int8_t sm[];
+    __shared__ int32_t s_pair[kExMaxTok];
+    __shared__ float s_sx[kExMaxTok];
+    __shared__ uint32_t s_amax[kExMaxTok];
+    __shared__ __attribute__((aligned(16))) float s_gs[F];
+    __shared__ __attribute__((aligned(16))) float s_us[F];
+    const int b = blockIdx.x, t = threadIdx.x;
+    const int32_t *tiles = reinterpret_cast<const int32_t *>(ws + L.tiles);
+    const int2 *tmeta = reinterpret_cast<const int2 *>(ws + L.tilemeta);
+    const int ntiles = tiles[0];
+    if (b >= ntiles) return;
+    const int e = tiles[1 + b] & 1023;
+    const int2 meta = tmeta[b];
+    for (int i = t; i < F; i += kExT) {
+        s_gs[i] = lp.s_gate[int64_t(e) * F + i];
+        s_us[i] = lp.s_up[int64_t(e) * F + i];
+    }
+    const int rsv = (meta.y + 15) / 16;
+    if (rsv <= 4)
+        ex_work<D, F, 4>(dm, L, lp, ws, e, meta, sm, s_pair, s_sx, s_amax, s_gs, s_us);
+    else if (rsv <= 8)
+        ex_work<D, F, 8>(dm, L, lp, ws, e, meta, sm, s_pair, s_sx, s_amax, s_gs, s_us);
+    else if (rsv <= 10)
+        ex_work<D, F, 10>(dm, L, lp, ws, e, meta, sm, s_pair, s_sx, s_amax, s_gs, s_us);
+    else
+        ex_work<D, F, 12>(dm, L, lp, ws, e, meta, sm, s_pair, s_sx, s_amax, s_gs, s_us);
+}
+
+template <int D, int F>
+int ex_run(const Dims &dm, const LayerPtrs &lp, int64_t T, const BatchedWs &L, uint8_t *ws, void *stream)
+{
+    constexpr size_t lds = ex_lds<D, F, kExMaxRS>();
+    static std::atomic<int> attr_set{0};
+    if (!attr_set.load(std::memory_order_relaxed)) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_pf_expert<D, F>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
+            return int(hipErrorInvalidValue);
+        attr_set.store(1, std::memory_order_relaxed);
+    }
+    const int nb = int(max_tiles(dm, T, kExMaxTok));
+    k_pf_expert<D, F><<<nb, kExT, lds, static_cast<hipStream_t>(stream)>>>(dm, L, lp, ws);
+    return int(hipGetLastError());
+}
+
 // One workgroup per tile slot; sel_ids != nullptr: the workgroups build the tile list themselves
 // (needs T k and E <= the workgroup size), else they read k_group's.
 template <int D, int F, int P, int MT, bool SELF>
@@ -532,6 +982,7 @@ int pf_dispatch(const Dims &dm, const LayerPtrs &lp, int64_t T, int planes, int 
                 const BatchedWs &L, uint8_t *ws, const int32_t *sel_ids, void *stream)
 {
     if (planes == 1) {
+        if (tile == kExMaxTok) return ex_run<D, F>(dm, lp, T, L, ws, stream);
         if (tile == 64) return pf_run<D, F, 1, 64, false>(dm, lp, T, L, ws, nullptr, stream);
         if (sel_ids) return pf_run<D, F, 1, 16, true>(dm, lp, T, L, ws, sel_ids, stream);
         return pf_run<D, F, 1, 16, false>(dm, lp, T, L, ws, nullptr, stream);
@@ -551,6 +1002,8 @@ bool grouped_mfma_serves(const Dims &dm, int64_t T, int planes, int *tile)
     // 64 tokens, two planes: 32 tokens), else of 16 rows (16 or 8 tokens)
     const bool big = T * dm.k * planes >= int64_t(32) * dm.E;
     *tile = planes == 1 ? (big ? 64 : 16) : (big ? 32 : 8);
+    // int8 activations with at least 96 tokens per expert on average: one work item per expert
+    if (planes == 1 && T * dm.k >= int64_t(96) * dm.E) *tile = kExMaxTok;
     return true;
 }
 

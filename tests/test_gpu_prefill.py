@@ -99,11 +99,55 @@ def test_prefill_int8_one_hot_experts_ragged_tiles(full):
     assert np.array_equal(bits(out)[sample], ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("T", [256, 1024])
+def skewed_ids(T, E, k, seed):
+    """Top-k ids with a heavy skew: slot 0 always expert 7, the other slots drawn without
+    replacement from 200 other experts (shuffled) with weights 1 / (rank + 1), so that per-expert
+    counts range from thousands to a handful, and E - 201 experts get none."""
+    rng = np.random.default_rng(seed)
+    order = rng.permutation([e for e in range(E) if e != 7])[:200]
+    p = 1.0 / (np.arange(len(order)) + 1.0)
+    p /= p.sum()
+    ids = np.empty((T, k), np.int32)
+    ids[:, 0] = 7
+    for i in range(T):
+        ids[i, 1:] = rng.choice(order, size=k - 1, replace=False, p=p)
+    return ids
+
+
+def test_prefill_int8_expert_items_skewed_counts(full):
+    # 4096 tokens, one work item per (expert, up to 176 tokens): expert 7 takes every token (24
+    # items, the last of 48 tokens), the rest range from hundreds of tokens to a handful or none,
+    # so items of every size class run side by side
+    T = 4096
+    x = synth.activations(synth.PREFILL_4096, T, seed=77).cuda()
+    ids_np = skewed_ids(T, 256, 8, seed=9)
+    counts = np.bincount(ids_np.ravel(), minlength=256)
+    rem = counts[counts > 0] % 176
+    # last items of every size class (16-token row blocks: up to 4, 5-8, 9, 10, 11)
+    for lo, hi in [(0, 16), (16, 64), (64, 128), (128, 144), (144, 160), (160, 175)]:
+        assert ((rem > lo) & (rem <= hi)).any(), (lo, hi)
+    assert counts.max() == T and (counts == 0).sum() == 256 - 201
+    ids = torch.from_numpy(ids_np).cuda()
+    g = torch.rand((T, 8), generator=torch.Generator().manual_seed(6)) + 0.05
+    gates = (g / g.sum(1, keepdim=True)).float().contiguous().cuda()
+    step("prefill int8 skewed routing T=4096 (one item per expert)")
+    out = run_int8(full.gpu, x, ids, gates)
+    step("4096 tokens through the dot4 path in 64-token calls")
+    ref_dot = dot_path_in_chunks(full.gpu, x, ids, gates)
+    assert np.array_equal(bits(out), bits(ref_dot))
+    sample = np.array([0, 1, 175, 176, 2047, T - 1])
+    step("oracle int8 spec on %d sampled tokens" % len(sample))
+    ref = oracle.ffn_batch_i8(full.ora, x.cpu()[sample], ids_np[sample], gates.cpu().numpy()[sample],
+                              n_threads=NTH)
+    assert np.array_equal(bits(out)[sample], ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("T", [256, 1024, 2048])
 def test_prefill_int8_second_shape(T):
     # d=1024, 64 experts, F=256, top-4: the second instantiation of the MFMA path; 256 tokens take
     # the small self-grouped tiles, 1024 tokens (64 pairs per expert) the 64-token tiles, whose
-    # ragged last tiles of at most 32 tokens take the half-size body
+    # ragged last tiles of at most 32 tokens take the half-size body, and 2048 tokens (128 pairs per
+    # expert) one work item per (expert, up to 176 tokens)
     wl = synth.MID_STACK_B1
     pair = make_pair(wl, pre=False)
     x = synth.activations(wl, T, seed=75).cuda()
@@ -185,7 +229,7 @@ def test_batched_int8_invalid_slots_contribute_nothing(full, T):
     assert torch.equal(out[5], x[5].float())
 
 
-@pytest.mark.parametrize("T,E,k", [(40, 8, 4), (300, 8, 4), (300, 16, 8)])
+@pytest.mark.parametrize("T,E,k", [(40, 8, 4), (150, 8, 4), (300, 8, 4), (300, 16, 8)])
 def test_int8_down_sums_outside_int16(T, E, k):
     # With int8 activations in 64-token tiles the grouped kernel keeps each down sum as an int16 and
     # marks the ones outside [-32767, 32767], which then come from 32-bit rows.  Expert 0 here has all-+1 gate and
@@ -194,8 +238,9 @@ def test_int8_down_sums_outside_int16(T, E, k):
     # r mod 513 positions and -1 after them, so the down sums are 127 (2 a - 512) for every a in
     # 0 .. 512: from -65024 to 65024, with 32766 the largest that fits and 33020 the smallest that
     # does not.  Expected: the oracle's int8 spec bit for bit.  T = 40: small self-grouped tiles
-    # (fp32 y rows); T = 300: 64-token tiles from the grouping kernel (16-bit sums), top-4 (the
-    # combine's slot count given at run time) and top-8 (fixed when compiled).
+    # (fp32 y rows); T = 150: 64-token tiles from the grouping kernel (16-bit sums); T = 300 (at
+    # least 96 pairs per expert): one work item per (expert, up to 176 tokens), also 16-bit sums,
+    # top-4 (the combine's slot count given at run time) and top-8 (fixed when compiled).
     wl = synth.PREFILL_4096
     d, F = wl.d_model, wl.d_ff
     w = synth.layer_weights(wl, 0, n_experts=E)
