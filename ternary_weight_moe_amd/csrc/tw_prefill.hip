@@ -775,6 +775,9 @@ __device__ __forceinline__ void ex_work(const Dims &dm, const BatchedWs &L, cons
             for (int S = 0; S < SD; S++)
                 dring[SLOT][bb][S] = *reinterpret_cast<const int4 *>(dbase + (2 * j + bb) * 16 * (F / 4) + 64 * S + dofs);
     };
+    // the last steps' slice loads (re-reads into buffers no step reads again) must land before the
+    // h tile reuses those LDS bytes
+    wait_vm<0>();
     issue_d(0, std::integral_constant<int, 0>{});
     __syncthreads();   // every h store and max of this item is done
 
