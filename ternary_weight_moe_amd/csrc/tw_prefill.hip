@@ -601,7 +601,8 @@ __device__ __forceinline__ void ex_work(const Dims &dm, const BatchedWs &L, cons
 
     // gate/up code units: unit g = pass * NSL + slice holds, for both of the wave's row blocks, the
     // 16 rows of gate and of up over the slice's 256 inputs (one 16-byte chunk per lane each).  Unit
-    // g sits in ring slot g % 2; a step decodes its unit and at once requests unit g + 2 into it.
+    // g sits in ring slot g % 2; once step g has decoded the slot's last words it requests unit g + 2
+    // into the same registers.
     int4 ring[2][4];
     const uint32_t gofs = uint32_t(l16 * (D / 4) + 16 * g4);
     const uint8_t *gbase = lp.w_gate + (int64_t(e) * F + rg * 32) * (D / 4);
