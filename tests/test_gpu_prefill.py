@@ -99,6 +99,27 @@ def test_prefill_int8_one_hot_experts_ragged_tiles(full):
     assert np.array_equal(bits(out)[sample], ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("T", [1024, 3072])
+def test_prefill_int8_bf16_output_is_the_fp32_result_rounded(full, T):
+    # The 16-bit down sums of the grouped kernels (64-token tiles at 1024 tokens, one work item per
+    # expert at 3072) with bf16 output: the combine rounds its fp32 result once, so every output is
+    # the fp32 output of the same call rounded to bf16 (the fp32 output is pinned to the oracle and
+    # the v_dot4 path by the tests above)
+    x = synth.activations(synth.PREFILL_4096, T, seed=79).cuda()
+    _, ids, gates = tw.moe_route_topk(x, full.gpu.w_router, 8)
+    step("prefill int8 T=%d, fp32 and bf16 outputs" % T)
+    out32 = run_int8(full.gpu, x, ids, gates)
+    out16 = tw.ternary_moe_ffn_batched(full.gpu, x, act="int8", out_dtype=torch.bfloat16,
+                                       expert_ids=ids, gate_w=gates)
+    torch.cuda.synchronize()
+    ref16 = oracle.round_bf16_bits(out32.cpu().numpy().astype(np.float64))
+    assert np.array_equal(out16.cpu().view(torch.int16).numpy().view(np.uint16), ref16)
+    sample = np.array([0, T // 2, T - 1])
+    ref = oracle.ffn_batch_i8(full.ora, x.cpu()[sample], ids.cpu().numpy()[sample],
+                              gates.cpu().numpy()[sample], n_threads=NTH)
+    assert np.array_equal(bits(out32)[sample], ref.view(np.uint32))
+
+
 def skewed_ids(T, E, k, seed):
     """Top-k ids with a heavy skew: slot 0 always expert 7, the other slots drawn without
     replacement from 200 other experts (shuffled) with weights 1 / (rank + 1), so that per-expert
