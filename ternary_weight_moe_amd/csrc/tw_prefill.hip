@@ -532,7 +532,8 @@ constexpr int kExMaxTok = 16 * kExMaxRS;    // 192 tokens per work item
 template <int D, int F, int RS>
 constexpr size_t ex_lds()
 {
-    constexpr size_t slices = 3 * size_t(RS) * 16 * kExKS + 1024, htile = size_t(RS) * 16 * (F + 16);
+    constexpr size_t slices = 3 * size_t(RS) * 16 * kExKS + 1024,
+                     htile = (size_t(RS) * 16 * (F + 16) + 1023) / 1024 * 1024 + 2 * 4 * 2 * (F / 256) * 1024;
     return slices > htile ? slices : htile;
 }
 
@@ -776,10 +777,30 @@ __device__ __forceinline__ void ex_work(const Dims &dm, const BatchedWs &L, cons
             for (int S = 0; S < SD; S++)
                 dring[SLOT][bb][S] = *reinterpret_cast<const int4 *>(dbase + (2 * j + bb) * 16 * (F / 4) + 64 * S + dofs);
     };
+    // the two token halves of a row group use the same down codes: the th = 0 wave loads them and
+    // passes them on through LDS (two buffers behind the h tile, lane-linear 16-byte chunks)
+    constexpr int CBUF = 4 * 2 * SD * 1024;
+    int8_t *const cbase = sm + ((NTK * (F + 16) + 1023) / 1024) * 1024 + (rg * 2 * SD) * 1024 + 16 * lane;
+    auto put_d = [&](int j, auto slot_c) __attribute__((always_inline)) {
+        constexpr int SLOT = decltype(slot_c)::value;
+#pragma unroll
+        for (int bb = 0; bb < 2; bb++)
+#pragma unroll
+            for (int S = 0; S < SD; S++)
+                *reinterpret_cast<int4 *>(cbase + (j & 1) * CBUF + (bb * SD + S) * 1024) = dring[SLOT][bb][S];
+    };
+    auto get_d = [&](int j, auto slot_c) __attribute__((always_inline)) {
+        constexpr int SLOT = decltype(slot_c)::value;
+#pragma unroll
+        for (int bb = 0; bb < 2; bb++)
+#pragma unroll
+            for (int S = 0; S < SD; S++)
+                dring[SLOT][bb][S] = *reinterpret_cast<const int4 *>(cbase + (j & 1) * CBUF + (bb * SD + S) * 1024);
+    };
     // the last steps' slice loads (re-reads into buffers no step reads again) must land before the
     // h tile reuses those LDS bytes
     wait_vm<0>();
-    issue_d(0, std::integral_constant<int, 0>{});
+    if (th == 0) issue_d(0, std::integral_constant<int, 0>{});
     __syncthreads();   // every h store and max of this item is done
 
     // h: per (token, 16-row group) re-quantised against the token's max |h| into the int8 tile (byte
@@ -831,7 +852,9 @@ __device__ __forceinline__ void ex_work(const Dims &dm, const BatchedWs &L, cons
         const float am = __uint_as_float(s_amax[t]);
         shp[s_pair[t]] = am > 0.0f ? am / 127.0f : 0.0f;   // the combine forms y from it
     }
+    if (th == 0) put_d(0, std::integral_constant<int, 0>{});
     __syncthreads();
+    if (th != 0) get_d(0, std::integral_constant<int, 0>{});
 
     // down, two 16-row blocks per step (pf_work's sums and 16-bit stores); sub-tiles past the item's
     // tokens store into spare rows
@@ -869,7 +892,7 @@ __device__ __forceinline__ void ex_work(const Dims &dm, const BatchedWs &L, cons
     v4i acc[2][2][HS];
     auto down_step = [&](int j, auto slot_c) __attribute__((always_inline)) {
         constexpr int SLOT = decltype(slot_c)::value;
-        issue_d(j + 1, std::integral_constant<int, 1 - SLOT>{});
+        if (th == 0) issue_d(j + 1, std::integral_constant<int, 1 - SLOT>{});
         const int4 (&cq)[2][SD] = dring[SLOT];
         v4i (&ac)[2][HS] = acc[SLOT];
         const v4i (&ap)[2][HS] = acc[1 - SLOT];
@@ -900,6 +923,11 @@ __device__ __forceinline__ void ex_work(const Dims &dm, const BatchedWs &L, cons
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+        if (j + 1 < NDS) {
+            if (th == 0) put_d(j + 1, std::integral_constant<int, 1 - SLOT>{});
+            lds_barrier();   // the next step's codes are in LDS
+            if (th != 0) get_d(j + 1, std::integral_constant<int, 1 - SLOT>{});
+        }
     };
     for (int j = 0; j < NDS; j += 2) {
         down_step(j, std::integral_constant<int, 0>{});
