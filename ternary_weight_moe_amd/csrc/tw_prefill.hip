@@ -533,7 +533,8 @@ template <int D, int F, int RS>
 constexpr size_t ex_lds()
 {
     constexpr size_t slices = 3 * size_t(RS) * 16 * kExKS + 1024,
-                     htile = (size_t(RS) * 16 * (F + 16) + 1023) / 1024 * 1024 + 2 * 4 * 2 * (F / 256) * 1024;
+                     htile = (size_t(RS) * 16 * (F + 16) + 1023) / 1024 * 1024 + 2 * 4 * 2 * (F / 256) * 1024 +
+                             kExW * 16 * 80;
     return slices > htile ? slices : htile;
 }
 
@@ -866,29 +867,39 @@ __device__ __forceinline__ void ex_work(const Dims &dm, const BatchedWs &L, cons
         yoff[i] = uint32_t(row) * uint32_t(2 * D) + uint32_t(2 * (rg * (D / 4) + 4 * g4));
     }
     const int8_t *hbase = sm + tofs(th * 16 + l16, 4 * g4, F);
-    // 16-bit sums of block bb, sub-tile 2 i + th of down step j (a sum outside [-32767, 32767] is
-    // stored as the marker -32768, and the lane's four sums go to the 32-bit rows as well); padding
-    // tokens of a sub-tile that holds real ones write spare rows
-    auto emit = [&](const v4i &v4, int bb, int i, int j) __attribute__((always_inline)) {
+    // 16-bit sums of both blocks of sub-tile 2 i + th of down step j (a sum outside [-32767, 32767]
+    // is stored as the marker -32768, and the lane's four sums go to the 32-bit rows as well);
+    // padding tokens of a sub-tile that holds real ones write spare rows.  The lane's 8-byte pieces
+    // of the two blocks pass through this wave's LDS area (token rows of 80 bytes) so that each lane
+    // stores 16 contiguous bytes: rows 8 g4 .. 8 g4 + 7 of the step's 32 (half the store requests).
+    int8_t *const wst = sm + ((NTK * (F + 16) + 1023) / 1024) * 1024 + 2 * (4 * 2 * SD * 1024) + wv * (16 * 80);
+    auto emit = [&](const v4i &a0, const v4i &a1, int i, int j) __attribute__((always_inline)) {
         if (i > 0 && 2 * i + th >= rsv) return;   // a sub-tile of padding rows only: nothing to keep
-        int32_t cl[4];
-        bool wide = false;
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
-            const int32_t v = v4[r];
-            cl[r] = min(max(v, -32768), 32768);
-            wide = wide || uint32_t(v + 32767) > 65534u;
+        for (int bb = 0; bb < 2; bb++) {
+            const v4i &v4 = bb == 0 ? a0 : a1;
+            int32_t cl[4];
+            bool wide = false;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int32_t v = v4[r];
+                cl[r] = min(max(v, -32768), 32768);
+                wide = wide || uint32_t(v + 32767) > 65534u;
+            }
+            *reinterpret_cast<uint2 *>(wst + l16 * 80 + 32 * bb + 8 * g4) =
+                make_uint2((uint32_t(cl[0]) & 0xffffu) | (uint32_t(cl[1]) << 16),
+                           (uint32_t(cl[2]) & 0xffffu) | (uint32_t(cl[3]) << 16));
+            // the same element in the 32-bit rows sits at twice the byte offset
+            if (wide)
+                *reinterpret_cast<int4 *>(reinterpret_cast<uint8_t *>(ywide) + (2u * yoff[i] + uint32_t(128 * j + 64 * bb))) =
+                    make_int4(v4[0], v4[1], v4[2], v4[3]);   // 2 yoff < 2^32: the rows end below 4 GiB
         }
-        const uint2 hv2 = make_uint2((uint32_t(cl[0]) & 0xffffu) | (uint32_t(cl[1]) << 16),
-                                     (uint32_t(cl[2]) & 0xffffu) | (uint32_t(cl[3]) << 16));
-        *reinterpret_cast<uint2 *>(reinterpret_cast<uint8_t *>(y16) + yoff[i] + 64 * j + 32 * bb) = hv2;
-        // the same element in the 32-bit rows sits at twice the byte offset
-        if (wide)
-            *reinterpret_cast<int4 *>(reinterpret_cast<uint8_t *>(ywide) + 2 * size_t(yoff[i]) + 128 * j + 64 * bb) =
-                make_int4(v4[0], v4[1], v4[2], v4[3]);
+        // this wave's own LDS writes, read back in order: rows 8 g4 .. of token l16
+        const uint4 q16 = *reinterpret_cast<const uint4 *>(wst + l16 * 80 + 16 * g4);
+        *reinterpret_cast<uint4 *>(reinterpret_cast<uint8_t *>(y16) + (yoff[i] - 8 * g4) + 64 * j + 16 * g4) = q16;
     };
     // step j sums into acc[j % 2]; the sums of step j - 1 are stored piece by piece while the
-    // products of step j run (one (block, sub-tile) piece after every 2 SD fragments)
+    // products of step j run (one sub-tile's two blocks after every 4 SD fragments)
     v4i acc[2][2][HS];
     auto down_step = [&](int j, auto slot_c) __attribute__((always_inline)) {
         constexpr int SLOT = decltype(slot_c)::value;
@@ -917,9 +928,9 @@ __device__ __forceinline__ void ex_work(const Dims &dm, const BatchedWs &L, cons
 #pragma unroll
             for (int bb = 0; bb < 2; bb++)   // the first product of a sum starts from zero
                 ac[bb][i] = mfma8(w[bb], hv[n % (kExPD + 1)], c == 0 ? v4i{0, 0, 0, 0} : ac[bb][i]);
-            if (j > 0 && n % (2 * SD) == 2 * SD - 1) {
-                const int pc = n / (2 * SD);   // 0 .. 2 HS - 1
-                emit(ap[pc & 1][pc >> 1], pc & 1, pc >> 1, j - 1);
+            if (j > 0 && n % (4 * SD) == 4 * SD - 1) {
+                const int pi = n / (4 * SD);   // 0 .. HS - 1
+                emit(ap[0][pi], ap[1][pi], pi, j - 1);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -935,9 +946,7 @@ __device__ __forceinline__ void ex_work(const Dims &dm, const BatchedWs &L, cons
     }
     // the last step's sums (NDS is even: they are in acc[1])
 #pragma unroll
-    for (int i = 0; i < HS; i++)
-#pragma unroll
-        for (int bb = 0; bb < 2; bb++) emit(acc[1][bb][i], bb, i, NDS - 1);
+    for (int i = 0; i < HS; i++) emit(acc[1][0][i], acc[1][1][i], i, NDS - 1);
 }
 
 template <int D, int F>
