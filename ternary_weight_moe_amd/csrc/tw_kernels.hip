@@ -1250,6 +1250,16 @@ __device__ __forceinline__ void combine_chunk(const void *__restrict__ x, void *
         bool ok[8];
 #pragma unroll
         for (int u = 0; u < 8; u++) pj[u] = tok * k + (j0 + u < k ? j0 + u : k - 1);
+        // the 16-bit rows first: their addresses need no id, so their loads are in flight while the
+        // ids arrive
+        [[maybe_unused]] int4 yq[8];
+        if constexpr (Y16) {
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                const i4v q = __builtin_nontemporal_load(reinterpret_cast<const i4v *>(yr.y16 + pj[u] * d) + c);
+                yq[u] = make_int4(q.x, q.y, q.z, q.w);
+            }
+        }
 #pragma unroll
         for (int u = 0; u < 8; u++) {
             id[u] = ids[pj[u]];
@@ -1260,13 +1270,7 @@ __device__ __forceinline__ void combine_chunk(const void *__restrict__ x, void *
         for (int u = 0; u < 8; u++) ok[u] = j0 + u < k && id[u] >= 0 && id[u] < E;
         float yy[8][8];
         if constexpr (Y16) {
-            int4 yq[8];
             f4 sd[8][2];
-#pragma unroll
-            for (int u = 0; u < 8; u++) {
-                const i4v q = __builtin_nontemporal_load(reinterpret_cast<const i4v *>(yr.y16 + pj[u] * d) + c);
-                yq[u] = make_int4(q.x, q.y, q.z, q.w);
-            }
 #pragma unroll
             for (int u = 0; u < 8; u++) {
                 const f4 *sp = reinterpret_cast<const f4 *>(yr.s_down + int64_t(ok[u] ? id[u] : 0) * d) + 2 * c;
