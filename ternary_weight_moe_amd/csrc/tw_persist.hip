@@ -75,8 +75,6 @@ constexpr uint32_t kSpinLimit = 1u << 21;
 // rows go through.  Measured on MI355X (24-layer stack, tokens/s): no waits 252.6 us per token;
 // 20 before the h words 232.6 (15: 234.8, 25: 234.0, 40: 243.9); and 10 before the residual words
 // 220.3 (5: 223.0, 15: 222.5, 20: 224.7); a wait before the logits or between polls adds nothing.
-// Swept again on the kernel at 182 us per token: residual 5 / 15 gave 186.4 / 184.6, h 12 / 28 gave
-// 183.9 / 186.4, against 182.0 for 10 and 20.
 constexpr int kSleepX = 10;            // before polling the residual words
 constexpr int kSleepH = 20;            // before polling the h words
 constexpr int kEM = 1;                 // router rows per workgroup: expert b (E <= 256)
