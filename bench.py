@@ -39,17 +39,21 @@ from ternary_weight_moe_amd import accounting  # noqa: E402
 
 METRIC = "decode tok/s, 24-layer ternary MoE FFN stack, B=1; achieved HBM GB/s vs peak"
 # sources of the kernel whose traffic counters are committed (the one-launch stacked decode)
-KERNEL_SRCS = [os.path.join(ROOT, "ternary_weight_moe_amd", "csrc", f)
-               for f in ("tw_persist.hip", "tw_device.h", "tw_internal.h")]
+# the sources of the dominant kernel of each workload that has committed counter runs
+# (profiles/traffic_<workload>.json): the counters stand only while these are unchanged
+KERNEL_SRCS = {w: [os.path.join(ROOT, "ternary_weight_moe_amd", "csrc", f) for f in fs] for w, fs in {
+    "stack24_b1": ("tw_persist.hip", "tw_device.h", "tw_internal.h"),
+    "prefill_4096": ("tw_prefill.hip", "tw_device.h", "tw_internal.h"),
+}.items()}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_hash() -> str:
+def kernel_hash(workload: str = "stack24_b1") -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SRCS:
+    for f in KERNEL_SRCS[workload]:
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
@@ -61,7 +65,7 @@ def traffic_from_profiles(workload: str):
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
-    if d.get("kernel_sha256_16") != kernel_hash():
+    if workload not in KERNEL_SRCS or d.get("kernel_sha256_16") != kernel_hash(workload):
         return None
     return d.get("hbm_bytes_per_step")
 
@@ -327,7 +331,8 @@ def run_single_layer(args, name):
         ops = accounting.int8_ops(wl, T * wl.top_k)
         tops = ops / (total / args.steps) / 1e12
         roof = dict(bound="mfma", achieved=tops, peak=accounting.INT8_MFMA_PEAK_OPS / 1e12,
-                    unit="TOP/s", frac=tops * 1e12 / accounting.INT8_MFMA_PEAK_OPS, traffic=None,
+                    unit="TOP/s", frac=tops * 1e12 / accounting.INT8_MFMA_PEAK_OPS,
+                    traffic=traffic_from_profiles(name),   # HBM bytes per k_pf_expert dispatch
                     kernel="one call: quantise x, group, k_pf_expert<2048,512>, combine",
                     ops_per_call=ops, hbm_gb_s=achieved)
     else:
