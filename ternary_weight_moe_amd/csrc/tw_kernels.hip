@@ -752,19 +752,24 @@ __global__ __launch_bounds__(256) void k_bat_quant_x(BatchedArgs a, const void *
 // depends on it: every pair is computed on its own), plus the list of (expert, tile of tt tokens)
 // work items: tiles[0] = their number, tiles[1 + i] = e | (tile << 10), tilemeta[i] = (position of the
 // tile's first pair in pairs[], its number of pairs).
-// One workgroup of 1024 threads; counts and placement use LDS atomics.  The ids are read in passes
-// of 32 per thread, all loads of a pass issued before any is used (one memory round trip per pass
-// instead of one per id); with a single pass they stay in registers for the placement.  Up to
-// kGrpStage pairs the placement is staged in LDS and written out with 16-byte stores (scattered
-// 4-byte stores from one workgroup are limited by its address rate).
+// Workgroups of 1024 threads; counts and placement use LDS atomics.  Workgroup g of G places the
+// pairs of the experts [E g / G, E (g + 1) / G) and writes their counts, offsets and tiles; each
+// counts every pair, since the offsets and tile numbers of its experts follow from all the experts
+// before them.  The ids are read in passes of 32 per thread, all loads of a pass issued before any
+// is used (one memory round trip per pass instead of one per id); with a single pass they stay in
+// registers for the placement.  Up to kGrpStage pairs the placement is staged in LDS (stage[j] is
+// pairs[a0 + j], a0 the range's first position rounded down to a multiple of 4) and written out
+// with 16-byte stores (scattered 4-byte stores from one workgroup are limited by its address rate).
 constexpr int kGrpPer = 32;                    // ids per thread per pass
 constexpr int kGrpPass = 1024 * kGrpPer;       // pairs per pass
-constexpr int kGrpStage = kGrpPass;            // pairs staged in LDS (128 KiB)
+constexpr int kGrpStage = kGrpPass;            // pairs staged in LDS (128 KiB, plus 3 for alignment)
+constexpr int kGrpWgs = 8;                     // grouping workgroups of k_quant_group
 
 __device__ __forceinline__ void group_pairs(const BatchedArgs &a, const int32_t *__restrict__ ids,
-                                            uint8_t *__restrict__ ws, int tt, int32_t *stage)
+                                            uint8_t *__restrict__ ws, int tt, int32_t *stage, int g, int G)
 {
     const int E = a.dm.E, t = threadIdx.x;
+    const int e_lo = int(int64_t(E) * g / G), e_hi = int(int64_t(E) * (g + 1) / G);
     const int64_t npairs = a.T * a.dm.k;
     const bool staged = npairs <= kGrpStage;
     int32_t *counts = reinterpret_cast<int32_t *>(ws + a.L.counts);
@@ -772,7 +777,7 @@ __device__ __forceinline__ void group_pairs(const BatchedArgs &a, const int32_t 
     int32_t *pairs = reinterpret_cast<int32_t *>(ws + a.L.pairs);
     int32_t *tiles = reinterpret_cast<int32_t *>(ws + a.L.tiles);
     int2 *tmeta = reinterpret_cast<int2 *>(ws + a.L.tilemeta);
-    __shared__ int32_t cnt[kMaxExperts], cur[kMaxExperts], s_wc[16], s_wt[16];
+    __shared__ int32_t cnt[kMaxExperts], cur[kMaxExperts], s_wc[16], s_wt[16], s_lo, s_hi;
     const int64_t npass = (npairs + kGrpPass - 1) / kGrpPass;
     int v[kGrpPer];
     // v[i] = id of pair base + t + 1024 i, or -1 past the end
@@ -820,68 +825,79 @@ __device__ __forceinline__ void group_pairs(const BatchedArgs &a, const int32_t 
         ntiles += s_wt[w];
     }
     const int off_e = bc + ic - c, tile0 = bt + it - nt;
-    if (t < E) {
+    if (t < E) cur[t] = off_e;
+    if (t >= e_lo && t < e_hi) {
         counts[t] = c;
         offsets[t] = off_e;
-        cur[t] = off_e;
         for (int i = 0; i < nt; i++) {
             tiles[1 + tile0 + i] = t | (i << 10);
             tmeta[tile0 + i] = make_int2(off_e + i * tt, min(tt, c - i * tt));
         }
     }
+    // the range's first and end positions
+    if (t < E && t == e_lo) s_lo = off_e;
+    if (t < E && t == e_hi) s_hi = off_e;
     if (t == 1023) {
-        offsets[E] = placed;
-        tiles[0] = ntiles;
+        if (e_lo >= E) s_lo = placed;
+        if (e_hi >= E) s_hi = placed;
+        if (g == 0) {
+            offsets[E] = placed;
+            tiles[0] = ntiles;
+        }
     }
     __syncthreads();
+    const int a0 = s_lo & ~3, p_hi = s_hi;
     for (int64_t ps = 0; ps < npass; ps++) {
         const int64_t base = ps * kGrpPass;
         if (npass > 1) load(base);
 #pragma unroll
         for (int i = 0; i < kGrpPer; i++)
-            if (v[i] >= 0 && v[i] < E) {
+            if (v[i] >= e_lo && v[i] < e_hi) {
                 const int pos = atomicAdd(&cur[v[i]], 1);
                 const int32_t pr = int32_t(base + t + 1024 * i);
                 if (staged)
-                    stage[pos] = pr;
+                    stage[pos - a0] = pr;
                 else
                     pairs[pos] = pr;
             }
     }
     if (!staged) return;
     __syncthreads();
-    // pairs is 256-byte aligned inside the workspace
-    for (int i = t; 4 * i < placed; i += 1024) {
-        if (4 * i + 3 < placed)
-            reinterpret_cast<int4 *>(pairs)[i] = reinterpret_cast<const int4 *>(stage)[i];
+    // pairs is 256-byte aligned inside the workspace, so pairs + a0 is 16-byte aligned; the stage
+    // holds positions s_lo .. p_hi - 1 at indices s_lo - a0 ..
+    const int j_lo = s_lo - a0, j_hi = p_hi - a0;
+    for (int i = t; 4 * i < j_hi; i += 1024) {
+        if (4 * i >= j_lo && 4 * i + 3 < j_hi)
+            reinterpret_cast<int4 *>(pairs + a0)[i] = reinterpret_cast<const int4 *>(stage)[i];
         else
-            for (int j = 4 * i; j < placed; j++) pairs[j] = stage[j];
+            for (int j = max(4 * i, j_lo); j < min(4 * i + 4, j_hi); j++) pairs[a0 + j] = stage[j];
     }
 }
 
 __global__ __launch_bounds__(1024) void k_group(BatchedArgs a, const int32_t *__restrict__ ids,
                                                 uint8_t *__restrict__ ws, int tt)
 {
-    extern __shared__ __attribute__((aligned(16))) int32_t stage[];   // [npairs] when staged
-    group_pairs(a, ids, ws, tt, stage);
+    extern __shared__ __attribute__((aligned(16))) int32_t stage[];   // [npairs + 3] when staged
+    group_pairs(a, ids, ws, tt, stage, 0, 1);
 }
 
 // The quantisation of the tokens and the grouping of the pairs in one launch (they are
-// independent): workgroup 0 groups, workgroup 1 + j quantises tokens 4 j .. 4 j + 3, one per
-// 256-thread quarter, so the grouping runs beside the quantisation instead of after it.
+// independent): workgroups 0 .. kGrpWgs - 1 group (one range of experts each), workgroup kGrpWgs + j
+// quantises tokens 4 j .. 4 j + 3, one per 256-thread quarter, so the grouping runs beside the
+// quantisation instead of after it.
 template <int P, bool INT8>
 __global__ __launch_bounds__(1024) void k_quant_group(BatchedArgs a, const void *__restrict__ x, int x_bf16,
                                                       const int32_t *__restrict__ ids,
                                                       uint8_t *__restrict__ ws, int tt)
 {
-    extern __shared__ __attribute__((aligned(16))) int32_t stage[];   // [npairs] when staged
+    extern __shared__ __attribute__((aligned(16))) int32_t stage[];   // [npairs + 3] when staged
     __shared__ float red[4][4][2];
-    if (blockIdx.x == 0) {
-        group_pairs(a, ids, ws, tt, stage);
+    if (blockIdx.x < kGrpWgs) {
+        group_pairs(a, ids, ws, tt, stage, int(blockIdx.x), kGrpWgs);
         return;
     }
     const int q = int(threadIdx.x) >> 8;
-    quant_token256<P, INT8>(a, x, x_bf16, ws, int64_t(blockIdx.x - 1) * 4 + q, int(threadIdx.x) & 255, red[q]);
+    quant_token256<P, INT8>(a, x, x_bf16, ws, int64_t(blockIdx.x - kGrpWgs) * 4 + q, int(threadIdx.x) & 255, red[q]);
 }
 
 template <int P, bool INT8>
@@ -889,16 +905,16 @@ int launch_quant_group(const BatchedArgs &a, const void *x, int x_bf16, const in
                        int tt, void *stream)
 {
     const int64_t npairs = a.T * a.dm.k;
-    const size_t lds = npairs <= kGrpStage ? size_t(npairs) * sizeof(int32_t) : 0;
+    const size_t lds = npairs <= kGrpStage ? size_t(npairs + 4) * sizeof(int32_t) : 0;
     static std::atomic<int> attr_set{0};
     if (lds > 0 && !attr_set.load(std::memory_order_relaxed)) {
         if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_quant_group<P, INT8>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                int(kGrpStage * sizeof(int32_t))) != hipSuccess)
+                                int((kGrpStage + 4) * sizeof(int32_t))) != hipSuccess)
             return int(hipErrorInvalidValue);
         attr_set.store(1, std::memory_order_relaxed);
     }
-    k_quant_group<P, INT8><<<unsigned(1 + (a.T + 3) / 4), 1024, lds, static_cast<hipStream_t>(stream)>>>(
+    k_quant_group<P, INT8><<<unsigned(kGrpWgs + (a.T + 3) / 4), 1024, lds, static_cast<hipStream_t>(stream)>>>(
         a, x, x_bf16, ids, ws, tt);
     return 0;
 }
@@ -907,12 +923,12 @@ int launch_quant_group(const BatchedArgs &a, const void *x, int x_bf16, const in
 int launch_group(const BatchedArgs &a, const int32_t *ids, uint8_t *ws, int tt, void *stream)
 {
     const int64_t npairs = a.T * a.dm.k;
-    const size_t lds = npairs <= kGrpStage ? size_t(npairs) * sizeof(int32_t) : 0;
+    const size_t lds = npairs <= kGrpStage ? size_t(npairs + 4) * sizeof(int32_t) : 0;
     static std::atomic<int> attr_set{0};
     if (lds > 0 && !attr_set.load(std::memory_order_relaxed)) {
         if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_group),
                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                int(kGrpStage * sizeof(int32_t))) != hipSuccess)
+                                int((kGrpStage + 4) * sizeof(int32_t))) != hipSuccess)
             return int(hipErrorInvalidValue);
         attr_set.store(1, std::memory_order_relaxed);
     }
